@@ -1,0 +1,28 @@
+"""CPU oracle for paged-KV decode attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, plain float64
+definition that the HIP path is checked against.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import it; the product path (the ``paged_attention_decode_attn_amd`` package
+and its C-ABI library) never imports, links or calls anything here, and the
+two share no code.
+
+Modules
+-------
+formats          bf16 and OCP float8 e4m3fn bit-level decoders
+paged_attention  dense softmax attention gathered through the block table
+split_merge      split-context partial states and their log-sum-exp merge
+
+Every function is pinned by ``-m "not gpu"`` tests against closed forms,
+invariants, brute force and independent library routines; no function here
+is "parity unpinned".
+"""
+from .formats import bf16_bits_to_f64, e4m3fn_bytes_to_f64, e4m3fn_table, e4m3fn_value
+from .paged_attention import BLOCK_SIZE, gather_sequence_kv, paged_decode_attention
+from .split_merge import merge_states, partial_state
+
+__all__ = [
+    "BLOCK_SIZE", "bf16_bits_to_f64", "e4m3fn_bytes_to_f64", "e4m3fn_table",
+    "e4m3fn_value", "gather_sequence_kv", "paged_decode_attention",
+    "merge_states", "partial_state",
+]

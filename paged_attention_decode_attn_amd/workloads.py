@@ -1,0 +1,269 @@
+"""Seeded synthetic decode workloads (inputs only; no attention arithmetic).
+
+This module is the one piece shared by the HIP path's callers (tests,
+benchmark) and by the CPU oracle's callers: it draws every input from a
+seeded ``torch.Generator`` on the host, so the GPU and the oracle read
+identical bytes.  It holds none of the attention computation.
+
+The shapes follow the decode regime the pages describe: one or a few new
+query tokens per sequence, GQA head grouping, ragged context lengths, a
+block-size-16 paged cache in bf16 or fp8 (ATOM configuration guide,
+"Master configuration (Config)": ``kv_cache_block_size``,
+``kv_cache_dtype``), and short causal query runs for MTP verification (ROCm
+blog "Optimizing ATOM and vLLM-ATOM for High-Interactivity Inference",
+"Multi-Token Prediction").  The pages measure on no public dataset for this
+path; every value is N(0, 1) noise.
+
+Generation order for a spec with seed ``s`` (``torch.Generator('cpu')``):
+
+1. context lengths (constant, or uniform integers in ``[lo, hi]``);
+2. one random permutation of the physical pool;
+3. Q, float32 N(0, 1) rounded to bf16;
+4. K for every used block, in table order (float32 N(0, 1)), then V the
+   same way; bf16 caches round to bf16, fp8 caches quantise each
+   (token, kv head) row of D values with scale ``absmax / 448`` (1 if the
+   row is all zero) and ``torch``'s round-to-nearest-even cast to
+   ``float8_e4m3fn``;
+5. block tables: sequence ``b`` takes the next ``ceil(L_b / 16)`` entries of
+   the permutation; unused table columns hold block 0 (or, with
+   ``poison=True``, an unused block filled with NaN).
+
+Unused pool blocks hold zeros (NaN with ``poison=True``; the tail slots past
+``L_b`` of each sequence's last block are NaN then as well).  Scales are
+stored physically ``[NB, Hkv, 16]`` so that one (block, kv head) reads 64
+contiguous bytes, and handed out as the logical ``[NB, 16, Hkv]`` view.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+BLOCK = 16
+FP8_MAX = 448.0
+
+__all__ = ["WorkloadSpec", "Workload", "CONFIGS", "CONFIG_ORDER", "generate", "kv_bytes"]
+
+
+@dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    batch: int
+    qlen: int
+    hq: int
+    hkv: int
+    head_dim: int
+    kv_dtype: str            # "bf16" or "fp8_e4m3fn"
+    ctx_lo: int
+    ctx_hi: int
+    pool_blocks: int
+    seed: int
+    scale: Optional[float] = None   # None: 1 / sqrt(head_dim)
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def table_width(self) -> int:
+        return (self.ctx_hi + BLOCK - 1) // BLOCK
+
+    def replace(self, **kw) -> "WorkloadSpec":
+        return dataclasses.replace(self, **kw)
+
+
+# The five decode workloads (sizes and seeds fixed; seed k for the k-th).
+CONFIGS = {
+    "tiny": WorkloadSpec("tiny_b1_q32kv8_d128_ctx512_bf16", batch=1, qlen=1, hq=32, hkv=8,
+                         head_dim=128, kv_dtype="bf16", ctx_lo=512, ctx_hi=512,
+                         pool_blocks=64, seed=1, scale=1.0 / math.sqrt(128)),
+    "llama3_8b": WorkloadSpec("llama3_8b_b4_q32kv8_d128_ctx1k-8k_bf16", batch=4, qlen=1,
+                              hq=32, hkv=8, head_dim=128, kv_dtype="bf16", ctx_lo=1024,
+                              ctx_hi=8192, pool_blocks=4096, seed=2),
+    "long_ctx": WorkloadSpec("long_ctx_b1_q64kv8_d128_ctx131072_bf16", batch=1, qlen=1,
+                             hq=64, hkv=8, head_dim=128, kv_dtype="bf16", ctx_lo=131072,
+                             ctx_hi=131072, pool_blocks=16384, seed=3),
+    "fp8": WorkloadSpec("fp8_b16_q64kv8_d64_ctx512-32k_e4m3fn", batch=16, qlen=1, hq=64,
+                        hkv=8, head_dim=64, kv_dtype="fp8_e4m3fn", ctx_lo=512, ctx_hi=32768,
+                        pool_blocks=32768, seed=4),
+    "mtp_verify": WorkloadSpec("mtp_verify_b64_qlen2_q64kv8_d128_ctx256-16k_bf16", batch=64,
+                               qlen=2, hq=64, hkv=8, head_dim=128, kv_dtype="bf16",
+                               ctx_lo=256, ctx_hi=16384, pool_blocks=65536, seed=5),
+}
+CONFIG_ORDER = ["tiny", "llama3_8b", "long_ctx", "fp8", "mtp_verify"]
+
+
+@dataclass
+class Workload:
+    spec: WorkloadSpec
+    q: torch.Tensor              # bf16 [B, Qmax, Hq, D]
+    k_cache: torch.Tensor        # bf16 or uint8 (e4m3fn bytes) [NB, 16, Hkv, D]
+    v_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]   # fp32 logical [NB, 16, Hkv] (physical [NB, Hkv, 16]) or None
+    v_scale: Optional[torch.Tensor]
+    block_tables: torch.Tensor   # int32 [B, W]
+    context_lens: torch.Tensor   # int32 [B]
+    query_lens: torch.Tensor     # int32 [B]
+    scale: float
+
+    def to(self, device) -> "Workload":
+        def mv(t):
+            return None if t is None else _move(t, device)
+        return Workload(self.spec, mv(self.q), mv(self.k_cache), mv(self.v_cache),
+                        mv(self.k_scale), mv(self.v_scale), mv(self.block_tables),
+                        mv(self.context_lens), mv(self.query_lens), self.scale)
+
+    def numpy_inputs(self) -> dict:
+        """The same bytes as NumPy arrays (bf16 as uint16 bit patterns,
+        e4m3fn as uint8), keyed like the attention call's arguments."""
+        def bits(t):
+            t = t.detach().cpu()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view("uint16")
+            return t.numpy()
+        d = dict(q_bits=bits(self.q), k_cache=bits(self.k_cache), v_cache=bits(self.v_cache),
+                 block_tables=self.block_tables.cpu().numpy(),
+                 context_lens=self.context_lens.cpu().numpy(),
+                 query_lens=self.query_lens.cpu().numpy(), scale=self.scale,
+                 kv_dtype=self.spec.kv_dtype, k_scale=None, v_scale=None)
+        if self.k_scale is not None:
+            d["k_scale"] = self.k_scale.cpu().numpy()
+            d["v_scale"] = self.v_scale.cpu().numpy()
+        return d
+
+
+def _move(t: torch.Tensor, device) -> torch.Tensor:
+    """Copy to ``device`` keeping the storage layout (scale views stay views
+    of a contiguous physical tensor)."""
+    if t.is_contiguous():
+        return t.to(device)
+    # the scale tensors: logical [NB, 16, Hkv] view of physical [NB, Hkv, 16]
+    phys = t.permute(0, 2, 1)
+    assert phys.is_contiguous()
+    return phys.to(device).permute(0, 2, 1)
+
+
+def kv_bytes(context_lens, hkv: int, head_dim: int, kv_dtype: str) -> int:
+    """Algorithmic KV bytes of one call: K and V rows of every attended
+    token, plus the fp32 per-token scales of an fp8 cache."""
+    tokens = int(torch.as_tensor(context_lens).to(torch.int64).sum())
+    elem = 1 if kv_dtype == "fp8_e4m3fn" else 2
+    per_token = 2 * hkv * head_dim * elem
+    if kv_dtype == "fp8_e4m3fn":
+        per_token += 2 * hkv * 4
+    return tokens * per_token
+
+
+def _nan_pattern(kv_dtype: str):
+    return (0x7F, torch.uint8) if kv_dtype == "fp8_e4m3fn" else (0x7FC0, torch.int16)
+
+
+def _fill_cache(cache, scales, block_ids, gen, spec, chunk_blocks):
+    """Draw N(0, 1) rows for ``block_ids`` (in order) and store them."""
+    H, D = spec.hkv, spec.head_dim
+    for start in range(0, block_ids.numel(), chunk_blocks):
+        ids = block_ids[start:start + chunk_blocks]
+        x = torch.randn(ids.numel(), BLOCK, H, D, generator=gen, dtype=torch.float32)
+        if spec.kv_dtype == "bf16":
+            cache[ids] = x.to(torch.bfloat16)
+        else:
+            amax = x.abs().amax(dim=-1)                              # [n, 16, H]
+            s = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+            y = (x / s[..., None]).clamp(-FP8_MAX, FP8_MAX)
+            cache[ids] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+            scales[ids] = s.permute(0, 2, 1).contiguous()            # physical [n, H, 16]
+
+
+def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = False,
+             context_lens=None, query_lens=None) -> Workload:
+    """Draw one workload on the host.  ``context_lens`` overrides step 1 and
+    ``query_lens`` the per-sequence query-row counts (edge-case tests; no
+    random draw is spent on either); ``poison`` fills everything the call
+    must not read with NaN."""
+    gen = torch.Generator("cpu").manual_seed(spec.seed if seed is None else seed)
+    B, Qn, Hq, H, D = spec.batch, spec.qlen, spec.hq, spec.hkv, spec.head_dim
+    if Hq % H:
+        raise ValueError("q heads must be a multiple of kv heads")
+    NB, W = spec.pool_blocks, spec.table_width
+
+    # 1. context lengths
+    if context_lens is not None:
+        ctx = torch.as_tensor(context_lens, dtype=torch.int64).clone()
+        if ctx.numel() != B:
+            raise ValueError("context_lens must have one entry per sequence")
+    elif spec.ctx_lo == spec.ctx_hi:
+        ctx = torch.full((B,), spec.ctx_lo, dtype=torch.int64)
+    else:
+        ctx = torch.randint(spec.ctx_lo, spec.ctx_hi + 1, (B,), generator=gen, dtype=torch.int64)
+    if ctx.numel() and int(ctx.max()) > BLOCK * W:
+        raise ValueError("a context is longer than the block table")
+    if ctx.numel() and int(ctx.min()) < 0:
+        raise ValueError("negative context length")
+    if query_lens is None:
+        qls = torch.full((B,), Qn, dtype=torch.int32)
+    else:
+        qls = torch.as_tensor(query_lens, dtype=torch.int32).clone()
+        if qls.numel() != B or (qls.numel() and (int(qls.min()) < 0 or int(qls.max()) > Qn)):
+            raise ValueError("query_lens must be in [0, qlen], one per sequence")
+    if bool((qls.to(torch.int64) > ctx).any()):
+        raise ValueError("a sequence has more query rows than context tokens")
+    nblk = (ctx + BLOCK - 1) // BLOCK
+    used = int(nblk.sum())
+    if used + (1 if poison else 0) > NB:
+        raise ValueError(f"pool of {NB} blocks cannot hold {used} used blocks")
+
+    # 2. pool placement
+    perm = torch.randperm(NB, generator=gen)
+
+    # 3. queries
+    q = torch.randn(B, Qn, Hq, D, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+    # 4. caches
+    fp8 = spec.kv_dtype == "fp8_e4m3fn"
+    if spec.kv_dtype not in ("bf16", "fp8_e4m3fn"):
+        raise ValueError(spec.kv_dtype)
+    cdtype = torch.uint8 if fp8 else torch.bfloat16
+    k_cache = torch.zeros(NB, BLOCK, H, D, dtype=cdtype)
+    v_cache = torch.zeros(NB, BLOCK, H, D, dtype=cdtype)
+    k_sc = torch.ones(NB, H, BLOCK, dtype=torch.float32) if fp8 else None
+    v_sc = torch.ones(NB, H, BLOCK, dtype=torch.float32) if fp8 else None
+    used_ids = perm[:used]
+    if poison:
+        pat, vdt = _nan_pattern(spec.kv_dtype)
+        for c in (k_cache, v_cache):
+            c.view(vdt).fill_(pat)
+        for s in (k_sc, v_sc):
+            if s is not None:
+                s.fill_(float("nan"))
+    chunk = max(1, (64 << 20) // (BLOCK * H * D * 4))
+    _fill_cache(k_cache, k_sc, used_ids, gen, spec, chunk)
+    _fill_cache(v_cache, v_sc, used_ids, gen, spec, chunk)
+
+    # 5. block tables
+    pad_id = int(perm[used]) if poison else 0
+    tables = torch.full((B, W), pad_id, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        n = int(nblk[b])
+        tables[b, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+        if poison and n:
+            tail = int(ctx[b]) - (n - 1) * BLOCK          # valid slots in the last block
+            if tail < BLOCK:
+                last = int(tables[b, n - 1])
+                pat, vdt = _nan_pattern(spec.kv_dtype)
+                k_cache[last, tail:].view(vdt).fill_(pat)
+                v_cache[last, tail:].view(vdt).fill_(pat)
+                if fp8:
+                    k_sc[last, :, tail:] = float("nan")
+                    v_sc[last, :, tail:] = float("nan")
+
+    return Workload(
+        spec=spec, q=q, k_cache=k_cache, v_cache=v_cache,
+        k_scale=None if k_sc is None else k_sc.permute(0, 2, 1),
+        v_scale=None if v_sc is None else v_sc.permute(0, 2, 1),
+        block_tables=tables, context_lens=ctx.to(torch.int32),
+        query_lens=qls, scale=spec.softmax_scale)
