@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+One step = one call of the C-ABI entry point (partition kernel + log-sum-exp
+merge kernel) over one batch of the chosen synthetic workload, with every
+input already resident in HBM.  The KV pools are rotated over several
+device copies so that each call reads its K/V from HBM rather than from the
+256 MB Infinity Cache.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config long_ctx]
+
+Default workload: the batch-1 long-context decode (1 sequence, 131072
+tokens, 64 query / 8 kv heads, head_dim 128, bf16 KV).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV GB/s (% of HBM peak) and µs/call at batch 1"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", "pa_device.hip")
+
+
+def parse_args():
+    from paged_attention_decode_attn_amd.workloads import CONFIG_ORDER
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER)
+    ap.add_argument("--partition-tokens", type=int, default=0, help="0 = the planner's choice")
+    ap.add_argument("--copies", type=int, default=0, help="rotated KV copies (0 = enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain 1 GiB device copies (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha256_16") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": 5}), flush=True)
+
+
+def cpu_baseline(w, seconds: float):
+    """The float64 oracle as it stands, on whole sequences of the same
+    workload, until about `seconds` of CPU time (at least one sequence)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_decode_attention
+    from paged_attention_decode_attn_amd.workloads import kv_bytes
+    inputs = w.numpy_inputs()
+    spec = w.spec
+    done_bytes, done_seqs, t = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        b = 0
+        while True:
+            t0 = time.perf_counter()
+            paged_decode_attention(**inputs, batch_subset=[b])
+            t += time.perf_counter() - t0
+            done_bytes += kv_bytes(w.context_lens[b:b + 1], spec.hkv, spec.head_dim, spec.kv_dtype)
+            done_seqs += 1
+            b = (b + 1) % spec.batch
+            if t >= seconds:
+                break
+    return {"value": done_bytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_seqs} whole-sequence oracle calls of this workload "
+                      f"({done_bytes} KV bytes, {t:.1f} s, 1 thread; "
+                      f"{len(os.sched_getaffinity(0))} host cores visible)",
+            "seconds": t}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the decode-attention path has no multi-GPU mode here.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from paged_attention_decode_attn_amd import binding as B
+    from paged_attention_decode_attn_amd.workloads import CONFIGS, generate, kv_bytes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    spec = CONFIGS[args.config]
+    print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
+    w = generate(spec)
+    kvb = kv_bytes(w.context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
+    dev = w.to("cuda")
+    pool_bytes = 2 * dev.k_cache.numel() * dev.k_cache.element_size()
+    copies = args.copies or max(2, math.ceil((1 << 30) / kvb) + 1)
+    copies = max(1, min(copies, int((64 << 30) // max(pool_bytes, 1))))
+    pools = [(dev.k_cache, dev.v_cache, dev.k_scale, dev.v_scale)]
+    for _ in range(copies - 1):
+        ks = None if dev.k_scale is None else dev.k_scale.permute(0, 2, 1).clone().permute(0, 2, 1)
+        vs = None if dev.v_scale is None else dev.v_scale.permute(0, 2, 1).clone().permute(0, 2, 1)
+        pools.append((dev.k_cache.clone(), dev.v_cache.clone(), ks, vs))
+    out = torch.empty_like(dev.q)
+    B.paged_attn_set_partition_tokens(args.partition_tokens)
+    plan = B.paged_attn_plan(spec.batch, spec.hq, spec.hkv, spec.head_dim, spec.qlen,
+                             spec.table_width, spec.kv_dtype,
+                             torch.cuda.get_device_properties(0).multi_processor_count)
+
+    def call(i):
+        kc, vc, ks, vs = pools[i % copies]
+        B.paged_attn_decode(dev.q, kc, vc, dev.block_tables, dev.context_lens, dev.query_lens,
+                            dev.scale, ks, vs, out)
+
+    print(f"[bench] warmup {args.warmup}, copies {copies}, plan {plan}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events recorded by the library on
+    # the same stream as the launches
+    B.paged_attn_profile_begin(args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    prof = B.paged_attn_profile_end()
+    ms_per_step = ms_total / args.steps
+
+    # the same loop without per-kernel events, for the events' own overhead
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_plain = start.elapsed_time(stop) / args.steps
+    B.paged_attn_set_partition_tokens(0)
+
+    part_ms = prof["partition_ms"] / max(prof["calls"], 1)
+    red_ms = prof["reduce_ms"] / max(prof["calls"], 1)
+    value = kvb / (ms_per_step * 1e-3) / 1e9
+    achieved = kvb / (part_ms * 1e-3) / 1e9
+    traffic = measured_traffic(spec.name)
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3fn-kv/bf16-mfma" if spec.kv_dtype == "fp8_e4m3fn" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "query_len": spec.qlen,
+                   "q_heads": spec.hq, "kv_heads": spec.hkv, "head_dim": spec.head_dim,
+                   "kv_dtype": spec.kv_dtype, "block_size": 16,
+                   "context_lens": ([int(x) for x in w.context_lens] if spec.batch <= 4
+                                    else f"U[{spec.ctx_lo}, {spec.ctx_hi}] (seed {spec.seed})"),
+                   "partition_tokens": plan["partition_tokens"],
+                   "num_partitions": plan["num_partitions"], "kv_copies_rotated": copies},
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "us_per_call_without_kernel_events": round(ms_plain * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_call": kvb,
+        "kernel_us": {"partition": round(part_ms * 1e3, 3), "reduce": round(red_ms * 1e3, 3)},
+        "wall_s_timed_region": round(t_wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": kvb,
+                     "kernel": "partition_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged-KV decode-attention library.
+ *
+ * The operation: one or a few new query tokens per sequence attend, with
+ * softmax attention, over that sequence's tokens in a paged KV cache that a
+ * per-sequence block table addresses.  Sources (web pages):
+ *   - ATOM model operations guide, "Attention operations" (decode dispatch to
+ *     paged-attention kernels; the q_heads / kv_heads ratio and the query
+ *     length that bound each kernel's envelope; per-token quantised layers
+ *     must not be served by a one-descale kernel) and "KV cache operations"
+ *     (bf16 cache writes, fp8 writes with per-token quantisation);
+ *   - ATOM configuration guide, "Master configuration (Config)"
+ *     (kv_cache_block_size 16, kv_cache_dtype "bf16" or "fp8") and
+ *     "Quick reference" (per-layer k/v caches and their scales);
+ *   - ROCm blog "Optimizing ATOM and vLLM-ATOM for High-Interactivity
+ *     Inference", "Attention Decode: Split Memory Work to Fill the Device"
+ *     (split the KV range so a single query fills the device; per-split
+ *     log-sum-exp kept in fp32) and "Host-Overhead Elimination: Keep Decode
+ *     Graph-Safe" (caller-provided outputs, no host-device synchronisation).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are described by pa_tensor: a data pointer, a dtype code, a rank
+ * and per-dimension sizes and strides (strides in ELEMENTS, not bytes).  The
+ * library never copies a descriptor's memory and keeps no pointer after a
+ * call returns; all device tensors stay owned by the caller.  Work is
+ * enqueued asynchronously on the given HIP stream (void* so this header is
+ * HIP-free; NULL = the default stream): inputs must stay alive and
+ * unmodified, and outputs unread, until the stream passes the call.
+ *
+ * Every entry point returns PA_OK (0) or a negative pa_status.  A negative
+ * status from paged_attn_decode means nothing was enqueued, except
+ * PA_ERR_HIP, which reports a launch failure.  paged_attn_strerror() maps a
+ * status to a fixed string; paged_attn_last_error() returns the calling
+ * thread's description of its most recent failure (which argument, which
+ * check).
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16      /* tokens per KV-cache block                  */
+#define PA_MAX_ROWS   64      /* max (q_heads / kv_heads) * query_len       */
+
+typedef enum pa_dtype {
+    PA_DTYPE_BF16        = 1,  /* bfloat16                                  */
+    PA_DTYPE_FP8_E4M3FN  = 2,  /* OCP float8 e4m3fn (bias 7, max 448, no inf) */
+    PA_DTYPE_FP32        = 3,
+    PA_DTYPE_INT32       = 4
+} pa_dtype;
+
+typedef enum pa_status {
+    PA_OK              = 0,
+    PA_ERR_NULL        = -1,  /* a required tensor or data pointer is NULL   */
+    PA_ERR_DTYPE       = -2,  /* a tensor has the wrong dtype                */
+    PA_ERR_SHAPE       = -3,  /* ranks or sizes disagree between tensors     */
+    PA_ERR_UNSUPPORTED = -4,  /* block size != 16, head_dim not 64/128,
+                                 q_heads % kv_heads != 0, rows > 64, ...     */
+    PA_ERR_LAYOUT      = -5,  /* inner stride != 1, misaligned base/stride   */
+    PA_ERR_CAPTURE     = -6,  /* workspace would have to grow while the
+                                 stream is being captured into a graph       */
+    PA_ERR_HIP         = -7,  /* a HIP runtime call or launch failed         */
+    PA_ERR_NOMEM       = -8,  /* workspace allocation failed                 */
+    PA_ERR_ARG         = -9   /* any other invalid argument                  */
+} pa_status;
+
+typedef struct pa_tensor {
+    void*   data;       /* device pointer (host pointer only where stated)   */
+    int32_t dtype;      /* pa_dtype                                          */
+    int32_t ndim;       /* 1..4                                              */
+    int64_t shape[4];
+    int64_t stride[4];  /* in elements                                       */
+} pa_tensor;
+
+/*
+ * paged_attn_decode -- softmax attention of the new query rows over a paged
+ * KV cache, written to `out`.
+ *
+ *   q             bf16 [B, Qmax, Hq, D] (rank 4) or [B, Hq, D] (rank 3,
+ *                 Qmax = 1).  Row (b, t) is the t-th new token of sequence
+ *                 b (the rectangular speculative-decode layout).
+ *   k_cache,      [NB, 16, Hkv, D], both bf16 or both fp8 e4m3fn.
+ *   v_cache       Token j of sequence b is slot j % 16 of physical block
+ *                 block_tables[b, j / 16].
+ *   block_tables  int32 [B, W].  Only the first ceil(context_lens[b] / 16)
+ *                 entries of row b are read; the rest may hold anything.
+ *                 Entries may repeat within and across rows (shared
+ *                 prefix blocks); the cache is only read.
+ *   context_lens  int32 [B]: L_b = number of tokens of sequence b in the
+ *                 cache, the new query tokens included (their K/V are
+ *                 written before this call).
+ *   query_lens    int32 [B]: n_b = number of new query rows of sequence b
+ *                 (0 <= n_b <= Qmax).  NULL means n_b = Qmax for all b.
+ *                 Query row t (t < n_b) is at position L_b - n_b + t and
+ *                 attends to keys 0 .. L_b - n_b + t (causal among the new
+ *                 tokens).  Rows t >= n_b are neither read nor written.
+ *   scale         softmax scale applied to q.k (e.g. 1/sqrt(D)); finite.
+ *   k_scale,      fp32, logically [NB, 16, Hkv]: one dequantisation scale
+ *   v_scale       per (block, slot, kv head), i.e. per token and head;
+ *                 required iff the cache is fp8, else must be NULL.  The
+ *                 slot dimension must be contiguous (stride[1] == 1), e.g.
+ *                 a [NB, Hkv, 16] tensor viewed as [NB, 16, Hkv].
+ *   out           bf16, same shape as q (its own strides); rows t < n_b
+ *                 receive the attention output rounded to nearest even.
+ *   stream        hipStream_t as void*, NULL = default stream.
+ *
+ * Query head h reads KV head h / (Hq / Hkv).  D must be 64 or 128,
+ * (Hq / Hkv) * Qmax <= 64.  Inner strides of q, out, caches and block_tables
+ * must be 1, the other strides of q/out/caches multiples of 16 bytes, data
+ * pointers 16-byte aligned; k_scale/v_scale strides of dims 0 and 2
+ * multiples of 4 and data 16-byte aligned.
+ *
+ * Device-side preconditions, not checked (checking would need a
+ * host-device synchronisation): n_b <= L_b <= 16 * W and
+ * 0 <= block_tables[b, i] < NB for i < ceil(L_b / 16).  Violations give
+ * unspecified output values but never an out-of-bounds access: the kernels
+ * clamp lengths to the tensors' extents and block ids into [0, NB).
+ * `out` must not overlap any input.
+ *
+ * Uses a per-(device, stream) workspace owned by the library for split-
+ * context partial results (fp32 partial outputs and log-sum-exp values);
+ * it grows on demand with hipMalloc outside stream capture.  Capture a
+ * call into a graph only after paged_attn_reserve() or an uncaptured call
+ * of the same or larger size on that stream; otherwise PA_ERR_CAPTURE.
+ * Calls on one stream are ordered; calls on different streams use
+ * different workspaces.
+ */
+int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* block_tables, const pa_tensor* context_lens,
+                      const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                      const pa_tensor* v_scale, pa_tensor* out, void* stream);
+
+/*
+ * paged_attn_check -- the host-side argument validation of
+ * paged_attn_decode, without touching the GPU or dereferencing any data
+ * pointer.  Same arguments (no stream); returns the status that
+ * paged_attn_decode would return for them before launching.
+ */
+int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                     const pa_tensor* block_tables, const pa_tensor* context_lens,
+                     const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                     const pa_tensor* v_scale, const pa_tensor* out);
+
+/*
+ * Split-context plan: how paged_attn_decode divides each (sequence, kv
+ * head) pair's context into partitions of partition_tokens tokens (a
+ * multiple of 32), chosen from shapes and the device's compute-unit count
+ * only (never from device data), so that one call fills the GPU and short
+ * contexts are not over-split.
+ */
+typedef struct pa_plan {
+    int32_t partition_tokens;   /* tokens per partition                    */
+    int32_t num_partitions;     /* ceil(16 * W / partition_tokens)         */
+    int32_t rows;               /* (Hq / Hkv) * Qmax query rows per kv head */
+    int32_t row_tiles;          /* ceil(rows / 16)                         */
+    int64_t partition_groups;   /* workgroups of the partition kernel      */
+    int64_t reduce_groups;      /* workgroups of the merge kernel (0: none) */
+    int64_t workspace_bytes;    /* fp32 partial outputs + log-sum-exp      */
+} pa_plan;
+
+/*
+ * paged_attn_plan -- the plan for the given sizes on a device with
+ * num_cus compute units (host only; no GPU access).  kv_dtype is a
+ * pa_dtype of the cache.  Honors paged_attn_set_partition_tokens().
+ */
+int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
+                    int64_t query_len, int64_t table_width, int32_t kv_dtype,
+                    int32_t num_cus, pa_plan* plan);
+
+/*
+ * paged_attn_set_partition_tokens -- override the planner's partition size
+ * for every later call in the process (tokens; a positive multiple of 32),
+ * or 0 to return to the automatic choice.  A test and tuning hook; not
+ * synchronised with concurrent calls.
+ */
+int paged_attn_set_partition_tokens(int32_t tokens);
+
+/*
+ * paged_attn_reserve -- grow the current device's workspace for `stream`
+ * to at least `bytes` (see pa_plan.workspace_bytes) so that later calls of
+ * that size can be captured into a HIP graph.  Allocates with hipMalloc;
+ * must not be called while `stream` is capturing.
+ */
+int paged_attn_reserve(int64_t bytes, void* stream);
+
+/*
+ * paged_attn_check_metadata -- host-side check of the device-side
+ * preconditions on HOST copies of the metadata: 0 <= query_lens[b] <= Qmax,
+ * query_lens[b] <= context_lens[b] <= 16 * W, and every used table entry in
+ * [0, NB).  query_lens may be NULL (all Qmax).  table_row_stride is in
+ * elements.  Returns PA_OK or PA_ERR_ARG (with the first offending
+ * sequence in paged_attn_last_error()).
+ */
+int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_lens,
+                              const int32_t* block_tables, int64_t batch, int64_t table_width,
+                              int64_t table_row_stride, int64_t query_len, int64_t num_blocks);
+
+/*
+ * Kernel timing for measurement: after paged_attn_profile_begin(n), the
+ * next n calls of paged_attn_decode (on any stream) record HIP events
+ * before and after each kernel they launch, on the call's stream.
+ * paged_attn_profile_end() waits for those events and returns the summed
+ * durations in milliseconds of the partition kernel and of the merge
+ * kernel and the number of calls recorded, then stops recording.
+ */
+int paged_attn_profile_begin(int32_t max_calls);
+int paged_attn_profile_end(double* partition_ms, double* reduce_ms, int32_t* calls);
+
+const char* paged_attn_strerror(int status);
+const char* paged_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,720 @@
+// HIP half of the library for gfx950 (CDNA4): the split-context partition
+// kernel, the log-sum-exp merge kernel, the per-stream workspace and the
+// paged_attn_decode entry point.
+//
+// Method (ROCm blog "Optimizing ATOM and vLLM-ATOM for High-Interactivity
+// Inference", "Attention Decode: Split Memory Work to Fill the Device"):
+// decode attention is a memory-bound, single-query operation, so the KV
+// range of every (sequence, kv head) pair is split into partitions that run
+// as separate workgroups; each keeps an online-softmax state and writes its
+// partial output plus a float32 log-sum-exp, and a second kernel merges the
+// partitions.  The partition size is chosen from shapes and the CU count
+// (pa_host.cpp), never from device data.
+//
+// Partition kernel, one 64-lane wave per (sequence b, kv head g, partition p):
+//  * All G*Qmax query rows that share kv head g form the N side of 16x16
+//    MFMA tiles (rows r = t*G + h_local; tiles of 16 rows), so every K/V
+//    byte is read from HBM once per kv head.
+//  * The wave walks its partition in 32-token steps (two 16-token blocks),
+//    prefetching the next step's K and V while computing the current one.
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: block mt of the step is the
+//    M side (token slot = lane % 16), head_dim the reduction.  Each lane then
+//    holds 8 scores of one query row: block (i / 4), slot 4*(lane/16) + i%4.
+//  * O^T += V^T P^T with the same MFMA: head_dim is the M side, the 32
+//    tokens the reduction, P (bf16) the N side.  The lane's 8 probabilities
+//    are already in B-operand order; V^T is formed in registers from 16-byte
+//    row loads by byte permutes (bf16) or fp8->f32 conversions (fp8).  The
+//    output tile puts a query row's accumulators in the same lanes as that
+//    row's softmax state, so rescaling needs no cross-lane traffic.
+//  * fp8 e4m3fn K/V are widened exactly to bf16 in registers; the
+//    per-(token, kv head) scales fold into the score column (k) and the
+//    probability (v) instead of multiplying every element.
+//  * Row max uses two cross-lane exchanges per step; row sums stay
+//    lane-partial until the epilogue.
+//  * Positions >= L_b and causally hidden keys get score -inf by selection;
+//    V rows and scales past L_b are zeroed, so NaN or garbage in unread
+//    cache slots never reaches the output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr unsigned kSelLo = 0x05040100u;   // v_perm: (src1.lo16, src0.lo16)
+constexpr unsigned kSelHi = 0x07060302u;   // v_perm: (src1.hi16, src0.hi16)
+
+struct PartArgs {
+    const char* q;   int64_t q_sb, q_st, q_sh;        // bytes
+    const char* k;   int64_t k_sblk, k_stok, k_sh;    // bytes
+    const char* v;   int64_t v_sblk, v_stok, v_sh;    // bytes
+    const float* ks; int64_t ks_sblk, ks_sh;          // floats
+    const float* vs; int64_t vs_sblk, vs_sh;
+    const int32_t* bt; int64_t bt_sb;
+    const int32_t* ctx; int64_t ctx_s;
+    const int32_t* ql;  int64_t ql_s;
+    char* out;       int64_t o_sb, o_st, o_sh;        // bytes
+    float* ws_o;     float* ws_lse;
+    float scale_log2;
+    int32_t Hq, Hkv, G, Qmax, W, NB, T, P, rows;
+};
+
+struct RedArgs {
+    const float* ws_o; const float* ws_lse;
+    const int32_t* ctx; int64_t ctx_s;
+    const int32_t* ql;  int64_t ql_s;
+    char* out;       int64_t o_sb, o_st, o_sh;        // bytes
+    int32_t Hq, Qmax, W, T, P;
+};
+
+__device__ __forceinline__ unsigned bits(float x) { return __builtin_bit_cast(unsigned, x); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
+    f32x2 f = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+// fp32 values that are exactly representable in bf16 (widened e4m3fn) ->
+// packed pair (a, b) by dropping the zero low halves.
+__device__ __forceinline__ unsigned pack_bf16_exact(float a, float b) {
+    return __builtin_amdgcn_perm(bits(b), bits(a), kSelHi);
+}
+
+// Per-step register tiles.  KL: 16-byte K loads per lane and block;
+// V: one load of D/16 elements per lane and token slot.
+template <int D, bool FP8> struct VLoad;
+template <> struct VLoad<128, false> { typedef u32x4 T; };
+template <> struct VLoad<64, false>  { typedef u32x2 T; };
+template <> struct VLoad<128, true>  { typedef u32x2 T; };
+template <> struct VLoad<64, true>   { typedef unsigned T; };
+
+template <int D, bool FP8> struct Step {
+    static constexpr int KL = FP8 ? D / 64 : D / 32;
+    u32x4 k[2][KL];
+    typename VLoad<D, FP8>::T v[8];
+    f32x4 ksc[2], vsc[2];
+};
+
+template <int D, bool FP8, int NT> struct State {
+    float m[NT], l[NT];
+    f32x4 acc[NT][D / 16];
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, int bid_lane, int step,
+                                          int g, int grp, const unsigned (&koff)[Step<D, FP8>::KL],
+                                          const unsigned (&voff)[4]) {
+    typedef typename VLoad<D, FP8>::T VT;
+    const int b0 = __builtin_amdgcn_readlane(bid_lane, 2 * step);
+    const int b1 = __builtin_amdgcn_readlane(bid_lane, 2 * step + 1);
+    const char* kb0 = a.k + (int64_t)b0 * a.k_sblk + (int64_t)g * a.k_sh;
+    const char* kb1 = a.k + (int64_t)b1 * a.k_sblk + (int64_t)g * a.k_sh;
+    const char* vb0 = a.v + (int64_t)b0 * a.v_sblk + (int64_t)g * a.v_sh;
+    const char* vb1 = a.v + (int64_t)b1 * a.v_sblk + (int64_t)g * a.v_sh;
+#pragma unroll
+    for (int c = 0; c < Step<D, FP8>::KL; ++c) {
+        st.k[0][c] = *reinterpret_cast<const u32x4*>(kb0 + koff[c]);
+        st.k[1][c] = *reinterpret_cast<const u32x4*>(kb1 + koff[c]);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        st.v[s] = *reinterpret_cast<const VT*>((s < 4 ? vb0 : vb1) + voff[s & 3]);
+    if constexpr (FP8) {
+        st.ksc[0] = *reinterpret_cast<const f32x4*>(a.ks + (int64_t)b0 * a.ks_sblk + (int64_t)g * a.ks_sh + 4 * grp);
+        st.ksc[1] = *reinterpret_cast<const f32x4*>(a.ks + (int64_t)b1 * a.ks_sblk + (int64_t)g * a.ks_sh + 4 * grp);
+        st.vsc[0] = *reinterpret_cast<const f32x4*>(a.vs + (int64_t)b0 * a.vs_sblk + (int64_t)g * a.vs_sh + 4 * grp);
+        st.vsc[1] = *reinterpret_cast<const f32x4*>(a.vs + (int64_t)b1 * a.vs_sblk + (int64_t)g * a.vs_sh + 4 * grp);
+    }
+}
+
+// V^T fragment of output tile j: element s = V[token slot s][d = (D/16)*m + j]
+// for this lane's m = lane % 16, packed as bf16 pairs (s, s+1).  bf16: the
+// pair is two half-words of the row loads, one v_perm each.
+template <int D>
+__device__ __forceinline__ bf16x8 vt_bf16(const typename VLoad<D, false>::T (&v)[8], int j) {
+    u32x4 x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        x[p] = __builtin_amdgcn_perm(v[2 * p + 1][j / 2], v[2 * p][j / 2], (j & 1) ? kSelHi : kSelLo);
+    return as_bf16x8(x);
+}
+
+// fp8: widen each slot's D/16 bytes to f32 (exact), then pair slots.
+template <int D>
+__device__ __forceinline__ void widen_v_fp8(const typename VLoad<D, true>::T (&v)[8], float (&f)[8][D / 16]) {
+    constexpr int J = D / 16;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int dw = 0; dw < J / 4; ++dw) {
+            unsigned word;
+            if constexpr (J == 4) word = v[s];
+            else word = v[s][dw];
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+            f[s][4 * dw + 0] = lo[0];
+            f[s][4 * dw + 1] = lo[1];
+            f[s][4 * dw + 2] = hi[0];
+            f[s][4 * dw + 3] = hi[1];
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 vt_fp8(const float (&f)[8][D / 16], int j) {
+    u32x4 x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[p] = pack_bf16_exact(f[2 * p][j], f[2 * p + 1][j]);
+    return as_bf16x8(x);
+}
+
+// K fragments (A operand of S^T) of block mt as bf16.
+template <int D, bool FP8>
+__device__ __forceinline__ void build_kf(const Step<D, FP8>& st, bf16x8 (&kf)[2][D / 32]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) kf[mt][kk] = as_bf16x8(st.k[mt][kk]);
+        } else {
+            // load c holds bytes e = 0..15 of d = (D/4)*grp + 16c + e;
+            // MFMA step kk = 2c + h takes bytes 8h .. 8h+7.
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    u32x4 x;
+#pragma unroll
+                    for (int p2 = 0; p2 < 2; ++p2) {
+                        const unsigned word = st.k[mt][c][2 * h + p2];
+                        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+                        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+                        x[2 * p2] = pack_bf16_exact(lo[0], lo[1]);
+                        x[2 * p2 + 1] = pack_bf16_exact(hi[0], hi[1]);
+                    }
+                    kf[mt][2 * c + h] = as_bf16x8(x);
+                }
+            }
+        }
+    }
+}
+
+template <int D, bool FP8, int NT>
+__device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>& s, const u32x4 (&qf)[NT][D / 32],
+                                             const PartArgs& a, int cbase, int L, int nq, int lane) {
+    constexpr int J = D / 16;
+    const int n16 = lane & 15, grp = lane >> 4;
+    const bool tail = cbase + 31 > L - nq;   // some key here is past L or causally hidden
+
+    if (tail) {
+        // zero V rows (and scales) of positions >= L so that p = 0 never
+        // meets NaN or garbage from unwritten slots
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tok = cbase + 16 * (i >> 2) + 4 * grp + (i & 3);
+            if (tok >= L) {
+                st.v[i] = typename VLoad<D, FP8>::T{};
+                if constexpr (FP8) {
+                    st.vsc[i >> 2][i & 3] = 0.f;
+                    st.ksc[i >> 2][i & 3] = 0.f;
+                }
+            }
+        }
+    }
+
+    bf16x8 kf[2][D / 32];
+    build_kf<D, FP8>(st, kf);
+    float vf[FP8 ? 8 : 1][FP8 ? J : 1];
+    if constexpr (FP8) widen_v_fp8<D>(st.v, vf);
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const bf16x8 qb = as_bf16x8(qf[nt][kk]);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qb, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qb, s1, 0, 0, 0);
+        }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (FP8) {
+                x[i] = s0[i] * (a.scale_log2 * st.ksc[0][i]);
+                x[4 + i] = s1[i] * (a.scale_log2 * st.ksc[1][i]);
+            } else {
+                x[i] = s0[i] * a.scale_log2;
+                x[4 + i] = s1[i] * a.scale_log2;
+            }
+        }
+        if (tail) {
+            const int row = 16 * nt + n16;
+            const int t = row / a.G;
+            const int lim = (row < a.rows && t < nq) ? L - nq + t : L - 1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int tok = cbase + 16 * (i >> 2) + 4 * grp + (i & 3);
+                x[i] = tok > lim ? -__builtin_inff() : x[i];
+            }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(s.m[nt], mx);
+        const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(s.m[nt] - m_use);
+        float p[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+            psum += p[i];
+        }
+        s.l[nt] = s.l[nt] * alpha + psum;
+        s.m[nt] = m_new;
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] *= st.vsc[0][i];
+                p[4 + i] *= st.vsc[1][i];
+            }
+        }
+        u32x4 pw;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pw[w] = pack_bf16_rne(p[2 * w], p[2 * w + 1]);
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            bf16x8 vt;
+            if constexpr (FP8) vt = vt_fp8<D>(vf, j);
+            else vt = vt_bf16<D>(st.v, j);
+            s.acc[nt][j] *= alpha;
+            s.acc[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, s.acc[nt][j], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, bool FP8, int NT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+void partition_kernel(PartArgs a) {
+    constexpr int J = D / 16;
+    constexpr int KL = Step<D, FP8>::KL;
+    constexpr int E = FP8 ? 1 : 2;
+    const int lane = threadIdx.x;
+    const int n16 = lane & 15, grp = lane >> 4;
+
+    int64_t id = blockIdx.x;
+    const int p = (int)(id % a.P);
+    id /= a.P;
+    const int g = (int)(id % a.Hkv);
+    const int b = (int)(id / a.Hkv);
+
+    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
+    const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+    if (L <= 0 || nq <= 0) return;
+    const int tok0 = p * a.T;
+    if (tok0 >= L) return;
+    const int tok1 = min(L, tok0 + a.T);
+    const int nsteps = (tok1 - tok0 + 31) / 32;
+    const int nblk_seq = (L + 15) / 16;
+    const bool direct = (L + a.T - 1) / a.T == 1;
+
+    // block ids of this partition, one per lane (at most 64 blocks),
+    // clamped to the sequence's used blocks and to the pool
+    int bid_lane;
+    {
+        const int idx = min(tok0 / 16 + lane, nblk_seq - 1);
+        const int v = a.bt[(int64_t)b * a.bt_sb + idx];
+        bid_lane = min(max(v, 0), a.NB - 1);
+    }
+
+    // query fragments: row r = 16*nt + n16 -> (t, h_local) = (r / G, r % G)
+    u32x4 qf[NT][D / 32];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int row = 16 * nt + n16;
+        const int t = row / a.G, hl = row - t * a.G;
+        const bool rv = row < a.rows && t < nq;
+        const char* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)t * a.q_st + (int64_t)(g * a.G + hl) * a.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const int d0 = FP8 ? (D / 4) * grp + 8 * kk : 32 * kk + 8 * grp;
+            qf[nt][kk] = rv ? *reinterpret_cast<const u32x4*>(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    unsigned koff[KL];
+#pragma unroll
+    for (int c = 0; c < KL; ++c)
+        koff[c] = (unsigned)(n16 * a.k_stok) + (FP8 ? (unsigned)((D / 4) * grp + 16 * c) : (unsigned)((32 * c + 8 * grp) * 2));
+    unsigned voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = (unsigned)((4 * grp + i) * a.v_stok) + (unsigned)((D / 16) * n16 * E);
+
+    State<D, FP8, NT> s;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        s.m[nt] = -__builtin_inff();
+        s.l[nt] = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) s.acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // two register buffers, next step's loads in flight during compute
+    // (one buffer when the row tiles leave no registers for a second)
+    Step<D, FP8> bufA, bufB;
+    if constexpr (NT > 2) {
+        for (int st = 0; st < nsteps; ++st) {
+            load_step<D, FP8>(bufA, a, bid_lane, st, g, grp, koff, voff);
+            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        }
+    } else {
+    load_step<D, FP8>(bufA, a, bid_lane, 0, g, grp, koff, voff);
+    int st = 0;
+    while (st + 2 < nsteps) {
+        load_step<D, FP8>(bufB, a, bid_lane, st + 1, g, grp, koff, voff);
+        compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        load_step<D, FP8>(bufA, a, bid_lane, st + 2, g, grp, koff, voff);
+        compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+        st += 2;
+    }
+    if (st + 1 < nsteps) {
+        load_step<D, FP8>(bufB, a, bid_lane, st + 1, g, grp, koff, voff);
+        compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+    } else {
+        compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+    }
+    }
+
+    // epilogue: lane holds d = (D/16)*(4*grp + i) + j, j < D/16, of row 16*nt + n16
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float lt = s.l[nt];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const int row = 16 * nt + n16;
+        const int t = row / a.G, hl = row - t * a.G;
+        if (!(row < a.rows && t < nq)) continue;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int h = g * a.G + hl;
+        if (direct) {
+            char* orow = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = J * (4 * grp + i);
+                if constexpr (J == 8) {
+                    u32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
+                    *reinterpret_cast<u32x4*>(orow + 2 * d0) = w;
+                } else {
+                    u32x2 w;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        w[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
+                    *reinterpret_cast<u32x2*>(orow + 2 * d0) = w;
+                }
+            }
+        } else {
+            const int64_t rowg = ((int64_t)b * a.Qmax + t) * a.Hq + h;
+            float* wo = a.ws_o + (rowg * a.P + p) * D;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = J * (4 * grp + i);
+#pragma unroll
+                for (int e = 0; e < J / 4; ++e) {
+                    f32x4 w;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w[k] = s.acc[nt][4 * e + k][i] * inv;
+                    *reinterpret_cast<f32x4*>(wo + d0 + 4 * e) = w;
+                }
+            }
+            if (grp == 0) a.ws_lse[rowg * a.P + p] = lt > 0.f ? s.m[nt] + __log2f(lt) : -__builtin_inff();
+        }
+    }
+}
+
+// Merge of the partitions of one query row (b, t, h): log-sum-exp weights
+// in base 2, float32 throughout, bf16 round-to-nearest-even at the end.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(RedArgs a) {
+    constexpr int V4 = D / 4;        // float4 columns of a row
+    constexpr int PS = 256 / V4;     // partitions read side by side
+    const int tid = threadIdx.x;
+    int64_t id = blockIdx.x;
+    const int h = (int)(id % a.Hq);
+    id /= a.Hq;
+    const int t = (int)(id % a.Qmax);
+    const int b = (int)(id / a.Qmax);
+    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
+    const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+    if (L <= 0 || t >= nq) return;
+    const int np = (L + a.T - 1) / a.T;
+    if (np <= 1) return;                        // written by the partition kernel
+    const int64_t rowg = blockIdx.x;
+    const float* lse = a.ws_lse + rowg * a.P;
+    const float* wo = a.ws_o + rowg * a.P * D;
+
+    __shared__ float smax[4];
+    __shared__ f32x4 sacc[PS][V4];
+    __shared__ float swt[PS];
+
+    float mx = -__builtin_inff();
+    for (int p = tid; p < np; p += 256) mx = fmaxf(mx, lse[p]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) smax[tid >> 6] = mx;
+    __syncthreads();
+    float M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+    if (M == -__builtin_inff()) M = 0.f;
+
+    const int d4 = tid % V4, ps = tid / V4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int p = ps; p < np; p += PS) {
+        const float w = __builtin_amdgcn_exp2f(lse[p] - M);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(wo + (int64_t)p * D + 4 * d4);
+        wsum += w;
+        acc += w * o;
+    }
+    sacc[ps][d4] = acc;
+    if (d4 == 0) swt[ps] = wsum;
+    __syncthreads();
+    if (ps == 0) {
+        f32x4 tot = sacc[0][d4];
+        float wt = swt[0];
+#pragma unroll
+        for (int q = 1; q < PS; ++q) {
+            tot += sacc[q][d4];
+            wt += swt[q];
+        }
+        const float inv = wt > 0.f ? 1.f / wt : 0.f;
+        u32x2 w;
+        w[0] = pack_bf16_rne(tot[0] * inv, tot[1] * inv);
+        w[1] = pack_bf16_rne(tot[2] * inv, tot[3] * inv);
+        char* orow = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
+        *reinterpret_cast<u32x2*>(orow + 8 * d4) = w;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+std::vector<int> g_cus;
+
+struct Profile {
+    bool active = false;
+    int max_calls = 0, calls = 0;
+    std::vector<hipEvent_t> ev;   // 3 per call: before, between, after
+    std::vector<bool> has_reduce;
+} g_prof;
+
+int device_cus(int dev) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_cus.size() <= dev) g_cus.resize(dev + 1, 0);
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cus[dev] = n;
+    }
+    return g_cus[dev];
+}
+
+int get_workspace(int dev, void* stream, size_t need, void** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.bytes >= need) {
+        *out = w.ptr;
+        return PA_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess)
+        return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(PA_ERR_CAPTURE, "workspace of %zu bytes needed (have %zu) while the stream is capturing",
+                    need, w.bytes);
+    if (w.ptr) {
+        // earlier calls on this stream may still read it
+        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+            return fail(PA_ERR_HIP, "hipStreamSynchronize failed");
+        (void)hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
+    }
+    const size_t bytes = need + need / 4;   // headroom against creeping sizes
+    if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        w.ptr = nullptr;
+        return fail(PA_ERR_NOMEM, "hipMalloc of %zu workspace bytes failed", bytes);
+    }
+    w.bytes = bytes;
+    *out = w.ptr;
+    return PA_OK;
+}
+
+template <int D, bool FP8>
+void launch_partition_d(int nt, dim3 grid, hipStream_t s, const PartArgs& a) {
+    switch (nt) {
+        case 1: hipLaunchKernelGGL((partition_kernel<D, FP8, 1>), grid, dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((partition_kernel<D, FP8, 2>), grid, dim3(64), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((partition_kernel<D, FP8, 3>), grid, dim3(64), 0, s, a); break;
+        default: hipLaunchKernelGGL((partition_kernel<D, FP8, 4>), grid, dim3(64), 0, s, a); break;
+    }
+}
+
+void launch_partition(int D, bool fp8, int nt, dim3 grid, hipStream_t s, const PartArgs& a) {
+    if (D == 128) {
+        if (fp8) launch_partition_d<128, true>(nt, grid, s, a);
+        else launch_partition_d<128, false>(nt, grid, s, a);
+    } else {
+        if (fp8) launch_partition_d<64, true>(nt, grid, s, a);
+        else launch_partition_d<64, false>(nt, grid, s, a);
+    }
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* block_tables, const pa_tensor* context_lens,
+                      const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                      const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+    using namespace pa;
+    Problem pr;
+    int st = validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
+                      out, &pr);
+    if (st) return st;
+    if (pr.B == 0) return PA_OK;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+    pa_plan plan;
+    if ((st = make_plan(pr.B, pr.Hq, pr.Hkv, pr.D, pr.Qmax, pr.W, pr.fp8, device_cus(dev), &plan))) return st;
+    void* ws = nullptr;
+    if (plan.workspace_bytes > 0 &&
+        (st = get_workspace(dev, stream, (size_t)plan.workspace_bytes, &ws)))
+        return st;
+
+    const int64_t rows_total = pr.B * pr.Qmax * pr.Hq;
+    PartArgs a;
+    a.q = static_cast<const char*>(pr.q); a.q_sb = pr.q_sb * 2; a.q_st = pr.q_st * 2; a.q_sh = pr.q_sh * 2;
+    a.k = static_cast<const char*>(pr.k); a.k_sblk = pr.k_sblk; a.k_stok = pr.k_stok; a.k_sh = pr.k_sh;
+    a.v = static_cast<const char*>(pr.v); a.v_sblk = pr.v_sblk; a.v_stok = pr.v_stok; a.v_sh = pr.v_sh;
+    a.ks = pr.ks; a.ks_sblk = pr.ks_sblk; a.ks_sh = pr.ks_sh;
+    a.vs = pr.vs; a.vs_sblk = pr.vs_sblk; a.vs_sh = pr.vs_sh;
+    a.bt = pr.bt; a.bt_sb = pr.bt_sb;
+    a.ctx = pr.ctx; a.ctx_s = pr.ctx_s;
+    a.ql = pr.ql; a.ql_s = pr.ql_s;
+    a.out = static_cast<char*>(pr.out); a.o_sb = pr.o_sb * 2; a.o_st = pr.o_st * 2; a.o_sh = pr.o_sh * 2;
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_lse = ws ? static_cast<float*>(ws) + rows_total * plan.num_partitions * pr.D : nullptr;
+    a.scale_log2 = pr.scale * kLog2e;
+    a.Hq = (int32_t)pr.Hq; a.Hkv = (int32_t)pr.Hkv; a.G = (int32_t)pr.G; a.Qmax = (int32_t)pr.Qmax;
+    a.W = (int32_t)pr.W; a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
+    a.T = plan.partition_tokens; a.P = plan.num_partitions; a.rows = plan.rows;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (g_prof.active && g_prof.calls < g_prof.max_calls) {
+            const int c = g_prof.calls++;
+            e0 = g_prof.ev[3 * c]; e1 = g_prof.ev[3 * c + 1]; e2 = g_prof.ev[3 * c + 2];
+            g_prof.has_reduce[c] = plan.reduce_groups > 0;
+        }
+    }
+    if (e0) (void)hipEventRecord(e0, s);
+    launch_partition((int)pr.D, pr.fp8, plan.row_tiles, dim3((unsigned)plan.partition_groups), s, a);
+    if (e1) (void)hipEventRecord(e1, s);
+    if (plan.reduce_groups > 0) {
+        RedArgs r;
+        r.ws_o = a.ws_o; r.ws_lse = a.ws_lse;
+        r.ctx = a.ctx; r.ctx_s = a.ctx_s; r.ql = a.ql; r.ql_s = a.ql_s;
+        r.out = a.out; r.o_sb = a.o_sb; r.o_st = a.o_st; r.o_sh = a.o_sh;
+        r.Hq = a.Hq; r.Qmax = a.Qmax; r.W = a.W; r.T = a.T; r.P = a.P;
+        if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, dim3((unsigned)plan.reduce_groups), dim3(256), 0, s, r);
+        else hipLaunchKernelGGL(reduce_kernel<64>, dim3((unsigned)plan.reduce_groups), dim3(256), 0, s, r);
+    }
+    if (e2) (void)hipEventRecord(e2, s);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return PA_OK;
+}
+
+int paged_attn_reserve(int64_t bytes, void* stream) {
+    if (bytes < 0) return pa::fail(PA_ERR_ARG, "reserve: negative size");
+    if (bytes == 0) return PA_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return pa::fail(PA_ERR_HIP, "hipGetDevice failed");
+    void* p = nullptr;
+    return pa::get_workspace(dev, stream, (size_t)bytes, &p);
+}
+
+int paged_attn_profile_begin(int32_t max_calls) {
+    using namespace pa;
+    if (max_calls < 1) return fail(PA_ERR_ARG, "profile_begin: max_calls must be >= 1");
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.assign(3 * (size_t)max_calls, nullptr);
+    for (auto& e : g_prof.ev)
+        if (hipEventCreate(&e) != hipSuccess) return fail(PA_ERR_HIP, "hipEventCreate failed");
+    g_prof.has_reduce.assign(max_calls, false);
+    g_prof.max_calls = max_calls;
+    g_prof.calls = 0;
+    g_prof.active = true;
+    return PA_OK;
+}
+
+int paged_attn_profile_end(double* partition_ms, double* reduce_ms, int32_t* calls) {
+    using namespace pa;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_prof.active) return fail(PA_ERR_ARG, "profile_end without profile_begin");
+    double part = 0, red = 0;
+    int st = PA_OK;
+    for (int c = 0; c < g_prof.calls; ++c) {
+        float ms = 0.f;
+        if (hipEventSynchronize(g_prof.ev[3 * c + 2]) != hipSuccess) { st = PA_ERR_HIP; break; }
+        if (hipEventElapsedTime(&ms, g_prof.ev[3 * c], g_prof.ev[3 * c + 1]) == hipSuccess) part += ms;
+        if (g_prof.has_reduce[c] &&
+            hipEventElapsedTime(&ms, g_prof.ev[3 * c + 1], g_prof.ev[3 * c + 2]) == hipSuccess)
+            red += ms;
+    }
+    if (partition_ms) *partition_ms = part;
+    if (reduce_ms) *reduce_ms = red;
+    if (calls) *calls = g_prof.calls;
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.active = false;
+    if (st) return fail(st, "profile_end: hipEventSynchronize failed");
+    return PA_OK;
+}
+
+}  // extern "C"

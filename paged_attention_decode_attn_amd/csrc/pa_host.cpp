@@ -1,0 +1,313 @@
+// Host-side half of the library: argument validation, the split-context
+// planner, metadata checks and error strings.  Plain C++ with no HIP calls,
+// so every function here runs (and is tested) on a machine without a GPU.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local char g_last_error[512] = "";
+std::atomic<int32_t> g_partition_override{0};
+
+int64_t elem_bytes(int32_t dtype) {
+    switch (dtype) {
+        case PA_DTYPE_BF16: return 2;
+        case PA_DTYPE_FP8_E4M3FN: return 1;
+        case PA_DTYPE_FP32: return 4;
+        case PA_DTYPE_INT32: return 4;
+        default: return 0;
+    }
+}
+
+const char* dtype_name(int32_t dtype) {
+    switch (dtype) {
+        case PA_DTYPE_BF16: return "BF16";
+        case PA_DTYPE_FP8_E4M3FN: return "FP8_E4M3FN";
+        case PA_DTYPE_FP32: return "FP32";
+        case PA_DTYPE_INT32: return "INT32";
+        default: return "unknown";
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Rank, dtype and non-negative sizes/strides of one descriptor.
+int check_desc(const pa_tensor* t, const char* name, int32_t dtype, int ndim_lo, int ndim_hi,
+               bool need_data) {
+    if (!t) return fail(PA_ERR_NULL, "%s: descriptor is NULL", name);
+    if (t->ndim < ndim_lo || t->ndim > ndim_hi)
+        return fail(PA_ERR_SHAPE, "%s: rank %d, expected %d..%d", name, t->ndim, ndim_lo, ndim_hi);
+    if (t->dtype != dtype)
+        return fail(PA_ERR_DTYPE, "%s: dtype %s, expected %s", name, dtype_name(t->dtype),
+                    dtype_name(dtype));
+    int64_t numel = 1;
+    for (int i = 0; i < t->ndim; ++i) {
+        if (t->shape[i] < 0) return fail(PA_ERR_SHAPE, "%s: negative size in dim %d", name, i);
+        if (t->stride[i] < 0) return fail(PA_ERR_LAYOUT, "%s: negative stride in dim %d", name, i);
+        numel *= t->shape[i];
+    }
+    if (need_data && numel > 0 && !t->data) return fail(PA_ERR_NULL, "%s: data pointer is NULL", name);
+    return PA_OK;
+}
+
+// Inner stride 1, other strides multiples of 16 bytes, base 16-byte aligned.
+int check_rows16(const pa_tensor* t, const char* name) {
+    const int64_t eb = elem_bytes(t->dtype);
+    if (t->stride[t->ndim - 1] != 1 && t->shape[t->ndim - 1] > 1)
+        return fail(PA_ERR_LAYOUT, "%s: innermost stride must be 1", name);
+    for (int i = 0; i + 1 < t->ndim; ++i)
+        if ((t->stride[i] * eb) % 16 != 0 && t->shape[i] > 1)
+            return fail(PA_ERR_LAYOUT, "%s: stride of dim %d is not a multiple of 16 bytes", name, i);
+    if (!aligned(t->data, 16)) return fail(PA_ERR_LAYOUT, "%s: data is not 16-byte aligned", name);
+    return PA_OK;
+}
+
+}  // namespace
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* bt,
+             const pa_tensor* ctx, const pa_tensor* ql, float scale, const pa_tensor* ks,
+             const pa_tensor* vs, const pa_tensor* out, Problem* pr) {
+    int st;
+    if ((st = check_desc(q, "q", PA_DTYPE_BF16, 3, 4, true))) return st;
+    if ((st = check_desc(out, "out", PA_DTYPE_BF16, 3, 4, true))) return st;
+    if (!kc) return fail(PA_ERR_NULL, "k_cache: descriptor is NULL");
+    if (!vc) return fail(PA_ERR_NULL, "v_cache: descriptor is NULL");
+    const int32_t kvt = kc->dtype;
+    if (kvt != PA_DTYPE_BF16 && kvt != PA_DTYPE_FP8_E4M3FN)
+        return fail(PA_ERR_DTYPE, "k_cache: dtype %s, expected BF16 or FP8_E4M3FN", dtype_name(kvt));
+    if ((st = check_desc(kc, "k_cache", kvt, 4, 4, true))) return st;
+    if ((st = check_desc(vc, "v_cache", kvt, 4, 4, true))) return st;
+    if ((st = check_desc(bt, "block_tables", PA_DTYPE_INT32, 2, 2, true))) return st;
+    if ((st = check_desc(ctx, "context_lens", PA_DTYPE_INT32, 1, 1, true))) return st;
+    if (ql && (st = check_desc(ql, "query_lens", PA_DTYPE_INT32, 1, 1, true))) return st;
+    const bool fp8 = kvt == PA_DTYPE_FP8_E4M3FN;
+    if (fp8) {
+        if (!ks || !vs) return fail(PA_ERR_NULL, "fp8 cache needs k_scale and v_scale");
+        if ((st = check_desc(ks, "k_scale", PA_DTYPE_FP32, 3, 3, true))) return st;
+        if ((st = check_desc(vs, "v_scale", PA_DTYPE_FP32, 3, 3, true))) return st;
+    } else if (ks || vs) {
+        return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
+    }
+    if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "scale is not finite");
+
+    // ---- sizes
+    const bool q3 = q->ndim == 3;
+    const int64_t B = q->shape[0];
+    const int64_t Qmax = q3 ? 1 : q->shape[1];
+    const int64_t Hq = q->shape[q3 ? 1 : 2];
+    const int64_t D = q->shape[q3 ? 2 : 3];
+    if (out->ndim != q->ndim)
+        return fail(PA_ERR_SHAPE, "out: rank %d, q has rank %d", out->ndim, q->ndim);
+    for (int i = 0; i < q->ndim; ++i)
+        if (out->shape[i] != q->shape[i])
+            return fail(PA_ERR_SHAPE, "out: size %lld in dim %d, q has %lld", (long long)out->shape[i],
+                        i, (long long)q->shape[i]);
+    for (int i = 0; i < 4; ++i)
+        if (kc->shape[i] != vc->shape[i])
+            return fail(PA_ERR_SHAPE, "v_cache: size %lld in dim %d, k_cache has %lld",
+                        (long long)vc->shape[i], i, (long long)kc->shape[i]);
+    const int64_t NB = kc->shape[0], Hkv = kc->shape[2];
+    if (kc->shape[1] != PA_BLOCK_SIZE)
+        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, only 16 is supported",
+                    (long long)kc->shape[1]);
+    if (kc->shape[3] != D)
+        return fail(PA_ERR_SHAPE, "k_cache: head_dim %lld, q has %lld", (long long)kc->shape[3], (long long)D);
+    if (D != 64 && D != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64 and 128 are supported", (long long)D);
+    if (Hkv < 1) return fail(PA_ERR_SHAPE, "k_cache: no kv heads");
+    if (Hq % Hkv != 0 || Hq == 0)
+        return fail(PA_ERR_UNSUPPORTED, "q_heads %lld is not a positive multiple of kv_heads %lld",
+                    (long long)Hq, (long long)Hkv);
+    const int64_t G = Hq / Hkv;
+    if (Qmax < 1) return fail(PA_ERR_SHAPE, "q: query length must be >= 1");
+    if (G * Qmax > PA_MAX_ROWS)
+        return fail(PA_ERR_UNSUPPORTED, "(q_heads / kv_heads) * query_len = %lld exceeds %d",
+                    (long long)(G * Qmax), PA_MAX_ROWS);
+    if (bt->shape[0] != B)
+        return fail(PA_ERR_SHAPE, "block_tables: %lld rows, batch is %lld", (long long)bt->shape[0], (long long)B);
+    const int64_t W = bt->shape[1];
+    if (ctx->shape[0] != B)
+        return fail(PA_ERR_SHAPE, "context_lens: %lld entries, batch is %lld", (long long)ctx->shape[0], (long long)B);
+    if (ql && ql->shape[0] != B)
+        return fail(PA_ERR_SHAPE, "query_lens: %lld entries, batch is %lld", (long long)ql->shape[0], (long long)B);
+    if (fp8) {
+        for (const pa_tensor* s : {ks, vs}) {
+            const char* nm = s == ks ? "k_scale" : "v_scale";
+            if (s->shape[0] != NB || s->shape[1] != PA_BLOCK_SIZE || s->shape[2] != Hkv)
+                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, 16, kv_heads]", nm);
+            if (s->stride[1] != 1)
+                return fail(PA_ERR_LAYOUT, "%s: the slot dimension must be contiguous", nm);
+            if (s->stride[0] % 4 || s->stride[2] % 4 || !aligned(s->data, 16))
+                return fail(PA_ERR_LAYOUT, "%s: strides of dims 0 and 2 must be multiples of 4 and data 16-byte aligned", nm);
+        }
+    }
+    if (B > 0) {
+        if (W < 1) return fail(PA_ERR_SHAPE, "block_tables: width must be >= 1");
+        if (NB < 1) return fail(PA_ERR_SHAPE, "k_cache: the pool has no blocks");
+        if (W > (int64_t(1) << 26)) return fail(PA_ERR_UNSUPPORTED, "block_tables: width too large");
+    }
+
+    // ---- layouts
+    if ((st = check_rows16(q, "q"))) return st;
+    if ((st = check_rows16(out, "out"))) return st;
+    if ((st = check_rows16(kc, "k_cache"))) return st;
+    if ((st = check_rows16(vc, "v_cache"))) return st;
+    if (bt->stride[1] != 1 && W > 1) return fail(PA_ERR_LAYOUT, "block_tables: innermost stride must be 1");
+    if (!aligned(bt->data, 4) || !aligned(ctx->data, 4) || (ql && !aligned(ql->data, 4)))
+        return fail(PA_ERR_LAYOUT, "int32 metadata must be 4-byte aligned");
+    const int64_t eb = fp8 ? 1 : 2;
+    // in-block byte offsets of the kernels are 32-bit
+    for (const pa_tensor* c : {kc, vc}) {
+        const int64_t span = (PA_BLOCK_SIZE - 1) * c->stride[1] * eb + (Hkv - 1) * c->stride[2] * eb + D * eb;
+        if (span >= (int64_t(1) << 31))
+            return fail(PA_ERR_LAYOUT, "%s: one block spans more than 2 GiB", c == kc ? "k_cache" : "v_cache");
+    }
+
+    if (pr) {
+        Problem& p = *pr;
+        p.B = B; p.Qmax = Qmax; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.D = D; p.NB = NB; p.W = W;
+        p.fp8 = fp8; p.scale = scale;
+        p.q = q->data;
+        p.q_sb = q->stride[0]; p.q_st = q3 ? 0 : q->stride[1]; p.q_sh = q->stride[q3 ? 1 : 2];
+        p.out = out->data;
+        p.o_sb = out->stride[0]; p.o_st = q3 ? 0 : out->stride[1]; p.o_sh = out->stride[q3 ? 1 : 2];
+        p.k = kc->data; p.k_sblk = kc->stride[0] * eb; p.k_stok = kc->stride[1] * eb; p.k_sh = kc->stride[2] * eb;
+        p.v = vc->data; p.v_sblk = vc->stride[0] * eb; p.v_stok = vc->stride[1] * eb; p.v_sh = vc->stride[2] * eb;
+        p.ks = fp8 ? static_cast<const float*>(ks->data) : nullptr;
+        p.vs = fp8 ? static_cast<const float*>(vs->data) : nullptr;
+        p.ks_sblk = fp8 ? ks->stride[0] : 0; p.ks_sh = fp8 ? ks->stride[2] : 0;
+        p.vs_sblk = fp8 ? vs->stride[0] : 0; p.vs_sh = fp8 ? vs->stride[2] : 0;
+        p.bt = static_cast<const int32_t*>(bt->data); p.bt_sb = bt->stride[0];
+        p.ctx = static_cast<const int32_t*>(ctx->data); p.ctx_s = ctx->stride[0];
+        p.ql = ql ? static_cast<const int32_t*>(ql->data) : nullptr; p.ql_s = ql ? ql->stride[0] : 0;
+    }
+    return PA_OK;
+}
+
+int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W, bool /*fp8*/,
+              int32_t num_cus, pa_plan* plan) {
+    if (!plan) return fail(PA_ERR_NULL, "plan: NULL");
+    if (B < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Qmax < 1 || W < 1 || num_cus < 1 || D < 1)
+        return fail(PA_ERR_ARG, "plan: invalid sizes");
+    const int64_t rows = (Hq / Hkv) * Qmax;
+    const int64_t max_tokens = int64_t(PA_BLOCK_SIZE) * W;
+    const int64_t units = B * Hkv;                 // (sequence, kv head) pairs
+    int64_t T = g_partition_override.load();
+    if (T <= 0) {
+        // Fill the chip: aim for about 4 single-wave workgroups per SIMD
+        // (4 SIMDs per CU) over all pairs, bounded below by one 32-token
+        // step so short contexts are not over-split.
+        const int64_t target = int64_t(num_cus) * 4 * 4;
+        const int64_t want = units > 0 ? (target + units - 1) / units : 1;
+        T = (max_tokens + want - 1) / want;
+    }
+    T = ((T + kChunk - 1) / kChunk) * kChunk;
+    if (T < kChunk) T = kChunk;
+    if (T > kMaxPartitionTokens) T = kMaxPartitionTokens;
+    int64_t P = (max_tokens + T - 1) / T;
+    while (P > kMaxPartitions && T < kMaxPartitionTokens) {   // unreachable for W <= 2^26 / 16
+        T += kChunk;
+        P = (max_tokens + T - 1) / T;
+    }
+    if (P > kMaxPartitions) return fail(PA_ERR_UNSUPPORTED, "context too long for the partition limit");
+    plan->partition_tokens = int32_t(T);
+    plan->num_partitions = int32_t(P);
+    plan->rows = int32_t(rows);
+    plan->row_tiles = int32_t((rows + 15) / 16);
+    plan->partition_groups = units * P;
+    plan->reduce_groups = P > 1 ? B * Qmax * Hq : 0;
+    plan->workspace_bytes = P > 1 ? B * Qmax * Hq * P * (D + 1) * int64_t(sizeof(float)) + 256 : 0;
+    if (plan->partition_groups >= (int64_t(1) << 31) || plan->reduce_groups >= (int64_t(1) << 31))
+        return fail(PA_ERR_UNSUPPORTED, "grid too large");
+    return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                     const pa_tensor* block_tables, const pa_tensor* context_lens,
+                     const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                     const pa_tensor* v_scale, const pa_tensor* out) {
+    return pa::validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
+                        v_scale, out, nullptr);
+}
+
+int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
+                    int64_t query_len, int64_t table_width, int32_t kv_dtype, int32_t num_cus,
+                    pa_plan* plan) {
+    if (kv_dtype != PA_DTYPE_BF16 && kv_dtype != PA_DTYPE_FP8_E4M3FN)
+        return pa::fail(PA_ERR_DTYPE, "plan: kv dtype must be BF16 or FP8_E4M3FN");
+    return pa::make_plan(batch, q_heads, kv_heads, head_dim, query_len, table_width,
+                         kv_dtype == PA_DTYPE_FP8_E4M3FN, num_cus, plan);
+}
+
+int paged_attn_set_partition_tokens(int32_t tokens) {
+    if (tokens < 0 || tokens % pa::kChunk || tokens > pa::kMaxPartitionTokens)
+        return pa::fail(PA_ERR_ARG, "partition tokens must be 0 or a multiple of 32 up to %d",
+                        pa::kMaxPartitionTokens);
+    pa::g_partition_override.store(tokens);
+    return PA_OK;
+}
+
+int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_lens,
+                              const int32_t* block_tables, int64_t batch, int64_t table_width,
+                              int64_t table_row_stride, int64_t query_len, int64_t num_blocks) {
+    if (batch < 0 || table_width < 0 || query_len < 1 || num_blocks < 0 || table_row_stride < table_width)
+        return pa::fail(PA_ERR_ARG, "check_metadata: invalid sizes");
+    if (batch > 0 && (!context_lens || !block_tables))
+        return pa::fail(PA_ERR_NULL, "check_metadata: NULL metadata");
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t L = context_lens[b];
+        const int64_t n = query_lens ? query_lens[b] : query_len;
+        if (n < 0 || n > query_len)
+            return pa::fail(PA_ERR_ARG, "sequence %lld: query_len %lld outside [0, %lld]", (long long)b,
+                            (long long)n, (long long)query_len);
+        if (L < n || L > PA_BLOCK_SIZE * table_width)
+            return pa::fail(PA_ERR_ARG, "sequence %lld: context_len %lld outside [%lld, %lld]", (long long)b,
+                            (long long)L, (long long)n, (long long)(PA_BLOCK_SIZE * table_width));
+        const int64_t used = (L + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+        for (int64_t i = 0; i < used; ++i) {
+            const int64_t blk = block_tables[b * table_row_stride + i];
+            if (blk < 0 || blk >= num_blocks)
+                return pa::fail(PA_ERR_ARG, "sequence %lld: block_tables[%lld] = %lld outside [0, %lld)",
+                                (long long)b, (long long)i, (long long)blk, (long long)num_blocks);
+        }
+    }
+    return PA_OK;
+}
+
+const char* paged_attn_strerror(int status) {
+    switch (status) {
+        case PA_OK: return "success";
+        case PA_ERR_NULL: return "a required tensor or data pointer is NULL";
+        case PA_ERR_DTYPE: return "a tensor has the wrong dtype";
+        case PA_ERR_SHAPE: return "tensor ranks or sizes are inconsistent";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_LAYOUT: return "unsupported memory layout (strides or alignment)";
+        case PA_ERR_CAPTURE: return "workspace must grow while the stream is capturing";
+        case PA_ERR_HIP: return "HIP runtime error";
+        case PA_ERR_NOMEM: return "out of device memory";
+        case PA_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+const char* paged_attn_last_error(void) { return pa::g_last_error; }
+
+}  // extern "C"

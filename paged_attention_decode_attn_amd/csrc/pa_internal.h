@@ -1,0 +1,46 @@
+// Internal interface between the host-side validation/planning code
+// (pa_host.cpp, plain C++) and the HIP launch code (pa_device.hip).
+#pragma once
+
+#include <cstdint>
+
+#include "paged_attn.h"
+
+namespace pa {
+
+// A fully validated call, with every stride converted to the units the
+// kernels use.  Element strides unless the name says bytes.
+struct Problem {
+    int64_t B, Qmax, Hq, Hkv, G, D, NB, W;
+    bool fp8;
+    float scale;
+
+    const void* q;  int64_t q_sb, q_st, q_sh;          // bf16 elements
+    void* out;      int64_t o_sb, o_st, o_sh;          // bf16 elements
+    const void* k;  int64_t k_sblk, k_stok, k_sh;      // bytes
+    const void* v;  int64_t v_sblk, v_stok, v_sh;      // bytes
+    const float* ks; int64_t ks_sblk, ks_sh;           // fp32 elements (slot stride 1)
+    const float* vs; int64_t vs_sblk, vs_sh;
+    const int32_t* bt; int64_t bt_sb;                  // int32 elements
+    const int32_t* ctx; int64_t ctx_s;
+    const int32_t* ql;  int64_t ql_s;                  // ql may be null
+};
+
+// Host-only validation shared by paged_attn_check and paged_attn_decode.
+int validate(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+             const pa_tensor* block_tables, const pa_tensor* context_lens,
+             const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+             const pa_tensor* v_scale, const pa_tensor* out, Problem* pr);
+
+// The split-context plan (see pa_plan in paged_attn.h).
+int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W,
+              bool fp8, int32_t num_cus, pa_plan* plan);
+
+// Records a failure description for paged_attn_last_error() and returns `status`.
+int fail(int status, const char* fmt, ...);
+
+constexpr int kChunk = 32;            // tokens per inner-loop step (two blocks)
+constexpr int kMaxPartitionTokens = 1024;   // one 64-entry block-id window per wave
+constexpr int kMaxPartitions = 8192;
+
+}  // namespace pa

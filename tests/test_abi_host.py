@@ -1,0 +1,218 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, validates descriptors, plans partitions and checks
+metadata.  No compute entry point is called here."""
+import ctypes
+
+import pytest
+import torch
+
+from paged_attention_decode_attn_amd import binding as B
+
+NB, HKV, D, BQ, QMAX, HQ, W = 10, 2, 128, 3, 2, 8, 4
+
+
+def _tensors(kv="bf16", d=D, hq=HQ, hkv=HKV, qmax=QMAX, block=16):
+    q = torch.zeros(BQ, qmax, hq, d, dtype=torch.bfloat16)
+    cdt = torch.uint8 if kv == "fp8" else torch.bfloat16
+    kc = torch.zeros(NB, block, hkv, d, dtype=cdt)
+    vc = torch.zeros(NB, block, hkv, d, dtype=cdt)
+    bt = torch.zeros(BQ, W, dtype=torch.int32)
+    ctx = torch.ones(BQ, dtype=torch.int32)
+    ql = torch.ones(BQ, dtype=torch.int32)
+    ks = vs = None
+    if kv == "fp8":
+        ks = torch.ones(NB, hkv, 16).permute(0, 2, 1)
+        vs = torch.ones(NB, hkv, 16).permute(0, 2, 1)
+    out = torch.empty_like(q)
+    return dict(q=q, k_cache=kc, v_cache=vc, block_tables=bt, context_lens=ctx, query_lens=ql,
+                scale=0.125, k_scale=ks, v_scale=vs, out=out)
+
+
+def _check(**kw):
+    return B.paged_attn_check(**kw)
+
+
+def test_library_exports_every_header_function():
+    L = B.lib()
+    names = B.header_functions()
+    assert "paged_attn_decode" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_valid_descriptors_pass_bf16_and_fp8():
+    assert _check(**_tensors()) == B.PA_OK
+    assert _check(**_tensors("fp8")) == B.PA_OK
+    t = _tensors(qmax=1)
+    t["q"] = t["q"][:, 0]
+    t["out"] = t["out"][:, 0]                      # rank-3 q: Qmax = 1
+    assert _check(**t) == B.PA_OK
+    t = _tensors()
+    t["query_lens"] = None                         # NULL query_lens: all Qmax
+    assert _check(**t) == B.PA_OK
+    t = _tensors(d=64, hq=64, hkv=8, qmax=1)
+    assert _check(**t) == B.PA_OK
+
+
+def _status(name):
+    return {v: k for k, v in B.STATUS_NAMES.items()}[name]
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda t: t.update(q=None), "PA_ERR_NULL"),
+    (lambda t: t.update(out=None), "PA_ERR_NULL"),
+    (lambda t: t.update(k_cache=None), "PA_ERR_NULL"),
+    (lambda t: t.update(q=t["q"].float()), "PA_ERR_DTYPE"),
+    (lambda t: t.update(out=t["out"].half()), "PA_ERR_DTYPE"),
+    (lambda t: t.update(block_tables=t["block_tables"].long()), "PA_ERR_DTYPE"),
+    (lambda t: t.update(context_lens=t["context_lens"].long()), "PA_ERR_DTYPE"),
+    (lambda t: t.update(v_cache=t["v_cache"].view(torch.int16).view(torch.uint8)[..., :D]), "PA_ERR_DTYPE"),
+    (lambda t: t.update(out=t["out"][:2]), "PA_ERR_SHAPE"),
+    (lambda t: t.update(block_tables=t["block_tables"][:2]), "PA_ERR_SHAPE"),
+    (lambda t: t.update(context_lens=t["context_lens"][:1]), "PA_ERR_SHAPE"),
+    (lambda t: t.update(query_lens=t["query_lens"][:2]), "PA_ERR_SHAPE"),
+    (lambda t: t.update(v_cache=t["v_cache"][:5]), "PA_ERR_SHAPE"),
+    (lambda t: t.update(k_scale=torch.ones(NB, HKV, 16).permute(0, 2, 1)), "PA_ERR_ARG"),
+    (lambda t: t.update(scale=float("nan")), "PA_ERR_ARG"),
+    (lambda t: t.update(scale=float("inf")), "PA_ERR_ARG"),
+    (lambda t: t.update(q=t["q"].transpose(2, 3).contiguous().transpose(2, 3),
+                        out=t["out"]), "PA_ERR_LAYOUT"),
+    (lambda t: t.update(k_cache=torch.zeros(NB * 16 * HKV * D + 1, dtype=torch.bfloat16)[1:]
+                        .view(NB, 16, HKV, D)), "PA_ERR_LAYOUT"),      # base off by 2 bytes
+    (lambda t: t.update(v_cache=torch.zeros(NB, 16, HKV, D + 4, dtype=torch.bfloat16)[..., :D]),
+     "PA_ERR_LAYOUT"),                                                  # token stride 264 B
+    (lambda t: t.update(block_tables=torch.zeros(W, BQ, dtype=torch.int32).t()), "PA_ERR_LAYOUT"),
+])
+def test_validation_errors(mutate, expect):
+    t = _tensors()
+    mutate(t)
+    assert _check(**t) == _status(expect)
+    assert B.paged_attn_last_error() != ""
+    assert B.paged_attn_strerror(_status(expect)) not in ("", "unknown status")
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(block=8), "PA_ERR_UNSUPPORTED"),
+    (dict(d=96), "PA_ERR_UNSUPPORTED"),
+    (dict(d=256), "PA_ERR_UNSUPPORTED"),
+    (dict(hq=6, hkv=4), "PA_ERR_UNSUPPORTED"),
+    (dict(hq=40, hkv=1, qmax=2), "PA_ERR_UNSUPPORTED"),      # 80 rows per kv head
+])
+def test_unsupported_configurations(kw, expect):
+    assert _check(**_tensors(**kw)) == _status(expect)
+
+
+def test_rows_limit_is_inclusive():
+    assert _check(**_tensors(hq=32, hkv=1, qmax=2)) == B.PA_OK      # exactly 64 rows
+
+
+def test_fp8_scale_rules():
+    t = _tensors("fp8")
+    t["k_scale"] = None
+    assert _check(**t) == _status("PA_ERR_NULL")
+    t = _tensors("fp8")
+    t["v_scale"] = torch.ones(NB, 16, HKV)                            # slot dim not contiguous
+    assert _check(**t) == _status("PA_ERR_LAYOUT")
+    t = _tensors("fp8")
+    t["k_scale"] = torch.ones(NB, 8, HKV).permute(0, 2, 1)            # wrong shape
+    assert _check(**t) == _status("PA_ERR_SHAPE")
+    t = _tensors("fp8")
+    t["k_scale"] = t["k_scale"].double()
+    assert _check(**t) == _status("PA_ERR_DTYPE")
+    t = _tensors("fp8")
+    t["v_cache"] = t["v_cache"].view(torch.int16).view(torch.bfloat16) if False else \
+        torch.zeros(NB, 16, HKV, D, dtype=torch.bfloat16)            # mixed K/V dtypes
+    assert _check(**t) == _status("PA_ERR_DTYPE")
+
+
+def test_misaligned_base_pointer():
+    t = _tensors()
+    d = [B.describe(t[k]) for k in ("q", "k_cache", "v_cache", "block_tables", "context_lens",
+                                    "query_lens", "out")]
+    assert B.paged_attn_check_descriptors(d[0], d[1], d[2], d[3], d[4], d[5], 0.1, None, None, d[6]) == 0
+    d[1].data = d[1].data + 2
+    assert B.paged_attn_check_descriptors(d[0], d[1], d[2], d[3], d[4], d[5], 0.1, None, None,
+                                          d[6]) == _status("PA_ERR_LAYOUT")
+    d[1].data = None
+    assert B.paged_attn_check_descriptors(d[0], d[1], d[2], d[3], d[4], d[5], 0.1, None, None,
+                                          d[6]) == _status("PA_ERR_NULL")
+
+
+def test_empty_batch_is_valid():
+    t = _tensors()
+    for k in ("q", "out", "block_tables", "context_lens", "query_lens"):
+        t[k] = t[k][:0]
+    assert _check(**t) == B.PA_OK
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 32, 8, 128, 1, 32), (4, 32, 8, 128, 1, 512), (1, 64, 8, 128, 1, 8192),
+    (16, 64, 8, 64, 1, 2048), (64, 64, 8, 128, 2, 1024), (3, 8, 8, 64, 4, 1),
+    (1, 4, 1, 128, 1, 1 << 16), (0, 8, 2, 128, 1, 4),
+])
+def test_plan_properties(shape):
+    b, hq, hkv, d, ql, w = shape
+    p = B.paged_attn_plan(b, hq, hkv, d, ql, w)
+    T, P = p["partition_tokens"], p["num_partitions"]
+    assert T % 32 == 0 and 32 <= T <= 1024
+    assert P * T >= 16 * w and (P - 1) * T < 16 * w          # covers the table, no empty tail
+    assert p["rows"] == hq // hkv * ql and p["row_tiles"] == (p["rows"] + 15) // 16
+    assert p["partition_groups"] == b * hkv * P
+    assert (p["reduce_groups"] > 0) == (P > 1 and b > 0) or b == 0
+    if P > 1:
+        assert p["workspace_bytes"] >= b * ql * hq * P * (d + 1) * 4
+    assert p == B.paged_attn_plan(b, hq, hkv, d, ql, w)      # deterministic
+
+
+def test_plan_fills_the_device_for_long_single_sequence():
+    p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=256)
+    assert p["partition_groups"] >= 1024                       # at least one wave per SIMD
+    small = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=8)
+    assert small["partition_groups"] <= p["partition_groups"]
+
+
+def test_partition_override_and_reset():
+    try:
+        B.paged_attn_set_partition_tokens(64)
+        p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
+        assert p["partition_tokens"] == 64 and p["num_partitions"] == 8
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_set_partition_tokens(48)
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_set_partition_tokens(2048)
+    finally:
+        B.paged_attn_set_partition_tokens(0)
+    assert B.paged_attn_plan(1, 32, 8, 128, 1, 32)["partition_tokens"] == 32
+
+
+def test_plan_rejects_bad_sizes():
+    with pytest.raises(B.PagedAttnError):
+        B.paged_attn_plan(1, 6, 4, 128, 1, 4)
+    with pytest.raises(B.PagedAttnError):
+        B.paged_attn_plan(1, 8, 8, 128, 1, 0)
+
+
+def test_check_metadata():
+    ctx = torch.tensor([5, 33], dtype=torch.int32)
+    ql = torch.tensor([1, 2], dtype=torch.int32)
+    bt = torch.tensor([[3, 9, 9], [0, 1, 2]], dtype=torch.int32)
+    B.paged_attn_check_metadata(ctx, ql, bt, 2, 10)
+    B.paged_attn_check_metadata(ctx, None, bt, 2, 10)
+    bad = [
+        (torch.tensor([5, 49], dtype=torch.int32), ql, bt),              # L > 16 W
+        (ctx, torch.tensor([1, 3], dtype=torch.int32), bt),              # n > Qmax
+        (torch.tensor([0, 33], dtype=torch.int32), ql, bt),              # n > L
+        (ctx, ql, torch.tensor([[3, 9, 9], [0, 10, 2]], dtype=torch.int32)),   # id >= NB
+        (ctx, ql, torch.tensor([[-1, 9, 9], [0, 1, 2]], dtype=torch.int32)),   # id < 0
+    ]
+    for c, q, t in bad:
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_check_metadata(c, q, t, 2, 10)
+    # entries past ceil(L / 16) are never read, so anything goes there
+    B.paged_attn_check_metadata(ctx, ql, torch.tensor([[3, -7, 99], [0, 1, 2]], dtype=torch.int32), 2, 10)
+
+
+def test_strerror_covers_every_status():
+    for code in B.STATUS_NAMES:
+        assert B.paged_attn_strerror(code) != "unknown status"
+    assert B.paged_attn_strerror(12345) == "unknown status"

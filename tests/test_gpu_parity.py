@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case prints its name, shapes and partition size before it touches the
+GPU.  Tolerance: |gpu - ref| <= 1e-2 + 1e-2 |ref| on every produced element
+(bf16 output vs the float64 oracle on the same stored bytes), plus a
+relative-L2 bound of 1e-2; rows past query_len must keep a canary.
+"""
+import numpy as np
+import pytest
+import torch
+
+from _parity import check, compare, note, oracle_out, run_gpu, small
+from paged_attention_decode_attn_amd import binding as B
+from paged_attention_decode_attn_amd.workloads import CONFIGS, generate
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# the five workload shapes at oracle-friendly sizes (several tiles, ragged tails)
+# --------------------------------------------------------------------------
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "llama3_8b": small("llama3_8b", ctx_lo=100, ctx_hi=1500, pool_blocks=400),
+    "long_ctx": small("long_ctx", ctx_lo=20001, ctx_hi=20001, pool_blocks=1300),
+    "fp8": small("fp8", batch=5, ctx_lo=100, ctx_hi=3000, pool_blocks=1000),
+    "mtp_verify": small("mtp_verify", batch=6, ctx_lo=2, ctx_hi=2000, pool_blocks=800),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("T", [0, 32, 256, 1024])
+def test_config_shapes(name, T):
+    w = generate(SMALL[name])
+    check(w, T, label=f"{name}/T{T}")
+
+
+# --------------------------------------------------------------------------
+# edge suite
+# --------------------------------------------------------------------------
+EDGE_CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1023, 1024, 1025]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("T", [0, 32, 64, 1024])
+def test_context_length_edges(kv, T):
+    spec = CONFIGS["llama3_8b"].replace(batch=len(EDGE_CTX), ctx_lo=1, ctx_hi=1025,
+                                        pool_blocks=300, kv_dtype=kv)
+    w = generate(spec, context_lens=EDGE_CTX)
+    check(w, T, label=f"edges/{kv}/T{T}")
+
+
+@pytest.mark.parametrize("T", [0, 32, 64])
+def test_two_query_rows_short_and_ragged(T):
+    ctx = [2, 2, 3, 17, 33, 64, 100, 5]
+    ql = [2, 1, 0, 2, 1, 2, 0, 2]
+    spec = CONFIGS["mtp_verify"].replace(batch=8, ctx_lo=2, ctx_hi=100, pool_blocks=64)
+    w = generate(spec, context_lens=ctx, query_lens=ql)
+    check(w, T, label=f"qlen2-ragged/T{T}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv,qlen", [(8, 8, 1), (8, 1, 1), (32, 8, 1), (64, 4, 1),
+                                         (64, 8, 2), (16, 1, 2), (16, 1, 3), (32, 1, 2),
+                                         (64, 1, 1), (12, 3, 3)])
+def test_head_groupings(kv, d, hq, hkv, qlen):
+    spec = CONFIGS["mtp_verify"].replace(batch=3, qlen=qlen, hq=hq, hkv=hkv, head_dim=d,
+                                         kv_dtype=kv, ctx_lo=qlen, ctx_hi=300, pool_blocks=64)
+    w = generate(spec)
+    check(w, 0, label=f"heads{hq}/{hkv}/q{qlen}/d{d}/{kv}")
+    check(w, 64, label=f"heads{hq}/{hkv}/q{qlen}/d{d}/{kv}/T64")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+def test_nan_in_unread_memory_never_reaches_output(kv):
+    spec = CONFIGS["mtp_verify"].replace(batch=5, ctx_lo=2, ctx_hi=500, pool_blocks=200, kv_dtype=kv)
+    w = generate(spec, poison=True)
+    for T in (0, 32, 96):
+        check(w, T, label=f"poison/{kv}/T{T}")
+
+
+def test_shared_and_duplicated_blocks():
+    spec = CONFIGS["mtp_verify"].replace(batch=3, ctx_lo=40, ctx_hi=200, pool_blocks=64)
+    w = generate(spec, context_lens=[200, 180, 120])
+    t = w.block_tables.clone()
+    t[1, :5] = t[0, :5]           # shared prefix
+    t[2, 3] = t[2, 1]             # duplicated entry within a row
+    w.block_tables = t
+    for T in (0, 32):
+        check(w, T, label=f"shared/T{T}")
+
+
+@pytest.mark.parametrize("factor", [4.0, 8.0])
+def test_sharpened_queries(factor):
+    for name in ("llama3_8b", "fp8", "mtp_verify"):
+        w = generate(SMALL[name])
+        w.q = (w.q.float() * factor).to(torch.bfloat16)     # power of two: exact
+        check(w, 0, label=f"sharp{factor}/{name}")
+        check(w, 64, label=f"sharp{factor}/{name}/T64")
+
+
+def test_huge_logit_spread_between_heads():
+    w = generate(SMALL["llama3_8b"].replace(batch=2))
+    q = w.q.float()
+    q[:, :, 0] *= 64.0
+    w.q = q.to(torch.bfloat16)
+    check(w, 0, label="logit-spread")
+    check(w, 32, label="logit-spread/T32")
+
+
+def test_rank3_query_and_strided_output():
+    w = generate(SMALL["llama3_8b"])
+    dev = w.to("cuda")
+    big = torch.empty(w.q.shape[0], 3, w.q.shape[2], w.q.shape[3] + 64, dtype=torch.bfloat16,
+                      device="cuda")
+    big.fill_(7.0)
+    out = big[:, 1, :, 32:32 + w.q.shape[3]]                 # rank 3, strided, 64 B aligned
+    q3 = dev.q[:, 0]
+    note("[gpu] rank3/strided")
+    B.paged_attn_decode(q3, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                        None, w.scale, None, None, out)
+    torch.cuda.synchronize()
+    ref = oracle_out(w)
+    compare(out[:, None], ref, torch.ones(w.q.shape[0], dtype=torch.int32), label="rank3")
+    assert torch.all(big[:, 0] == 7.0) and torch.all(big[:, 2] == 7.0)
+    assert torch.all(big[:, 1, :, :32] == 7.0) and torch.all(big[:, 1, :, 32 + w.q.shape[3]:] == 7.0)
+
+
+def test_empty_batch_is_a_no_op():
+    w = generate(SMALL["tiny"]).to("cuda")
+    note("[gpu] empty batch")
+    out = torch.empty_like(w.q[:0])
+    B.paged_attn_decode(w.q[:0], w.k_cache, w.v_cache, w.block_tables[:0], w.context_lens[:0],
+                        w.query_lens[:0], w.scale, None, None, out)
+    torch.cuda.synchronize()
+
+
+def test_fp8_every_code_decodes_exactly():
+    # single-token context: the output row is the (scaled) value row itself
+    spec = CONFIGS["fp8"].replace(batch=1, hq=4, hkv=4, head_dim=64, ctx_lo=1, ctx_hi=16,
+                                  pool_blocks=4)
+    w = generate(spec, context_lens=[1])
+    blk = int(w.block_tables[0, 0])
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(4, 64)
+    w.v_cache[blk, 0] = codes
+    w.v_scale[blk, 0] = 1.0
+    note("[gpu] fp8 codes")
+    out = run_gpu(w).float().cpu()[0, 0]                       # [4 heads, 64]
+    expect = codes.view(torch.float8_e4m3fn).float()
+    nan = torch.isnan(expect)
+    assert torch.equal(torch.isnan(out), nan)
+    assert torch.equal(out[~nan], expect[~nan])
+    # a power-of-two scale stays exact
+    w.v_scale[blk, 0] = 0.25
+    out = run_gpu(w).float().cpu()[0, 0]
+    assert torch.equal(out[~nan], expect[~nan] * 0.25)
+
+
+def test_bf16_single_token_returns_value_row_exactly():
+    spec = CONFIGS["tiny"].replace(ctx_lo=1, ctx_hi=1, pool_blocks=4)
+    w = generate(spec)
+    note("[gpu] bf16 single token")
+    out = run_gpu(w).cpu()[0, 0]                                # [32, 128]
+    v = w.v_cache[int(w.block_tables[0, 0]), 0]                 # [8, 128]
+    assert torch.equal(out.view(torch.int16), v.repeat_interleave(4, dim=0).view(torch.int16))
+
+
+def test_repeat_calls_are_bitwise_identical_and_stream_ordered():
+    w = generate(SMALL["mtp_verify"]).to("cuda")
+    s = torch.cuda.Stream()
+    outs = []
+    note("[gpu] determinism / side stream")
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            o = torch.empty_like(w.q)
+            B.paged_attn_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                                w.query_lens, w.scale, None, None, o)
+            outs.append(o)
+    s.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_argument_errors_launch_nothing():
+    w = generate(SMALL["tiny"]).to("cuda")
+    out = torch.full_like(w.q, 3.0)
+    note("[gpu] argument errors")
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                            w.query_lens, float("nan"), None, None, out)
+    assert e.value.name == "PA_ERR_ARG"
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_decode(w.q, w.k_cache, w.v_cache.float(), w.block_tables, w.context_lens,
+                            w.query_lens, w.scale, None, None, out)
+    assert e.value.name == "PA_ERR_DTYPE"
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+def test_profile_events_measure_both_kernels():
+    w = generate(SMALL["llama3_8b"]).to("cuda")
+    note("[gpu] profile events")
+    B.paged_attn_profile_begin(4)
+    for _ in range(3):
+        B.paged_attn_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                            w.query_lens, w.scale)
+    r = B.paged_attn_profile_end()
+    assert r["calls"] == 3 and r["partition_ms"] > 0 and r["reduce_ms"] > 0
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark
+# times, checked on sampled sequences
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,subset", [
+    ("tiny", None), ("llama3_8b", None), ("long_ctx", None), ("fp8", [0, 7, 15]),
+    ("mtp_verify", [0, 21, 63]),
+])
+def test_full_size_configs_sampled(name, subset):
+    w = generate(CONFIGS[name])
+    check(w, 0, batch_subset=subset, label=f"full/{name}")
