@@ -149,16 +149,22 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
 /*
  * Split-context plan: how paged_attn_decode divides each (sequence, kv
  * head) pair's context into partitions of partition_tokens tokens (a
- * multiple of 32), chosen from shapes and the device's compute-unit count
- * only (never from device data), so that one call fills the GPU and short
- * contexts are not over-split.
+ * multiple of 32, at most 1024), each run by one wave; the waves serving
+ * heads_per_group adjacent kv heads of a partition form one workgroup.
+ * Chosen from shapes and the device's compute-unit count only (never from
+ * device data), so that one call fills the GPU and short contexts are not
+ * over-split.  The partition kernel is persistent: it launches at most as
+ * many workgroups as the device holds at once, each looping over its share
+ * of the partition_groups items that are non-empty for the actual lengths.
  */
 typedef struct pa_plan {
-    int32_t partition_tokens;   /* tokens per partition                    */
+    int32_t partition_tokens;   /* tokens per partition (one wave)         */
     int32_t num_partitions;     /* ceil(16 * W / partition_tokens)         */
     int32_t rows;               /* (Hq / Hkv) * Qmax query rows per kv head */
     int32_t row_tiles;          /* ceil(rows / 16)                         */
-    int64_t partition_groups;   /* workgroups of the partition kernel      */
+    int32_t heads_per_group;    /* kv heads (one wave each) per workgroup  */
+    int32_t reduce_threads;     /* threads per merge workgroup             */
+    int64_t partition_groups;   /* (sequence, partition, head group) items */
     int64_t reduce_groups;      /* workgroups of the merge kernel (0: none) */
     int64_t workspace_bytes;    /* fp32 partial outputs + log-sum-exp      */
 } pa_plan;
@@ -174,11 +180,20 @@ int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t he
 
 /*
  * paged_attn_set_partition_tokens -- override the planner's partition size
- * for every later call in the process (tokens; a positive multiple of 32),
- * or 0 to return to the automatic choice.  A test and tuning hook; not
- * synchronised with concurrent calls.
+ * for every later call in the process (a positive multiple of 32 up to
+ * 1024 tokens), or 0 to return to the automatic choice.  A test and tuning
+ * hook; not synchronised with concurrent calls.
  */
 int paged_attn_set_partition_tokens(int32_t tokens);
+
+/*
+ * paged_attn_set_heads_per_group -- override the planner's kv heads per
+ * partition workgroup for every later call in the process (1..8; it must
+ * divide kv_heads, and be at most 4 when (Hq / Hkv) * Qmax > 16, or the call
+ * fails with PA_ERR_ARG), or 0 for the automatic choice.  A tuning hook;
+ * not synchronised with concurrent calls.
+ */
+int paged_attn_set_heads_per_group(int32_t heads);
 
 /*
  * paged_attn_reserve -- grow the current device's workspace for `stream`

@@ -17,7 +17,12 @@ from typing import Optional
 
 import torch
 
-from .build import LIB_PATH, INCLUDE
+from .build import INCLUDE
+from .build import LIB_PATH as _BUILT_LIB
+
+# PAGED_ATTN_LIB may name another build of the same library (A/B builds of
+# the same sources); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("PAGED_ATTN_LIB", _BUILT_LIB)
 
 PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3FN, PA_DTYPE_FP32, PA_DTYPE_INT32 = 1, 2, 3, 4
 PA_OK = 0
@@ -34,6 +39,7 @@ class PaTensor(ctypes.Structure):
 class PaPlan(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("rows", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+                ("heads_per_group", ctypes.c_int32), ("reduce_threads", ctypes.c_int32),
                 ("partition_groups", ctypes.c_int64), ("reduce_groups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
 
@@ -70,6 +76,7 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, ctypes.c_int32,
                                                                      ctypes.POINTER(PaPlan)]
                 L.paged_attn_set_partition_tokens.argtypes = [ctypes.c_int32]
+                L.paged_attn_set_heads_per_group.argtypes = [ctypes.c_int32]
                 L.paged_attn_reserve.argtypes = [ctypes.c_int64, ctypes.c_void_p]
                 i32p = ctypes.POINTER(ctypes.c_int32)
                 L.paged_attn_check_metadata.argtypes = [i32p, i32p, i32p] + [ctypes.c_int64] * 5
@@ -82,7 +89,8 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_last_error.argtypes = []
                 L.paged_attn_last_error.restype = ctypes.c_char_p
                 for name in ("paged_attn_decode", "paged_attn_check", "paged_attn_plan",
-                             "paged_attn_set_partition_tokens", "paged_attn_reserve",
+                             "paged_attn_set_partition_tokens", "paged_attn_set_heads_per_group",
+                             "paged_attn_reserve",
                              "paged_attn_check_metadata", "paged_attn_profile_begin",
                              "paged_attn_profile_end"):
                     getattr(L, name).restype = ctypes.c_int
@@ -190,6 +198,10 @@ def paged_attn_plan(batch, q_heads, kv_heads, head_dim, query_len, table_width,
 
 def paged_attn_set_partition_tokens(tokens: int) -> None:
     _raise(lib().paged_attn_set_partition_tokens(int(tokens)), "paged_attn_set_partition_tokens")
+
+
+def paged_attn_set_heads_per_group(heads: int) -> None:
+    _raise(lib().paged_attn_set_heads_per_group(int(heads)), "paged_attn_set_heads_per_group")
 
 
 def paged_attn_reserve(nbytes: int, stream=None) -> None:

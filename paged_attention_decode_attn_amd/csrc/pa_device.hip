@@ -36,9 +36,11 @@
 //    cache slots never reaches the output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -70,7 +72,7 @@ struct PartArgs {
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
     float* ws_o;     float* ws_lse;
     float scale_log2;
-    int32_t Hq, Hkv, G, Qmax, W, NB, T, P, rows;
+    int32_t B, Hq, Hkv, G, Qmax, W, NB, T, P, rows, HG;
 };
 
 struct RedArgs {
@@ -80,6 +82,11 @@ struct RedArgs {
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
     int32_t Hq, Qmax, W, T, P;
 };
+
+template <typename T>
+__device__ __forceinline__ T ldg(const char* p) {
+    return *reinterpret_cast<const T*>(p);
+}
 
 __device__ __forceinline__ unsigned bits(float x) { return __builtin_bit_cast(unsigned, x); }
 
@@ -118,23 +125,25 @@ template <int D, bool FP8, int NT> struct State {
 
 template <int D, bool FP8>
 __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, int bid_lane, int step,
-                                          int g, int grp, const unsigned (&koff)[Step<D, FP8>::KL],
-                                          const unsigned (&voff)[4]) {
+                                          int last_blk, int g, int grp,
+                                          const unsigned (&koff)[Step<D, FP8>::KL], const unsigned (&voff)[4]) {
     typedef typename VLoad<D, FP8>::T VT;
-    const int b0 = __builtin_amdgcn_readlane(bid_lane, 2 * step);
-    const int b1 = __builtin_amdgcn_readlane(bid_lane, 2 * step + 1);
+    // a step's second block may lie past the sequence: read its last block
+    // again instead (those positions are masked)
+    const int b0 = __builtin_amdgcn_readlane(bid_lane, min(2 * step, last_blk));
+    const int b1 = __builtin_amdgcn_readlane(bid_lane, min(2 * step + 1, last_blk));
     const char* kb0 = a.k + (int64_t)b0 * a.k_sblk + (int64_t)g * a.k_sh;
     const char* kb1 = a.k + (int64_t)b1 * a.k_sblk + (int64_t)g * a.k_sh;
     const char* vb0 = a.v + (int64_t)b0 * a.v_sblk + (int64_t)g * a.v_sh;
     const char* vb1 = a.v + (int64_t)b1 * a.v_sblk + (int64_t)g * a.v_sh;
 #pragma unroll
     for (int c = 0; c < Step<D, FP8>::KL; ++c) {
-        st.k[0][c] = *reinterpret_cast<const u32x4*>(kb0 + koff[c]);
-        st.k[1][c] = *reinterpret_cast<const u32x4*>(kb1 + koff[c]);
+        st.k[0][c] = ldg<u32x4>(kb0 + koff[c]);
+        st.k[1][c] = ldg<u32x4>(kb1 + koff[c]);
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        st.v[s] = *reinterpret_cast<const VT*>((s < 4 ? vb0 : vb1) + voff[s & 3]);
+        st.v[s] = ldg<VT>((s < 4 ? vb0 : vb1) + voff[s & 3]);
     if constexpr (FP8) {
         st.ksc[0] = *reinterpret_cast<const f32x4*>(a.ks + (int64_t)b0 * a.ks_sblk + (int64_t)g * a.ks_sh + 4 * grp);
         st.ksc[1] = *reinterpret_cast<const f32x4*>(a.ks + (int64_t)b1 * a.ks_sblk + (int64_t)g * a.ks_sh + 4 * grp);
@@ -312,53 +321,55 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
     }
 }
 
+// One work item = (sequence b, kv head g, partition p) of T tokens, run by
+// one wave: the partition's online-softmax state ends as the output row when
+// the sequence has a single partition, otherwise as the normalised fp32
+// partial output and its base-2 log-sum-exp for the merge kernel.
 template <int D, bool FP8, int NT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
-void partition_kernel(PartArgs a) {
+__device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, int p, int lane) {
     constexpr int J = D / 16;
     constexpr int KL = Step<D, FP8>::KL;
     constexpr int E = FP8 ? 1 : 2;
-    const int lane = threadIdx.x;
     const int n16 = lane & 15, grp = lane >> 4;
 
-    int64_t id = blockIdx.x;
-    const int p = (int)(id % a.P);
-    id /= a.P;
-    const int g = (int)(id % a.Hkv);
-    const int b = (int)(id / a.Hkv);
-
-    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
-    const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
-    if (L <= 0 || nq <= 0) return;
+    // Issue every start-up load at once: the sequence's lengths, this
+    // partition's block-table slice and the query fragments do not depend
+    // on each other, so the first K/V loads wait for one round trip only.
     const int tok0 = p * a.T;
-    if (tok0 >= L) return;
-    const int tok1 = min(L, tok0 + a.T);
-    const int nsteps = (tok1 - tok0 + 31) / 32;
-    const int nblk_seq = (L + 15) / 16;
-    const bool direct = (L + a.T - 1) / a.T == 1;
-
-    // block ids of this partition, one per lane (at most 64 blocks),
-    // clamped to the sequence's used blocks and to the pool
-    int bid_lane;
+    int bid_lane;        // block-table entry tok0/16 + lane (clamped to the table)
     {
-        const int idx = min(tok0 / 16 + lane, nblk_seq - 1);
+        const int idx = min(tok0 / 16 + lane, a.W - 1);
         const int v = a.bt[(int64_t)b * a.bt_sb + idx];
         bid_lane = min(max(v, 0), a.NB - 1);
     }
-
-    // query fragments: row r = 16*nt + n16 -> (t, h_local) = (r / G, r % G)
+    // query fragments: row r = 16*nt + n16 -> (t, h_local) = (r / G, r % G);
+    // rows t < Qmax are in bounds, rows past query_len are zeroed below
     u32x4 qf[NT][D / 32];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int row = 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
-        const bool rv = row < a.rows && t < nq;
         const char* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)t * a.q_st + (int64_t)(g * a.G + hl) * a.q_sh;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const int d0 = FP8 ? (D / 4) * grp + 8 * kk : 32 * kk + 8 * grp;
-            qf[nt][kk] = rv ? *reinterpret_cast<const u32x4*>(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
+            qf[nt][kk] = row < a.rows ? *reinterpret_cast<const u32x4*>(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
         }
+    }
+    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
+    const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+    if (L <= 0 || nq <= 0 || tok0 >= L) return;
+    const bool direct = (L + a.T - 1) / a.T == 1;
+    const int nsteps = (min(L, tok0 + a.T) - tok0 + 31) / 32;
+    // last block of the sequence relative to the slice: block-table entries
+    // past it are never used (their blocks are replaced by this one)
+    const int last_blk = (L + 15) / 16 - 1 - tok0 / 16;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int row = 16 * nt + n16;
+        if (row / a.G >= nq)
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) qf[nt][kk] = u32x4{0u, 0u, 0u, 0u};
     }
 
     unsigned koff[KL];
@@ -378,31 +389,33 @@ void partition_kernel(PartArgs a) {
         for (int j = 0; j < J; ++j) s.acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // two register buffers, next step's loads in flight during compute
-    // (one buffer when the row tiles leave no registers for a second)
+    // two register buffers: the next step's loads are in flight while the
+    // current step computes; straight-line code on every path keeps the
+    // memory-counter waits exact (one buffer when the row tiles leave no
+    // registers for a second)
     Step<D, FP8> bufA, bufB;
     if constexpr (NT > 2) {
         for (int st = 0; st < nsteps; ++st) {
-            load_step<D, FP8>(bufA, a, bid_lane, st, g, grp, koff, voff);
+            load_step<D, FP8>(bufA, a, bid_lane, st, last_blk, g, grp, koff, voff);
             compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
         }
     } else {
-    load_step<D, FP8>(bufA, a, bid_lane, 0, g, grp, koff, voff);
-    int st = 0;
-    while (st + 2 < nsteps) {
-        load_step<D, FP8>(bufB, a, bid_lane, st + 1, g, grp, koff, voff);
-        compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-        load_step<D, FP8>(bufA, a, bid_lane, st + 2, g, grp, koff, voff);
-        compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
-        st += 2;
-    }
-    if (st + 1 < nsteps) {
-        load_step<D, FP8>(bufB, a, bid_lane, st + 1, g, grp, koff, voff);
-        compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-        compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
-    } else {
-        compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-    }
+        load_step<D, FP8>(bufA, a, bid_lane, 0, last_blk, g, grp, koff, voff);
+        int st = 0;
+        while (st + 2 < nsteps) {
+            load_step<D, FP8>(bufB, a, bid_lane, st + 1, last_blk, g, grp, koff, voff);
+            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+            load_step<D, FP8>(bufA, a, bid_lane, st + 2, last_blk, g, grp, koff, voff);
+            compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+            st += 2;
+        }
+        if (st + 1 < nsteps) {
+            load_step<D, FP8>(bufB, a, bid_lane, st + 1, last_blk, g, grp, koff, voff);
+            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+            compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+        } else {
+            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        }
     }
 
     // epilogue: lane holds d = (D/16)*(4*grp + i) + j, j < D/16, of row 16*nt + n16
@@ -454,13 +467,80 @@ void partition_kernel(PartArgs a) {
     }
 }
 
+// Persistent partition kernel.  A workgroup is HG waves, wave w serving kv
+// head g0 + w of one (sequence, partition) item at a time, so the waves of a
+// CU read the adjacent head rows of the same tokens (whole contiguous token
+// rows of the cache).  As many workgroups run as the chip holds at once;
+// workgroup w takes items w, w + grid, w + 2 grid, ... of the list of
+// non-empty (sequence, partition) pairs times the head groups, so every
+// workgroup gets the same number of equal-sized items to within one,
+// whatever the ragged context lengths, and no slot is spent on empty
+// partitions.  Wave 0 scans the per-sequence partition counts into LDS;
+// every wave maps an item to its sequence with a 64-wide ballot over that
+// prefix (the items of a workgroup only increase).
+template <int D, bool FP8, int NT>
+__global__ __launch_bounds__(NT == 1 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(NT == 1 ? (FP8 && D == 64 ? 3 : 2) : 1)))
+void partition_kernel(PartArgs a) {
+    extern __shared__ int s_pre[];               // inclusive prefix of partitions per sequence
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave == 0) {
+        int carry = 0;
+        for (int b0 = 0; b0 < a.B; b0 += 64) {
+            const int b = b0 + lane;
+            int np = 0;
+            if (b < a.B) {
+                const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
+                const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+                np = (L > 0 && nq > 0) ? (L + a.T - 1) / a.T : 0;
+            }
+            int x = np;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o) x += y;
+            }
+            if (b < a.B) s_pre[b] = carry + x;
+            carry += __shfl(x, 63);
+        }
+    }
+    __syncthreads();
+    const int S = a.B > 0 ? s_pre[a.B - 1] : 0;  // non-empty (sequence, partition) pairs
+    const int ngrp = a.Hkv / a.HG;
+    const int total = S * ngrp;
+    int bbase = 0;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int sp = item / ngrp, g = (item - sp * ngrp) * a.HG + wave;
+        // sequence b = number of sequences whose inclusive prefix is <= sp
+        int b;
+        for (;;) {
+            const int idx = bbase + lane;
+            const bool le = idx < a.B && s_pre[idx] <= sp;
+            const int k = __popcll(__ballot(le));
+            if (k < 64) { b = bbase + k; break; }
+            bbase += 64;
+        }
+        bbase = b & ~63;
+        const int first = b > 0 ? s_pre[b - 1] : 0;
+        process_item<D, FP8, NT>(a, b, g, sp - first, lane);
+    }
+}
+
 // Merge of the partitions of one query row (b, t, h): log-sum-exp weights
 // in base 2, float32 throughout, bf16 round-to-nearest-even at the end.
+// blockDim.x = (D/4) columns x PS partition lanes; each partition lane runs
+// an online merge over partitions ps, ps + PS, ... with U loads in flight,
+// then the PS partial merges combine through LDS.
+constexpr int kRedMaxThreads = 1024;
+constexpr int kRedUnroll = 4;
+
 template <int D>
-__global__ __launch_bounds__(256) void reduce_kernel(RedArgs a) {
-    constexpr int V4 = D / 4;        // float4 columns of a row
-    constexpr int PS = 256 / V4;     // partitions read side by side
+__global__ __launch_bounds__(kRedMaxThreads) void reduce_kernel(RedArgs a) {
+    constexpr int V4 = D / 4;
+    constexpr int U = kRedUnroll;
     const int tid = threadIdx.x;
+    const int PS = blockDim.x / V4;
     int64_t id = blockIdx.x;
     const int h = (int)(id % a.Hq);
     id /= a.Hq;
@@ -475,38 +555,58 @@ __global__ __launch_bounds__(256) void reduce_kernel(RedArgs a) {
     const float* lse = a.ws_lse + rowg * a.P;
     const float* wo = a.ws_o + rowg * a.P * D;
 
-    __shared__ float smax[4];
-    __shared__ f32x4 sacc[PS][V4];
-    __shared__ float swt[PS];
-
-    float mx = -__builtin_inff();
-    for (int p = tid; p < np; p += 256) mx = fmaxf(mx, lse[p]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((tid & 63) == 0) smax[tid >> 6] = mx;
-    __syncthreads();
-    float M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
-    if (M == -__builtin_inff()) M = 0.f;
+    __shared__ float sm[kRedMaxThreads / V4], sw[kRedMaxThreads / V4];
+    __shared__ f32x4 sacc[kRedMaxThreads / V4][V4];
 
     const int d4 = tid % V4, ps = tid / V4;
+    const float ninf = -__builtin_inff();
+    float m = ninf, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    for (int p = ps; p < np; p += PS) {
-        const float w = __builtin_amdgcn_exp2f(lse[p] - M);
-        const f32x4 o = *reinterpret_cast<const f32x4*>(wo + (int64_t)p * D + 4 * d4);
-        wsum += w;
-        acc += w * o;
+    for (int p0 = ps; p0 < np; p0 += PS * U) {
+        float l[U];
+        f32x4 o[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * PS;
+            if (p < np) {
+                l[u] = lse[p];
+                o[u] = *reinterpret_cast<const f32x4*>(wo + (int64_t)p * D + 4 * d4);
+            } else {
+                l[u] = ninf;
+                o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mn = fmaxf(mn, l[u]);
+        const float mu = mn == ninf ? 0.f : mn;
+        const float c = __builtin_amdgcn_exp2f(m - mu);
+        wsum *= c;
+        acc *= c;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = __builtin_amdgcn_exp2f(l[u] - mu);
+            wsum += w;
+            acc += w * o[u];
+        }
+        m = mn;
+    }
+    if (d4 == 0) {
+        sm[ps] = m;
+        sw[ps] = wsum;
     }
     sacc[ps][d4] = acc;
-    if (d4 == 0) swt[ps] = wsum;
     __syncthreads();
     if (ps == 0) {
-        f32x4 tot = sacc[0][d4];
-        float wt = swt[0];
-#pragma unroll
-        for (int q = 1; q < PS; ++q) {
-            tot += sacc[q][d4];
-            wt += swt[q];
+        float M = sm[0];
+        for (int q = 1; q < PS; ++q) M = fmaxf(M, sm[q]);
+        const float Mu = M == ninf ? 0.f : M;
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+        float wt = 0.f;
+        for (int q = 0; q < PS; ++q) {
+            const float c = __builtin_amdgcn_exp2f(sm[q] - Mu);
+            tot += c * sacc[q][d4];
+            wt += c * sw[q];
         }
         const float inv = wt > 0.f ? 1.f / wt : 0.f;
         u32x2 w;
@@ -578,24 +678,38 @@ int get_workspace(int dev, void* stream, size_t need, void** out) {
     return PA_OK;
 }
 
-template <int D, bool FP8>
-void launch_partition_d(int nt, dim3 grid, hipStream_t s, const PartArgs& a) {
-    switch (nt) {
-        case 1: hipLaunchKernelGGL((partition_kernel<D, FP8, 1>), grid, dim3(64), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((partition_kernel<D, FP8, 2>), grid, dim3(64), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((partition_kernel<D, FP8, 3>), grid, dim3(64), 0, s, a); break;
-        default: hipLaunchKernelGGL((partition_kernel<D, FP8, 4>), grid, dim3(64), 0, s, a); break;
+template <int D, bool FP8, int NT>
+const void* kernel_of() { return reinterpret_cast<const void*>(&partition_kernel<D, FP8, NT>); }
+
+const void* partition_kernel_of(int D, bool fp8, int nt) {
+    if (D == 128) {
+        if (fp8) return nt == 1 ? kernel_of<128, true, 1>() : nt == 2 ? kernel_of<128, true, 2>()
+                      : nt == 3 ? kernel_of<128, true, 3>() : kernel_of<128, true, 4>();
+        return nt == 1 ? kernel_of<128, false, 1>() : nt == 2 ? kernel_of<128, false, 2>()
+             : nt == 3 ? kernel_of<128, false, 3>() : kernel_of<128, false, 4>();
     }
+    if (fp8) return nt == 1 ? kernel_of<64, true, 1>() : nt == 2 ? kernel_of<64, true, 2>()
+                  : nt == 3 ? kernel_of<64, true, 3>() : kernel_of<64, true, 4>();
+    return nt == 1 ? kernel_of<64, false, 1>() : nt == 2 ? kernel_of<64, false, 2>()
+         : nt == 3 ? kernel_of<64, false, 3>() : kernel_of<64, false, 4>();
 }
 
-void launch_partition(int D, bool fp8, int nt, dim3 grid, hipStream_t s, const PartArgs& a) {
-    if (D == 128) {
-        if (fp8) launch_partition_d<128, true>(nt, grid, s, a);
-        else launch_partition_d<128, false>(nt, grid, s, a);
-    } else {
-        if (fp8) launch_partition_d<64, true>(nt, grid, s, a);
-        else launch_partition_d<64, false>(nt, grid, s, a);
+// Resident workgroups per CU for a kernel variant, block size and LDS size
+// (cached; the occupancy query is host-only).
+std::map<std::tuple<const void*, int, int, size_t>, int> g_occ;
+
+int resident_groups_per_cu(const void* fn, int dev, int threads, size_t lds) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    const auto key = std::make_tuple(fn, dev, threads, lds);
+    auto it = g_occ.find(key);
+    if (it != g_occ.end()) return it->second;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess || nb < 1) {
+        (void)hipGetLastError();
+        nb = 1;
     }
+    g_occ[key] = nb;
+    return nb;
 }
 
 }  // namespace
@@ -624,6 +738,11 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         return st;
 
     const int64_t rows_total = pr.B * pr.Qmax * pr.Hq;
+    const size_t lds = (size_t)pr.B * sizeof(int);
+    const void* fn = partition_kernel_of((int)pr.D, pr.fp8, plan.row_tiles);
+    const int HG = plan.heads_per_group;
+    const int64_t slots = (int64_t)resident_groups_per_cu(fn, dev, 64 * HG, lds) * device_cus(dev);
+    const int64_t groups = std::min<int64_t>(slots, plan.partition_groups);
     PartArgs a;
     a.q = static_cast<const char*>(pr.q); a.q_sb = pr.q_sb * 2; a.q_st = pr.q_st * 2; a.q_sh = pr.q_sh * 2;
     a.k = static_cast<const char*>(pr.k); a.k_sblk = pr.k_sblk; a.k_stok = pr.k_stok; a.k_sh = pr.k_sh;
@@ -635,11 +754,12 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
     a.ql = pr.ql; a.ql_s = pr.ql_s;
     a.out = static_cast<char*>(pr.out); a.o_sb = pr.o_sb * 2; a.o_st = pr.o_st * 2; a.o_sh = pr.o_sh * 2;
     a.ws_o = static_cast<float*>(ws);
-    a.ws_lse = ws ? static_cast<float*>(ws) + rows_total * plan.num_partitions * pr.D : nullptr;
+    a.ws_lse = a.ws_o + rows_total * plan.num_partitions * pr.D;
     a.scale_log2 = pr.scale * kLog2e;
-    a.Hq = (int32_t)pr.Hq; a.Hkv = (int32_t)pr.Hkv; a.G = (int32_t)pr.G; a.Qmax = (int32_t)pr.Qmax;
+    a.B = (int32_t)pr.B; a.Hq = (int32_t)pr.Hq; a.Hkv = (int32_t)pr.Hkv; a.G = (int32_t)pr.G; a.Qmax = (int32_t)pr.Qmax;
     a.W = (int32_t)pr.W; a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
-    a.T = plan.partition_tokens; a.P = plan.num_partitions; a.rows = plan.rows;
+    a.T = plan.partition_tokens; a.P = plan.num_partitions; a.rows = plan.rows; a.HG = HG;
+
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr;
@@ -652,7 +772,11 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         }
     }
     if (e0) (void)hipEventRecord(e0, s);
-    launch_partition((int)pr.D, pr.fp8, plan.row_tiles, dim3((unsigned)plan.partition_groups), s, a);
+    if (groups > 0) {
+        void* args[] = {&a};
+        if (hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * HG), args, lds, s) != hipSuccess)
+            return fail(PA_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(hipGetLastError()));
+    }
     if (e1) (void)hipEventRecord(e1, s);
     if (plan.reduce_groups > 0) {
         RedArgs r;
@@ -660,8 +784,9 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         r.ctx = a.ctx; r.ctx_s = a.ctx_s; r.ql = a.ql; r.ql_s = a.ql_s;
         r.out = a.out; r.o_sb = a.o_sb; r.o_st = a.o_st; r.o_sh = a.o_sh;
         r.Hq = a.Hq; r.Qmax = a.Qmax; r.W = a.W; r.T = a.T; r.P = a.P;
-        if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, dim3((unsigned)plan.reduce_groups), dim3(256), 0, s, r);
-        else hipLaunchKernelGGL(reduce_kernel<64>, dim3((unsigned)plan.reduce_groups), dim3(256), 0, s, r);
+        const dim3 rgrid((unsigned)plan.reduce_groups), rblock((unsigned)plan.reduce_threads);
+        if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, rgrid, rblock, 0, s, r);
+        else hipLaunchKernelGGL(reduce_kernel<64>, rgrid, rblock, 0, s, r);
     }
     if (e2) (void)hipEventRecord(e2, s);
     const hipError_t err = hipGetLastError();

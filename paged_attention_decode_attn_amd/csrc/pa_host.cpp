@@ -14,6 +14,7 @@ namespace pa {
 namespace {
 thread_local char g_last_error[512] = "";
 std::atomic<int32_t> g_partition_override{0};
+std::atomic<int32_t> g_group_override{0};
 
 int64_t elem_bytes(int32_t dtype) {
     switch (dtype) {
@@ -139,6 +140,8 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
                     (long long)(G * Qmax), PA_MAX_ROWS);
     if (bt->shape[0] != B)
         return fail(PA_ERR_SHAPE, "block_tables: %lld rows, batch is %lld", (long long)bt->shape[0], (long long)B);
+    if (B > kMaxBatch)
+        return fail(PA_ERR_UNSUPPORTED, "batch %lld exceeds %d sequences", (long long)B, kMaxBatch);
     const int64_t W = bt->shape[1];
     if (ctx->shape[0] != B)
         return fail(PA_ERR_SHAPE, "context_lens: %lld entries, batch is %lld", (long long)ctx->shape[0], (long long)B);
@@ -198,37 +201,75 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     return PA_OK;
 }
 
-int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W, bool /*fp8*/,
+int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W, bool fp8,
               int32_t num_cus, pa_plan* plan) {
     if (!plan) return fail(PA_ERR_NULL, "plan: NULL");
     if (B < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Qmax < 1 || W < 1 || num_cus < 1 || D < 1)
         return fail(PA_ERR_ARG, "plan: invalid sizes");
     const int64_t rows = (Hq / Hkv) * Qmax;
+    const int64_t row_tiles = (rows + 15) / 16;
     const int64_t max_tokens = int64_t(PA_BLOCK_SIZE) * W;
-    const int64_t units = B * Hkv;                 // (sequence, kv head) pairs
+    // waves one CU holds for the kernel variant (register budget) and the
+    // largest kv-head group (one wave per head) a workgroup may carry
+    const int64_t cu_waves = row_tiles == 1 ? (fp8 && D == 64 ? 12 : 8) : 4;
+    const int64_t hg_cap = row_tiles == 1 ? 8 : 4;
+    auto largest_group = [&](int64_t cap) {
+        for (int64_t h = cap; h >= 1; --h)
+            if (Hkv % h == 0 && cu_waves % h == 0) return h;
+        return int64_t(1);
+    };
+    // Expected context per sequence: the table width for one sequence, half
+    // of it for a ragged batch (only shapes are known here, never lengths).
+    const int64_t expect = B > 1 ? (max_tokens + 1) / 2 : max_tokens;
+    auto items = [&](int64_t hg, int64_t t) { return B * (Hkv / hg) * ((expect + t - 1) / t); };
+    auto slots = [&](int64_t hg) { return int64_t(num_cus) * (cu_waves / hg); };
+
+    const int64_t hg_over = g_group_override.load();
+    int64_t HG = hg_over > 0 ? hg_over : largest_group(hg_cap);
+    if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
+    auto largest_filling = [&](int64_t hg) {      // largest T with an item for every slot
+        for (int64_t t = kMaxWaveTokens; t >= kChunk; t /= 2)
+            if (items(hg, t) >= slots(hg)) return t;
+        return int64_t(kChunk);
+    };
     int64_t T = g_partition_override.load();
     if (T <= 0) {
-        // Fill the chip: aim for about 4 single-wave workgroups per SIMD
-        // (4 SIMDs per CU) over all pairs, bounded below by one 32-token
-        // step so short contexts are not over-split.
-        const int64_t target = int64_t(num_cus) * 4 * 4;
-        const int64_t want = units > 0 ? (target + units - 1) / units : 1;
-        T = (max_tokens + want - 1) / want;
+        if (max_tokens <= 16 * kChunk) {
+            // short contexts: one partition per (sequence, head), no merge
+            // kernel, heads spread over the chip
+            if (hg_over <= 0) HG = 1;
+            T = max_tokens;
+        } else {
+            // heads grouped per CU (whole token rows read together) with the
+            // largest partition that gives every workgroup slot an item; if
+            // that needs partitions under 256 tokens, the call is small:
+            // spread the heads instead; ragged batches prefer 256 tokens when
+            // that leaves >= 4 items per slot (equal shares to within one)
+            T = largest_filling(HG);
+            if (T < 256 && hg_over <= 0 && HG > 1) {
+                HG = 1;
+                T = largest_filling(HG);
+            }
+            if (B > 1 && T > 256 && items(HG, 256) >= 4 * slots(HG)) T = 256;
+        }
     }
     T = ((T + kChunk - 1) / kChunk) * kChunk;
     if (T < kChunk) T = kChunk;
-    if (T > kMaxPartitionTokens) T = kMaxPartitionTokens;
-    int64_t P = (max_tokens + T - 1) / T;
-    while (P > kMaxPartitions && T < kMaxPartitionTokens) {   // unreachable for W <= 2^26 / 16
-        T += kChunk;
-        P = (max_tokens + T - 1) / T;
-    }
+    if (T > kMaxWaveTokens) T = kMaxWaveTokens;
+    const int64_t P = (max_tokens + T - 1) / T;
     if (P > kMaxPartitions) return fail(PA_ERR_UNSUPPORTED, "context too long for the partition limit");
+    // merge workgroup: D/4 columns x enough partition lanes that every lane
+    // has at most 4 partitions (one round of loads), up to 1024 threads
+    const int64_t cols = D / 4;
+    int64_t lanes = 1;
+    while (lanes * 4 < P && cols * lanes * 2 <= 1024) lanes *= 2;
     plan->partition_tokens = int32_t(T);
     plan->num_partitions = int32_t(P);
     plan->rows = int32_t(rows);
-    plan->row_tiles = int32_t((rows + 15) / 16);
-    plan->partition_groups = units * P;
+    plan->row_tiles = int32_t(row_tiles);
+    plan->heads_per_group = int32_t(HG);
+    plan->reduce_threads = int32_t(cols * lanes);
+    plan->partition_groups = B * (Hkv / HG) * P;
     plan->reduce_groups = P > 1 ? B * Qmax * Hq : 0;
     plan->workspace_bytes = P > 1 ? B * Qmax * Hq * P * (D + 1) * int64_t(sizeof(float)) + 256 : 0;
     if (plan->partition_groups >= (int64_t(1) << 31) || plan->reduce_groups >= (int64_t(1) << 31))
@@ -258,10 +299,16 @@ int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t he
 }
 
 int paged_attn_set_partition_tokens(int32_t tokens) {
-    if (tokens < 0 || tokens % pa::kChunk || tokens > pa::kMaxPartitionTokens)
+    if (tokens < 0 || tokens % pa::kChunk || tokens > pa::kMaxWaveTokens)
         return pa::fail(PA_ERR_ARG, "partition tokens must be 0 or a multiple of 32 up to %d",
-                        pa::kMaxPartitionTokens);
+                        pa::kMaxWaveTokens);
     pa::g_partition_override.store(tokens);
+    return PA_OK;
+}
+
+int paged_attn_set_heads_per_group(int32_t heads) {
+    if (heads < 0 || heads > 8) return pa::fail(PA_ERR_ARG, "heads per group must be 0 (automatic) or 1..8");
+    pa::g_group_override.store(heads);
     return PA_OK;
 }
 

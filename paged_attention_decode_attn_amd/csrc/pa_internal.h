@@ -39,8 +39,9 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
 // Records a failure description for paged_attn_last_error() and returns `status`.
 int fail(int status, const char* fmt, ...);
 
-constexpr int kChunk = 32;            // tokens per inner-loop step (two blocks)
-constexpr int kMaxPartitionTokens = 1024;   // one 64-entry block-id window per wave
-constexpr int kMaxPartitions = 8192;
+constexpr int kChunk = 32;                  // tokens per inner-loop step (two blocks)
+constexpr int kMaxWaveTokens = 1024;        // one 64-entry block-id window per wave
+constexpr int kMaxPartitions = 1 << 16;
+constexpr int kMaxBatch = 16384;            // per-sequence partition counts live in LDS
 
 }  // namespace pa

@@ -157,7 +157,10 @@ def test_plan_properties(shape):
     assert T % 32 == 0 and 32 <= T <= 1024
     assert P * T >= 16 * w and (P - 1) * T < 16 * w          # covers the table, no empty tail
     assert p["rows"] == hq // hkv * ql and p["row_tiles"] == (p["rows"] + 15) // 16
-    assert p["partition_groups"] == b * hkv * P
+    hg = p["heads_per_group"]
+    assert hkv % hg == 0 and 1 <= hg <= (8 if p["row_tiles"] == 1 else 4)
+    assert p["partition_groups"] == b * (hkv // hg) * P
+    assert p["reduce_threads"] % (d // 4) == 0 and p["reduce_threads"] <= 1024
     assert (p["reduce_groups"] > 0) == (P > 1 and b > 0) or b == 0
     if P > 1:
         assert p["workspace_bytes"] >= b * ql * hq * P * (d + 1) * 4
@@ -166,7 +169,7 @@ def test_plan_properties(shape):
 
 def test_plan_fills_the_device_for_long_single_sequence():
     p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=256)
-    assert p["partition_groups"] >= 1024                       # at least one wave per SIMD
+    assert p["partition_groups"] * p["heads_per_group"] >= 1024   # at least one wave per SIMD
     small = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=8)
     assert small["partition_groups"] <= p["partition_groups"]
 
@@ -176,13 +179,42 @@ def test_partition_override_and_reset():
         B.paged_attn_set_partition_tokens(64)
         p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
         assert p["partition_tokens"] == 64 and p["num_partitions"] == 8
+        B.paged_attn_set_partition_tokens(1024)
+        p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
+        assert p["num_partitions"] == 1 and p["reduce_groups"] == 0
         with pytest.raises(B.PagedAttnError):
             B.paged_attn_set_partition_tokens(48)
         with pytest.raises(B.PagedAttnError):
             B.paged_attn_set_partition_tokens(2048)
     finally:
         B.paged_attn_set_partition_tokens(0)
-    assert B.paged_attn_plan(1, 32, 8, 128, 1, 32)["partition_tokens"] == 32
+    p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)                  # a tiny call: one partition
+    assert p["partition_tokens"] == 512 and p["num_partitions"] == 1
+
+
+def test_heads_per_group_override():
+    try:
+        B.paged_attn_set_heads_per_group(2)
+        assert B.paged_attn_plan(1, 64, 8, 128, 1, 8192)["heads_per_group"] == 2
+        B.paged_attn_set_heads_per_group(3)                     # does not divide 8 kv heads
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_plan(1, 64, 8, 128, 1, 8192)
+        B.paged_attn_set_heads_per_group(8)                     # 64 rows: at most 4 heads
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_plan(1, 64, 1, 128, 1, 8192)
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_set_heads_per_group(9)
+    finally:
+        B.paged_attn_set_heads_per_group(0)
+
+
+def test_plan_spreads_small_calls_over_the_chip():
+    p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)                  # one 512-token sequence
+    assert p["heads_per_group"] == 1 and p["num_partitions"] == 1 and p["reduce_groups"] == 0
+    p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)                 # 4 x <= 8192 tokens
+    assert p["heads_per_group"] == 1 and p["partition_groups"] >= 2048
+    p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192)                # 131072 tokens, batch 1
+    assert p["heads_per_group"] == 8 and p["partition_groups"] >= 256
 
 
 def test_plan_rejects_bad_sizes():

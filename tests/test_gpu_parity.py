@@ -35,6 +35,16 @@ def test_config_shapes(name, T):
     check(w, T, label=f"{name}/T{T}")
 
 
+@pytest.mark.parametrize("hg", [1, 2, 4, 8])
+@pytest.mark.parametrize("T", [32, 256])
+def test_heads_per_workgroup(hg, T):
+    # every kv-head grouping of the persistent workgroups, ragged batch with
+    # more items than resident workgroups at T = 32
+    for name in ("mtp_verify", "fp8"):
+        w = generate(SMALL[name])
+        check(w, T, label=f"hg{hg}/{name}/T{T}", heads_per_group=hg)
+
+
 # --------------------------------------------------------------------------
 # edge suite
 # --------------------------------------------------------------------------
