@@ -44,6 +44,10 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 1 GiB device copies (HBM counter calibration)")
+    ap.add_argument("--summarize", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="turn rocprofv3 output directories of this workload into the text "
+                         "summary and traffic record under profiles/ (no GPU needed)")
+    ap.add_argument("--command", default="", help="with --summarize: the commands that made the runs")
     return ap.parse_args()
 
 
@@ -63,6 +67,81 @@ def measured_traffic(workload: str):
     if not rec or rec.get("kernel_source_sha256_16") != source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _db_rows(path, sql):
+    import glob
+    import sqlite3
+    rows = []
+    for db in sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(db)
+        rows += con.execute(sql).fetchall()
+        con.close()
+    return rows
+
+
+def summarize(args):
+    """Kernel-trace statistics and calibrated HBM traffic of one workload."""
+    from paged_attention_decode_attn_amd.workloads import CONFIGS, generate, kv_bytes
+    trace, fetch, write, cfetch, cwrite = args.summarize
+    spec = CONFIGS[args.config]
+    kvb = kv_bytes(generate(spec).context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
+    stats = _db_rows(trace, "select name, count(*), avg(duration), min(duration), max(duration) "
+                            "from kernels group by name")
+
+    def counter(path, name, like):
+        r = _db_rows(path, f"select avg(value), count(*) from counters_collection where "
+                           f"counter_name = '{name}' and kernel_name like '{like}'")
+        return r[0] if r and r[0][0] is not None else (None, 0)
+    n_copy = 1 << 30
+    cf = n_copy / (counter(cfetch, "FETCH_SIZE", "%copyBuffer%")[0] * 1024)
+    cw = n_copy / (counter(cwrite, "WRITE_SIZE", "%copyBuffer%")[0] * 1024)
+    lines = [f"# rocprofv3 summary: paged decode attention, workload {spec.name}", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += ["    " + c for c in args.command.split(" ;; ") if c]
+    lines += ["", f"Algorithmic KV bytes per call: {kvb}", "",
+              "Kernel trace (durations in ns):", "",
+              "| kernel | calls | avg | min | max |", "|---|---|---|---|---|"]
+    for name, n, avg, mn, mx in sorted(stats, key=lambda r: -r[2] * r[1]):
+        short = name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {short} | {n} | {avg:.0f} | {mn:.0f} | {mx:.0f} |")
+    lines += ["", f"HBM counter calibration with a plain 1 GiB device copy: FETCH_SIZE x {cf:.3f}, "
+              f"WRITE_SIZE x {cw:.3f} gives true bytes.", "",
+              "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | calibrated HBM bytes/dispatch |",
+              "|---|---|---|---|"]
+    record = {}
+    for like, label in (("%partition_kernel%", "partition_kernel"), ("%reduce_kernel%", "reduce_kernel")):
+        fk, nf = counter(fetch, "FETCH_SIZE", like)
+        wk, nw = counter(write, "WRITE_SIZE", like)
+        if fk is None or wk is None:
+            continue
+        hbm = fk * 1024 * cf + wk * 1024 * cw
+        lines.append(f"| {label} | {fk:.0f} | {wk:.0f} | {hbm:.0f} |")
+        record[label] = hbm
+    part = [r for r in stats if "partition_kernel" in r[0]]
+    if part:
+        avg_ns = part[0][2]
+        lines += ["", f"partition_kernel: {kvb / avg_ns:.1f} GB/s algorithmic "
+                      f"({100 * kvb / avg_ns / HBM_PEAK_GBS:.1f}% of 8 TB/s) at the traced average "
+                      f"duration; HBM traffic {record.get('partition_kernel', 0) / kvb:.3f} x the "
+                      f"algorithmic bytes."]
+    kname = "partition_kernel"
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), f"{kname}_{args.config}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    if "partition_kernel" in record:
+        allrec[spec.name] = {"kernel_source_sha256_16": source_digest(),
+                             "hbm_bytes_per_launch": round(record["partition_kernel"]),
+                             "algorithmic_bytes": kvb,
+                             "calibration": {"fetch": round(cf, 4), "write": round(cw, 4)}}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(allrec, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
 
 
 def calibrate_copy():
@@ -108,6 +187,9 @@ def cpu_baseline(w, seconds: float):
 
 def main():
     args = parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -134,7 +216,7 @@ def main():
     kvb = kv_bytes(w.context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
     dev = w.to("cuda")
     pool_bytes = 2 * dev.k_cache.numel() * dev.k_cache.element_size()
-    copies = args.copies or max(2, math.ceil((1 << 30) / kvb) + 1)
+    copies = args.copies or min(64, max(2, math.ceil((1 << 30) / kvb) + 1))
     copies = max(1, min(copies, int((64 << 30) // max(pool_bytes, 1))))
     pools = [(dev.k_cache, dev.v_cache, dev.k_scale, dev.v_scale)]
     for _ in range(copies - 1):
@@ -157,9 +239,7 @@ def main():
         call(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-kernel HIP events recorded by the library on
-    # the same stream as the launches
-    B.paged_attn_profile_begin(args.steps)
+    # timed region: exactly K steps, bracketed by synchronisation
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -169,18 +249,21 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(stop)
-    prof = B.paged_attn_profile_end()
-    ms_per_step = ms_total / args.steps
+    ms_per_step = start.elapsed_time(stop) / args.steps
 
-    # the same loop without per-kernel events, for the events' own overhead
+    # the same K steps again with HIP events recorded by the library around
+    # each of its kernels, on the stream the kernels run on: per-kernel
+    # durations for the roofline (events between launches add their own
+    # gaps, so the step time above is measured without them)
+    B.paged_attn_profile_begin(args.steps)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
         call(i)
     stop.record()
     torch.cuda.synchronize()
-    ms_plain = start.elapsed_time(stop) / args.steps
+    prof = B.paged_attn_profile_end()
+    ms_with_events = start.elapsed_time(stop) / args.steps
     B.paged_attn_set_partition_tokens(0)
 
     part_ms = prof["partition_ms"] / max(prof["calls"], 1)
@@ -202,7 +285,7 @@ def main():
                    "partition_tokens": plan["partition_tokens"],
                    "num_partitions": plan["num_partitions"], "kv_copies_rotated": copies},
         "us_per_call": round(ms_per_step * 1e3, 3),
-        "us_per_call_without_kernel_events": round(ms_plain * 1e3, 3),
+        "us_per_call_with_kernel_events": round(ms_with_events * 1e3, 3),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_per_call": kvb,
         "kernel_us": {"partition": round(part_ms * 1e3, 3), "reduce": round(red_ms * 1e3, 3)},
