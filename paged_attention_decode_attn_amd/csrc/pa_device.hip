@@ -59,19 +59,28 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr unsigned kSelLo = 0x05040100u;   // v_perm: (src1.lo16, src0.lo16)
 constexpr unsigned kSelHi = 0x07060302u;   // v_perm: (src1.hi16, src0.hi16)
+constexpr unsigned kSelByte01 = 0x05010400u;  // v_perm: src1.b0, src0.b0, src1.b1, src0.b1
+constexpr unsigned kSelByte23 = 0x07030602u;  // v_perm: src1.b2, src0.b2, src1.b3, src0.b3
+constexpr int kRsrcWord3 = 0x00020000;        // raw buffer resource, 32-bit data format
+constexpr float kRescaleLog2 = 8.0f;          // lazy rescale threshold (log2 units)
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 struct PartArgs {
     const char* q;   int64_t q_sb, q_st, q_sh;        // bytes
-    const char* k;   int64_t k_sblk, k_stok, k_sh;    // bytes
-    const char* v;   int64_t v_sblk, v_stok, v_sh;    // bytes
-    const float* ks; int64_t ks_sblk, ks_sh;          // floats
-    const float* vs; int64_t vs_sblk, vs_sh;
+    const char* k;   int64_t k_stok, k_sh;            // bytes
+    const char* v;   int64_t v_stok, v_sh;            // bytes
+    const float* ks; int64_t ks_sh;                   // floats
+    const float* vs; int64_t vs_sh;
+    uint32_t k_sblk, v_sblk, ks_sblk, vs_sblk;        // block strides, bytes (< 2^31)
     const int32_t* bt; int64_t bt_sb;
     const int32_t* ctx; int64_t ctx_s;
     const int32_t* ql;  int64_t ql_s;
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
     float* ws_o;     float* ws_lse;
-    float scale_log2;
+    float scale_log2;                                  // |scale| * log2(e)
+    int32_t q_neg;                                     // scale < 0: negate q
+    int32_t k_span, v_span;                            // bytes of one (block, head) slice
     int32_t B, Hq, Hkv, G, Qmax, W, NB, T, P, rows, HG;
 };
 
@@ -97,12 +106,6 @@ __device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
 
-// fp32 values that are exactly representable in bf16 (widened e4m3fn) ->
-// packed pair (a, b) by dropping the zero low halves.
-__device__ __forceinline__ unsigned pack_bf16_exact(float a, float b) {
-    return __builtin_amdgcn_perm(bits(b), bits(a), kSelHi);
-}
-
 // Per-step register tiles.  KL: 16-byte K loads per lane and block;
 // V: one load of D/16 elements per lane and token slot.
 template <int D, bool FP8> struct VLoad;
@@ -123,33 +126,69 @@ template <int D, bool FP8, int NT> struct State {
     f32x4 acc[NT][D / 16];
 };
 
+// Buffer resource over one (block, kv head) slice: the base is wave-uniform
+// and lives in SGPRs, the lane offsets are loop-invariant VGPRs, and the
+// range check returns zeros (without a memory access) for offsets past
+// `bytes`, so a block that lies past the sequence costs no traffic.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+template <typename T> __device__ __forceinline__ T bload(Rsrc r, unsigned off);
+template <> __device__ __forceinline__ u32x4 bload<u32x4>(Rsrc r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ u32x2 bload<u32x2>(Rsrc r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ unsigned bload<unsigned>(Rsrc r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Per-item bases: the kv head's slice of block 0 of each cache array.
+struct HeadBase {
+    const char* k; const char* v; const char* ks; const char* vs;
+};
+
 template <int D, bool FP8>
-__device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, int bid_lane, int step,
-                                          int last_blk, int g, int grp,
-                                          const unsigned (&koff)[Step<D, FP8>::KL], const unsigned (&voff)[4]) {
+__device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, const HeadBase& hb, int bid_lane,
+                                          int step, int last_blk, const unsigned (&koff)[Step<D, FP8>::KL],
+                                          const unsigned (&voff)[4], unsigned soff) {
     typedef typename VLoad<D, FP8>::T VT;
-    // a step's second block may lie past the sequence: read its last block
-    // again instead (those positions are masked)
-    const int b0 = __builtin_amdgcn_readlane(bid_lane, min(2 * step, last_blk));
+    // block 2*step always holds keys of the sequence; block 2*step + 1 may
+    // lie past it, and then reads as zeros through an empty range
+    const int b0 = __builtin_amdgcn_readlane(bid_lane, 2 * step);
     const int b1 = __builtin_amdgcn_readlane(bid_lane, min(2 * step + 1, last_blk));
-    const char* kb0 = a.k + (int64_t)b0 * a.k_sblk + (int64_t)g * a.k_sh;
-    const char* kb1 = a.k + (int64_t)b1 * a.k_sblk + (int64_t)g * a.k_sh;
-    const char* vb0 = a.v + (int64_t)b0 * a.v_sblk + (int64_t)g * a.v_sh;
-    const char* vb1 = a.v + (int64_t)b1 * a.v_sblk + (int64_t)g * a.v_sh;
+    const bool has1 = 2 * step + 1 <= last_blk;
+    const uint32_t u0 = (uint32_t)b0, u1 = (uint32_t)b1;
+    const Rsrc k0 = make_rsrc(hb.k + (uint64_t)u0 * a.k_sblk, a.k_span);
+    const Rsrc k1 = make_rsrc(hb.k + (uint64_t)u1 * a.k_sblk, has1 ? a.k_span : 0);
+    const Rsrc v0 = make_rsrc(hb.v + (uint64_t)u0 * a.v_sblk, a.v_span);
+    const Rsrc v1 = make_rsrc(hb.v + (uint64_t)u1 * a.v_sblk, has1 ? a.v_span : 0);
 #pragma unroll
     for (int c = 0; c < Step<D, FP8>::KL; ++c) {
-        st.k[0][c] = ldg<u32x4>(kb0 + koff[c]);
-        st.k[1][c] = ldg<u32x4>(kb1 + koff[c]);
+        st.k[0][c] = bload<u32x4>(k0, koff[c]);
+        st.k[1][c] = bload<u32x4>(k1, koff[c]);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-        st.v[s] = ldg<VT>((s < 4 ? vb0 : vb1) + voff[s & 3]);
+    for (int s = 0; s < 8; ++s) st.v[s] = bload<VT>(s < 4 ? v0 : v1, voff[s & 3]);
     if constexpr (FP8) {
-        st.ksc[0] = *reinterpret_cast<const f32x4*>(a.ks + (int64_t)b0 * a.ks_sblk + (int64_t)g * a.ks_sh + 4 * grp);
-        st.ksc[1] = *reinterpret_cast<const f32x4*>(a.ks + (int64_t)b1 * a.ks_sblk + (int64_t)g * a.ks_sh + 4 * grp);
-        st.vsc[0] = *reinterpret_cast<const f32x4*>(a.vs + (int64_t)b0 * a.vs_sblk + (int64_t)g * a.vs_sh + 4 * grp);
-        st.vsc[1] = *reinterpret_cast<const f32x4*>(a.vs + (int64_t)b1 * a.vs_sblk + (int64_t)g * a.vs_sh + 4 * grp);
+        // one block's 16 slot scales of this kv head are contiguous (64 bytes)
+        const Rsrc s0 = make_rsrc(hb.ks + (uint64_t)u0 * a.ks_sblk, 64);
+        const Rsrc s1 = make_rsrc(hb.ks + (uint64_t)u1 * a.ks_sblk, has1 ? 64 : 0);
+        const Rsrc t0 = make_rsrc(hb.vs + (uint64_t)u0 * a.vs_sblk, 64);
+        const Rsrc t1 = make_rsrc(hb.vs + (uint64_t)u1 * a.vs_sblk, has1 ? 64 : 0);
+        st.ksc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(s0, soff));
+        st.ksc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(s1, soff));
+        st.vsc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(t0, soff));
+        st.vsc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(t1, soff));
     }
+}
+
+// Two e4m3fn bytes (bytes 0-1, or 2-3 with HI, of `w`) -> packed bf16 pair, exact:
+// every e4m3fn value, subnormals included, is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ unsigned fp8x2_to_bf16x2(unsigned w) {
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // V^T fragment of output tile j: element s = V[token slot s][d = (D/16)*m + j]
@@ -164,33 +203,27 @@ __device__ __forceinline__ bf16x8 vt_bf16(const typename VLoad<D, false>::T (&v)
     return as_bf16x8(x);
 }
 
-// fp8: widen each slot's D/16 bytes to f32 (exact), then pair slots.
+// fp8: the same fragments for every tile at once.  A byte permute
+// interleaves slots 2p and 2p+1 (bytes e of both words side by side), and
+// each half of the result widens to the bf16 pair of d-index 4*dw + e.
 template <int D>
-__device__ __forceinline__ void widen_v_fp8(const typename VLoad<D, true>::T (&v)[8], float (&f)[8][D / 16]) {
+__device__ __forceinline__ void vt_fp8(const typename VLoad<D, true>::T (&v)[8], u32x4 (&vt)[D / 16]) {
     constexpr int J = D / 16;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int p = 0; p < 4; ++p) {
 #pragma unroll
         for (int dw = 0; dw < J / 4; ++dw) {
-            unsigned word;
-            if constexpr (J == 4) word = v[s];
-            else word = v[s][dw];
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-            f[s][4 * dw + 0] = lo[0];
-            f[s][4 * dw + 1] = lo[1];
-            f[s][4 * dw + 2] = hi[0];
-            f[s][4 * dw + 3] = hi[1];
+            unsigned w0, w1;
+            if constexpr (J == 4) { w0 = v[2 * p]; w1 = v[2 * p + 1]; }
+            else { w0 = v[2 * p][dw]; w1 = v[2 * p + 1][dw]; }
+            const unsigned lo = __builtin_amdgcn_perm(w1, w0, kSelByte01);
+            const unsigned hi = __builtin_amdgcn_perm(w1, w0, kSelByte23);
+            vt[4 * dw + 0][p] = fp8x2_to_bf16x2<false>(lo);
+            vt[4 * dw + 1][p] = fp8x2_to_bf16x2<true>(lo);
+            vt[4 * dw + 2][p] = fp8x2_to_bf16x2<false>(hi);
+            vt[4 * dw + 3][p] = fp8x2_to_bf16x2<true>(hi);
         }
     }
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8 vt_fp8(const float (&f)[8][D / 16], int j) {
-    u32x4 x;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) x[p] = pack_bf16_exact(f[2 * p][j], f[2 * p + 1][j]);
-    return as_bf16x8(x);
 }
 
 // K fragments (A operand of S^T) of block mt as bf16.
@@ -203,7 +236,8 @@ __device__ __forceinline__ void build_kf(const Step<D, FP8>& st, bf16x8 (&kf)[2]
             for (int kk = 0; kk < D / 32; ++kk) kf[mt][kk] = as_bf16x8(st.k[mt][kk]);
         } else {
             // load c holds bytes e = 0..15 of d = (D/4)*grp + 16c + e;
-            // MFMA step kk = 2c + h takes bytes 8h .. 8h+7.
+            // MFMA step kk = 2c + h takes bytes 8h .. 8h+7, i.e. the
+            // adjacent-d pairs of two words
 #pragma unroll
             for (int c = 0; c < D / 64; ++c) {
 #pragma unroll
@@ -212,10 +246,8 @@ __device__ __forceinline__ void build_kf(const Step<D, FP8>& st, bf16x8 (&kf)[2]
 #pragma unroll
                     for (int p2 = 0; p2 < 2; ++p2) {
                         const unsigned word = st.k[mt][c][2 * h + p2];
-                        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-                        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-                        x[2 * p2] = pack_bf16_exact(lo[0], lo[1]);
-                        x[2 * p2 + 1] = pack_bf16_exact(hi[0], hi[1]);
+                        x[2 * p2] = fp8x2_to_bf16x2<false>(word);
+                        x[2 * p2 + 1] = fp8x2_to_bf16x2<true>(word);
                     }
                     kf[mt][2 * c + h] = as_bf16x8(x);
                 }
@@ -224,14 +256,24 @@ __device__ __forceinline__ void build_kf(const Step<D, FP8>& st, bf16x8 (&kf)[2]
     }
 }
 
-template <int D, bool FP8, int NT>
+// One 32-token step of the online softmax for every row tile.  MASK: some
+// key of the step is past L or causally hidden from some row (only the
+// last steps of a partition); without it no mask code is emitted.
+//
+// Scores stay unscaled (y = q.k, times the fp8 k scale) until the
+// exponent, p = exp2(c*y - m) with c = |scale|*log2(e) >= 0 (a negative
+// scale flips the sign of q instead), so the row max of c*y is c times the
+// max of y.  The running max m is raised only when a row's max exceeds it by
+// more than kRescaleLog2 (any row of the wave: the branch is uniform);
+// otherwise p <= 2^kRescaleLog2 and l and the accumulators keep their scale.
+// The result is the same: m, l and O all refer to one m.
+template <int D, bool FP8, int NT, bool MASK>
 __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>& s, const u32x4 (&qf)[NT][D / 32],
                                              const PartArgs& a, int cbase, int L, int nq, int lane) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
-    const bool tail = cbase + 31 > L - nq;   // some key here is past L or causally hidden
 
-    if (tail) {
+    if constexpr (MASK) {
         // zero V rows (and scales) of positions >= L so that p = 0 never
         // meets NaN or garbage from unwritten slots
 #pragma unroll
@@ -249,8 +291,9 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
 
     bf16x8 kf[2][D / 32];
     build_kf<D, FP8>(st, kf);
-    float vf[FP8 ? 8 : 1][FP8 ? J : 1];
-    if constexpr (FP8) widen_v_fp8<D>(st.v, vf);
+    u32x4 vtf[FP8 ? J : 1];
+    if constexpr (FP8) vt_fp8<D>(st.v, vtf);
+    const float c = a.scale_log2;
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -261,44 +304,52 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qb, s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qb, s1, 0, 0, 0);
         }
-        float x[8];
+        float y[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (FP8) {
-                x[i] = s0[i] * (a.scale_log2 * st.ksc[0][i]);
-                x[4 + i] = s1[i] * (a.scale_log2 * st.ksc[1][i]);
+                y[i] = s0[i] * st.ksc[0][i];
+                y[4 + i] = s1[i] * st.ksc[1][i];
             } else {
-                x[i] = s0[i] * a.scale_log2;
-                x[4 + i] = s1[i] * a.scale_log2;
+                y[i] = s0[i];
+                y[4 + i] = s1[i];
             }
         }
-        if (tail) {
+        bool hidden[8];
+        if constexpr (MASK) {
             const int row = 16 * nt + n16;
             const int t = row / a.G;
             const int lim = (row < a.rows && t < nq) ? L - nq + t : L - 1;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int tok = cbase + 16 * (i >> 2) + 4 * grp + (i & 3);
-                x[i] = tok > lim ? -__builtin_inff() : x[i];
+                hidden[i] = tok > lim;
+                y[i] = hidden[i] ? -__builtin_inff() : y[i];
             }
         }
-        float mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+        float mx = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(s.m[nt], mx);
-        const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(s.m[nt] - m_use);
+        float mxs = c * mx;
+        if constexpr (MASK) mxs = mx == -__builtin_inff() ? -__builtin_inff() : mxs;
+        if (__any(mxs > s.m[nt] + kRescaleLog2)) {
+            const float m_new = fmaxf(s.m[nt], mxs);
+            const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(s.m[nt] - m_new);
+            s.l[nt] *= alpha;
+#pragma unroll
+            for (int j = 0; j < J; ++j) s.acc[nt][j] *= alpha;
+            s.m[nt] = m_new;
+        }
+        const float neg_m = s.m[nt] == -__builtin_inff() ? 0.f : -s.m[nt];
         float p[8];
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c, neg_m));
+            if constexpr (MASK) p[i] = hidden[i] ? 0.f : p[i];
             psum += p[i];
         }
-        s.l[nt] = s.l[nt] * alpha + psum;
-        s.m[nt] = m_new;
+        s.l[nt] += psum;
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -313,9 +364,8 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             bf16x8 vt;
-            if constexpr (FP8) vt = vt_fp8<D>(vf, j);
+            if constexpr (FP8) vt = as_bf16x8(vtf[j]);
             else vt = vt_bf16<D>(st.v, j);
-            s.acc[nt][j] *= alpha;
             s.acc[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, s.acc[nt][j], 0, 0, 0);
         }
     }
@@ -361,17 +411,24 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
     if (L <= 0 || nq <= 0 || tok0 >= L) return;
     const bool direct = (L + a.T - 1) / a.T == 1;
     const int nsteps = (min(L, tok0 + a.T) - tok0 + 31) / 32;
-    // last block of the sequence relative to the slice: block-table entries
-    // past it are never used (their blocks are replaced by this one)
+    // steps [0, nclean) hold only keys below L that every query row sees
+    const int nclean = min(nsteps, max(0, L - nq + 1 - tok0) / 32);
+    // last block of the sequence relative to the slice
     const int last_blk = (L + 15) / 16 - 1 - tok0 / 16;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int row = 16 * nt + n16;
-        if (row / a.G >= nq)
+        const bool live = row / a.G < nq;
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) qf[nt][kk] = u32x4{0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < D / 32; ++kk)
+            qf[nt][kk] = live ? (a.q_neg ? qf[nt][kk] ^ 0x80008000u : qf[nt][kk]) : u32x4{0u, 0u, 0u, 0u};
     }
 
+    HeadBase hb;
+    hb.k = a.k + (int64_t)g * a.k_sh;
+    hb.v = a.v + (int64_t)g * a.v_sh;
+    hb.ks = reinterpret_cast<const char*>(a.ks + (int64_t)g * a.ks_sh);
+    hb.vs = reinterpret_cast<const char*>(a.vs + (int64_t)g * a.vs_sh);
     unsigned koff[KL];
 #pragma unroll
     for (int c = 0; c < KL; ++c)
@@ -379,6 +436,7 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
     unsigned voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) voff[i] = (unsigned)((4 * grp + i) * a.v_stok) + (unsigned)((D / 16) * n16 * E);
+    const unsigned soff = 16u * (unsigned)grp;
 
     State<D, FP8, NT> s;
 #pragma unroll
@@ -392,29 +450,42 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
     // two register buffers: the next step's loads are in flight while the
     // current step computes; straight-line code on every path keeps the
     // memory-counter waits exact (one buffer when the row tiles leave no
-    // registers for a second)
+    // registers for a second).  The last one or two steps take the masked
+    // variant whether they need it or not.
     Step<D, FP8> bufA, bufB;
     if constexpr (NT > 2) {
-        for (int st = 0; st < nsteps; ++st) {
-            load_step<D, FP8>(bufA, a, bid_lane, st, last_blk, g, grp, koff, voff);
-            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        int st = 0;
+        for (; st < nclean; ++st) {
+            load_step<D, FP8>(bufA, a, hb, bid_lane, st, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, false>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        }
+        for (; st < nsteps; ++st) {
+            load_step<D, FP8>(bufA, a, hb, bid_lane, st, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
         }
     } else {
-        load_step<D, FP8>(bufA, a, bid_lane, 0, last_blk, g, grp, koff, voff);
+        load_step<D, FP8>(bufA, a, hb, bid_lane, 0, last_blk, koff, voff, soff);
         int st = 0;
+        while (st + 2 < nsteps && st + 1 < nclean) {
+            load_step<D, FP8>(bufB, a, hb, bid_lane, st + 1, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, false>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+            load_step<D, FP8>(bufA, a, hb, bid_lane, st + 2, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, false>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+            st += 2;
+        }
         while (st + 2 < nsteps) {
-            load_step<D, FP8>(bufB, a, bid_lane, st + 1, last_blk, g, grp, koff, voff);
-            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-            load_step<D, FP8>(bufA, a, bid_lane, st + 2, last_blk, g, grp, koff, voff);
-            compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+            load_step<D, FP8>(bufB, a, hb, bid_lane, st + 1, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+            load_step<D, FP8>(bufA, a, hb, bid_lane, st + 2, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, true>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
             st += 2;
         }
         if (st + 1 < nsteps) {
-            load_step<D, FP8>(bufB, a, bid_lane, st + 1, last_blk, g, grp, koff, voff);
-            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-            compute_step<D, FP8, NT>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
+            load_step<D, FP8>(bufB, a, hb, bid_lane, st + 1, last_blk, koff, voff, soff);
+            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+            compute_step<D, FP8, NT, true>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
         } else {
-            compute_step<D, FP8, NT>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
         }
     }
 
@@ -745,17 +816,22 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
     const int64_t groups = std::min<int64_t>(slots, plan.partition_groups);
     PartArgs a;
     a.q = static_cast<const char*>(pr.q); a.q_sb = pr.q_sb * 2; a.q_st = pr.q_st * 2; a.q_sh = pr.q_sh * 2;
-    a.k = static_cast<const char*>(pr.k); a.k_sblk = pr.k_sblk; a.k_stok = pr.k_stok; a.k_sh = pr.k_sh;
-    a.v = static_cast<const char*>(pr.v); a.v_sblk = pr.v_sblk; a.v_stok = pr.v_stok; a.v_sh = pr.v_sh;
-    a.ks = pr.ks; a.ks_sblk = pr.ks_sblk; a.ks_sh = pr.ks_sh;
-    a.vs = pr.vs; a.vs_sblk = pr.vs_sblk; a.vs_sh = pr.vs_sh;
+    a.k = static_cast<const char*>(pr.k); a.k_stok = pr.k_stok; a.k_sh = pr.k_sh;
+    a.v = static_cast<const char*>(pr.v); a.v_stok = pr.v_stok; a.v_sh = pr.v_sh;
+    a.ks = pr.ks; a.ks_sh = pr.ks_sh;
+    a.vs = pr.vs; a.vs_sh = pr.vs_sh;
+    a.k_sblk = (uint32_t)pr.k_sblk; a.v_sblk = (uint32_t)pr.v_sblk;
+    a.ks_sblk = (uint32_t)(pr.ks_sblk * 4); a.vs_sblk = (uint32_t)(pr.vs_sblk * 4);
     a.bt = pr.bt; a.bt_sb = pr.bt_sb;
     a.ctx = pr.ctx; a.ctx_s = pr.ctx_s;
     a.ql = pr.ql; a.ql_s = pr.ql_s;
     a.out = static_cast<char*>(pr.out); a.o_sb = pr.o_sb * 2; a.o_st = pr.o_st * 2; a.o_sh = pr.o_sh * 2;
     a.ws_o = static_cast<float*>(ws);
     a.ws_lse = a.ws_o + rows_total * plan.num_partitions * pr.D;
-    a.scale_log2 = pr.scale * kLog2e;
+    a.scale_log2 = std::fabs(pr.scale) * kLog2e;
+    a.q_neg = pr.scale < 0.f;
+    a.k_span = (int32_t)(15 * pr.k_stok + pr.D * (pr.fp8 ? 1 : 2));
+    a.v_span = (int32_t)(15 * pr.v_stok + pr.D * (pr.fp8 ? 1 : 2));
     a.B = (int32_t)pr.B; a.Hq = (int32_t)pr.Hq; a.Hkv = (int32_t)pr.Hkv; a.G = (int32_t)pr.G; a.Qmax = (int32_t)pr.Qmax;
     a.W = (int32_t)pr.W; a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
     a.T = plan.partition_tokens; a.P = plan.num_partitions; a.rows = plan.rows; a.HG = HG;

@@ -178,7 +178,14 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
         const int64_t span = (PA_BLOCK_SIZE - 1) * c->stride[1] * eb + (Hkv - 1) * c->stride[2] * eb + D * eb;
         if (span >= (int64_t(1) << 31))
             return fail(PA_ERR_LAYOUT, "%s: one block spans more than 2 GiB", c == kc ? "k_cache" : "v_cache");
+        // block strides are 32-bit byte counts in the kernels
+        if (c->stride[0] * eb >= (int64_t(1) << 32))
+            return fail(PA_ERR_LAYOUT, "%s: block stride of 4 GiB or more", c == kc ? "k_cache" : "v_cache");
     }
+    if (fp8)
+        for (const pa_tensor* s : {ks, vs})
+            if (s->stride[0] * 4 >= (int64_t(1) << 32) || s->stride[2] * 4 >= (int64_t(1) << 31))
+                return fail(PA_ERR_LAYOUT, "%s: block stride of 4 GiB or more", s == ks ? "k_scale" : "v_scale");
 
     if (pr) {
         Problem& p = *pr;
