@@ -38,7 +38,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER)
-    ap.add_argument("--partition-tokens", type=int, default=0, help="0 = the planner's choice")
+    ap.add_argument("--workgroups", type=int, default=0, help="partition-kernel grid (0 = the planner's)")
+    ap.add_argument("--min-share", type=int, default=0, help="smallest share in 32-token chunks (0 = the planner's)")
     ap.add_argument("--copies", type=int, default=0, help="rotated KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -224,7 +225,8 @@ def main():
         vs = None if dev.v_scale is None else dev.v_scale.permute(0, 2, 1).clone().permute(0, 2, 1)
         pools.append((dev.k_cache.clone(), dev.v_cache.clone(), ks, vs))
     out = torch.empty_like(dev.q)
-    B.paged_attn_set_partition_tokens(args.partition_tokens)
+    B.paged_attn_set_workgroups(args.workgroups)
+    B.paged_attn_set_min_share(args.min_share)
     plan = B.paged_attn_plan(spec.batch, spec.hq, spec.hkv, spec.head_dim, spec.qlen,
                              spec.table_width, spec.kv_dtype,
                              torch.cuda.get_device_properties(0).multi_processor_count)
@@ -264,7 +266,8 @@ def main():
     torch.cuda.synchronize()
     prof = B.paged_attn_profile_end()
     ms_with_events = start.elapsed_time(stop) / args.steps
-    B.paged_attn_set_partition_tokens(0)
+    B.paged_attn_set_workgroups(0)
+    B.paged_attn_set_min_share(0)
 
     part_ms = prof["partition_ms"] / max(prof["calls"], 1)
     red_ms = prof["reduce_ms"] / max(prof["calls"], 1)
@@ -282,8 +285,8 @@ def main():
                    "kv_dtype": spec.kv_dtype, "block_size": 16,
                    "context_lens": ([int(x) for x in w.context_lens] if spec.batch <= 4
                                     else f"U[{spec.ctx_lo}, {spec.ctx_hi}] (seed {spec.seed})"),
-                   "partition_tokens": plan["partition_tokens"],
-                   "num_partitions": plan["num_partitions"], "kv_copies_rotated": copies},
+                   "workgroups": plan["workgroups"], "heads_per_group": plan["heads_per_group"],
+                   "min_share_chunks": plan["min_share_chunks"], "kv_copies_rotated": copies},
         "us_per_call": round(ms_per_step * 1e3, 3),
         "us_per_call_with_kernel_events": round(ms_with_events * 1e3, 3),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -123,7 +123,8 @@ typedef struct pa_tensor {
  * `out` must not overlap any input.
  *
  * Uses a per-(device, stream) workspace owned by the library for split-
- * context partial results (fp32 partial outputs and log-sum-exp values);
+ * context partial results (fp32 partial outputs and log-sum-exp values,
+ * and the per-sequence chunk scan the merge kernel reads);
  * it grows on demand with hipMalloc outside stream capture.  Capture a
  * call into a graph only after paged_attn_reserve() or an uncaptured call
  * of the same or larger size on that stream; otherwise PA_ERR_CAPTURE.
@@ -147,44 +148,59 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
                      const pa_tensor* v_scale, const pa_tensor* out);
 
 /*
- * Split-context plan: how paged_attn_decode divides each (sequence, kv
- * head) pair's context into partitions of partition_tokens tokens (a
- * multiple of 32, at most 1024), each run by one wave; the waves serving
- * heads_per_group adjacent kv heads of a partition form one workgroup.
- * Chosen from shapes and the device's compute-unit count only (never from
- * device data), so that one call fills the GPU and short contexts are not
- * over-split.  The partition kernel is persistent: it launches at most as
- * many workgroups as the device holds at once, each looping over its share
- * of the partition_groups items that are non-empty for the actual lengths.
+ * Split-context plan: how paged_attn_decode divides the work so that one
+ * call fills the GPU whatever the batch and the ragged context lengths.
+ * Every (sequence, kv-head group) pair is a segment of ceil(L_b / 32)
+ * chunks of 32 tokens; the chunks of all segments, sequence-major, are
+ * dealt out in equal contiguous shares (to within one chunk) to
+ * `workgroups` workgroups of `heads_per_group` waves (one wave per kv head
+ * of the group).  A share may start and end inside a sequence, so each
+ * workgroup leaves at most two fp32 partial results (online-softmax state
+ * of the segments cut by its share boundaries) per wave and query row; a
+ * segment inside one share is written to `out` directly.  The merge kernel
+ * combines a row's partials by their log-sum-exp.  Chosen from shapes and
+ * the device's compute-unit count only (never from device data): the grid
+ * is one workgroup per resident slot, fewer when shares would drop under
+ * min_share_chunks chunks even at the longest contexts the table allows;
+ * the kernel lowers it further for the actual lengths by the same rule.
  */
 typedef struct pa_plan {
-    int32_t partition_tokens;   /* tokens per partition (one wave)         */
-    int32_t num_partitions;     /* ceil(16 * W / partition_tokens)         */
     int32_t rows;               /* (Hq / Hkv) * Qmax query rows per kv head */
     int32_t row_tiles;          /* ceil(rows / 16)                         */
     int32_t heads_per_group;    /* kv heads (one wave each) per workgroup  */
-    int32_t reduce_threads;     /* threads per merge workgroup             */
-    int64_t partition_groups;   /* (sequence, partition, head group) items */
+    int32_t min_share_chunks;   /* smallest share, in 32-token chunks      */
+    int32_t reduce_rows;        /* merge workgroup: query rows,            */
+    int32_t reduce_col4;        /*   float4 columns per row,               */
+    int32_t reduce_lanes;       /*   partial lanes per (row, column)       */
+    int32_t expected_partials;  /* partials per row for alike lengths      */
+    int64_t workgroups;         /* partition-kernel grid                   */
     int64_t reduce_groups;      /* workgroups of the merge kernel (0: none) */
-    int64_t workspace_bytes;    /* fp32 partial outputs + log-sum-exp      */
+    int64_t workspace_bytes;    /* fp32 partials + log-sum-exp + chunk scan */
 } pa_plan;
 
 /*
  * paged_attn_plan -- the plan for the given sizes on a device with
  * num_cus compute units (host only; no GPU access).  kv_dtype is a
- * pa_dtype of the cache.  Honors paged_attn_set_partition_tokens().
+ * pa_dtype of the cache.  Honors the overrides below.
  */
 int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
                     int64_t query_len, int64_t table_width, int32_t kv_dtype,
                     int32_t num_cus, pa_plan* plan);
 
 /*
- * paged_attn_set_partition_tokens -- override the planner's partition size
- * for every later call in the process (a positive multiple of 32 up to
- * 1024 tokens), or 0 to return to the automatic choice.  A test and tuning
+ * paged_attn_set_workgroups -- override the planner's partition-kernel
+ * grid for every later call in the process (positive; the min-share rule
+ * still lowers it), or 0 for the automatic choice.  A test and tuning
  * hook; not synchronised with concurrent calls.
  */
-int paged_attn_set_partition_tokens(int32_t tokens);
+int paged_attn_set_workgroups(int32_t workgroups);
+
+/*
+ * paged_attn_set_min_share -- override the smallest share of 32-token
+ * chunks per workgroup (positive), or 0 for the default of 1.  A tuning
+ * hook; not synchronised with concurrent calls.
+ */
+int paged_attn_set_min_share(int32_t chunks);
 
 /*
  * paged_attn_set_heads_per_group -- override the planner's kv heads per

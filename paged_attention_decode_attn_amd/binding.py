@@ -37,10 +37,11 @@ class PaTensor(ctypes.Structure):
 
 
 class PaPlan(ctypes.Structure):
-    _fields_ = [("partition_tokens", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
-                ("rows", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
-                ("heads_per_group", ctypes.c_int32), ("reduce_threads", ctypes.c_int32),
-                ("partition_groups", ctypes.c_int64), ("reduce_groups", ctypes.c_int64),
+    _fields_ = [("rows", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+                ("heads_per_group", ctypes.c_int32), ("min_share_chunks", ctypes.c_int32),
+                ("reduce_rows", ctypes.c_int32), ("reduce_col4", ctypes.c_int32),
+                ("reduce_lanes", ctypes.c_int32), ("expected_partials", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("reduce_groups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
@@ -75,7 +76,8 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_check.argtypes = args11 + [_P]
                 L.paged_attn_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, ctypes.c_int32,
                                                                      ctypes.POINTER(PaPlan)]
-                L.paged_attn_set_partition_tokens.argtypes = [ctypes.c_int32]
+                L.paged_attn_set_workgroups.argtypes = [ctypes.c_int32]
+                L.paged_attn_set_min_share.argtypes = [ctypes.c_int32]
                 L.paged_attn_set_heads_per_group.argtypes = [ctypes.c_int32]
                 L.paged_attn_reserve.argtypes = [ctypes.c_int64, ctypes.c_void_p]
                 i32p = ctypes.POINTER(ctypes.c_int32)
@@ -89,7 +91,8 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_last_error.argtypes = []
                 L.paged_attn_last_error.restype = ctypes.c_char_p
                 for name in ("paged_attn_decode", "paged_attn_check", "paged_attn_plan",
-                             "paged_attn_set_partition_tokens", "paged_attn_set_heads_per_group",
+                             "paged_attn_set_workgroups", "paged_attn_set_min_share",
+                             "paged_attn_set_heads_per_group",
                              "paged_attn_reserve",
                              "paged_attn_check_metadata", "paged_attn_profile_begin",
                              "paged_attn_profile_end"):
@@ -196,8 +199,12 @@ def paged_attn_plan(batch, q_heads, kv_heads, head_dim, query_len, table_width,
     return p.as_dict()
 
 
-def paged_attn_set_partition_tokens(tokens: int) -> None:
-    _raise(lib().paged_attn_set_partition_tokens(int(tokens)), "paged_attn_set_partition_tokens")
+def paged_attn_set_workgroups(workgroups: int) -> None:
+    _raise(lib().paged_attn_set_workgroups(int(workgroups)), "paged_attn_set_workgroups")
+
+
+def paged_attn_set_min_share(chunks: int) -> None:
+    _raise(lib().paged_attn_set_min_share(int(chunks)), "paged_attn_set_min_share")
 
 
 def paged_attn_set_heads_per_group(heads: int) -> None:

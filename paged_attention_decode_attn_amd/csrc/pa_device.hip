@@ -40,7 +40,6 @@
 #include <cmath>
 #include <map>
 #include <mutex>
-#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -63,6 +62,8 @@ constexpr unsigned kSelByte01 = 0x05010400u;  // v_perm: src1.b0, src0.b0, src1.
 constexpr unsigned kSelByte23 = 0x07030602u;  // v_perm: src1.b2, src0.b2, src1.b3, src0.b3
 constexpr int kRsrcWord3 = 0x00020000;        // raw buffer resource, 32-bit data format
 constexpr float kRescaleLog2 = 8.0f;          // lazy rescale threshold (log2 units)
+constexpr int kChunkTokens = 32;              // tokens per step (two 16-token blocks)
+constexpr int kWindowChunks = 32;             // chunks per 64-entry block-table window
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
@@ -72,24 +73,25 @@ struct PartArgs {
     const char* v;   int64_t v_stok, v_sh;            // bytes
     const float* ks; int64_t ks_sh;                   // floats
     const float* vs; int64_t vs_sh;
-    uint32_t k_sblk, v_sblk, ks_sblk, vs_sblk;        // block strides, bytes (< 2^31)
+    uint32_t k_sblk, v_sblk, ks_sblk, vs_sblk;        // block strides, bytes (< 2^32)
     const int32_t* bt; int64_t bt_sb;
     const int32_t* ctx; int64_t ctx_s;
     const int32_t* ql;  int64_t ql_s;
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
-    float* ws_o;     float* ws_lse;
-    float scale_log2;                                  // |scale| * log2(e)
-    int32_t q_neg;                                     // scale < 0: negate q
-    int32_t k_span, v_span;                            // bytes of one (block, head) slice
-    int32_t B, Hq, Hkv, G, Qmax, W, NB, T, P, rows, HG;
+    float* ws_o;     float* ws_lse;                   // partial results: 2 slots per (workgroup, wave, row)
+    int32_t* ws_pre;                                  // chunk prefix per sequence, for the merge (may be null)
+    float scale_log2;                                 // |scale| * log2(e)
+    int32_t q_neg;                                    // scale < 0: negate q
+    int32_t k_span, v_span;                           // bytes of one (block, head) slice
+    int32_t B, Hq, Hkv, G, Qmax, W, NB, rows, HG, min_share;
 };
 
 struct RedArgs {
-    const float* ws_o; const float* ws_lse;
-    const int32_t* ctx; int64_t ctx_s;
+    const float* ws_o; const float* ws_lse; const int32_t* ws_pre;
     const int32_t* ql;  int64_t ql_s;
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
-    int32_t Hq, Qmax, W, T, P;
+    int32_t B, Hq, Hkv, G, Qmax, rows, HG, grid, min_share;
+    int32_t red_rows, red_col4, red_lanes;            // merge workgroup shape (see reduce_kernel)
 };
 
 template <typename T>
@@ -114,11 +116,19 @@ template <> struct VLoad<64, false>  { typedef u32x2 T; };
 template <> struct VLoad<128, true>  { typedef u32x2 T; };
 template <> struct VLoad<64, true>   { typedef unsigned T; };
 
+// fp8 with head_dim 64: a lane's piece of a V row is only 4 bytes, so V and
+// the scales travel in 16-byte loads shared by each quad of lanes and are
+// spread over the quad in registers (unpack_quad): 5 load instructions per
+// step instead of 14.
+template <int D, bool FP8> constexpr bool kQuadV = FP8 && D == 64;
+
 template <int D, bool FP8> struct Step {
     static constexpr int KL = FP8 ? D / 64 : D / 32;
     u32x4 k[2][KL];
     typename VLoad<D, FP8>::T v[8];
     f32x4 ksc[2], vsc[2];
+    u32x4 vq[2];     // kQuadV: 16-byte V pieces of blocks 0 and 1
+    u32x4 sq;        // kQuadV: one 16-byte piece of the step's scales
 };
 
 template <int D, bool FP8, int NT> struct State {
@@ -151,36 +161,101 @@ struct HeadBase {
 
 template <int D, bool FP8>
 __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, const HeadBase& hb, int bid_lane,
-                                          int step, int last_blk, const unsigned (&koff)[Step<D, FP8>::KL],
-                                          const unsigned (&voff)[4], unsigned soff) {
+                                          int step, int nsteps, int last_blk,
+                                          const unsigned (&koff)[Step<D, FP8>::KL], const unsigned (&voff)[4],
+                                          unsigned soff) {
     typedef typename VLoad<D, FP8>::T VT;
-    // block 2*step always holds keys of the sequence; block 2*step + 1 may
-    // lie past it, and then reads as zeros through an empty range
-    const int b0 = __builtin_amdgcn_readlane(bid_lane, 2 * step);
-    const int b1 = __builtin_amdgcn_readlane(bid_lane, min(2 * step + 1, last_blk));
-    const bool has1 = 2 * step + 1 <= last_blk;
+    // For step < nsteps, block 2*step holds keys of the sequence and block
+    // 2*step + 1 may lie past it; a block past the sequence, or a whole step
+    // past the window (a prefetch beyond its end), reads as zeros through an
+    // empty range, which costs no memory traffic.
+    const bool has0 = step < nsteps;
+    const bool has1 = has0 && 2 * step + 1 <= last_blk;
+    const int sc = min(step, nsteps - 1);
+    const int b0 = __builtin_amdgcn_readlane(bid_lane, 2 * sc);
+    const int b1 = __builtin_amdgcn_readlane(bid_lane, min(2 * sc + 1, last_blk));
     const uint32_t u0 = (uint32_t)b0, u1 = (uint32_t)b1;
-    const Rsrc k0 = make_rsrc(hb.k + (uint64_t)u0 * a.k_sblk, a.k_span);
+    const Rsrc k0 = make_rsrc(hb.k + (uint64_t)u0 * a.k_sblk, has0 ? a.k_span : 0);
     const Rsrc k1 = make_rsrc(hb.k + (uint64_t)u1 * a.k_sblk, has1 ? a.k_span : 0);
-    const Rsrc v0 = make_rsrc(hb.v + (uint64_t)u0 * a.v_sblk, a.v_span);
+    const Rsrc v0 = make_rsrc(hb.v + (uint64_t)u0 * a.v_sblk, has0 ? a.v_span : 0);
     const Rsrc v1 = make_rsrc(hb.v + (uint64_t)u1 * a.v_sblk, has1 ? a.v_span : 0);
 #pragma unroll
     for (int c = 0; c < Step<D, FP8>::KL; ++c) {
         st.k[0][c] = bload<u32x4>(k0, koff[c]);
         st.k[1][c] = bload<u32x4>(k1, koff[c]);
     }
+    if constexpr (kQuadV<D, FP8>) {
+        // lane (n16 = 4q + r, grp): bytes 16q..16q+15 of slot 4grp + r of
+        // each block, and one scale piece: quad position r picks k scales of
+        // block 0 or 1 or v scales of block 0 or 1, slots 4grp..4grp+3 (the
+        // block ids are valid pool blocks, so the plain load stays in bounds;
+        // scales of positions past L are zeroed before use)
+        st.vq[0] = bload<u32x4>(v0, voff[0]);
+        st.vq[1] = bload<u32x4>(v1, voff[0]);
+        const int r = __lane_id() & 3;
+        const char* base = (r & 2) ? hb.vs : hb.ks;
+        const uint64_t sblk = (r & 2) ? a.vs_sblk : a.ks_sblk;
+        st.sq = *reinterpret_cast<const u32x4*>(base + (uint64_t)((r & 1) ? u1 : u0) * sblk + soff);
+        return;
+    }
 #pragma unroll
     for (int s = 0; s < 8; ++s) st.v[s] = bload<VT>(s < 4 ? v0 : v1, voff[s & 3]);
     if constexpr (FP8) {
         // one block's 16 slot scales of this kv head are contiguous (64 bytes)
-        const Rsrc s0 = make_rsrc(hb.ks + (uint64_t)u0 * a.ks_sblk, 64);
+        const Rsrc s0 = make_rsrc(hb.ks + (uint64_t)u0 * a.ks_sblk, has0 ? 64 : 0);
         const Rsrc s1 = make_rsrc(hb.ks + (uint64_t)u1 * a.ks_sblk, has1 ? 64 : 0);
-        const Rsrc t0 = make_rsrc(hb.vs + (uint64_t)u0 * a.vs_sblk, 64);
+        const Rsrc t0 = make_rsrc(hb.vs + (uint64_t)u0 * a.vs_sblk, has0 ? 64 : 0);
         const Rsrc t1 = make_rsrc(hb.vs + (uint64_t)u1 * a.vs_sblk, has1 ? 64 : 0);
         st.ksc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(s0, soff));
         st.ksc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(s1, soff));
         st.vsc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(t0, soff));
         st.vsc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(t1, soff));
+    }
+}
+
+// DPP quad permutations (lane i of each quad reads lane sel[i]).
+template <int CTRL>
+__device__ __forceinline__ unsigned quad_perm(unsigned x) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadXor2 = 0x4E;      // [2, 3, 0, 1]
+constexpr int kQuadXor1 = 0xB1;      // [1, 0, 3, 2]
+
+// 4x4 transpose of dwords within each quad of lanes: dword k of quad lane r
+// becomes dword r of quad lane k.  Two exchange rounds (partner r^2 swaps
+// dword pairs, partner r^1 swaps single dwords).
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 m, int r) {
+    const bool hi = r & 2, odd = r & 1;
+    unsigned x0 = hi ? m[0] : m[2], x1 = hi ? m[1] : m[3];
+    x0 = quad_perm<kQuadXor2>(x0);
+    x1 = quad_perm<kQuadXor2>(x1);
+    m[0] = hi ? x0 : m[0]; m[1] = hi ? x1 : m[1];
+    m[2] = hi ? m[2] : x0; m[3] = hi ? m[3] : x1;
+    x0 = odd ? m[0] : m[1];
+    x1 = odd ? m[2] : m[3];
+    x0 = quad_perm<kQuadXor1>(x0);
+    x1 = quad_perm<kQuadXor1>(x1);
+    m[0] = odd ? x0 : m[0]; m[2] = odd ? x1 : m[2];
+    m[1] = odd ? m[1] : x0; m[3] = odd ? m[3] : x1;
+    return m;
+}
+
+// kQuadV: spread the quad-shared loads into the per-lane layout of the other
+// variants: v[i] = 4 bytes (d = 4*n16 ..) of this lane's token slot i, and
+// the k/v scales of its 4 slots in each block.
+template <int D, bool FP8>
+__device__ __forceinline__ void unpack_quad(Step<D, FP8>& st, int lane) {
+    const int r = lane & 3;
+    const u32x4 t0 = quad_transpose(st.vq[0], r);
+    const u32x4 t1 = quad_transpose(st.vq[1], r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        st.v[i] = t0[i];
+        st.v[4 + i] = t1[i];
+        st.ksc[0][i] = __builtin_bit_cast(float, quad_perm<0x00>(st.sq[i]));
+        st.ksc[1][i] = __builtin_bit_cast(float, quad_perm<0x55>(st.sq[i]));
+        st.vsc[0][i] = __builtin_bit_cast(float, quad_perm<0xAA>(st.sq[i]));
+        st.vsc[1][i] = __builtin_bit_cast(float, quad_perm<0xFF>(st.sq[i]));
     }
 }
 
@@ -272,6 +347,7 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
                                              const PartArgs& a, int cbase, int L, int nq, int lane) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
+    if constexpr (kQuadV<D, FP8>) unpack_quad<D, FP8>(st, lane);
 
     if constexpr (MASK) {
         // zero V rows (and scales) of positions >= L so that p = 0 never
@@ -371,27 +447,34 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
     }
 }
 
-// One work item = (sequence b, kv head g, partition p) of T tokens, run by
-// one wave: the partition's online-softmax state ends as the output row when
-// the sequence has a single partition, otherwise as the normalised fp32
-// partial output and its base-2 log-sum-exp for the merge kernel.
+// Block-table window of a piece: entry 2*pc + lane of sequence b (clamped to
+// the table), its block id clamped into the pool.
+__device__ __forceinline__ int load_window(const PartArgs& a, int b, int pc, int lane) {
+    const int idx = min(2 * pc + lane, a.W - 1);
+    const int v = a.bt[(int64_t)b * a.bt_sb + idx];
+    return min(max(v, 0), a.NB - 1);
+}
+
+// One segment = chunks [c0, c1) of the cb chunks (32 tokens each) of
+// sequence b for kv head g, run by one wave of workgroup w.  The segment's
+// online-softmax state ends as the output row when the segment is the whole
+// sequence, otherwise as a normalised fp32 partial output and its base-2
+// log-sum-exp in the workgroup's partial slot `slot` (0: the first segment
+// of its share, 1: the last) for the merge kernel.  Chunks are processed in
+// pieces of up to 32 (one 64-entry block-table window per piece).
 template <int D, bool FP8, int NT>
-__device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, int p, int lane) {
+__device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g, int wave, int c0, int c1, int cb,
+                                                int w, int slot, int lane) {
     constexpr int J = D / 16;
     constexpr int KL = Step<D, FP8>::KL;
     constexpr int E = FP8 ? 1 : 2;
+    constexpr int R = NT > 2 ? 1 : 2;    // register buffers: loads of R-1 steps ahead in flight
     const int n16 = lane & 15, grp = lane >> 4;
 
-    // Issue every start-up load at once: the sequence's lengths, this
-    // partition's block-table slice and the query fragments do not depend
-    // on each other, so the first K/V loads wait for one round trip only.
-    const int tok0 = p * a.T;
-    int bid_lane;        // block-table entry tok0/16 + lane (clamped to the table)
-    {
-        const int idx = min(tok0 / 16 + lane, a.W - 1);
-        const int v = a.bt[(int64_t)b * a.bt_sb + idx];
-        bid_lane = min(max(v, 0), a.NB - 1);
-    }
+    // Start-up loads issued together: the first block-table window, the
+    // query fragments and the lengths do not depend on each other, so the
+    // first K/V loads wait for one round trip only.
+    int bid_lane = load_window(a, b, c0, lane);
     // query fragments: row r = 16*nt + n16 -> (t, h_local) = (r / G, r % G);
     // rows t < Qmax are in bounds, rows past query_len are zeroed below
     u32x4 qf[NT][D / 32];
@@ -408,13 +491,6 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
     }
     const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
     const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
-    if (L <= 0 || nq <= 0 || tok0 >= L) return;
-    const bool direct = (L + a.T - 1) / a.T == 1;
-    const int nsteps = (min(L, tok0 + a.T) - tok0 + 31) / 32;
-    // steps [0, nclean) hold only keys below L that every query row sees
-    const int nclean = min(nsteps, max(0, L - nq + 1 - tok0) / 32);
-    // last block of the sequence relative to the slice
-    const int last_blk = (L + 15) / 16 - 1 - tok0 / 16;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int row = 16 * nt + n16;
@@ -436,6 +512,7 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
     unsigned voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) voff[i] = (unsigned)((4 * grp + i) * a.v_stok) + (unsigned)((D / 16) * n16 * E);
+    if constexpr (kQuadV<D, FP8>) voff[0] = (unsigned)((4 * grp + (n16 & 3)) * a.v_stok) + 16u * (unsigned)(n16 >> 2);
     const unsigned soff = 16u * (unsigned)grp;
 
     State<D, FP8, NT> s;
@@ -447,49 +524,42 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
         for (int j = 0; j < J; ++j) s.acc[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // two register buffers: the next step's loads are in flight while the
-    // current step computes; straight-line code on every path keeps the
-    // memory-counter waits exact (one buffer when the row tiles leave no
-    // registers for a second).  The last one or two steps take the masked
-    // variant whether they need it or not.
-    Step<D, FP8> bufA, bufB;
-    if constexpr (NT > 2) {
+    for (int pc = c0; pc < c1; pc += kWindowChunks) {
+        if (pc != c0) bid_lane = load_window(a, b, pc, lane);
+        const int tok0 = kChunkTokens * pc;
+        const int nsteps = min(c1, pc + kWindowChunks) - pc;
+        // steps [0, nclean) hold only keys below L that every query row sees
+        const int nclean = min(nsteps, max(0, L - nq + 1 - tok0) / kChunkTokens);
+        // last block of the sequence, relative to the window
+        const int last_blk = (L + 15) / 16 - 1 - 2 * pc;
+        // A ring of R register buffers: while a step computes, the loads of
+        // the next R-1 steps are in flight.  Loads are issued on every path
+        // (past the window they read nothing), so the code between a load
+        // and its use is straight-line and the memory-counter waits exact;
+        // the last steps of the piece take the masked variant.
+        Step<D, FP8> buf[R];
+#pragma unroll
+        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8>(buf[i], a, hb, bid_lane, i, nsteps, last_blk, koff, voff, soff);
         int st = 0;
-        for (; st < nclean; ++st) {
-            load_step<D, FP8>(bufA, a, hb, bid_lane, st, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, false>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        for (; st + R <= nclean; st += R) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                load_step<D, FP8>(buf[(i + R - 1) % R], a, hb, bid_lane, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                compute_step<D, FP8, NT, false>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, lane);
+            }
         }
-        for (; st < nsteps; ++st) {
-            load_step<D, FP8>(bufA, a, hb, bid_lane, st, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-        }
-    } else {
-        load_step<D, FP8>(bufA, a, hb, bid_lane, 0, last_blk, koff, voff, soff);
-        int st = 0;
-        while (st + 2 < nsteps && st + 1 < nclean) {
-            load_step<D, FP8>(bufB, a, hb, bid_lane, st + 1, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, false>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-            load_step<D, FP8>(bufA, a, hb, bid_lane, st + 2, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, false>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
-            st += 2;
-        }
-        while (st + 2 < nsteps) {
-            load_step<D, FP8>(bufB, a, hb, bid_lane, st + 1, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-            load_step<D, FP8>(bufA, a, hb, bid_lane, st + 2, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, true>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
-            st += 2;
-        }
-        if (st + 1 < nsteps) {
-            load_step<D, FP8>(bufB, a, hb, bid_lane, st + 1, last_blk, koff, voff, soff);
-            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
-            compute_step<D, FP8, NT, true>(bufB, s, qf, a, tok0 + 32 * (st + 1), L, nq, lane);
-        } else {
-            compute_step<D, FP8, NT, true>(bufA, s, qf, a, tok0 + 32 * st, L, nq, lane);
+        for (; st < nsteps; st += R) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                load_step<D, FP8>(buf[(i + R - 1) % R], a, hb, bid_lane, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                if (st + i < nsteps)
+                    compute_step<D, FP8, NT, true>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, lane);
+            }
         }
     }
 
     // epilogue: lane holds d = (D/16)*(4*grp + i) + j, j < D/16, of row 16*nt + n16
+    const bool direct = c0 == 0 && c1 == cb;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float lt = s.l[nt];
@@ -506,185 +576,226 @@ __device__ __forceinline__ void process_item(const PartArgs& a, int b, int g, in
             for (int i = 0; i < 4; ++i) {
                 const int d0 = J * (4 * grp + i);
                 if constexpr (J == 8) {
-                    u32x4 w;
+                    u32x4 wv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        w[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
-                    *reinterpret_cast<u32x4*>(orow + 2 * d0) = w;
+                        wv[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
+                    *reinterpret_cast<u32x4*>(orow + 2 * d0) = wv;
                 } else {
-                    u32x2 w;
+                    u32x2 wv;
 #pragma unroll
                     for (int e = 0; e < 2; ++e)
-                        w[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
-                    *reinterpret_cast<u32x2*>(orow + 2 * d0) = w;
+                        wv[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
+                    *reinterpret_cast<u32x2*>(orow + 2 * d0) = wv;
                 }
             }
         } else {
-            const int64_t rowg = ((int64_t)b * a.Qmax + t) * a.Hq + h;
-            float* wo = a.ws_o + (rowg * a.P + p) * D;
+            const int64_t pid = ((int64_t)(2 * w + slot) * a.HG + wave) * a.rows + row;
+            float* wo = a.ws_o + pid * D;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = J * (4 * grp + i);
 #pragma unroll
                 for (int e = 0; e < J / 4; ++e) {
-                    f32x4 w;
+                    f32x4 wv;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) w[k] = s.acc[nt][4 * e + k][i] * inv;
-                    *reinterpret_cast<f32x4*>(wo + d0 + 4 * e) = w;
+                    for (int k = 0; k < 4; ++k) wv[k] = s.acc[nt][4 * e + k][i] * inv;
+                    *reinterpret_cast<f32x4*>(wo + d0 + 4 * e) = wv;
                 }
             }
-            if (grp == 0) a.ws_lse[rowg * a.P + p] = lt > 0.f ? s.m[nt] + __log2f(lt) : -__builtin_inff();
+            if (grp == 0) a.ws_lse[pid] = lt > 0.f ? s.m[nt] + __log2f(lt) : -__builtin_inff();
         }
     }
 }
 
-// Persistent partition kernel.  A workgroup is HG waves, wave w serving kv
-// head g0 + w of one (sequence, partition) item at a time, so the waves of a
-// CU read the adjacent head rows of the same tokens (whole contiguous token
-// rows of the cache).  As many workgroups run as the chip holds at once;
-// workgroup w takes items w, w + grid, w + 2 grid, ... of the list of
-// non-empty (sequence, partition) pairs times the head groups, so every
-// workgroup gets the same number of equal-sized items to within one,
-// whatever the ragged context lengths, and no slot is spent on empty
-// partitions.  Wave 0 scans the per-sequence partition counts into LDS;
-// every wave maps an item to its sequence with a 64-wide ballot over that
-// prefix (the items of a workgroup only increase).
+// Even shares of the chunk space.  The chunks (32-token pieces) of every
+// (sequence, kv-head group) segment, sequence-major, are numbered 0..C-1;
+// workgroup w of n takes [w*C/n, (w+1)*C/n).  n is the launched grid,
+// lowered so that every share holds at least min_share chunks.  The merge
+// kernel recomputes the same numbers to find a row's partial results.
+__device__ __forceinline__ int share_count(int grid, int64_t C, int min_share) {
+    const int64_t cap = C / max(min_share, 1);
+    return (int)max<int64_t>(1, min<int64_t>(grid, cap));
+}
+__device__ __forceinline__ int64_t share_begin(int w, int64_t C, int n) { return (int64_t)w * C / n; }
+// the workgroup whose share holds chunk c (the largest w with share_begin(w) <= c)
+__device__ __forceinline__ int share_owner(int64_t c, int64_t C, int n) {
+    return (int)(((c + 1) * n + C - 1) / C) - 1;
+}
+
+// Partition kernel.  A workgroup is HG waves, wave v serving kv head
+// gg*HG + v of the segments in its share, so the waves of a CU read the
+// adjacent head rows of the same tokens (whole contiguous token rows of the
+// cache).  Every workgroup gets the same number of chunks to within one,
+// whatever the ragged context lengths: a share may start and end inside a
+// sequence and may hold several whole sequences.  Wave 0 scans the
+// per-sequence chunk counts into LDS (workgroup 0 also stores the scan for
+// the merge kernel); every wave finds a chunk's sequence with a 64-wide
+// ballot over that prefix (a share's chunks only increase).
 template <int D, bool FP8, int NT>
 __global__ __launch_bounds__(NT == 1 ? 512 : 256)
 __attribute__((amdgpu_waves_per_eu(NT == 1 ? (FP8 && D == 64 ? 3 : 2) : 1)))
 void partition_kernel(PartArgs a) {
-    extern __shared__ int s_pre[];               // inclusive prefix of partitions per sequence
+    extern __shared__ int s_pre[];               // inclusive prefix of chunks per sequence
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave == 0) {
         int carry = 0;
         for (int b0 = 0; b0 < a.B; b0 += 64) {
             const int b = b0 + lane;
-            int np = 0;
+            int nc = 0;
             if (b < a.B) {
                 const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
                 const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
-                np = (L > 0 && nq > 0) ? (L + a.T - 1) / a.T : 0;
+                nc = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens : 0;
             }
-            int x = np;
+            int x = nc;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const int y = __shfl_up(x, o);
                 if (lane >= o) x += y;
             }
-            if (b < a.B) s_pre[b] = carry + x;
+            if (b < a.B) {
+                s_pre[b] = carry + x;
+                if (blockIdx.x == 0 && a.ws_pre) a.ws_pre[b] = carry + x;
+            }
             carry += __shfl(x, 63);
         }
     }
     __syncthreads();
-    const int S = a.B > 0 ? s_pre[a.B - 1] : 0;  // non-empty (sequence, partition) pairs
     const int ngrp = a.Hkv / a.HG;
-    const int total = S * ngrp;
+    const int64_t C = (int64_t)(a.B > 0 ? s_pre[a.B - 1] : 0) * ngrp;
+    const int n = share_count((int)gridDim.x, C, a.min_share);
+    const int w = blockIdx.x;
+    if (w >= n) return;
+    const int64_t lo = share_begin(w, C, n), hi = share_begin(w + 1, C, n);
     int bbase = 0;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int sp = item / ngrp, g = (item - sp * ngrp) * a.HG + wave;
-        // sequence b = number of sequences whose inclusive prefix is <= sp
+    for (int64_t pos = lo; pos < hi;) {
+        // sequence b = number of sequences whose segments end at or before pos
         int b;
         for (;;) {
             const int idx = bbase + lane;
-            const bool le = idx < a.B && s_pre[idx] <= sp;
+            const bool le = idx < a.B && (int64_t)s_pre[idx] * ngrp <= pos;
             const int k = __popcll(__ballot(le));
             if (k < 64) { b = bbase + k; break; }
             bbase += 64;
         }
         bbase = b & ~63;
-        const int first = b > 0 ? s_pre[b - 1] : 0;
-        process_item<D, FP8, NT>(a, b, g, sp - first, lane);
+        const int pre = b > 0 ? s_pre[b - 1] : 0;
+        const int cb = s_pre[b] - pre;
+        const int within = (int)(pos - (int64_t)pre * ngrp);
+        const int gg = within / cb;
+        const int c0 = within - gg * cb;
+        const int c1 = (int)min<int64_t>(cb, c0 + (hi - pos));
+        process_segment<D, FP8, NT>(a, b, gg * a.HG + wave, wave, c0, c1, cb, w, pos == lo ? 0 : 1, lane);
+        pos += c1 - c0;
     }
 }
 
-// Merge of the partitions of one query row (b, t, h): log-sum-exp weights
-// in base 2, float32 throughout, bf16 round-to-nearest-even at the end.
-// blockDim.x = (D/4) columns x PS partition lanes; each partition lane runs
-// an online merge over partitions ps, ps + PS, ... with U loads in flight,
-// then the PS partial merges combine through LDS.
-constexpr int kRedMaxThreads = 1024;
-constexpr int kRedUnroll = 4;
-
+// Merge of the partial results of query rows: log-sum-exp weights in base
+// 2, float32 throughout, bf16 round-to-nearest-even at the end.  The rows
+// of one (sequence b, query t, kv head g) share a segment, which spans the
+// shares of workgroups first..last; each of those left one partial per row
+// in its slot (slot 1 for the first workgroup when the segment is not the
+// first of its share).  A merge workgroup takes RG of those rows and CB
+// float4 columns; each (row, column) has PL partial lanes, each running an
+// online merge over partials pl, pl + PL, ... with U loads in flight, and
+// the lanes combine through LDS.  The host picks RG, CB and PL from the
+// expected partials per row, so that short lists merge in one round of
+// loads over many rows and long lists spread over many lanes.
 template <int D>
-__global__ __launch_bounds__(kRedMaxThreads) void reduce_kernel(RedArgs a) {
-    constexpr int V4 = D / 4;
+__global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
     constexpr int U = kRedUnroll;
     const int tid = threadIdx.x;
-    const int PS = blockDim.x / V4;
+    const int RG = a.red_rows, CB = a.red_col4, PL = a.red_lanes;
+    const int ncb = (D / 4) / CB, nrg = a.G / RG;
     int64_t id = blockIdx.x;
-    const int h = (int)(id % a.Hq);
-    id /= a.Hq;
+    const int cbi = (int)(id % ncb); id /= ncb;
+    const int rgi = (int)(id % nrg); id /= nrg;
+    const int g = (int)(id % a.Hkv); id /= a.Hkv;
     const int t = (int)(id % a.Qmax);
     const int b = (int)(id / a.Qmax);
-    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
     const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
-    if (L <= 0 || t >= nq) return;
-    const int np = (L + a.T - 1) / a.T;
-    if (np <= 1) return;                        // written by the partition kernel
-    const int64_t rowg = blockIdx.x;
-    const float* lse = a.ws_lse + rowg * a.P;
-    const float* wo = a.ws_o + rowg * a.P * D;
+    if (t >= nq) return;
+    const int pre = b > 0 ? a.ws_pre[b - 1] : 0;
+    const int cb = a.ws_pre[b] - pre;
+    if (cb <= 0) return;
+    const int ngrp = a.Hkv / a.HG;
+    const int64_t C = (int64_t)a.ws_pre[a.B - 1] * ngrp;
+    const int n = share_count(a.grid, C, a.min_share);
+    const int gg = g / a.HG, wave = g - gg * a.HG;
+    const int64_t S = (int64_t)pre * ngrp + (int64_t)gg * cb;
+    const int first = share_owner(S, C, n), last = share_owner(S + cb - 1, C, n);
+    if (first == last) return;                  // written by the partition kernel
+    const int np = last - first + 1;
+    const int slot0 = share_begin(first, C, n) == S ? 0 : 1;
 
-    __shared__ float sm[kRedMaxThreads / V4], sw[kRedMaxThreads / V4];
-    __shared__ f32x4 sacc[kRedMaxThreads / V4][V4];
-
-    const int d4 = tid % V4, ps = tid / V4;
+    // thread = (pl, rg, c): columns fastest, so a wave reads whole partial rows
+    const int c = tid % CB, rg = (tid / CB) % RG, pl = tid / (CB * RG);
+    const bool active = pl < PL;
+    const int hl = rgi * RG + rg;                 // query head within the group
+    const int r = t * a.G + hl;                   // row within the kv head's rows
+    const int col = 4 * (cbi * CB + c);
     const float ninf = -__builtin_inff();
     float m = ninf, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = ps; p0 < np; p0 += PS * U) {
-        float l[U];
-        f32x4 o[U];
+    if (active) {
+        for (int p0 = pl; p0 < np; p0 += PL * U) {
+            float l[U];
+            f32x4 o[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 + u * PS;
-            if (p < np) {
-                l[u] = lse[p];
-                o[u] = *reinterpret_cast<const f32x4*>(wo + (int64_t)p * D + 4 * d4);
-            } else {
-                l[u] = ninf;
-                o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + u * PL;
+                if (p < np) {
+                    const int64_t pid = ((int64_t)(2 * (first + p) + (p == 0 ? slot0 : 0)) * a.HG + wave) * a.rows + r;
+                    l[u] = a.ws_lse[pid];
+                    o[u] = *reinterpret_cast<const f32x4*>(a.ws_o + pid * D + col);
+                } else {
+                    l[u] = ninf;
+                    o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
-        }
-        float mn = m;
+            float mn = m;
 #pragma unroll
-        for (int u = 0; u < U; ++u) mn = fmaxf(mn, l[u]);
-        const float mu = mn == ninf ? 0.f : mn;
-        const float c = __builtin_amdgcn_exp2f(m - mu);
-        wsum *= c;
-        acc *= c;
+            for (int u = 0; u < U; ++u) mn = fmaxf(mn, l[u]);
+            const float mu = mn == ninf ? 0.f : mn;
+            const float sc = __builtin_amdgcn_exp2f(m - mu);
+            wsum *= sc;
+            acc *= sc;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float w = __builtin_amdgcn_exp2f(l[u] - mu);
-            wsum += w;
-            acc += w * o[u];
+            for (int u = 0; u < U; ++u) {
+                const float wt = __builtin_amdgcn_exp2f(l[u] - mu);
+                wsum += wt;
+                acc += wt * o[u];
+            }
+            m = mn;
         }
-        m = mn;
     }
-    if (d4 == 0) {
-        sm[ps] = m;
-        sw[ps] = wsum;
-    }
-    sacc[ps][d4] = acc;
+    __shared__ float sm[kRedThreads], sw[kRedThreads];
+    __shared__ f32x4 sacc[kRedThreads];
+    sm[tid] = m;
+    sw[tid] = wsum;
+    sacc[tid] = acc;
     __syncthreads();
-    if (ps == 0) {
-        float M = sm[0];
-        for (int q = 1; q < PS; ++q) M = fmaxf(M, sm[q]);
+    if (active && pl == 0) {
+        const int stride = CB * RG;
+        float M = m;
+        for (int q = 1; q < PL; ++q) M = fmaxf(M, sm[tid + q * stride]);
         const float Mu = M == ninf ? 0.f : M;
         f32x4 tot = {0.f, 0.f, 0.f, 0.f};
         float wt = 0.f;
-        for (int q = 0; q < PS; ++q) {
-            const float c = __builtin_amdgcn_exp2f(sm[q] - Mu);
-            tot += c * sacc[q][d4];
-            wt += c * sw[q];
+        for (int q = 0; q < PL; ++q) {
+            const float sc = __builtin_amdgcn_exp2f(sm[tid + q * stride] - Mu);
+            tot += sc * sacc[tid + q * stride];
+            wt += sc * sw[tid + q * stride];
         }
         const float inv = wt > 0.f ? 1.f / wt : 0.f;
-        u32x2 w;
-        w[0] = pack_bf16_rne(tot[0] * inv, tot[1] * inv);
-        w[1] = pack_bf16_rne(tot[2] * inv, tot[3] * inv);
+        u32x2 wv;
+        wv[0] = pack_bf16_rne(tot[0] * inv, tot[1] * inv);
+        wv[1] = pack_bf16_rne(tot[2] * inv, tot[3] * inv);
+        const int h = g * a.G + hl;
         char* orow = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
-        *reinterpret_cast<u32x2*>(orow + 8 * d4) = w;
+        *reinterpret_cast<u32x2*>(orow + 2 * col) = wv;
     }
 }
 
@@ -765,24 +876,6 @@ const void* partition_kernel_of(int D, bool fp8, int nt) {
          : nt == 3 ? kernel_of<64, false, 3>() : kernel_of<64, false, 4>();
 }
 
-// Resident workgroups per CU for a kernel variant, block size and LDS size
-// (cached; the occupancy query is host-only).
-std::map<std::tuple<const void*, int, int, size_t>, int> g_occ;
-
-int resident_groups_per_cu(const void* fn, int dev, int threads, size_t lds) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    const auto key = std::make_tuple(fn, dev, threads, lds);
-    auto it = g_occ.find(key);
-    if (it != g_occ.end()) return it->second;
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess || nb < 1) {
-        (void)hipGetLastError();
-        nb = 1;
-    }
-    g_occ[key] = nb;
-    return nb;
-}
-
 }  // namespace
 }  // namespace pa
 
@@ -808,12 +901,11 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         (st = get_workspace(dev, stream, (size_t)plan.workspace_bytes, &ws)))
         return st;
 
-    const int64_t rows_total = pr.B * pr.Qmax * pr.Hq;
     const size_t lds = (size_t)pr.B * sizeof(int);
     const void* fn = partition_kernel_of((int)pr.D, pr.fp8, plan.row_tiles);
     const int HG = plan.heads_per_group;
-    const int64_t slots = (int64_t)resident_groups_per_cu(fn, dev, 64 * HG, lds) * device_cus(dev);
-    const int64_t groups = std::min<int64_t>(slots, plan.partition_groups);
+    const int64_t grid = plan.workgroups;
+    const int64_t nslot = 2 * grid * HG * plan.rows;      // partial slots (see PartArgs)
     PartArgs a;
     a.q = static_cast<const char*>(pr.q); a.q_sb = pr.q_sb * 2; a.q_st = pr.q_st * 2; a.q_sh = pr.q_sh * 2;
     a.k = static_cast<const char*>(pr.k); a.k_stok = pr.k_stok; a.k_sh = pr.k_sh;
@@ -827,15 +919,15 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
     a.ql = pr.ql; a.ql_s = pr.ql_s;
     a.out = static_cast<char*>(pr.out); a.o_sb = pr.o_sb * 2; a.o_st = pr.o_st * 2; a.o_sh = pr.o_sh * 2;
     a.ws_o = static_cast<float*>(ws);
-    a.ws_lse = a.ws_o + rows_total * plan.num_partitions * pr.D;
+    a.ws_lse = ws ? a.ws_o + nslot * pr.D : nullptr;
+    a.ws_pre = ws ? reinterpret_cast<int32_t*>(a.ws_lse + nslot) : nullptr;
     a.scale_log2 = std::fabs(pr.scale) * kLog2e;
     a.q_neg = pr.scale < 0.f;
     a.k_span = (int32_t)(15 * pr.k_stok + pr.D * (pr.fp8 ? 1 : 2));
     a.v_span = (int32_t)(15 * pr.v_stok + pr.D * (pr.fp8 ? 1 : 2));
     a.B = (int32_t)pr.B; a.Hq = (int32_t)pr.Hq; a.Hkv = (int32_t)pr.Hkv; a.G = (int32_t)pr.G; a.Qmax = (int32_t)pr.Qmax;
     a.W = (int32_t)pr.W; a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
-    a.T = plan.partition_tokens; a.P = plan.num_partitions; a.rows = plan.rows; a.HG = HG;
-
+    a.rows = plan.rows; a.HG = HG; a.min_share = plan.min_share_chunks;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr;
@@ -848,19 +940,21 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         }
     }
     if (e0) (void)hipEventRecord(e0, s);
-    if (groups > 0) {
+    {
         void* args[] = {&a};
-        if (hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * HG), args, lds, s) != hipSuccess)
+        if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * HG), args, lds, s) != hipSuccess)
             return fail(PA_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(hipGetLastError()));
     }
     if (e1) (void)hipEventRecord(e1, s);
     if (plan.reduce_groups > 0) {
         RedArgs r;
-        r.ws_o = a.ws_o; r.ws_lse = a.ws_lse;
-        r.ctx = a.ctx; r.ctx_s = a.ctx_s; r.ql = a.ql; r.ql_s = a.ql_s;
+        r.ws_o = a.ws_o; r.ws_lse = a.ws_lse; r.ws_pre = a.ws_pre;
+        r.ql = a.ql; r.ql_s = a.ql_s;
         r.out = a.out; r.o_sb = a.o_sb; r.o_st = a.o_st; r.o_sh = a.o_sh;
-        r.Hq = a.Hq; r.Qmax = a.Qmax; r.W = a.W; r.T = a.T; r.P = a.P;
-        const dim3 rgrid((unsigned)plan.reduce_groups), rblock((unsigned)plan.reduce_threads);
+        r.B = a.B; r.Hq = a.Hq; r.Hkv = a.Hkv; r.G = a.G; r.Qmax = a.Qmax; r.rows = a.rows; r.HG = HG;
+        r.grid = (int32_t)grid; r.min_share = a.min_share;
+        r.red_rows = plan.reduce_rows; r.red_col4 = plan.reduce_col4; r.red_lanes = plan.reduce_lanes;
+        const dim3 rgrid((unsigned)plan.reduce_groups), rblock((unsigned)kRedThreads);
         if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, rgrid, rblock, 0, s, r);
         else hipLaunchKernelGGL(reduce_kernel<64>, rgrid, rblock, 0, s, r);
     }

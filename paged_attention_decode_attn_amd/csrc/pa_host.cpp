@@ -1,6 +1,7 @@
 // Host-side half of the library: argument validation, the split-context
 // planner, metadata checks and error strings.  Plain C++ with no HIP calls,
 // so every function here runs (and is tested) on a machine without a GPU.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -13,8 +14,9 @@ namespace pa {
 
 namespace {
 thread_local char g_last_error[512] = "";
-std::atomic<int32_t> g_partition_override{0};
+std::atomic<int32_t> g_grid_override{0};
 std::atomic<int32_t> g_group_override{0};
+std::atomic<int32_t> g_share_override{0};
 
 int64_t elem_bytes(int32_t dtype) {
     switch (dtype) {
@@ -215,72 +217,57 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
         return fail(PA_ERR_ARG, "plan: invalid sizes");
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
-    const int64_t max_tokens = int64_t(PA_BLOCK_SIZE) * W;
     // waves one CU holds for the kernel variant (register budget) and the
     // largest kv-head group (one wave per head) a workgroup may carry
     const int64_t cu_waves = row_tiles == 1 ? (fp8 && D == 64 ? 12 : 8) : 4;
     const int64_t hg_cap = row_tiles == 1 ? 8 : 4;
-    auto largest_group = [&](int64_t cap) {
-        for (int64_t h = cap; h >= 1; --h)
-            if (Hkv % h == 0 && cu_waves % h == 0) return h;
-        return int64_t(1);
-    };
-    // Expected context per sequence: the table width for one sequence, half
-    // of it for a ragged batch (only shapes are known here, never lengths).
-    const int64_t expect = B > 1 ? (max_tokens + 1) / 2 : max_tokens;
-    auto items = [&](int64_t hg, int64_t t) { return B * (Hkv / hg) * ((expect + t - 1) / t); };
-    auto slots = [&](int64_t hg) { return int64_t(num_cus) * (cu_waves / hg); };
-
     const int64_t hg_over = g_group_override.load();
-    int64_t HG = hg_over > 0 ? hg_over : largest_group(hg_cap);
-    if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
-    auto largest_filling = [&](int64_t hg) {      // largest T with an item for every slot
-        for (int64_t t = kMaxWaveTokens; t >= kChunk; t /= 2)
-            if (items(hg, t) >= slots(hg)) return t;
-        return int64_t(kChunk);
-    };
-    int64_t T = g_partition_override.load();
-    if (T <= 0) {
-        if (max_tokens <= 16 * kChunk) {
-            // short contexts: one partition per (sequence, head), no merge
-            // kernel, heads spread over the chip
-            if (hg_over <= 0) HG = 1;
-            T = max_tokens;
-        } else {
-            // heads grouped per CU (whole token rows read together) with the
-            // largest partition that gives every workgroup slot an item; if
-            // that needs partitions under 256 tokens, the call is small:
-            // spread the heads instead; ragged batches prefer 256 tokens when
-            // that leaves >= 4 items per slot (equal shares to within one)
-            T = largest_filling(HG);
-            if (T < 256 && hg_over <= 0 && HG > 1) {
-                HG = 1;
-                T = largest_filling(HG);
-            }
-            if (B > 1 && T > 256 && items(HG, 256) >= 4 * slots(HG)) T = 256;
-        }
+    int64_t HG = 1;
+    if (hg_over > 0) {
+        HG = hg_over;
+    } else {
+        for (int64_t h = hg_cap; h >= 1; --h)
+            if (Hkv % h == 0 && cu_waves % h == 0) { HG = h; break; }
     }
-    T = ((T + kChunk - 1) / kChunk) * kChunk;
-    if (T < kChunk) T = kChunk;
-    if (T > kMaxWaveTokens) T = kMaxWaveTokens;
-    const int64_t P = (max_tokens + T - 1) / T;
-    if (P > kMaxPartitions) return fail(PA_ERR_UNSUPPORTED, "context too long for the partition limit");
-    // merge workgroup: D/4 columns x enough partition lanes that every lane
-    // has at most 4 partitions (one round of loads), up to 1024 threads
-    const int64_t cols = D / 4;
-    int64_t lanes = 1;
-    while (lanes * 4 < P && cols * lanes * 2 <= 1024) lanes *= 2;
-    plan->partition_tokens = int32_t(T);
-    plan->num_partitions = int32_t(P);
+    if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
+    // chunk space: 32-token chunks of every (sequence, head group) segment;
+    // only its upper bound is known here (lengths live on the device)
+    const int64_t seq_chunks = (int64_t(PA_BLOCK_SIZE) * W + kChunkTokens - 1) / kChunkTokens;
+    const int64_t max_chunks = B * (Hkv / HG) * seq_chunks;
+    if (max_chunks >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "batch x context too large for the chunk index");
+    const int64_t share_over = g_share_override.load();
+    const int64_t min_share = share_over > 0 ? share_over : kDefaultMinShare;
+    // one workgroup per resident slot (every wave of the chip streams from
+    // the first cycle to the last), fewer when the chunks cannot fill them
+    const int64_t slots = int64_t(num_cus) * (cu_waves / HG);
+    const int64_t grid_over = g_grid_override.load();
+    int64_t n = grid_over > 0 ? grid_over : slots;
+    n = std::max<int64_t>(1, std::min<int64_t>(n, max_chunks / min_share));
+    // Merge shape.  Expected partials per row: one per workgroup whose share
+    // meets the row's segment, about n / (B * groups) + 1 when the lengths are
+    // alike (a lopsided batch only takes more rounds of loads).  PL lanes
+    // with 8 loads in flight each cover that in one round; the rest of the
+    // 256 threads go to float4 columns (CB) and rows of the same segment (RG).
+    const int64_t expected = (n + std::max<int64_t>(1, B * (Hkv / HG)) - 1) / std::max<int64_t>(1, B * (Hkv / HG)) + 1;
+    int64_t PL = 1;
+    while (PL * kRedUnroll < expected && PL < 16) PL *= 2;
+    const int64_t G = Hq / Hkv;
+    const int64_t col4 = D / 4;
+    const int64_t CB = std::min<int64_t>(col4, kRedThreads / PL);
+    int64_t RG = 1;
+    while (RG * 2 * CB * PL <= kRedThreads && G % (RG * 2) == 0) RG *= 2;
     plan->rows = int32_t(rows);
     plan->row_tiles = int32_t(row_tiles);
     plan->heads_per_group = int32_t(HG);
-    plan->reduce_threads = int32_t(cols * lanes);
-    plan->partition_groups = B * (Hkv / HG) * P;
-    plan->reduce_groups = P > 1 ? B * Qmax * Hq : 0;
-    plan->workspace_bytes = P > 1 ? B * Qmax * Hq * P * (D + 1) * int64_t(sizeof(float)) + 256 : 0;
-    if (plan->partition_groups >= (int64_t(1) << 31) || plan->reduce_groups >= (int64_t(1) << 31))
-        return fail(PA_ERR_UNSUPPORTED, "grid too large");
+    plan->min_share_chunks = int32_t(min_share);
+    plan->reduce_rows = int32_t(RG);
+    plan->reduce_col4 = int32_t(CB);
+    plan->reduce_lanes = int32_t(PL);
+    plan->expected_partials = int32_t(std::min<int64_t>(expected, INT32_MAX));
+    plan->workgroups = n;
+    plan->reduce_groups = n > 1 ? B * Qmax * Hkv * (G / RG) * (col4 / CB) : 0;
+    plan->workspace_bytes = n > 1 ? 2 * n * HG * rows * (D + 1) * int64_t(sizeof(float)) + B * int64_t(sizeof(int32_t)) : 0;
+    if (plan->reduce_groups >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "grid too large");
     return PA_OK;
 }
 
@@ -305,11 +292,15 @@ int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t he
                          kv_dtype == PA_DTYPE_FP8_E4M3FN, num_cus, plan);
 }
 
-int paged_attn_set_partition_tokens(int32_t tokens) {
-    if (tokens < 0 || tokens % pa::kChunk || tokens > pa::kMaxWaveTokens)
-        return pa::fail(PA_ERR_ARG, "partition tokens must be 0 or a multiple of 32 up to %d",
-                        pa::kMaxWaveTokens);
-    pa::g_partition_override.store(tokens);
+int paged_attn_set_workgroups(int32_t workgroups) {
+    if (workgroups < 0) return pa::fail(PA_ERR_ARG, "workgroups must be 0 (automatic) or positive");
+    pa::g_grid_override.store(workgroups);
+    return PA_OK;
+}
+
+int paged_attn_set_min_share(int32_t chunks) {
+    if (chunks < 0) return pa::fail(PA_ERR_ARG, "min share must be 0 (automatic) or positive");
+    pa::g_share_override.store(chunks);
     return PA_OK;
 }
 

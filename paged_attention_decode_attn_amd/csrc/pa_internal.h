@@ -39,9 +39,10 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
 // Records a failure description for paged_attn_last_error() and returns `status`.
 int fail(int status, const char* fmt, ...);
 
-constexpr int kChunk = 32;                  // tokens per inner-loop step (two blocks)
-constexpr int kMaxWaveTokens = 1024;        // one 64-entry block-id window per wave
-constexpr int kMaxPartitions = 1 << 16;
-constexpr int kMaxBatch = 16384;            // per-sequence partition counts live in LDS
+constexpr int kChunkTokens = 32;            // tokens per chunk: the unit of work splitting
+constexpr int kDefaultMinShare = 1;         // smallest share of chunks per workgroup
+constexpr int kMaxBatch = 16384;            // per-sequence chunk counts live in LDS
+constexpr int kRedThreads = 256;            // merge workgroup size (reduce_kernel)
+constexpr int kRedUnroll = 8;               // partial loads in flight per merge lane
 
 }  // namespace pa

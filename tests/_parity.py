@@ -30,21 +30,24 @@ def small(name: str, **kw):
     return CONFIGS[name].replace(**kw)
 
 
-def run_gpu(w, partition_tokens: int = 0, out=None, heads_per_group: int = 0):
-    """Decode on cuda:0; rows the call must not write keep a canary."""
+def run_gpu(w, workgroups: int = 0, out=None, heads_per_group: int = 0, min_share: int = 0):
+    """Decode on cuda:0 with the given split overrides (0 = the planner's
+    choice); rows the call must not write keep a canary."""
     dev = w.to("cuda")
     if out is None:
         out = torch.empty_like(dev.q)
     out.view(torch.int16).fill_(CANARY)
-    B.paged_attn_set_partition_tokens(partition_tokens)
+    B.paged_attn_set_workgroups(workgroups)
     B.paged_attn_set_heads_per_group(heads_per_group)
+    B.paged_attn_set_min_share(min_share)
     try:
         B.paged_attn_decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
                             dev.query_lens, dev.scale, dev.k_scale, dev.v_scale, out)
         torch.cuda.synchronize()
     finally:
-        B.paged_attn_set_partition_tokens(0)
+        B.paged_attn_set_workgroups(0)
         B.paged_attn_set_heads_per_group(0)
+        B.paged_attn_set_min_share(0)
     return out
 
 
@@ -88,9 +91,10 @@ def compare(gpu_out, ref, query_lens, batch_subset=None, label=""):
     return worst, rel
 
 
-def check(w, partition_tokens: int = 0, batch_subset=None, label="", heads_per_group: int = 0):
+def check(w, workgroups: int = 0, batch_subset=None, label="", heads_per_group: int = 0,
+          min_share: int = 0):
     note(f"[gpu] {label or w.spec.name}: B={w.spec.batch} ctx={w.context_lens.tolist()[:8]} "
-         f"T={partition_tokens or 'auto'} HG={heads_per_group or 'auto'}")
-    out = run_gpu(w, partition_tokens, heads_per_group=heads_per_group)
+         f"groups={workgroups or 'auto'} HG={heads_per_group or 'auto'} share={min_share or 'auto'}")
+    out = run_gpu(w, workgroups, heads_per_group=heads_per_group, min_share=min_share)
     ref = oracle_out(w, batch_subset)
     return compare(out, ref, w.query_lens, batch_subset, label or w.spec.name)

@@ -153,43 +153,56 @@ def test_empty_batch_is_valid():
 def test_plan_properties(shape):
     b, hq, hkv, d, ql, w = shape
     p = B.paged_attn_plan(b, hq, hkv, d, ql, w)
-    T, P = p["partition_tokens"], p["num_partitions"]
-    assert T % 32 == 0 and 32 <= T <= 1024
-    assert P * T >= 16 * w and (P - 1) * T < 16 * w          # covers the table, no empty tail
     assert p["rows"] == hq // hkv * ql and p["row_tiles"] == (p["rows"] + 15) // 16
     hg = p["heads_per_group"]
     assert hkv % hg == 0 and 1 <= hg <= (8 if p["row_tiles"] == 1 else 4)
-    assert p["partition_groups"] == b * (hkv // hg) * P
-    assert p["reduce_threads"] % (d // 4) == 0 and p["reduce_threads"] <= 1024
-    assert (p["reduce_groups"] > 0) == (P > 1 and b > 0) or b == 0
-    if P > 1:
-        assert p["workspace_bytes"] >= b * ql * hq * P * (d + 1) * 4
+    seq_chunks = (16 * w + 31) // 32
+    max_chunks = b * (hkv // hg) * seq_chunks
+    n = p["workgroups"]
+    assert n >= 1 and p["min_share_chunks"] >= 1
+    assert n == 1 or n * p["min_share_chunks"] <= max_chunks          # no share below the minimum
+    rg, cb, pl = p["reduce_rows"], p["reduce_col4"], p["reduce_lanes"]
+    assert rg * cb * pl <= 256 and (hq // hkv) % rg == 0 and (d // 4) % cb == 0
+    assert pl * 8 >= min(p["expected_partials"], 128)      # one round of loads (up to 16 lanes)
+    assert (p["reduce_groups"] > 0) == (n > 1)
+    if n > 1:
+        assert p["reduce_groups"] == b * ql * hkv * (hq // hkv // rg) * (d // 4 // cb)
+        assert p["workspace_bytes"] == 2 * n * hg * p["rows"] * (d + 1) * 4 + 4 * b
+    else:
+        assert p["workspace_bytes"] == 0
     assert p == B.paged_attn_plan(b, hq, hkv, d, ql, w)      # deterministic
 
 
 def test_plan_fills_the_device_for_long_single_sequence():
     p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=256)
-    assert p["partition_groups"] * p["heads_per_group"] >= 1024   # at least one wave per SIMD
+    assert p["workgroups"] * p["heads_per_group"] >= 1024          # at least one wave per SIMD
     small = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=8)
-    assert small["partition_groups"] <= p["partition_groups"]
+    assert small["workgroups"] < p["workgroups"]
 
 
-def test_partition_override_and_reset():
+def test_workgroup_and_share_overrides_and_reset():
     try:
-        B.paged_attn_set_partition_tokens(64)
+        B.paged_attn_set_workgroups(5)
+        p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)
+        assert p["workgroups"] == 5
+        B.paged_attn_set_workgroups(1)
+        p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)
+        assert p["workgroups"] == 1 and p["reduce_groups"] == 0 and p["workspace_bytes"] == 0
+        B.paged_attn_set_workgroups(1 << 30)                      # capped by the chunk count
         p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
-        assert p["partition_tokens"] == 64 and p["num_partitions"] == 8
-        B.paged_attn_set_partition_tokens(1024)
+        assert p["workgroups"] == 16 // p["min_share_chunks"] * (8 // p["heads_per_group"])
+        B.paged_attn_set_workgroups(0)
+        B.paged_attn_set_min_share(4)
         p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
-        assert p["num_partitions"] == 1 and p["reduce_groups"] == 0
+        assert p["min_share_chunks"] == 4 and p["workgroups"] * 4 <= 16 * (8 // p["heads_per_group"])
         with pytest.raises(B.PagedAttnError):
-            B.paged_attn_set_partition_tokens(48)
+            B.paged_attn_set_workgroups(-1)
         with pytest.raises(B.PagedAttnError):
-            B.paged_attn_set_partition_tokens(2048)
+            B.paged_attn_set_min_share(-3)
     finally:
-        B.paged_attn_set_partition_tokens(0)
-    p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)                  # a tiny call: one partition
-    assert p["partition_tokens"] == 512 and p["num_partitions"] == 1
+        B.paged_attn_set_workgroups(0)
+        B.paged_attn_set_min_share(0)
+    assert B.paged_attn_plan(1, 32, 8, 128, 1, 32)["min_share_chunks"] == 1
 
 
 def test_heads_per_group_override():
@@ -208,13 +221,22 @@ def test_heads_per_group_override():
         B.paged_attn_set_heads_per_group(0)
 
 
-def test_plan_spreads_small_calls_over_the_chip():
+def test_plan_grids():
     p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)                  # one 512-token sequence
-    assert p["heads_per_group"] == 1 and p["num_partitions"] == 1 and p["reduce_groups"] == 0
+    assert p["workgroups"] * p["heads_per_group"] == 8 * 16       # one chunk per wave
     p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)                 # 4 x <= 8192 tokens
-    assert p["heads_per_group"] == 1 and p["partition_groups"] >= 2048
+    assert p["workgroups"] * p["heads_per_group"] == 2048         # every slot of 256 CUs
     p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192)                # 131072 tokens, batch 1
-    assert p["heads_per_group"] == 8 and p["partition_groups"] >= 256
+    assert p["heads_per_group"] == 8 and p["workgroups"] == 256
+    p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048)                # fp8-sized rows, bf16 cache
+    assert p["workgroups"] * p["heads_per_group"] == 2048
+    p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048, kv_dtype="fp8_e4m3fn")
+    assert p["workgroups"] * p["heads_per_group"] == 3072        # 3 waves per SIMD
+
+
+def test_plan_rejects_chunk_index_overflow():
+    with pytest.raises(B.PagedAttnError):
+        B.paged_attn_plan(16384, 8, 8, 128, 1, 1 << 20)
 
 
 def test_plan_rejects_bad_sizes():
