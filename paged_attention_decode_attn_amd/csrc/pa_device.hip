@@ -64,6 +64,7 @@ constexpr int kRsrcWord3 = 0x00020000;        // raw buffer resource, 32-bit dat
 constexpr float kRescaleLog2 = 8.0f;          // lazy rescale threshold (log2 units)
 constexpr int kChunkTokens = 32;              // tokens per step (two 16-token blocks)
 constexpr int kWindowChunks = 32;             // chunks per 64-entry block-table window
+constexpr int kLockstep = 4;                  // steps between workgroup barriers (power of 2)
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
@@ -540,11 +541,18 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         Step<D, FP8> buf[R];
 #pragma unroll
         for (int i = 0; i + 1 < R; ++i) load_step<D, FP8>(buf[i], a, hb, bid_lane, i, nsteps, last_blk, koff, voff, soff);
+        // Every kLockstep steps the workgroup's waves meet at a barrier.  Two
+        // waves share each SIMD, and the older one otherwise wins the issue
+        // and memory arbitration until it is done, leaving the younger to
+        // finish alone; held within a few steps of each other, the waves
+        // keep the CU's load pipeline full to the end of the share.  Every
+        // wave of a workgroup runs the same chunks, so the barriers match.
         int st = 0;
         for (; st + R <= nclean; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 load_step<D, FP8>(buf[(i + R - 1) % R], a, hb, bid_lane, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                if (((st + i) & (kLockstep - 1)) == 0) __syncthreads();
                 compute_step<D, FP8, NT, false>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, lane);
             }
         }

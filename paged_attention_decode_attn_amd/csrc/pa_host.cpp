@@ -218,7 +218,11 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
     // waves one CU holds for the kernel variant (register budget) and the
-    // largest kv-head group (one wave per head) a workgroup may carry
+    // largest kv-head group (one wave per head) a workgroup may carry.  The
+    // largest group that divides kv_heads wins even when it leaves wave
+    // slots of a CU idle: the waves of a workgroup then read whole token rows
+    // (all heads of a token are adjacent in the cache), which the memory
+    // system serves faster than the same bytes in per-head pieces.
     const int64_t cu_waves = row_tiles == 1 ? (fp8 && D == 64 ? 12 : 8) : 4;
     const int64_t hg_cap = row_tiles == 1 ? 8 : 4;
     const int64_t hg_over = g_group_override.load();
@@ -227,7 +231,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
         HG = hg_over;
     } else {
         for (int64_t h = hg_cap; h >= 1; --h)
-            if (Hkv % h == 0 && cu_waves % h == 0) { HG = h; break; }
+            if (Hkv % h == 0 && h <= cu_waves) { HG = h; break; }
     }
     if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
     // chunk space: 32-token chunks of every (sequence, head group) segment;

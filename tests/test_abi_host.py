@@ -231,7 +231,7 @@ def test_plan_grids():
     p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048)                # fp8-sized rows, bf16 cache
     assert p["workgroups"] * p["heads_per_group"] == 2048
     p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048, kv_dtype="fp8_e4m3fn")
-    assert p["workgroups"] * p["heads_per_group"] == 3072        # 3 waves per SIMD
+    assert p["heads_per_group"] == 8 and p["workgroups"] == 256   # whole token rows per workgroup
 
 
 def test_plan_rejects_chunk_index_overflow():
