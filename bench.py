@@ -28,7 +28,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: KV GB/s (% of HBM peak) and µs/call at batch 1"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", "pa_device.hip")
+# the kernels and the planner that sets their launch shape
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", f)
+                  for f in ("pa_device.hip", "pa_host.cpp", "pa_internal.h")]
 
 
 def parse_args():
@@ -53,8 +55,11 @@ def parse_args():
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -269,6 +274,29 @@ def main():
     B.paged_attn_set_workgroups(0)
     B.paged_attn_set_min_share(0)
 
+    # the same K steps captured into one HIP graph and replayed: the device
+    # time of a call without the host's per-call launch cost (the pages'
+    # engine replays its decode step as a graph); the workspace exists on
+    # the capture stream before capture begins
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        for i in range(2):
+            call(i)
+    gs.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        for i in range(args.steps):
+            call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
+    del graph
+
     part_ms = prof["partition_ms"] / max(prof["calls"], 1)
     red_ms = prof["reduce_ms"] / max(prof["calls"], 1)
     value = kvb / (ms_per_step * 1e-3) / 1e9
@@ -289,6 +317,8 @@ def main():
                    "min_share_chunks": plan["min_share_chunks"], "kv_copies_rotated": copies},
         "us_per_call": round(ms_per_step * 1e3, 3),
         "us_per_call_with_kernel_events": round(ms_with_events * 1e3, 3),
+        "us_per_call_graph": round(ms_graph * 1e3, 3),
+        "kv_GBs_graph": round(kvb / (ms_graph * 1e-3) / 1e9, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_per_call": kvb,
         "kernel_us": {"partition": round(part_ms * 1e3, 3), "reduce": round(red_ms * 1e3, 3)},

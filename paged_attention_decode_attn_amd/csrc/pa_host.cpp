@@ -218,43 +218,55 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
     // waves one CU holds for the kernel variant (register budget) and the
-    // largest kv-head group (one wave per head) a workgroup may carry.  The
-    // largest group that divides kv_heads wins even when it leaves wave
-    // slots of a CU idle: the waves of a workgroup then read whole token rows
-    // (all heads of a token are adjacent in the cache), which the memory
-    // system serves faster than the same bytes in per-head pieces.
+    // largest kv-head group (one wave per head) a workgroup may carry
     const int64_t cu_waves = row_tiles == 1 ? (fp8 && D == 64 ? 12 : 8) : 4;
     const int64_t hg_cap = row_tiles == 1 ? 8 : 4;
+    // chunk space: 32-token chunks of every (sequence, head group) segment;
+    // only its upper bound is known here (lengths live on the device)
+    const int64_t seq_chunks = (int64_t(PA_BLOCK_SIZE) * W + kChunkTokens - 1) / kChunkTokens;
+    // Waves: about kStepsPerWave chunks each for the (kv head, chunk) pairs
+    // the shapes suggest (the whole table for one sequence, half of it per
+    // sequence of a ragged batch), at least a quarter of the CUs, at most
+    // what the chip holds.  Each wave has a startup chain (prefix scan,
+    // block-table window, first loads) and an epilogue that few steps cannot
+    // amortise, while a call that is short overall wants many CUs.
+    const int64_t per_seq = B > 1 ? (seq_chunks + 1) / 2 : seq_chunks;
+    const int64_t wave_slots = int64_t(num_cus) * cu_waves;
+    const int64_t waves = std::max<int64_t>(std::min<int64_t>(B * Hkv * per_seq / kStepsPerWave, wave_slots),
+                                            std::max<int64_t>(1, num_cus / 4));
+    // Heads per workgroup: the largest group that divides kv_heads, fits the
+    // CU and still leaves a workgroup for every CU.  The waves of a workgroup
+    // read the adjacent head rows of the same tokens (all heads of a token
+    // are adjacent in the cache), which the memory system serves faster
+    // than the same bytes in per-head pieces.
     const int64_t hg_over = g_group_override.load();
     int64_t HG = 1;
     if (hg_over > 0) {
         HG = hg_over;
     } else {
         for (int64_t h = hg_cap; h >= 1; --h)
-            if (Hkv % h == 0 && h <= cu_waves) { HG = h; break; }
+            if (Hkv % h == 0 && h <= cu_waves && waves / h >= num_cus) { HG = h; break; }
     }
     if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
-    // chunk space: 32-token chunks of every (sequence, head group) segment;
-    // only its upper bound is known here (lengths live on the device)
-    const int64_t seq_chunks = (int64_t(PA_BLOCK_SIZE) * W + kChunkTokens - 1) / kChunkTokens;
     const int64_t max_chunks = B * (Hkv / HG) * seq_chunks;
     if (max_chunks >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "batch x context too large for the chunk index");
     const int64_t share_over = g_share_override.load();
     const int64_t min_share = share_over > 0 ? share_over : kDefaultMinShare;
-    // one workgroup per resident slot (every wave of the chip streams from
-    // the first cycle to the last), fewer when the chunks cannot fill them
-    const int64_t slots = int64_t(num_cus) * (cu_waves / HG);
+    const int64_t slots = int64_t(num_cus) * std::max<int64_t>(1, cu_waves / HG);
     const int64_t grid_over = g_grid_override.load();
-    int64_t n = grid_over > 0 ? grid_over : slots;
+    int64_t n = grid_over > 0 ? grid_over : std::min<int64_t>(std::max<int64_t>(1, waves / HG), slots);
     n = std::max<int64_t>(1, std::min<int64_t>(n, max_chunks / min_share));
     // Merge shape.  Expected partials per row: one per workgroup whose share
     // meets the row's segment, about n / (B * groups) + 1 when the lengths are
-    // alike (a lopsided batch only takes more rounds of loads).  PL lanes
-    // with 8 loads in flight each cover that in one round; the rest of the
-    // 256 threads go to float4 columns (CB) and rows of the same segment (RG).
-    const int64_t expected = (n + std::max<int64_t>(1, B * (Hkv / HG)) - 1) / std::max<int64_t>(1, B * (Hkv / HG)) + 1;
+    // alike (a lopsided batch only takes more rounds of loads), exactly n for
+    // a single segment.  PL lanes with 8 loads in flight each cover that in
+    // one round; the rest of the 256 threads go to float4 columns (CB, at
+    // least 8: 128 contiguous bytes of each partial) and rows of the same
+    // segment (RG).
+    const int64_t segs = std::max<int64_t>(1, B * (Hkv / HG));
+    const int64_t expected = segs == 1 ? n : (n + segs - 1) / segs + 1;
     int64_t PL = 1;
-    while (PL * kRedUnroll < expected && PL < 16) PL *= 2;
+    while (PL * kRedUnroll < expected && PL < 32) PL *= 2;
     const int64_t G = Hq / Hkv;
     const int64_t col4 = D / 4;
     const int64_t CB = std::min<int64_t>(col4, kRedThreads / PL);

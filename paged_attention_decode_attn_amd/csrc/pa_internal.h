@@ -41,6 +41,7 @@ int fail(int status, const char* fmt, ...);
 
 constexpr int kChunkTokens = 32;            // tokens per chunk: the unit of work splitting
 constexpr int kDefaultMinShare = 1;         // smallest share of chunks per workgroup
+constexpr int kStepsPerWave = 8;            // planner's target chunks per wave
 constexpr int kMaxBatch = 16384;            // per-sequence chunk counts live in LDS
 constexpr int kRedThreads = 256;            // merge workgroup size (reduce_kernel)
 constexpr int kRedUnroll = 8;               // partial loads in flight per merge lane

@@ -163,7 +163,7 @@ def test_plan_properties(shape):
     assert n == 1 or n * p["min_share_chunks"] <= max_chunks          # no share below the minimum
     rg, cb, pl = p["reduce_rows"], p["reduce_col4"], p["reduce_lanes"]
     assert rg * cb * pl <= 256 and (hq // hkv) % rg == 0 and (d // 4) % cb == 0
-    assert pl * 8 >= min(p["expected_partials"], 128)      # one round of loads (up to 16 lanes)
+    assert pl * 8 >= min(p["expected_partials"], 256)      # one round of loads (up to 32 lanes)
     assert (p["reduce_groups"] > 0) == (n > 1)
     if n > 1:
         assert p["reduce_groups"] == b * ql * hkv * (hq // hkv // rg) * (d // 4 // cb)
@@ -222,16 +222,22 @@ def test_heads_per_group_override():
 
 
 def test_plan_grids():
+    # about 8 chunks per wave, at least a quarter of the CUs, at most the
+    # chip; the largest head group that still gives every CU a workgroup
     p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)                  # one 512-token sequence
-    assert p["workgroups"] * p["heads_per_group"] == 8 * 16       # one chunk per wave
+    assert p["heads_per_group"] == 1 and p["workgroups"] == 64    # latency bound: spread out
     p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)                 # 4 x <= 8192 tokens
-    assert p["workgroups"] * p["heads_per_group"] == 2048         # every slot of 256 CUs
+    assert p["heads_per_group"] == 2 and p["workgroups"] == 256
     p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192)                # 131072 tokens, batch 1
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256
     p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048)                # fp8-sized rows, bf16 cache
-    assert p["workgroups"] * p["heads_per_group"] == 2048
+    assert p["heads_per_group"] == 8 and p["workgroups"] == 256
     p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048, kv_dtype="fp8_e4m3fn")
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256   # whole token rows per workgroup
+    p = B.paged_attn_plan(64, 64, 8, 128, 2, 1024)               # MTP verify
+    assert p["heads_per_group"] == 8 and p["workgroups"] == 256
+    p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=8)     # a small device
+    assert p["workgroups"] == 8
 
 
 def test_plan_rejects_chunk_index_overflow():

@@ -246,3 +246,48 @@ def test_profile_events_measure_both_kernels():
 def test_full_size_configs_sampled(name, subset):
     w = generate(CONFIGS[name])
     check(w, 0, batch_subset=subset, label=f"full/{name}")
+
+
+# --------------------------------------------------------------------------
+# graph capture: the call is graph-safe once its workspace exists
+# --------------------------------------------------------------------------
+def test_graph_capture_replays_match_eager():
+    w = generate(SMALL["mtp_verify"])
+    dev = w.to("cuda")
+    ref = oracle_out(w)
+    s = torch.cuda.Stream()
+    note("[gpu] graph capture: eager warm-up on the capture stream")
+    eager = torch.empty_like(dev.q)
+    with torch.cuda.stream(s):
+        B.paged_attn_decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                            dev.query_lens, dev.scale, None, None, eager)
+    s.synchronize()
+    compare(eager, ref, w.query_lens, label="graph/eager")
+    out = torch.empty_like(dev.q)
+    g = torch.cuda.CUDAGraph()
+    note("[gpu] graph capture: capturing")
+    with torch.cuda.graph(g, stream=s):
+        B.paged_attn_decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                            dev.query_lens, dev.scale, None, None, out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        note(f"[gpu] graph capture: replay {r}")
+        out.view(torch.int16).fill_(0x7F7B)                  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
+
+
+def test_capture_without_workspace_is_refused():
+    w = generate(SMALL["long_ctx"]).to("cuda")
+    s = torch.cuda.Stream()                                  # no workspace on this stream yet
+    out = torch.empty_like(w.q)
+    g = torch.cuda.CUDAGraph()
+    note("[gpu] capture without workspace")
+    with pytest.raises(B.PagedAttnError) as e:
+        with torch.cuda.graph(g, stream=s):
+            B.paged_attn_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                                w.query_lens, w.scale, None, None, out)
+    assert e.value.name == "PA_ERR_CAPTURE"
+    torch.cuda.synchronize()
