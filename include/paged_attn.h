@@ -148,6 +148,51 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
                      const pa_tensor* v_scale, const pa_tensor* out);
 
 /*
+ * paged_attn_reshape_and_cache -- write the new tokens' K and V rows into
+ * the paged cache (the step that precedes paged_attn_decode in a decode
+ * step).  Sources: ATOM model operations guide, "KV cache operations" (the
+ * standard write for a bf16 cache, the fp8 write with per-token
+ * quantisation) and its slot-mapping file (which KV slot a token is
+ * written to); ROCm blog "Optimizing ATOM and vLLM-ATOM for
+ * High-Interactivity Inference", "Attention Input Fusion" (fp8 scales are
+ * calculated as K/V are written into the paged cache).
+ *
+ *   k_new, v_new  bf16 [T, Hkv, D]: the new tokens' rows (D 64 or 128).
+ *   slot_mapping  int32 [T]: slot s of token t is position s % 16 of block
+ *                 s / 16.  Entries < 0 (padding tokens) and >= NB * 16 are
+ *                 skipped; the others must be distinct (two tokens on one
+ *                 slot leave either token's row).
+ *   k_cache,      [NB, 16, Hkv, D], both bf16 or both fp8 e4m3fn; written
+ *   v_cache       at the mapped slots only.
+ *   k_scale,      fp32, logically [NB, 16, Hkv], slot dimension contiguous;
+ *   v_scale       required iff the cache is fp8, else NULL.  For an fp8
+ *                 cache every written (token, kv head) row gets
+ *                 scale = max_d |x_d| / 448 (1 for an all-zero row) and
+ *                 codes e4m3fn(clamp(x_d / scale, -448, 448)), rounded to
+ *                 nearest, ties to even, both divisions in IEEE float32.
+ *                 A bf16 cache receives the rows bit for bit.
+ *   stream        hipStream_t as void*, NULL = default stream.
+ *
+ * Layout rules as for paged_attn_decode (inner stride 1, other strides of
+ * the bf16 and cache tensors multiples of 16 bytes, 16-byte aligned data);
+ * scale data 4-byte aligned.  No workspace; nothing is allocated.  Returns
+ * PA_OK or a negative pa_status (nothing enqueued except on PA_ERR_HIP).
+ */
+int paged_attn_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,
+                                 const pa_tensor* slot_mapping, pa_tensor* k_cache,
+                                 pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale,
+                                 void* stream);
+
+/*
+ * paged_attn_check_reshape_and_cache -- the host-side argument validation
+ * of paged_attn_reshape_and_cache, without touching the GPU or any data.
+ */
+int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,
+                                       const pa_tensor* slot_mapping, const pa_tensor* k_cache,
+                                       const pa_tensor* v_cache, const pa_tensor* k_scale,
+                                       const pa_tensor* v_scale);
+
+/*
  * Split-context plan: how paged_attn_decode divides the work so that one
  * call fills the GPU whatever the batch and the ragged context lengths.
  * Every (sequence, kv-head group) pair is a segment of ceil(L_b / 32)

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
                 args11 = [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
                 L.paged_attn_decode.argtypes = args11 + [_P, ctypes.c_void_p]
                 L.paged_attn_check.argtypes = args11 + [_P]
+                L.paged_attn_reshape_and_cache.argtypes = [_P] * 7 + [ctypes.c_void_p]
+                L.paged_attn_check_reshape_and_cache.argtypes = [_P] * 7
                 L.paged_attn_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, ctypes.c_int32,
                                                                      ctypes.POINTER(PaPlan)]
                 L.paged_attn_set_workgroups.argtypes = [ctypes.c_int32]
@@ -91,6 +93,7 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_last_error.argtypes = []
                 L.paged_attn_last_error.restype = ctypes.c_char_p
                 for name in ("paged_attn_decode", "paged_attn_check", "paged_attn_plan",
+                             "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
                              "paged_attn_set_workgroups", "paged_attn_set_min_share",
                              "paged_attn_set_heads_per_group",
                              "paged_attn_reserve",
@@ -179,6 +182,24 @@ def paged_attn_check(q, k_cache, v_cache, block_tables, context_lens, query_lens
     return lib().paged_attn_check(*[_ref(d) for d in descs], ctypes.c_float(scale),
                                   _ref(describe(k_scale)), _ref(describe(v_scale)),
                                   _ref(describe(out)))
+
+
+def paged_attn_reshape_and_cache(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None,
+                                 v_scale=None, stream=None) -> None:
+    """Write the new tokens' K/V (bf16 ``[T, Hkv, D]``) into the paged cache
+    at ``slot_mapping`` (int32 ``[T]``), quantising per token when the cache
+    is fp8 (then ``k_scale`` / ``v_scale`` are written too).  Raises
+    PagedAttnError on any non-zero status."""
+    d = [describe(x) for x in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
+    st = lib().paged_attn_reshape_and_cache(*[_ref(x) for x in d], _stream_handle(k_new, stream))
+    _raise(st, "paged_attn_reshape_and_cache")
+
+
+def paged_attn_check_reshape_and_cache(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None,
+                                       v_scale=None) -> int:
+    """Status of the cache write's host-side validation (no GPU access)."""
+    d = [describe(x) for x in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
+    return lib().paged_attn_check_reshape_and_cache(*[_ref(x) for x in d])
 
 
 def paged_attn_check_descriptors(q, k_cache, v_cache, block_tables, context_lens, query_lens,

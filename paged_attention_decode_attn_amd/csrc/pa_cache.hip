@@ -1,0 +1,152 @@
+// Paged KV-cache write for gfx950: the new tokens' K and V rows go to the
+// cache slots a slot mapping names, copied as bf16 or quantised per token to
+// OCP fp8 e4m3fn with one fp32 scale per (token, kv head).
+//
+// The operation: ATOM model operations guide, "KV cache operations" (the
+// standard write for a bf16 cache and the fp8 write with per-token
+// quantisation) and its slot-mapping file ("which KV slot a token is written
+// to"); the ROCm blog "Optimizing ATOM and vLLM-ATOM for High-Interactivity
+// Inference", "Attention Input Fusion" (fp8 scales calculated as K/V are
+// written into the paged cache).  Scale rule: the row's absolute maximum
+// divided by 448, the largest finite e4m3fn value (1 for an all-zero row);
+// codes round to nearest, ties to even.
+//
+// One thread takes 8 consecutive elements (16 bytes of bf16) of one
+// (token, kv head) row of both K and V, so a wave reads and writes whole
+// contiguous token rows.  The D/8 threads of a row sit in one aligned lane
+// group of the wave and reduce the row's maximum with cross-lane exchanges.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kFp8Max = 448.0f;
+constexpr int kWriteThreads = 256;
+
+struct WriteArgs {
+    const char* k_new; const char* v_new; int64_t n_st, n_sh, vn_st, vn_sh;   // bytes
+    const int32_t* slots; int64_t slot_s;                                     // elements
+    char* kc; char* vc; int64_t k_sblk, k_stok, k_sh, v_sblk, v_stok, v_sh;   // bytes
+    float* ks; float* vs; int64_t ks_sblk, ks_sh, vs_sblk, vs_sh;             // floats
+    int64_t T, slots_total;
+    int32_t Hkv, D;
+};
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// x / s clamped to +-448 for the two bf16 values of one dword
+__device__ __forceinline__ float q_lo(unsigned w, float s) {
+    return fminf(fmaxf(__fdiv_rn(bf16_lo(w), s), -kFp8Max), kFp8Max);
+}
+__device__ __forceinline__ float q_hi(unsigned w, float s) {
+    return fminf(fmaxf(__fdiv_rn(bf16_hi(w), s), -kFp8Max), kFp8Max);
+}
+
+// 8 bf16 values -> 8 e4m3fn bytes of x / s (s > 0): each conversion packs
+// two codes into the low or the high half of a dword.
+__device__ __forceinline__ u32x2 encode8(const u32x4& x, float s) {
+    u32x2 out;
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[0], s), q_hi(x[0], s), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[1], s), q_hi(x[1], s), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[2], s), q_hi(x[2], s), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[3], s), q_hi(x[3], s), w1, true);
+    out[0] = (unsigned)w0;
+    out[1] = (unsigned)w1;
+    return out;
+}
+
+__device__ __forceinline__ float absmax8(const u32x4& x) {
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[w])), fabsf(bf16_hi(x[w]))));
+    return m;
+}
+
+template <bool FP8, int R8>
+__global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
+    const int64_t per_token = (int64_t)a.Hkv * R8;
+    const int64_t t = gid / per_token;
+    const int rem = (int)(gid - t * per_token);
+    const int h = rem / R8, r = rem - h * R8;
+    // every lane of a row group takes part in the reductions below, so the
+    // group is either wholly in range or wholly out (R8 divides 64)
+    const bool live_token = t < a.T;
+    const int64_t slot = live_token ? (int64_t)a.slots[t * a.slot_s] : -1;
+    const bool live = slot >= 0 && slot < a.slots_total;
+    u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+    if (live) {
+        k = *reinterpret_cast<const u32x4*>(a.k_new + t * a.n_st + h * a.n_sh + 16 * r);
+        v = *reinterpret_cast<const u32x4*>(a.v_new + t * a.vn_st + h * a.vn_sh + 16 * r);
+    }
+    const int64_t blk = slot >> 4, pos = slot & 15;
+    if constexpr (!FP8) {
+        if (live) {
+            *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k;
+            *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) = v;
+        }
+    } else {
+        float mk = absmax8(k), mv = absmax8(v);
+#pragma unroll
+        for (int o = 1; o < R8; o <<= 1) {
+            mk = fmaxf(mk, __shfl_xor(mk, o));
+            mv = fmaxf(mv, __shfl_xor(mv, o));
+        }
+        const float sk = mk > 0.f ? __fdiv_rn(mk, kFp8Max) : 1.f;
+        const float sv = mv > 0.f ? __fdiv_rn(mv, kFp8Max) : 1.f;
+        if (live) {
+            *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) = encode8(k, sk);
+            *reinterpret_cast<u32x2*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 8 * r) = encode8(v, sv);
+            if (r == 0) {
+                a.ks[blk * a.ks_sblk + h * a.ks_sh + pos] = sk;
+                a.vs[blk * a.vs_sblk + h * a.vs_sh + pos] = sv;
+            }
+        }
+    }
+}
+
+template <bool FP8>
+const void* write_kernel_of(int D) {
+    return D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 16>)
+                    : reinterpret_cast<const void*>(&cache_write_kernel<FP8, 8>);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int paged_attn_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,
+                                            const pa_tensor* slot_mapping, pa_tensor* k_cache,
+                                            pa_tensor* v_cache, pa_tensor* k_scale, pa_tensor* v_scale,
+                                            void* stream) {
+    using namespace pa;
+    WriteProblem p;
+    int st = validate_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, &p);
+    if (st) return st;
+    if (p.T == 0) return PA_OK;
+    WriteArgs a;
+    a.k_new = static_cast<const char*>(p.k_new); a.n_st = p.kn_st; a.n_sh = p.kn_sh;
+    a.v_new = static_cast<const char*>(p.v_new); a.vn_st = p.vn_st; a.vn_sh = p.vn_sh;
+    a.slots = p.slots; a.slot_s = p.slot_s;
+    a.kc = static_cast<char*>(p.kc); a.k_sblk = p.k_sblk; a.k_stok = p.k_stok; a.k_sh = p.k_sh;
+    a.vc = static_cast<char*>(p.vc); a.v_sblk = p.v_sblk; a.v_stok = p.v_stok; a.v_sh = p.v_sh;
+    a.ks = p.ks; a.ks_sblk = p.ks_sblk; a.ks_sh = p.ks_sh;
+    a.vs = p.vs; a.vs_sblk = p.vs_sblk; a.vs_sh = p.vs_sh;
+    a.T = p.T; a.slots_total = p.NB * PA_BLOCK_SIZE;
+    a.Hkv = (int32_t)p.Hkv; a.D = (int32_t)p.D;
+    const int64_t threads = p.T * p.Hkv * (p.D / 8);
+    const int64_t groups = (threads + kWriteThreads - 1) / kWriteThreads;
+    const void* fn = p.fp8 ? write_kernel_of<true>((int)p.D) : write_kernel_of<false>((int)p.D);
+    void* args[] = {&a};
+    if (hipLaunchKernel(fn, dim3((unsigned)groups), dim3(kWriteThreads), args, 0,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PA_OK;
+}

@@ -100,8 +100,6 @@ __device__ __forceinline__ T ldg(const char* p) {
     return *reinterpret_cast<const T*>(p);
 }
 
-__device__ __forceinline__ unsigned bits(float x) { return __builtin_bit_cast(unsigned, x); }
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 __device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {

@@ -210,6 +210,81 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     return PA_OK;
 }
 
+int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm, const pa_tensor* kc,
+                   const pa_tensor* vc, const pa_tensor* ks, const pa_tensor* vs, WriteProblem* pr) {
+    int st;
+    if ((st = check_desc(kn, "k_new", PA_DTYPE_BF16, 3, 3, true))) return st;
+    if ((st = check_desc(vn, "v_new", PA_DTYPE_BF16, 3, 3, true))) return st;
+    if ((st = check_desc(sm, "slot_mapping", PA_DTYPE_INT32, 1, 1, true))) return st;
+    if (!kc) return fail(PA_ERR_NULL, "k_cache: descriptor is NULL");
+    if (!vc) return fail(PA_ERR_NULL, "v_cache: descriptor is NULL");
+    const int32_t kvt = kc->dtype;
+    if (kvt != PA_DTYPE_BF16 && kvt != PA_DTYPE_FP8_E4M3FN)
+        return fail(PA_ERR_DTYPE, "k_cache: dtype %s, expected BF16 or FP8_E4M3FN", dtype_name(kvt));
+    if ((st = check_desc(kc, "k_cache", kvt, 4, 4, true))) return st;
+    if ((st = check_desc(vc, "v_cache", kvt, 4, 4, true))) return st;
+    const bool fp8 = kvt == PA_DTYPE_FP8_E4M3FN;
+    if (fp8) {
+        if (!ks || !vs) return fail(PA_ERR_NULL, "fp8 cache needs k_scale and v_scale");
+        if ((st = check_desc(ks, "k_scale", PA_DTYPE_FP32, 3, 3, true))) return st;
+        if ((st = check_desc(vs, "v_scale", PA_DTYPE_FP32, 3, 3, true))) return st;
+    } else if (ks || vs) {
+        return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
+    }
+    const int64_t T = kn->shape[0], Hkv = kn->shape[1], D = kn->shape[2];
+    for (int i = 0; i < 3; ++i)
+        if (vn->shape[i] != kn->shape[i])
+            return fail(PA_ERR_SHAPE, "v_new: size %lld in dim %d, k_new has %lld", (long long)vn->shape[i], i,
+                        (long long)kn->shape[i]);
+    if (sm->shape[0] != T)
+        return fail(PA_ERR_SHAPE, "slot_mapping: %lld entries, %lld new tokens", (long long)sm->shape[0], (long long)T);
+    for (int i = 0; i < 4; ++i)
+        if (kc->shape[i] != vc->shape[i])
+            return fail(PA_ERR_SHAPE, "v_cache: size %lld in dim %d, k_cache has %lld", (long long)vc->shape[i], i,
+                        (long long)kc->shape[i]);
+    const int64_t NB = kc->shape[0];
+    if (kc->shape[1] != PA_BLOCK_SIZE)
+        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, only 16 is supported", (long long)kc->shape[1]);
+    if (kc->shape[2] != Hkv || kc->shape[3] != D)
+        return fail(PA_ERR_SHAPE, "k_cache: [%lld, 16, %lld, %lld], new tokens are [T, %lld, %lld]",
+                    (long long)NB, (long long)kc->shape[2], (long long)kc->shape[3], (long long)Hkv, (long long)D);
+    if (D != 64 && D != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64 and 128 are supported", (long long)D);
+    if (Hkv < 1) return fail(PA_ERR_SHAPE, "no kv heads");
+    if (NB * PA_BLOCK_SIZE >= (int64_t(1) << 31))
+        return fail(PA_ERR_UNSUPPORTED, "pool of %lld blocks: slots do not fit int32", (long long)NB);
+    if (T * Hkv * (D / 8) >= (int64_t(1) << 40)) return fail(PA_ERR_UNSUPPORTED, "too many new tokens");
+    if (fp8) {
+        for (const pa_tensor* s : {ks, vs}) {
+            const char* nm = s == ks ? "k_scale" : "v_scale";
+            if (s->shape[0] != NB || s->shape[1] != PA_BLOCK_SIZE || s->shape[2] != Hkv)
+                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, 16, kv_heads]", nm);
+            if (s->stride[1] != 1) return fail(PA_ERR_LAYOUT, "%s: the slot dimension must be contiguous", nm);
+            if (!aligned(s->data, 4)) return fail(PA_ERR_LAYOUT, "%s: data is not 4-byte aligned", nm);
+        }
+    }
+    if ((st = check_rows16(kn, "k_new"))) return st;
+    if ((st = check_rows16(vn, "v_new"))) return st;
+    if ((st = check_rows16(kc, "k_cache"))) return st;
+    if ((st = check_rows16(vc, "v_cache"))) return st;
+    if (!aligned(sm->data, 4)) return fail(PA_ERR_LAYOUT, "slot_mapping: data is not 4-byte aligned");
+    if (pr) {
+        WriteProblem& p = *pr;
+        const int64_t eb = fp8 ? 1 : 2;
+        p.T = T; p.Hkv = Hkv; p.D = D; p.NB = NB; p.fp8 = fp8;
+        p.k_new = kn->data; p.kn_st = kn->stride[0] * 2; p.kn_sh = kn->stride[1] * 2;
+        p.v_new = vn->data; p.vn_st = vn->stride[0] * 2; p.vn_sh = vn->stride[1] * 2;
+        p.slots = static_cast<const int32_t*>(sm->data); p.slot_s = sm->stride[0];
+        p.kc = kc->data; p.k_sblk = kc->stride[0] * eb; p.k_stok = kc->stride[1] * eb; p.k_sh = kc->stride[2] * eb;
+        p.vc = vc->data; p.v_sblk = vc->stride[0] * eb; p.v_stok = vc->stride[1] * eb; p.v_sh = vc->stride[2] * eb;
+        p.ks = fp8 ? static_cast<float*>(ks->data) : nullptr;
+        p.vs = fp8 ? static_cast<float*>(vs->data) : nullptr;
+        p.ks_sblk = fp8 ? ks->stride[0] : 0; p.ks_sh = fp8 ? ks->stride[2] : 0;
+        p.vs_sblk = fp8 ? vs->stride[0] : 0; p.vs_sh = fp8 ? vs->stride[2] : 0;
+    }
+    return PA_OK;
+}
+
 int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W, bool fp8,
               int32_t num_cus, pa_plan* plan) {
     if (!plan) return fail(PA_ERR_NULL, "plan: NULL");
@@ -297,6 +372,13 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
                      const pa_tensor* v_scale, const pa_tensor* out) {
     return pa::validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
                         v_scale, out, nullptr);
+}
+
+int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,
+                                       const pa_tensor* slot_mapping, const pa_tensor* k_cache,
+                                       const pa_tensor* v_cache, const pa_tensor* k_scale,
+                                       const pa_tensor* v_scale) {
+    return pa::validate_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, nullptr);
 }
 
 int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,

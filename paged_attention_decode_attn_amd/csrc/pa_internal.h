@@ -26,6 +26,23 @@ struct Problem {
     const int32_t* ql;  int64_t ql_s;                  // ql may be null
 };
 
+// A validated cache write (paged_attn_reshape_and_cache).
+struct WriteProblem {
+    int64_t T, Hkv, D, NB;
+    bool fp8;
+    const void* k_new; int64_t kn_st, kn_sh;           // bytes
+    const void* v_new; int64_t vn_st, vn_sh;           // bytes
+    const int32_t* slots; int64_t slot_s;              // int32 elements
+    void* kc; int64_t k_sblk, k_stok, k_sh;            // bytes
+    void* vc; int64_t v_sblk, v_stok, v_sh;            // bytes
+    float* ks; int64_t ks_sblk, ks_sh;                 // fp32 elements (slot stride 1)
+    float* vs; int64_t vs_sblk, vs_sh;
+};
+
+int validate_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                   const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* k_scale,
+                   const pa_tensor* v_scale, WriteProblem* p);
+
 // Host-only validation shared by paged_attn_check and paged_attn_decode.
 int validate(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
              const pa_tensor* block_tables, const pa_tensor* context_lens,

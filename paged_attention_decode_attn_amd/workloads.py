@@ -267,3 +267,64 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
         v_scale=None if v_sc is None else v_sc.permute(0, 2, 1),
         block_tables=tables, context_lens=ctx.to(torch.int32),
         query_lens=qls, scale=spec.softmax_scale)
+
+
+@dataclass
+class CacheWrite:
+    """Inputs of one paged KV-cache write: the new tokens' K/V rows and
+    their slots, plus the workload whose pool (caches, scales) they go to."""
+    base: Workload
+    k_new: torch.Tensor          # bf16 [T, Hkv, D]
+    v_new: torch.Tensor
+    slot_mapping: torch.Tensor   # int32 [T]; -1 marks a padding token
+
+    def to(self, device) -> "CacheWrite":
+        return CacheWrite(self.base.to(device), self.k_new.to(device), self.v_new.to(device),
+                          self.slot_mapping.to(device))
+
+
+def generate_cache_write(spec: WorkloadSpec, *, bulk_tokens: Optional[int] = None, pad: int = 0,
+                         seed: Optional[int] = None, **kw) -> CacheWrite:
+    """A cache write shaped like the workload's decode step: the new tokens
+    are the last ``query_lens[b]`` positions of every sequence (their slots
+    through the block table), rows N(0, 1) rounded to bf16 from a generator
+    seeded with ``seed`` (default: the workload's seed + 1000).  With
+    ``bulk_tokens``, ``T`` tokens take distinct slots drawn from the whole
+    pool instead (a prefill-sized write).  ``pad`` extra tokens carry slot
+    -1 (padding, not written).  ``kw`` goes to ``generate``."""
+    base = generate(spec, **kw)
+    gen = torch.Generator("cpu").manual_seed((spec.seed + 1000) if seed is None else seed)
+    if bulk_tokens is None:
+        slots = []
+        for b in range(spec.batch):
+            L, n = int(base.context_lens[b]), int(base.query_lens[b])
+            for pos in range(L - n, L):
+                slots.append(int(base.block_tables[b, pos // BLOCK]) * BLOCK + pos % BLOCK)
+        slots = torch.tensor(slots, dtype=torch.int64)
+    else:
+        total = spec.pool_blocks * BLOCK
+        if bulk_tokens > total:
+            raise ValueError("more tokens than pool slots")
+        slots = torch.randperm(total, generator=gen)[:bulk_tokens]
+    if pad:
+        at = torch.randint(0, slots.numel() + 1, (pad,), generator=gen)
+        for p in sorted(at.tolist(), reverse=True):
+            slots = torch.cat([slots[:p], torch.tensor([-1]), slots[p:]])
+    T = slots.numel()
+    k_new = torch.randn(T, spec.hkv, spec.head_dim, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    v_new = torch.randn(T, spec.hkv, spec.head_dim, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    return CacheWrite(base, k_new, v_new, slots.to(torch.int32))
+
+
+def write_bytes(slot_mapping, hkv: int, head_dim: int, kv_dtype: str, num_blocks: int) -> int:
+    """Algorithmic bytes of one cache write: the bf16 K and V rows read, the
+    cache rows written (and the fp32 scales for an fp8 cache), for the
+    tokens whose slot lies in the pool."""
+    s = torch.as_tensor(slot_mapping).to(torch.int64)
+    n = int(((s >= 0) & (s < num_blocks * BLOCK)).sum())
+    per_token = 2 * hkv * head_dim * 2
+    if kv_dtype == "fp8_e4m3fn":
+        per_token += 2 * hkv * head_dim + 2 * hkv * 4
+    else:
+        per_token += 2 * hkv * head_dim * 2
+    return n * per_token

@@ -276,3 +276,42 @@ def test_strerror_covers_every_status():
     for code in B.STATUS_NAMES:
         assert B.paged_attn_strerror(code) != "unknown status"
     assert B.paged_attn_strerror(12345) == "unknown status"
+
+
+def _write_tensors(kv="bf16", T=5, hkv=HKV, d=D):
+    kn = torch.zeros(T, hkv, d, dtype=torch.bfloat16)
+    vn = torch.zeros(T, hkv, d, dtype=torch.bfloat16)
+    sm = torch.zeros(T, dtype=torch.int32)
+    cdt = torch.uint8 if kv == "fp8" else torch.bfloat16
+    kc = torch.zeros(NB, 16, hkv, d, dtype=cdt)
+    vc = torch.zeros(NB, 16, hkv, d, dtype=cdt)
+    ks = vs = None
+    if kv == "fp8":
+        ks = torch.ones(NB, hkv, 16).permute(0, 2, 1)
+        vs = torch.ones(NB, hkv, 16).permute(0, 2, 1)
+    return dict(k_new=kn, v_new=vn, slot_mapping=sm, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_cache_write_validation_accepts_good_arguments(kv):
+    assert B.paged_attn_check_reshape_and_cache(**_write_tensors(kv)) == B.PA_OK
+    t = _write_tensors(kv, T=0)                                   # nothing to write
+    assert B.paged_attn_check_reshape_and_cache(**t) == B.PA_OK
+
+
+def test_cache_write_validation_rejects_bad_arguments():
+    def status(**over):
+        t = _write_tensors(over.pop("kv", "bf16"))
+        t.update(over)
+        return B.STATUS_NAMES[B.paged_attn_check_reshape_and_cache(**t)]
+    assert status(k_new=torch.zeros(5, HKV, D)) == "PA_ERR_DTYPE"                      # fp32 rows
+    assert status(slot_mapping=torch.zeros(5, dtype=torch.int64)) == "PA_ERR_DTYPE"
+    assert status(slot_mapping=torch.zeros(4, dtype=torch.int32)) == "PA_ERR_SHAPE"
+    assert status(v_new=torch.zeros(5, HKV, 64, dtype=torch.bfloat16)) == "PA_ERR_SHAPE"
+    assert status(k_cache=torch.zeros(NB, 8, HKV, D, dtype=torch.bfloat16),
+                  v_cache=torch.zeros(NB, 8, HKV, D, dtype=torch.bfloat16)) == "PA_ERR_UNSUPPORTED"
+    assert status(kv="fp8", k_scale=None) == "PA_ERR_NULL"
+    assert status(k_scale=torch.ones(NB, 16, HKV)) == "PA_ERR_ARG"                    # scales with bf16
+    assert status(kv="fp8", k_scale=torch.ones(NB, 16, HKV)) == "PA_ERR_LAYOUT"       # slot dim not contiguous
+    assert status(k_new=torch.zeros(5, HKV, 2 * D, dtype=torch.bfloat16)[:, :, 1:D + 1]) == "PA_ERR_LAYOUT"
+    assert status(k_new=None) == "PA_ERR_NULL"
