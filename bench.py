@@ -40,6 +40,12 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER)
+    ap.add_argument("--op", default="decode", choices=["decode", "cache_write"],
+                    help="decode: the attention call (default); cache_write: the paged KV-cache "
+                         "write before it, on --config's decode step or a bulk write (--bulk)")
+    ap.add_argument("--bulk", type=int, default=0,
+                    help="with --op cache_write: write this many tokens to distinct random slots "
+                         "of a large pool instead of the config's decode step")
     ap.add_argument("--workgroups", type=int, default=0, help="partition-kernel grid (0 = the planner's)")
     ap.add_argument("--min-share", type=int, default=0, help="smallest share in 32-token chunks (0 = the planner's)")
     ap.add_argument("--copies", type=int, default=0, help="rotated KV copies (0 = enough for >= 1 GiB)")
@@ -86,12 +92,35 @@ def _db_rows(path, sql):
     return rows
 
 
+def cache_write_workload(args):
+    """(spec, inputs, workload name, algorithmic bytes) of the cache write
+    that ``--op cache_write`` times: the config's decode step, or ``--bulk``
+    tokens to distinct random slots of a pool of at least twice as many."""
+    from paged_attention_decode_attn_amd.workloads import CONFIGS, generate_cache_write, write_bytes
+    spec = CONFIGS[args.config]
+    if args.bulk:
+        pool = max(spec.pool_blocks, -(-2 * args.bulk // 16))
+        spec = spec.replace(batch=1, ctx_lo=16, ctx_hi=16, pool_blocks=pool)
+    cw = generate_cache_write(spec, bulk_tokens=args.bulk or None)
+    name = (f"bulk{args.bulk}_" if args.bulk else "decode_step_") + spec.name
+    wb = write_bytes(cw.slot_mapping, spec.hkv, spec.head_dim, spec.kv_dtype, spec.pool_blocks)
+    return spec, cw, name, wb
+
+
 def summarize(args):
     """Kernel-trace statistics and calibrated HBM traffic of one workload."""
     from paged_attention_decode_attn_amd.workloads import CONFIGS, generate, kv_bytes
     trace, fetch, write, cfetch, cwrite = args.summarize
-    spec = CONFIGS[args.config]
-    kvb = kv_bytes(generate(spec).context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
+    if args.op == "cache_write":
+        spec, _, wname, kvb = cache_write_workload(args)
+        kname, title, unit = "cache_write_kernel", "paged KV-cache write", "bytes (rows read + cache written)"
+        kernels = (("%cache_write_kernel%", "cache_write_kernel"),)
+    else:
+        spec = CONFIGS[args.config]
+        wname = spec.name
+        kvb = kv_bytes(generate(spec).context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
+        kname, title, unit = "partition_kernel", "paged decode attention", "KV bytes"
+        kernels = (("%partition_kernel%", "partition_kernel"), ("%reduce_kernel%", "reduce_kernel"))
     stats = _db_rows(trace, "select name, count(*), avg(duration), min(duration), max(duration) "
                             "from kernels group by name")
 
@@ -102,10 +131,10 @@ def summarize(args):
     n_copy = 1 << 30
     cf = n_copy / (counter(cfetch, "FETCH_SIZE", "%copyBuffer%")[0] * 1024)
     cw = n_copy / (counter(cwrite, "WRITE_SIZE", "%copyBuffer%")[0] * 1024)
-    lines = [f"# rocprofv3 summary: paged decode attention, workload {spec.name}", "",
+    lines = [f"# rocprofv3 summary: {title}, workload {wname}", "",
              "Commands (run from the repository root on one MI355X):", ""]
     lines += ["    " + c for c in args.command.split(" ;; ") if c]
-    lines += ["", f"Algorithmic KV bytes per call: {kvb}", "",
+    lines += ["", f"Algorithmic {unit} per call: {kvb}", "",
               "Kernel trace (durations in ns):", "",
               "| kernel | calls | avg | min | max |", "|---|---|---|---|---|"]
     for name, n, avg, mn, mx in sorted(stats, key=lambda r: -r[2] * r[1]):
@@ -116,7 +145,7 @@ def summarize(args):
               "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | calibrated HBM bytes/dispatch |",
               "|---|---|---|---|"]
     record = {}
-    for like, label in (("%partition_kernel%", "partition_kernel"), ("%reduce_kernel%", "reduce_kernel")):
+    for like, label in kernels:
         fk, nf = counter(fetch, "FETCH_SIZE", like)
         wk, nw = counter(write, "WRITE_SIZE", like)
         if fk is None or wk is None:
@@ -124,25 +153,25 @@ def summarize(args):
         hbm = fk * 1024 * cf + wk * 1024 * cw
         lines.append(f"| {label} | {fk:.0f} | {wk:.0f} | {hbm:.0f} |")
         record[label] = hbm
-    part = [r for r in stats if "partition_kernel" in r[0]]
+    part = [r for r in stats if kname in r[0]]
     if part:
         avg_ns = part[0][2]
-        lines += ["", f"partition_kernel: {kvb / avg_ns:.1f} GB/s algorithmic "
+        lines += ["", f"{kname}: {kvb / avg_ns:.1f} GB/s algorithmic "
                       f"({100 * kvb / avg_ns / HBM_PEAK_GBS:.1f}% of 8 TB/s) at the traced average "
-                      f"duration; HBM traffic {record.get('partition_kernel', 0) / kvb:.3f} x the "
+                      f"duration; HBM traffic {record.get(kname, 0) / kvb:.3f} x the "
                       f"algorithmic bytes."]
-    kname = "partition_kernel"
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), f"{kname}_{args.config}.md"), "w") as f:
+    fname = f"{kname}_{args.config}{'_bulk' + str(args.bulk) if args.op == 'cache_write' and args.bulk else ''}.md"
+    with open(os.path.join(os.path.dirname(TRAFFIC_FILE), fname), "w") as f:
         f.write("\n".join(lines) + "\n")
     try:
         with open(TRAFFIC_FILE) as f:
             allrec = json.load(f)
     except (OSError, ValueError):
         allrec = {}
-    if "partition_kernel" in record:
-        allrec[spec.name] = {"kernel_source_sha256_16": source_digest(),
-                             "hbm_bytes_per_launch": round(record["partition_kernel"]),
+    if kname in record:
+        allrec[wname] = {"kernel_source_sha256_16": source_digest(),
+                             "hbm_bytes_per_launch": round(record[kname]),
                              "algorithmic_bytes": kvb,
                              "calibration": {"fetch": round(cf, 4), "write": round(cw, 4)}}
         with open(TRAFFIC_FILE, "w") as f:
@@ -191,6 +220,99 @@ def cpu_baseline(w, seconds: float):
             "seconds": t}
 
 
+WRITE_METRIC = "paged KV-cache write: GB/s (% of HBM peak) and µs/call"
+
+
+def bench_cache_write(args):
+    """The paged KV-cache write: the new tokens' K/V rows of the config's
+    decode step (or ``--bulk`` tokens to random slots of a large pool) into
+    the cache, timed like the attention call; rows rotated over copies so
+    they are read from HBM."""
+    import torch
+
+    from paged_attention_decode_attn_amd import binding as B
+    from paged_attention_decode_attn_amd.workloads import write_bytes
+
+    spec, cw, name, wb = cache_write_workload(args)
+    d = cw.to("cuda")
+    w = d.base
+    row_bytes = 2 * d.k_new.numel() * 2
+    copies = max(2, min(64, math.ceil((1 << 30) / max(row_bytes, 1)) + 1))
+    rows = [(d.k_new.clone(), d.v_new.clone()) for _ in range(copies)]
+
+    def call(i):
+        kn, vn = rows[i % copies]
+        B.paged_attn_reshape_and_cache(kn, vn, d.slot_mapping, w.k_cache, w.v_cache, w.k_scale, w.v_scale)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    gs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        for i in range(args.steps):
+            call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
+    del graph
+    value = wb / (ms * 1e-3) / 1e9
+    # one kernel per call: its launch duration is the faster of the two
+    # timings (eager calls are host-bound when the write is small)
+    achieved = wb / (min(ms, ms_graph) * 1e-3) / 1e9
+    res = {
+        "metric": WRITE_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->fp8_e4m3fn+fp32 scales" if spec.kv_dtype == "fp8_e4m3fn" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": int(cw.k_new.shape[0]), "kv_heads": spec.hkv,
+                   "head_dim": spec.head_dim, "kv_dtype": spec.kv_dtype, "pool_blocks": spec.pool_blocks,
+                   "row_copies_rotated": copies},
+        "us_per_call": round(ms * 1e3, 3), "us_per_call_graph": round(ms_graph * 1e3, 3),
+        "bytes_per_call": wb,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
+                     "algorithmic_bytes": wb,
+                     "kernel": "cache_write_kernel",
+                     "timing": "faster of the eager and graph-replayed timed steps"},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle.cache_write import reshape_and_cache
+        h = cw.base
+
+        def bits(t):
+            return t.view(torch.int16).numpy().view("uint16") if t.dtype == torch.bfloat16 else t.numpy()
+        n = min(cw.k_new.shape[0], 4096)
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            reshape_and_cache(bits(cw.k_new[:n]), bits(cw.v_new[:n]), cw.slot_mapping[:n].numpy(),
+                              bits(h.k_cache), bits(h.v_cache),
+                              None if h.k_scale is None else h.k_scale.numpy(),
+                              None if h.v_scale is None else h.v_scale.numpy(), spec.kv_dtype)
+        t = time.perf_counter() - t0
+        nb = write_bytes(cw.slot_mapping[:n], spec.hkv, spec.head_dim, spec.kv_dtype, spec.pool_blocks)
+        res["cpu_baseline"] = {"value": nb / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle write of {n} tokens ({nb} bytes, {t:.2f} s incl. "
+                                         f"copying the pool, 1 thread)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse_args()
     if args.summarize:
@@ -214,6 +336,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.op == "cache_write":
+        bench_cache_write(args)
         return
 
     spec = CONFIGS[args.config]

@@ -168,8 +168,9 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
  *   v_scale       required iff the cache is fp8, else NULL.  For an fp8
  *                 cache every written (token, kv head) row gets
  *                 scale = max_d |x_d| / 448 (1 for an all-zero row) and
- *                 codes e4m3fn(clamp(x_d / scale, -448, 448)), rounded to
- *                 nearest, ties to even, both divisions in IEEE float32.
+ *                 codes e4m3fn(clamp(x_d * (448 / max_d |x_d|), -448, 448))
+ *                 (x_d * 1 for an all-zero row), rounded to nearest, ties
+ *                 to even; divisions and products in IEEE float32.
  *                 A bf16 cache receives the rows bit for bit.
  *   stream        hipStream_t as void*, NULL = default stream.
  *

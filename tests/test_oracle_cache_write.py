@@ -144,7 +144,9 @@ import sys  # noqa: E402
 
 _ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 CW_MUTANTS = {
-    "scale_max": ("np.where(amax > 0, amax / np.float32(FP8_MAX)", "np.where(amax > 0, amax / np.float32(224.0)"),
+    "scale_max": ("np.where(nonzero, amax / np.float32(FP8_MAX)", "np.where(nonzero, amax / np.float32(224.0)"),
+    "inv_max": ("np.where(nonzero, np.float32(FP8_MAX) / safe", "np.where(nonzero, np.float32(224.0) / safe"),
+    "divide_by_inv": ("y = (x * inv[..., None])", "y = (x / inv[..., None])"),
     "ties_away": ("(_POS_CODES[hi] % 2 == 0)", "(_POS_CODES[hi] >= 0)"),
     "truncate": ("take_hi = (d_hi < d_lo)", "take_hi = (d_hi < 0 * d_lo)"),
     "sign_lost": ("return (code | sign).astype(np.uint8)", "return code.astype(np.uint8)"),
@@ -152,7 +154,7 @@ CW_MUTANTS = {
                         "pos, blk = int(s // BLOCK_SIZE) % BLOCK_SIZE, int(s % BLOCK_SIZE) % nb"),
     "v_from_k": ("((k_new_bits, kc, ks), (v_new_bits, vc, vs))", "((k_new_bits, kc, ks), (k_new_bits, vc, vs))"),
     "skip_slot_zero": ("if s < 0 or s >= nb * BLOCK_SIZE:", "if s <= 0 or s >= nb * BLOCK_SIZE:"),
-    "zero_row_scale": ("np.float32(1.0)).astype(np.float32)", "np.float32(0.0)).astype(np.float32)"),
+    "zero_row_scale": ("amax / np.float32(FP8_MAX), np.float32(1.0))", "amax / np.float32(FP8_MAX), np.float32(0.0))"),
 }
 
 
