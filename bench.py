@@ -34,12 +34,12 @@ KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", 
 
 
 def parse_args():
-    from paged_attention_decode_attn_amd.workloads import CONFIG_ORDER
+    from paged_attention_decode_attn_amd.workloads import CONFIG_ORDER, NEXT_CONFIG_ORDER
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER)
+    ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER + NEXT_CONFIG_ORDER)
     ap.add_argument("--op", default="decode", choices=["decode", "cache_write"],
                     help="decode: the attention call (default); cache_write: the paged KV-cache "
                          "write before it, on --config's decode step or a bulk write (--bulk)")
@@ -433,7 +433,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3fn-kv/bf16-mfma" if spec.kv_dtype == "fp8_e4m3fn" else "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "batch": spec.batch, "query_len": spec.qlen,
+        "config": {"workload": spec.name, "batch": spec.batch,
+                   "query_len": (f"U[{spec.qlen_lo}, {spec.qlen}] (seed {spec.seed})" if spec.qlen_lo
+                                 else spec.qlen),
                    "q_heads": spec.hq, "kv_heads": spec.hkv, "head_dim": spec.head_dim,
                    "kv_dtype": spec.kv_dtype, "block_size": 16,
                    "context_lens": ([int(x) for x in w.context_lens] if spec.batch <= 4

@@ -16,7 +16,8 @@ path; every value is N(0, 1) noise.
 
 Generation order for a spec with seed ``s`` (``torch.Generator('cpu')``):
 
-1. context lengths (constant, or uniform integers in ``[lo, hi]``);
+1. context lengths (constant, or uniform integers in ``[lo, hi]``), then,
+   for specs with ``qlen_lo``, query lengths uniform in ``[qlen_lo, qlen]``;
 2. one random permutation of the physical pool;
 3. Q, float32 N(0, 1) rounded to bf16;
 4. K for every used block, in table order (float32 N(0, 1)), then V the
@@ -45,7 +46,8 @@ import torch
 BLOCK = 16
 FP8_MAX = 448.0
 
-__all__ = ["WorkloadSpec", "Workload", "CONFIGS", "CONFIG_ORDER", "generate", "kv_bytes"]
+__all__ = ["WorkloadSpec", "Workload", "CONFIGS", "CONFIG_ORDER", "NEXT_CONFIG_ORDER", "generate", "kv_bytes",
+           "CacheWrite", "generate_cache_write", "write_bytes"]
 
 
 @dataclass(frozen=True)
@@ -62,6 +64,7 @@ class WorkloadSpec:
     pool_blocks: int
     seed: int
     scale: Optional[float] = None   # None: 1 / sqrt(head_dim)
+    qlen_lo: Optional[int] = None   # ragged query lengths, uniform in [qlen_lo, qlen]
 
     @property
     def softmax_scale(self) -> float:
@@ -94,6 +97,21 @@ CONFIGS = {
                                ctx_lo=256, ctx_hi=16384, pool_blocks=65536, seed=5),
 }
 CONFIG_ORDER = ["tiny", "llama3_8b", "long_ctx", "fp8", "mtp_verify"]
+
+# Wider speculative verification (query length 4, and ragged query lengths
+# 1..4 per sequence): the ROCm blog "Optimizing ATOM and vLLM-ATOM for
+# High-Interactivity Inference" ("Multi-Token Prediction") verifies draft
+# tokens in one decode step, and the model operations guide's paged-kernel
+# envelope table bounds query length x q/kv head ratio; here 4 x 8 = 32 rows.
+CONFIGS.update({
+    "mtp_verify_q4": WorkloadSpec("mtp_verify_b64_qlen4_q64kv8_d128_ctx256-16k_bf16", batch=64, qlen=4,
+                                  hq=64, hkv=8, head_dim=128, kv_dtype="bf16", ctx_lo=256, ctx_hi=16384,
+                                  pool_blocks=65536, seed=6),
+    "mtp_verify_ragged": WorkloadSpec("mtp_verify_b64_qlen1-4_q64kv8_d128_ctx256-16k_bf16", batch=64,
+                                      qlen=4, hq=64, hkv=8, head_dim=128, kv_dtype="bf16", ctx_lo=256,
+                                      ctx_hi=16384, pool_blocks=65536, seed=7, qlen_lo=1),
+})
+NEXT_CONFIG_ORDER = ["mtp_verify_q4", "mtp_verify_ragged"]
 
 
 @dataclass
@@ -202,7 +220,9 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
         raise ValueError("a context is longer than the block table")
     if ctx.numel() and int(ctx.min()) < 0:
         raise ValueError("negative context length")
-    if query_lens is None:
+    if query_lens is None and spec.qlen_lo is not None:
+        qls = torch.randint(spec.qlen_lo, Qn + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    elif query_lens is None:
         qls = torch.full((B,), Qn, dtype=torch.int32)
     else:
         qls = torch.as_tensor(query_lens, dtype=torch.int32).clone()

@@ -29,6 +29,9 @@ SMALL = {
     "long_ctx": small("long_ctx", ctx_lo=20001, ctx_hi=20001, pool_blocks=1300),
     "fp8": small("fp8", batch=5, ctx_lo=100, ctx_hi=3000, pool_blocks=1000),
     "mtp_verify": small("mtp_verify", batch=6, ctx_lo=2, ctx_hi=2000, pool_blocks=800),
+    # wider and ragged speculative verification (32 query rows per kv head)
+    "mtp_verify_q4": small("mtp_verify_q4", batch=6, ctx_lo=4, ctx_hi=2000, pool_blocks=800),
+    "mtp_verify_ragged": small("mtp_verify_ragged", batch=9, ctx_lo=4, ctx_hi=2000, pool_blocks=1200),
 }
 
 
@@ -241,7 +244,7 @@ def test_profile_events_measure_both_kernels():
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("name,subset", [
     ("tiny", None), ("llama3_8b", None), ("long_ctx", None), ("fp8", [0, 7, 15]),
-    ("mtp_verify", [0, 21, 63]),
+    ("mtp_verify", [0, 21, 63]), ("mtp_verify_q4", [0, 33, 63]), ("mtp_verify_ragged", [1, 30, 62]),
 ])
 def test_full_size_configs_sampled(name, subset):
     w = generate(CONFIGS[name])

@@ -92,3 +92,15 @@ def test_numpy_inputs_are_the_same_bytes():
 def test_rejects_pool_too_small():
     with pytest.raises(ValueError):
         generate(CONFIGS["tiny"].replace(pool_blocks=16))
+
+
+def test_ragged_query_lengths_are_drawn_in_range_and_reproducibly():
+    from paged_attention_decode_attn_amd.workloads import CONFIGS, generate
+    spec = CONFIGS["mtp_verify_ragged"].replace(batch=40, ctx_lo=8, ctx_hi=300, pool_blocks=1000)
+    a, b = generate(spec), generate(spec)
+    ql = a.query_lens
+    assert ql.dtype == torch.int32 and int(ql.min()) >= 1 and int(ql.max()) <= 4
+    assert len(set(ql.tolist())) > 1                                # actually ragged
+    assert torch.equal(ql, b.query_lens) and torch.equal(a.k_cache, b.k_cache)
+    # specs without qlen_lo draw nothing extra: the five workloads are unchanged
+    assert CONFIGS["mtp_verify"].qlen_lo is None
