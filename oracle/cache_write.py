@@ -20,9 +20,9 @@ scales and writes K/V straight into the paged cache.
 
 For every new token ``t`` with slot ``s = slot_mapping[t]``:
 
-* ``s < 0`` (a padding token) or ``s >= num_blocks * 16``: nothing is
-  written;
-* otherwise block ``s // 16``, position ``s % 16`` receives, for each kv
+* ``s < 0`` (a padding token) or ``s >= num_blocks * BS``: nothing is
+  written (``BS`` = the block size, the cache's second dimension);
+* otherwise block ``s // BS``, position ``s % BS`` receives, for each kv
   head ``h``:
     - bf16 cache: the token's bf16 row, bit for bit;
     - fp8 cache: ``a = max_d |x_d|`` over the row (x widened exactly to
@@ -46,7 +46,6 @@ from .formats import bf16_bits_to_f64, e4m3fn_table
 __all__ = ["FP8_MAX", "e4m3fn_encode", "quantize_rows_e4m3fn", "reshape_and_cache"]
 
 FP8_MAX = 448.0
-BLOCK_SIZE = 16
 
 # The finite non-negative e4m3fn values in code order (codes 0x00 .. 0x7E):
 # the encoding is monotone for non-negative codes, so neighbouring codes are
@@ -95,21 +94,21 @@ def reshape_and_cache(k_new_bits, v_new_bits, slot_mapping, k_cache, v_cache,
 
     ``k_new_bits`` / ``v_new_bits``: bf16 bit patterns ``[T, Hkv, D]``;
     ``slot_mapping``: ``[T]`` integers; ``k_cache`` / ``v_cache``: uint16
-    (bf16 bits) or uint8 (e4m3fn) ``[NB, 16, Hkv, D]``; ``k_scale`` /
-    ``v_scale``: float32 ``[NB, 16, Hkv]`` for an fp8 cache.  Returns new
+    (bf16 bits) or uint8 (e4m3fn) ``[NB, BS, Hkv, D]``; ``k_scale`` /
+    ``v_scale``: float32 ``[NB, BS, Hkv]`` for an fp8 cache.  Returns new
     arrays ``(k_cache, v_cache, k_scale, v_scale)``; the inputs are not
     modified.
     """
     kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
     ks = None if k_scale is None else np.array(k_scale, dtype=np.float32, copy=True)
     vs = None if v_scale is None else np.array(v_scale, dtype=np.float32, copy=True)
-    nb = kc.shape[0]
+    nb, bs = kc.shape[0], kc.shape[1]
     fp8 = kv_dtype == "fp8_e4m3fn"
     slots = np.asarray(slot_mapping).astype(np.int64)
     for t, s in enumerate(slots):
-        if s < 0 or s >= nb * BLOCK_SIZE:
+        if s < 0 or s >= nb * bs:
             continue
-        blk, pos = int(s // BLOCK_SIZE), int(s % BLOCK_SIZE)
+        blk, pos = int(s // bs), int(s % bs)
         for src, cache, sc in ((k_new_bits, kc, ks), (v_new_bits, vc, vs)):
             row = np.asarray(src[t])                                   # [Hkv, D] bf16 bits
             if fp8:

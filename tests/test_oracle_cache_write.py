@@ -77,21 +77,23 @@ def _bf16_bits(a):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
-def test_write_touches_exactly_the_mapped_slots(kv):
+@pytest.mark.parametrize("bs", [16, 64])
+def test_write_touches_exactly_the_mapped_slots(kv, bs):
     rng = np.random.default_rng(9)
     NB, H, D, T = 6, 2, 64, 7
     kn = _bf16_bits(rng.normal(0, 1, (T, H, D)))
     vn = _bf16_bits(rng.normal(0, 1, (T, H, D)))
-    slots = np.array([5, -1, 17, 95, 40, 96, 0])             # -1 and 96 (= NB*16) are skipped
+    # a negative slot and NB*bs (one past the pool) are skipped
+    slots = np.array([5, -1, 17, NB * bs - 1, 40, NB * bs, 0])
     cdt = np.uint8 if kv == "fp8_e4m3fn" else np.uint16
-    kc = np.full((NB, 16, H, D), 0x3C, cdt)
-    vc = np.full((NB, 16, H, D), 0x3C, cdt)
-    ks = np.full((NB, 16, H), 7.0, np.float32) if kv == "fp8_e4m3fn" else None
-    vs = np.full((NB, 16, H), 7.0, np.float32) if kv == "fp8_e4m3fn" else None
+    kc = np.full((NB, bs, H, D), 0x3C, cdt)
+    vc = np.full((NB, bs, H, D), 0x3C, cdt)
+    ks = np.full((NB, bs, H), 7.0, np.float32) if kv == "fp8_e4m3fn" else None
+    vs = np.full((NB, bs, H), 7.0, np.float32) if kv == "fp8_e4m3fn" else None
     k2, v2, ks2, vs2 = reshape_and_cache(kn, vn, slots, kc, vc, ks, vs, kv)
-    written = {5, 17, 95, 40, 0}
-    for s in range(NB * 16):
-        b, p = divmod(s, 16)
+    written = {5, 17, NB * bs - 1, 40, 0}
+    for s in range(NB * bs):
+        b, p = divmod(s, bs)
         if s in written:
             t = int(np.nonzero(slots == s)[0][0])
             for new, cache, sc in ((kn, k2, ks2), (vn, v2, vs2)):
@@ -150,10 +152,11 @@ CW_MUTANTS = {
     "ties_away": ("(_POS_CODES[hi] % 2 == 0)", "(_POS_CODES[hi] >= 0)"),
     "truncate": ("take_hi = (d_hi < d_lo)", "take_hi = (d_hi < 0 * d_lo)"),
     "sign_lost": ("return (code | sign).astype(np.uint8)", "return code.astype(np.uint8)"),
-    "slot_block_swap": ("blk, pos = int(s // BLOCK_SIZE), int(s % BLOCK_SIZE)",
-                        "pos, blk = int(s // BLOCK_SIZE) % BLOCK_SIZE, int(s % BLOCK_SIZE) % nb"),
+    "slot_block_swap": ("blk, pos = int(s // bs), int(s % bs)",
+                        "pos, blk = int(s // bs) % bs, int(s % bs) % nb"),
+    "block_size_16": ("blk, pos = int(s // bs), int(s % bs)", "blk, pos = int(s // 16) % nb, int(s % 16)"),
     "v_from_k": ("((k_new_bits, kc, ks), (v_new_bits, vc, vs))", "((k_new_bits, kc, ks), (k_new_bits, vc, vs))"),
-    "skip_slot_zero": ("if s < 0 or s >= nb * BLOCK_SIZE:", "if s <= 0 or s >= nb * BLOCK_SIZE:"),
+    "skip_slot_zero": ("if s < 0 or s >= nb * bs:", "if s <= 0 or s >= nb * bs:"),
     "zero_row_scale": ("amax / np.float32(FP8_MAX), np.float32(1.0))", "amax / np.float32(FP8_MAX), np.float32(0.0))"),
 }
 
@@ -212,6 +215,16 @@ def _cw_battery(cw, orc) -> bool:
                         c, sref = quantize_rows_e4m3fn(bf16_bits_to_f64(new[t]).astype(np.float32))
                         if not (np.array_equal(cache[b, p], c) and np.array_equal(sc[b, p], sref)):
                             return False
+        # block size 64: slot s is position s % 64 of block s // 64
+        kc = np.zeros((3, 64, H, D), np.uint16)
+        slots64 = np.array([0, 63, 64, 130, 191])
+        k2, _, _, _ = cw.reshape_and_cache(kn, vn, slots64, kc, kc.copy(), None, None, "bf16")
+        for t, s in enumerate(slots64):
+            b, p = divmod(int(s), 64)
+            if not np.array_equal(k2[b, p], kn[t]):
+                return False
+        if np.count_nonzero(np.any(k2 != 0, axis=(2, 3))) != len(slots64):
+            return False
         return True
     except Exception:
         return False

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 from test_oracle import _bf16_bits, _case, _page, _sdpa_reference
+from test_oracle_variants import variant_battery
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
@@ -27,12 +28,17 @@ MUTANTS = {
     "dropped_scale": ("paged_attention.py", "x = s * np.matmul", "x = np.matmul"),
     "causal_offset": ("paged_attention.py", "pos = L - n + np.arange(n)", "pos = np.arange(n) + L - 1"),
     "causal_off_by_one": ("paged_attention.py", "<= pos[:, None]", "< pos[:, None] + 0 * 1"),
-    "block_index": ("paged_attention.py", "[j // BLOCK_SIZE]", "[(j // BLOCK_SIZE) % 2]"),
-    "slot_index": ("paged_attention.py", "slot = j % BLOCK_SIZE", "slot = (j + 1) % BLOCK_SIZE"),
+    "block_index": ("paged_attention.py", "[j // bs]", "[(j // bs) % 2]"),
+    "slot_index": ("paged_attention.py", "slot = j % bs", "slot = (j + 1) % bs"),
     "fp8_scale_head": ("paged_attention.py", "vals = vals * s[:, :, None]", "vals = vals * s[:, :1, None]"),
-    "normaliser": ("paged_attention.py", "/ e.sum(axis=-1, keepdims=True))", "/ e.sum(axis=-1, keepdims=True).max())"),
+    "normaliser": ("paged_attention.py", "den = e.sum(axis=-1, keepdims=True)", "den = e.sum(axis=-1, keepdims=True).max()"),
     "values_are_keys": ("paged_attention.py", "np.matmul(e, V[:, g, :])", "np.matmul(e, K[:, g, :])"),
-    "no_max_shift": ("paged_attention.py", "x = x - x.max(axis=-1, keepdims=True)", "x = x - x.max()"),
+    "no_max_shift": ("paged_attention.py", "mx = x.max(axis=-1, keepdims=True)", "mx = x.max()"),
+    "window_off_by_one": ("paged_attention.py", "> (pos - window)[:, None]", ">= (pos - window)[:, None]"),
+    "sink_head_index": ("paged_attention.py", "sink[g * G:(g + 1) * G]", "sink[g:g + G]"),
+    "sink_not_in_max": ("paged_attention.py", "mx = np.maximum(mx, sk)", "mx = mx + 0 * sk"),
+    "sink_dropped": ("paged_attention.py", "+ np.exp(sk - mx)", "+ 0 * np.exp(sk - mx)"),
+    "block_size_fixed": ("paged_attention.py", "bs = np.asarray(cache).shape[1]", "bs = 16"),
     "e4m3_subnormal": ("formats.py", "man_field * 2.0 ** -9", "man_field * 2.0 ** -10"),
     "e4m3_bias": ("formats.py", "2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
     "e4m3_mantissa": ("formats.py", "(1.0 + man_field / 8.0)", "(1.0 + man_field / 16.0)"),
@@ -123,6 +129,9 @@ def _battery(orc) -> bool:
         x = np.array([700.0, 0.0])
         m, l, o = orc.partial_state(x, np.eye(2))
         if not np.all(np.isfinite(o)):
+            return False
+        # block sizes, sliding window, sinks
+        if not variant_battery(orc):
             return False
     except Exception:
         return False
