@@ -30,7 +30,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the kernels and the planner that sets their launch shape
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", f)
-                  for f in ("pa_device.hip", "pa_host.cpp", "pa_internal.h")]
+                  for f in ("pa_device.hip", "pa_cache.hip", "pa_host.cpp", "pa_internal.h")]
 
 
 def parse_args():
@@ -99,11 +99,12 @@ def cache_write_workload(args):
     from paged_attention_decode_attn_amd.workloads import CONFIGS, generate_cache_write, write_bytes
     spec = CONFIGS[args.config]
     if args.bulk:
-        pool = max(spec.pool_blocks, -(-2 * args.bulk // 16))
+        pool = max(spec.pool_blocks, -(-2 * args.bulk // spec.block_size))
         spec = spec.replace(batch=1, ctx_lo=16, ctx_hi=16, pool_blocks=pool)
     cw = generate_cache_write(spec, bulk_tokens=args.bulk or None)
     name = (f"bulk{args.bulk}_" if args.bulk else "decode_step_") + spec.name
-    wb = write_bytes(cw.slot_mapping, spec.hkv, spec.head_dim, spec.kv_dtype, spec.pool_blocks)
+    wb = write_bytes(cw.slot_mapping, spec.hkv, spec.head_dim, spec.kv_dtype, spec.pool_blocks,
+                     spec.block_size)
     return spec, cw, name, wb
 
 
@@ -118,7 +119,9 @@ def summarize(args):
     else:
         spec = CONFIGS[args.config]
         wname = spec.name
-        kvb = kv_bytes(generate(spec).context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
+        w0 = generate(spec)
+        kvb = kv_bytes(w0.context_lens, spec.hkv, spec.head_dim, spec.kv_dtype, w0.query_lens,
+                       spec.sliding_window)
         kname, title, unit = "partition_kernel", "paged decode attention", "KV bytes"
         kernels = (("%partition_kernel%", "partition_kernel"), ("%reduce_kernel%", "reduce_kernel"))
     stats = _db_rows(trace, "select name, count(*), avg(duration), min(duration), max(duration) "
@@ -208,7 +211,8 @@ def cpu_baseline(w, seconds: float):
             t0 = time.perf_counter()
             paged_decode_attention(**inputs, batch_subset=[b])
             t += time.perf_counter() - t0
-            done_bytes += kv_bytes(w.context_lens[b:b + 1], spec.hkv, spec.head_dim, spec.kv_dtype)
+            done_bytes += kv_bytes(w.context_lens[b:b + 1], spec.hkv, spec.head_dim, spec.kv_dtype,
+                                   w.query_lens[b:b + 1], spec.sliding_window)
             done_seqs += 1
             b = (b + 1) % spec.batch
             if t >= seconds:
@@ -306,7 +310,8 @@ def bench_cache_write(args):
                               None if h.k_scale is None else h.k_scale.numpy(),
                               None if h.v_scale is None else h.v_scale.numpy(), spec.kv_dtype)
         t = time.perf_counter() - t0
-        nb = write_bytes(cw.slot_mapping[:n], spec.hkv, spec.head_dim, spec.kv_dtype, spec.pool_blocks)
+        nb = write_bytes(cw.slot_mapping[:n], spec.hkv, spec.head_dim, spec.kv_dtype, spec.pool_blocks,
+                         spec.block_size)
         res["cpu_baseline"] = {"value": nb / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                                "sample": f"oracle write of {n} tokens ({nb} bytes, {t:.2f} s incl. "
                                          f"copying the pool, 1 thread)"}
@@ -344,7 +349,7 @@ def main():
     spec = CONFIGS[args.config]
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
     w = generate(spec)
-    kvb = kv_bytes(w.context_lens, spec.hkv, spec.head_dim, spec.kv_dtype)
+    kvb = kv_bytes(w.context_lens, spec.hkv, spec.head_dim, spec.kv_dtype, w.query_lens, spec.sliding_window)
     dev = w.to("cuda")
     pool_bytes = 2 * dev.k_cache.numel() * dev.k_cache.element_size()
     copies = args.copies or min(64, max(2, math.ceil((1 << 30) / kvb) + 1))
@@ -357,14 +362,23 @@ def main():
     out = torch.empty_like(dev.q)
     B.paged_attn_set_workgroups(args.workgroups)
     B.paged_attn_set_min_share(args.min_share)
-    plan = B.paged_attn_plan(spec.batch, spec.hq, spec.hkv, spec.head_dim, spec.qlen,
-                             spec.table_width, spec.kv_dtype,
+    # the most tokens a sequence's rows read (the table's reach, or the
+    # window plus the query rows over one more chunk)
+    max_ctx = spec.block_size * spec.table_width
+    if spec.sliding_window > 0:
+        max_ctx = min(max_ctx, 32 * (-(-(spec.sliding_window + spec.qlen - 1) // 32) + 1))
+    plan = B.paged_attn_plan(spec.batch, spec.hq, spec.hkv, spec.head_dim, spec.qlen, max_ctx, spec.kv_dtype,
                              torch.cuda.get_device_properties(0).multi_processor_count)
+    ext = spec.sliding_window > 0 or dev.sinks is not None
 
     def call(i):
         kc, vc, ks, vs = pools[i % copies]
-        B.paged_attn_decode(dev.q, kc, vc, dev.block_tables, dev.context_lens, dev.query_lens,
-                            dev.scale, ks, vs, out)
+        if ext:
+            B.paged_attn_decode_ext(dev.q, kc, vc, dev.block_tables, dev.context_lens, dev.query_lens,
+                                    dev.scale, ks, vs, spec.sliding_window, dev.sinks, out)
+        else:
+            B.paged_attn_decode(dev.q, kc, vc, dev.block_tables, dev.context_lens, dev.query_lens,
+                                dev.scale, ks, vs, out)
 
     print(f"[bench] warmup {args.warmup}, copies {copies}, plan {plan}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -437,7 +451,8 @@ def main():
                    "query_len": (f"U[{spec.qlen_lo}, {spec.qlen}] (seed {spec.seed})" if spec.qlen_lo
                                  else spec.qlen),
                    "q_heads": spec.hq, "kv_heads": spec.hkv, "head_dim": spec.head_dim,
-                   "kv_dtype": spec.kv_dtype, "block_size": 16,
+                   "kv_dtype": spec.kv_dtype, "block_size": spec.block_size,
+                   "sliding_window": spec.sliding_window or None, "sinks": spec.sinks,
                    "context_lens": ([int(x) for x in w.context_lens] if spec.batch <= 4
                                     else f"U[{spec.ctx_lo}, {spec.ctx_hi}] (seed {spec.seed})"),
                    "workgroups": plan["workgroups"], "heads_per_group": plan["heads_per_group"],

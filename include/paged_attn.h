@@ -10,8 +10,9 @@
  *     must not be served by a one-descale kernel) and "KV cache operations"
  *     (bf16 cache writes, fp8 writes with per-token quantisation);
  *   - ATOM configuration guide, "Master configuration (Config)"
- *     (kv_cache_block_size 16, kv_cache_dtype "bf16" or "fp8") and
- *     "Quick reference" (per-layer k/v caches and their scales);
+ *     (kv_cache_block_size: 16 by default, a multiple of 16; kv_cache_dtype
+ *     "bf16" or "fp8") and "Quick reference" (per-layer k/v caches and
+ *     their scales);
  *   - ROCm blog "Optimizing ATOM and vLLM-ATOM for High-Interactivity
  *     Inference", "Attention Decode: Split Memory Work to Fill the Device"
  *     (split the KV range so a single query fills the device; per-split
@@ -44,7 +45,8 @@
 extern "C" {
 #endif
 
-#define PA_BLOCK_SIZE 16      /* tokens per KV-cache block                  */
+#define PA_BLOCK_SIZE 16      /* default tokens per KV-cache block; a block
+                                 holds any multiple of 16 up to 4096 tokens  */
 #define PA_MAX_ROWS   64      /* max (q_heads / kv_heads) * query_len       */
 
 typedef enum pa_dtype {
@@ -59,7 +61,8 @@ typedef enum pa_status {
     PA_ERR_NULL        = -1,  /* a required tensor or data pointer is NULL   */
     PA_ERR_DTYPE       = -2,  /* a tensor has the wrong dtype                */
     PA_ERR_SHAPE       = -3,  /* ranks or sizes disagree between tensors     */
-    PA_ERR_UNSUPPORTED = -4,  /* block size != 16, head_dim not 64/128,
+    PA_ERR_UNSUPPORTED = -4,  /* block size not a multiple of 16, head_dim
+                                 not 64/128,
                                  q_heads % kv_heads != 0, rows > 64, ...     */
     PA_ERR_LAYOUT      = -5,  /* inner stride != 1, misaligned base/stride   */
     PA_ERR_CAPTURE     = -6,  /* workspace would have to grow while the
@@ -84,10 +87,11 @@ typedef struct pa_tensor {
  *   q             bf16 [B, Qmax, Hq, D] (rank 4) or [B, Hq, D] (rank 3,
  *                 Qmax = 1).  Row (b, t) is the t-th new token of sequence
  *                 b (the rectangular speculative-decode layout).
- *   k_cache,      [NB, 16, Hkv, D], both bf16 or both fp8 e4m3fn.
- *   v_cache       Token j of sequence b is slot j % 16 of physical block
- *                 block_tables[b, j / 16].
- *   block_tables  int32 [B, W].  Only the first ceil(context_lens[b] / 16)
+ *   k_cache,      [NB, BS, Hkv, D], both bf16 or both fp8 e4m3fn; the block
+ *   v_cache       size BS is a multiple of 16 (16 by default, up to 4096).
+ *                 Token j of sequence b is slot j % BS of physical block
+ *                 block_tables[b, j / BS].
+ *   block_tables  int32 [B, W].  Only the first ceil(context_lens[b] / BS)
  *                 entries of row b are read; the rest may hold anything.
  *                 Entries may repeat within and across rows (shared
  *                 prefix blocks); the cache is only read.
@@ -100,11 +104,11 @@ typedef struct pa_tensor {
  *                 attends to keys 0 .. L_b - n_b + t (causal among the new
  *                 tokens).  Rows t >= n_b are neither read nor written.
  *   scale         softmax scale applied to q.k (e.g. 1/sqrt(D)); finite.
- *   k_scale,      fp32, logically [NB, 16, Hkv]: one dequantisation scale
+ *   k_scale,      fp32, logically [NB, BS, Hkv]: one dequantisation scale
  *   v_scale       per (block, slot, kv head), i.e. per token and head;
  *                 required iff the cache is fp8, else must be NULL.  The
  *                 slot dimension must be contiguous (stride[1] == 1), e.g.
- *                 a [NB, Hkv, 16] tensor viewed as [NB, 16, Hkv].
+ *                 a [NB, Hkv, BS] tensor viewed as [NB, BS, Hkv].
  *   out           bf16, same shape as q (its own strides); rows t < n_b
  *                 receive the attention output rounded to nearest even.
  *   stream        hipStream_t as void*, NULL = default stream.
@@ -116,8 +120,8 @@ typedef struct pa_tensor {
  * multiples of 4 and data 16-byte aligned.
  *
  * Device-side preconditions, not checked (checking would need a
- * host-device synchronisation): n_b <= L_b <= 16 * W and
- * 0 <= block_tables[b, i] < NB for i < ceil(L_b / 16).  Violations give
+ * host-device synchronisation): n_b <= L_b <= BS * W and
+ * 0 <= block_tables[b, i] < NB for i < ceil(L_b / BS).  Violations give
  * unspecified output values but never an out-of-bounds access: the kernels
  * clamp lengths to the tensors' extents and block ids into [0, NB).
  * `out` must not overlap any input.
@@ -137,6 +141,36 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
                       const pa_tensor* v_scale, pa_tensor* out, void* stream);
 
 /*
+ * paged_attn_decode_ext -- paged_attn_decode with a sliding window and
+ * attention sinks.  Sources: ATOM model operations guide, "Attention
+ * operations" (the decode dispatch takes a sliding_window, -1 for none);
+ * the ATOM landing page's model table (GPT-OSS: sliding window + attention
+ * sinks).  The pages give no formulas; the definitions below are the
+ * common ones.  With sliding_window <= 0 and sinks NULL the call is
+ * paged_attn_decode.
+ *
+ *   sliding_window  w > 0: query row t at position p = L_b - n_b + t sees
+ *                 only keys max(0, p - w + 1) .. p (its w most recent
+ *                 positions).  w <= 0: no window.  Block-table entries
+ *                 wholly below the earliest row's window may hold anything
+ *                 (e.g. blocks already freed): the kernels clamp them into
+ *                 [0, NB) and never use what they address.
+ *   sinks         NULL, or fp32 [Hq] (any stride, 4-byte aligned): one
+ *                 logit s_h per query head, in the units of scale * q.k,
+ *                 added to the softmax normaliser only:
+ *                 out = sum_j e^{x_j} v_j / (e^{s_h} + sum_j e^{x_j}).
+ *                 -inf turns a head's sink off; +inf and NaN are not
+ *                 allowed (not checked: device data).
+ *
+ * Every other argument, rule and error as for paged_attn_decode.
+ */
+int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                          const pa_tensor* block_tables, const pa_tensor* context_lens,
+                          const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                          const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
+                          pa_tensor* out, void* stream);
+
+/*
  * paged_attn_check -- the host-side argument validation of
  * paged_attn_decode, without touching the GPU or dereferencing any data
  * pointer.  Same arguments (no stream); returns the status that
@@ -146,6 +180,13 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
                      const pa_tensor* block_tables, const pa_tensor* context_lens,
                      const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
                      const pa_tensor* v_scale, const pa_tensor* out);
+
+/* paged_attn_check_ext -- the same for paged_attn_decode_ext. */
+int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                         const pa_tensor* block_tables, const pa_tensor* context_lens,
+                         const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                         const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
+                         const pa_tensor* out);
 
 /*
  * paged_attn_reshape_and_cache -- write the new tokens' K and V rows into
@@ -158,13 +199,14 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
  * calculated as K/V are written into the paged cache).
  *
  *   k_new, v_new  bf16 [T, Hkv, D]: the new tokens' rows (D 64 or 128).
- *   slot_mapping  int32 [T]: slot s of token t is position s % 16 of block
- *                 s / 16.  Entries < 0 (padding tokens) and >= NB * 16 are
+ *   slot_mapping  int32 [T]: slot s of token t is position s % BS of block
+ *                 s / BS.  Entries < 0 (padding tokens) and >= NB * BS are
  *                 skipped; the others must be distinct (two tokens on one
  *                 slot leave either token's row).
- *   k_cache,      [NB, 16, Hkv, D], both bf16 or both fp8 e4m3fn; written
- *   v_cache       at the mapped slots only.
- *   k_scale,      fp32, logically [NB, 16, Hkv], slot dimension contiguous;
+ *   k_cache,      [NB, BS, Hkv, D], both bf16 or both fp8 e4m3fn, BS a
+ *   v_cache       multiple of 16 (up to 4096); written at the mapped slots
+ *                 only.
+ *   k_scale,      fp32, logically [NB, BS, Hkv], slot dimension contiguous;
  *   v_scale       required iff the cache is fp8, else NULL.  For an fp8
  *                 cache every written (token, kv head) row gets
  *                 scale = max_d |x_d| / 448 (1 for an all-zero row) and
@@ -197,7 +239,9 @@ int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* 
  * Split-context plan: how paged_attn_decode divides the work so that one
  * call fills the GPU whatever the batch and the ragged context lengths.
  * Every (sequence, kv-head group) pair is a segment of ceil(L_b / 32)
- * chunks of 32 tokens; the chunks of all segments, sequence-major, are
+ * chunks of 32 tokens (with a sliding window, the chunks from the one that
+ * holds the earliest row's first key); the chunks of all segments,
+ * sequence-major, are
  * dealt out in equal contiguous shares (to within one chunk) to
  * `workgroups` workgroups of `heads_per_group` waves (one wave per kv head
  * of the group).  A share may start and end inside a sequence, so each
@@ -209,6 +253,10 @@ int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* 
  * is one workgroup per resident slot, fewer when shares would drop under
  * min_share_chunks chunks even at the longest contexts the table allows;
  * the kernel lowers it further for the actual lengths by the same rule.
+ * When every segment is short (at most 2 * 8 chunks: a short table or a
+ * sliding window) and there are enough of them to give every compute unit
+ * a workgroup, the plan takes whole segments instead: one workgroup per
+ * segment, output written directly, no partials and no merge.
  */
 typedef struct pa_plan {
     int32_t rows;               /* (Hq / Hkv) * Qmax query rows per kv head */
@@ -219,6 +267,8 @@ typedef struct pa_plan {
     int32_t reduce_col4;        /*   float4 columns per row,               */
     int32_t reduce_lanes;       /*   partial lanes per (row, column)       */
     int32_t expected_partials;  /* partials per row for alike lengths      */
+    int32_t whole_segments;     /* 1: one workgroup per segment, no merge  */
+    int32_t reserved;           /* 0                                       */
     int64_t workgroups;         /* partition-kernel grid                   */
     int64_t reduce_groups;      /* workgroups of the merge kernel (0: none) */
     int64_t workspace_bytes;    /* fp32 partials + log-sum-exp + chunk scan */
@@ -227,10 +277,13 @@ typedef struct pa_plan {
 /*
  * paged_attn_plan -- the plan for the given sizes on a device with
  * num_cus compute units (host only; no GPU access).  kv_dtype is a
- * pa_dtype of the cache.  Honors the overrides below.
+ * pa_dtype of the cache.  max_context is the most cache tokens one
+ * sequence's rows can read: block size x table width, or with a sliding
+ * window w at most 32 * (ceil((w + query_len - 1) / 32) + 1) of them
+ * (1 <= max_context <= 2^30).  Honors the overrides below.
  */
 int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
-                    int64_t query_len, int64_t table_width, int32_t kv_dtype,
+                    int64_t query_len, int64_t max_context, int32_t kv_dtype,
                     int32_t num_cus, pa_plan* plan);
 
 /*
@@ -268,18 +321,23 @@ int paged_attn_reserve(int64_t bytes, void* stream);
 /*
  * paged_attn_check_metadata -- host-side check of the device-side
  * preconditions on HOST copies of the metadata: 0 <= query_lens[b] <= Qmax,
- * query_lens[b] <= context_lens[b] <= 16 * W, and every used table entry in
- * [0, NB).  query_lens may be NULL (all Qmax).  table_row_stride is in
- * elements.  Returns PA_OK or PA_ERR_ARG (with the first offending
- * sequence in paged_attn_last_error()).
+ * query_lens[b] <= context_lens[b] <= block_size * W, and every table
+ * entry that holds a key some row sees (all of the first
+ * ceil(L_b / block_size) without a window; with sliding_window > 0 those
+ * from the block of the earliest row's first key) in [0, NB).  query_lens
+ * may be NULL (all Qmax).  table_row_stride is in elements.  Returns PA_OK
+ * or PA_ERR_ARG (with the first offending sequence in
+ * paged_attn_last_error()).
  */
 int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_lens,
                               const int32_t* block_tables, int64_t batch, int64_t table_width,
-                              int64_t table_row_stride, int64_t query_len, int64_t num_blocks);
+                              int64_t table_row_stride, int64_t query_len, int64_t num_blocks,
+                              int64_t block_size, int32_t sliding_window);
 
 /*
  * Kernel timing for measurement: after paged_attn_profile_begin(n), the
- * next n calls of paged_attn_decode (on any stream) record HIP events
+ * next n calls of paged_attn_decode or paged_attn_decode_ext (on any
+ * stream) record HIP events
  * before and after each kernel they launch, on the call's stream.
  * paged_attn_profile_end() waits for those events and returns the summed
  * durations in milliseconds of the partition kernel and of the merge

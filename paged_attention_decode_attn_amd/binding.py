@@ -41,6 +41,7 @@ class PaPlan(ctypes.Structure):
                 ("heads_per_group", ctypes.c_int32), ("min_share_chunks", ctypes.c_int32),
                 ("reduce_rows", ctypes.c_int32), ("reduce_col4", ctypes.c_int32),
                 ("reduce_lanes", ctypes.c_int32), ("expected_partials", ctypes.c_int32),
+                ("whole_segments", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("reduce_groups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
                 args11 = [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
                 L.paged_attn_decode.argtypes = args11 + [_P, ctypes.c_void_p]
                 L.paged_attn_check.argtypes = args11 + [_P]
+                L.paged_attn_decode_ext.argtypes = args11 + [ctypes.c_int32, _P, _P, ctypes.c_void_p]
+                L.paged_attn_check_ext.argtypes = args11 + [ctypes.c_int32, _P, _P]
                 L.paged_attn_reshape_and_cache.argtypes = [_P] * 7 + [ctypes.c_void_p]
                 L.paged_attn_check_reshape_and_cache.argtypes = [_P] * 7
                 L.paged_attn_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, ctypes.c_int32,
@@ -83,7 +86,7 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_set_heads_per_group.argtypes = [ctypes.c_int32]
                 L.paged_attn_reserve.argtypes = [ctypes.c_int64, ctypes.c_void_p]
                 i32p = ctypes.POINTER(ctypes.c_int32)
-                L.paged_attn_check_metadata.argtypes = [i32p, i32p, i32p] + [ctypes.c_int64] * 5
+                L.paged_attn_check_metadata.argtypes = [i32p, i32p, i32p] + [ctypes.c_int64] * 6 + [ctypes.c_int32]
                 L.paged_attn_profile_begin.argtypes = [ctypes.c_int32]
                 L.paged_attn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double),
                                                      ctypes.POINTER(ctypes.c_double),
@@ -93,6 +96,7 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_last_error.argtypes = []
                 L.paged_attn_last_error.restype = ctypes.c_char_p
                 for name in ("paged_attn_decode", "paged_attn_check", "paged_attn_plan",
+                             "paged_attn_decode_ext", "paged_attn_check_ext",
                              "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
                              "paged_attn_set_workgroups", "paged_attn_set_min_share",
                              "paged_attn_set_heads_per_group",
@@ -184,6 +188,32 @@ def paged_attn_check(q, k_cache, v_cache, block_tables, context_lens, query_lens
                                   _ref(describe(out)))
 
 
+def paged_attn_decode_ext(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale,
+                          k_scale=None, v_scale=None, sliding_window=0, sinks=None, out=None,
+                          stream=None):
+    """``paged_attn_decode`` with a sliding window (``<= 0``: none) and
+    per-query-head sink logits (fp32 ``[Hq]`` or None)."""
+    if out is None:
+        out = torch.empty_like(q)
+    descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, query_lens)]
+    st = lib().paged_attn_decode_ext(*[_ref(d) for d in descs], ctypes.c_float(scale),
+                                     _ref(describe(k_scale)), _ref(describe(v_scale)),
+                                     ctypes.c_int32(int(sliding_window)), _ref(describe(sinks)),
+                                     _ref(describe(out)), _stream_handle(q, stream))
+    _raise(st, "paged_attn_decode_ext")
+    return out
+
+
+def paged_attn_check_ext(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale,
+                         k_scale=None, v_scale=None, sliding_window=0, sinks=None, out=None) -> int:
+    """Status of the host-side validation of ``paged_attn_decode_ext``."""
+    descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, query_lens)]
+    return lib().paged_attn_check_ext(*[_ref(d) for d in descs], ctypes.c_float(scale),
+                                      _ref(describe(k_scale)), _ref(describe(v_scale)),
+                                      ctypes.c_int32(int(sliding_window)), _ref(describe(sinks)),
+                                      _ref(describe(out)))
+
+
 def paged_attn_reshape_and_cache(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None,
                                  v_scale=None, stream=None) -> None:
     """Write the new tokens' K/V (bf16 ``[T, Hkv, D]``) into the paged cache
@@ -210,11 +240,13 @@ def paged_attn_check_descriptors(q, k_cache, v_cache, block_tables, context_lens
                                   _ref(k_scale), _ref(v_scale), _ref(out))
 
 
-def paged_attn_plan(batch, q_heads, kv_heads, head_dim, query_len, table_width,
+def paged_attn_plan(batch, q_heads, kv_heads, head_dim, query_len, max_context,
                     kv_dtype="bf16", num_cus=256) -> dict:
+    """The split-context plan; ``max_context`` is the most cache tokens one
+    sequence's rows can read (block size x table width)."""
     code = PA_DTYPE_FP8_E4M3FN if kv_dtype == "fp8_e4m3fn" else PA_DTYPE_BF16
     p = PaPlan()
-    st = lib().paged_attn_plan(batch, q_heads, kv_heads, head_dim, query_len, table_width, code,
+    st = lib().paged_attn_plan(batch, q_heads, kv_heads, head_dim, query_len, max_context, code,
                                num_cus, ctypes.byref(p))
     _raise(st, "paged_attn_plan")
     return p.as_dict()
@@ -239,7 +271,7 @@ def paged_attn_reserve(nbytes: int, stream=None) -> None:
 
 
 def paged_attn_check_metadata(context_lens, query_lens, block_tables, query_len: int,
-                              num_blocks: int) -> None:
+                              num_blocks: int, block_size: int = 16, sliding_window: int = 0) -> None:
     """Check the device-side preconditions on host copies (raises on violation)."""
     ctx = context_lens.detach().to("cpu", torch.int32).contiguous()
     tbl = block_tables.detach().to("cpu", torch.int32).contiguous()
@@ -249,7 +281,7 @@ def paged_attn_check_metadata(context_lens, query_lens, block_tables, query_len:
         ctypes.cast(ctx.data_ptr(), i32p),
         None if ql is None else ctypes.cast(ql.data_ptr(), i32p),
         ctypes.cast(tbl.data_ptr(), i32p), ctx.numel(), tbl.shape[1], tbl.stride(0),
-        query_len, num_blocks)
+        query_len, num_blocks, block_size, ctypes.c_int32(int(sliding_window)))
     _raise(st, "paged_attn_check_metadata")
 
 

@@ -38,6 +38,7 @@ struct WriteArgs {
     float* ks; float* vs; int64_t ks_sblk, ks_sh, vs_sblk, vs_sh;             // floats
     int64_t T, slots_total;
     int32_t Hkv, D;
+    uint32_t bs;                                                              // tokens per block
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
@@ -88,7 +89,9 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
         k = *reinterpret_cast<const u32x4*>(a.k_new + t * a.n_st + h * a.n_sh + 16 * r);
         v = *reinterpret_cast<const u32x4*>(a.v_new + t * a.vn_st + h * a.vn_sh + 16 * r);
     }
-    const int64_t blk = slot >> 4, pos = slot & 15;
+    // slots are below 2^31, so the block / position split is 32-bit
+    const uint32_t us = (uint32_t)max<int64_t>(slot, 0);
+    const int64_t blk = us / a.bs, pos = us - (uint32_t)blk * a.bs;
     if constexpr (!FP8) {
         if (live) {
             *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k;
@@ -143,8 +146,8 @@ extern "C" int paged_attn_reshape_and_cache(const pa_tensor* k_new, const pa_ten
     a.vc = static_cast<char*>(p.vc); a.v_sblk = p.v_sblk; a.v_stok = p.v_stok; a.v_sh = p.v_sh;
     a.ks = p.ks; a.ks_sblk = p.ks_sblk; a.ks_sh = p.ks_sh;
     a.vs = p.vs; a.vs_sblk = p.vs_sblk; a.vs_sh = p.vs_sh;
-    a.T = p.T; a.slots_total = p.NB * PA_BLOCK_SIZE;
-    a.Hkv = (int32_t)p.Hkv; a.D = (int32_t)p.D;
+    a.T = p.T; a.slots_total = p.NB * p.BS;
+    a.Hkv = (int32_t)p.Hkv; a.D = (int32_t)p.D; a.bs = (uint32_t)p.BS;
     const int64_t threads = p.T * p.Hkv * (p.D / 8);
     const int64_t groups = (threads + kWriteThreads - 1) / kWriteThreads;
     const void* fn = p.fp8 ? write_kernel_of<true>((int)p.D) : write_kernel_of<false>((int)p.D);

@@ -31,9 +31,16 @@
 //    probability (v) instead of multiplying every element.
 //  * Row max uses two cross-lane exchanges per step; row sums stay
 //    lane-partial until the epilogue.
-//  * Positions >= L_b and causally hidden keys get score -inf by selection;
-//    V rows and scales past L_b are zeroed, so NaN or garbage in unread
-//    cache slots never reaches the output.
+//  * Positions >= L_b, causally hidden keys and keys below a sliding
+//    window get score -inf by selection; V rows and scales past L_b or below
+//    every row's window are zeroed, so NaN or garbage in unread cache slots
+//    never reaches the output.
+//  * A cache block of BS = 16m tokens is m contiguous 16-token sub-blocks;
+//    the kernel addresses sub-blocks (block-table entry i / m, sub-block
+//    i % m), so every block size runs the same 16-token code.
+//  * A sliding window only narrows a sequence's chunk range and adds a
+//    lower mask bound; attention sinks (one logit per query head) join the
+//    softmax normaliser in the epilogue or the merge.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -75,21 +82,28 @@ struct PartArgs {
     const float* ks; int64_t ks_sh;                   // floats
     const float* vs; int64_t vs_sh;
     uint32_t k_sblk, v_sblk, ks_sblk, vs_sblk;        // block strides, bytes (< 2^32)
+    uint32_t k_ssub, v_ssub;                          // bytes between 16-token sub-blocks of a block
     const int32_t* bt; int64_t bt_sb;
     const int32_t* ctx; int64_t ctx_s;
     const int32_t* ql;  int64_t ql_s;
+    const float* sinks; int64_t sinks_s;              // per query head, may be null
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
     float* ws_o;     float* ws_lse;                   // partial results: 2 slots per (workgroup, wave, row)
     int32_t* ws_pre;                                  // chunk prefix per sequence, for the merge (may be null)
     float scale_log2;                                 // |scale| * log2(e)
     int32_t q_neg;                                    // scale < 0: negate q
-    int32_t k_span, v_span;                           // bytes of one (block, head) slice
-    int32_t B, Hq, Hkv, G, Qmax, W, NB, rows, HG, min_share;
+    int32_t k_span, v_span;                           // bytes of one (16-token sub-block, head) slice
+    int32_t bsub;                                     // 16-token sub-blocks per cache block
+    int32_t wsub;                                     // sub-blocks a table row reaches (W * bsub)
+    int32_t window;                                   // sliding window in tokens, 0 = none
+    int32_t B, Hq, Hkv, G, Qmax, NB, rows, HG, min_share;
+    int32_t whole;                                    // 1: workgroup w runs segment w whole
 };
 
 struct RedArgs {
     const float* ws_o; const float* ws_lse; const int32_t* ws_pre;
     const int32_t* ql;  int64_t ql_s;
+    const float* sinks; int64_t sinks_s;              // per query head, may be null
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
     int32_t B, Hq, Hkv, G, Qmax, rows, HG, grid, min_share;
     int32_t red_rows, red_col4, red_lanes;            // merge workgroup shape (see reduce_kernel)
@@ -158,26 +172,37 @@ struct HeadBase {
     const char* k; const char* v; const char* ks; const char* vs;
 };
 
-template <int D, bool FP8>
-__device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, const HeadBase& hb, int bid_lane,
+// A lane's block-table window entry: the cache block and the 16-token
+// sub-block within it of sub-block 2*pc + lane of the sequence.
+struct BlockRef {
+    int blk, sub;
+};
+
+// GEN: the general variant (cache blocks of more than 16 tokens, a sliding
+// window, attention sinks); without it blocks are 16 tokens, there is no
+// window and no sink, and none of their code is emitted.
+template <int D, bool FP8, bool GEN>
+__device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, const HeadBase& hb, BlockRef br,
                                           int step, int nsteps, int last_blk,
                                           const unsigned (&koff)[Step<D, FP8>::KL], const unsigned (&voff)[4],
                                           unsigned soff) {
     typedef typename VLoad<D, FP8>::T VT;
-    // For step < nsteps, block 2*step holds keys of the sequence and block
-    // 2*step + 1 may lie past it; a block past the sequence, or a whole step
-    // past the window (a prefetch beyond its end), reads as zeros through an
-    // empty range, which costs no memory traffic.
+    // For step < nsteps, sub-block 2*step holds keys of the sequence and
+    // sub-block 2*step + 1 may lie past it; a sub-block past the sequence, or
+    // a whole step past the window (a prefetch beyond its end), reads as
+    // zeros through an empty range, which costs no memory traffic.
     const bool has0 = step < nsteps;
     const bool has1 = has0 && 2 * step + 1 <= last_blk;
     const int sc = min(step, nsteps - 1);
-    const int b0 = __builtin_amdgcn_readlane(bid_lane, 2 * sc);
-    const int b1 = __builtin_amdgcn_readlane(bid_lane, min(2 * sc + 1, last_blk));
-    const uint32_t u0 = (uint32_t)b0, u1 = (uint32_t)b1;
-    const Rsrc k0 = make_rsrc(hb.k + (uint64_t)u0 * a.k_sblk, has0 ? a.k_span : 0);
-    const Rsrc k1 = make_rsrc(hb.k + (uint64_t)u1 * a.k_sblk, has1 ? a.k_span : 0);
-    const Rsrc v0 = make_rsrc(hb.v + (uint64_t)u0 * a.v_sblk, has0 ? a.v_span : 0);
-    const Rsrc v1 = make_rsrc(hb.v + (uint64_t)u1 * a.v_sblk, has1 ? a.v_span : 0);
+    const int l0 = 2 * sc, l1 = min(2 * sc + 1, last_blk);
+    const uint32_t u0 = (uint32_t)__builtin_amdgcn_readlane(br.blk, l0);
+    const uint32_t u1 = (uint32_t)__builtin_amdgcn_readlane(br.blk, l1);
+    const uint32_t s0 = GEN ? (uint32_t)__builtin_amdgcn_readlane(br.sub, l0) : 0u;
+    const uint32_t s1 = GEN ? (uint32_t)__builtin_amdgcn_readlane(br.sub, l1) : 0u;
+    const Rsrc k0 = make_rsrc(hb.k + (uint64_t)u0 * a.k_sblk + s0 * a.k_ssub, has0 ? a.k_span : 0);
+    const Rsrc k1 = make_rsrc(hb.k + (uint64_t)u1 * a.k_sblk + s1 * a.k_ssub, has1 ? a.k_span : 0);
+    const Rsrc v0 = make_rsrc(hb.v + (uint64_t)u0 * a.v_sblk + s0 * a.v_ssub, has0 ? a.v_span : 0);
+    const Rsrc v1 = make_rsrc(hb.v + (uint64_t)u1 * a.v_sblk + s1 * a.v_ssub, has1 ? a.v_span : 0);
 #pragma unroll
     for (int c = 0; c < Step<D, FP8>::KL; ++c) {
         st.k[0][c] = bload<u32x4>(k0, koff[c]);
@@ -194,21 +219,23 @@ __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, c
         const int r = __lane_id() & 3;
         const char* base = (r & 2) ? hb.vs : hb.ks;
         const uint64_t sblk = (r & 2) ? a.vs_sblk : a.ks_sblk;
-        st.sq = *reinterpret_cast<const u32x4*>(base + (uint64_t)((r & 1) ? u1 : u0) * sblk + soff);
+        // a sub-block's 16 slot scales are 64 contiguous bytes
+        st.sq = *reinterpret_cast<const u32x4*>(base + (uint64_t)((r & 1) ? u1 : u0) * sblk +
+                                                 64u * ((r & 1) ? s1 : s0) + soff);
         return;
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) st.v[s] = bload<VT>(s < 4 ? v0 : v1, voff[s & 3]);
     if constexpr (FP8) {
         // one block's 16 slot scales of this kv head are contiguous (64 bytes)
-        const Rsrc s0 = make_rsrc(hb.ks + (uint64_t)u0 * a.ks_sblk, has0 ? 64 : 0);
-        const Rsrc s1 = make_rsrc(hb.ks + (uint64_t)u1 * a.ks_sblk, has1 ? 64 : 0);
-        const Rsrc t0 = make_rsrc(hb.vs + (uint64_t)u0 * a.vs_sblk, has0 ? 64 : 0);
-        const Rsrc t1 = make_rsrc(hb.vs + (uint64_t)u1 * a.vs_sblk, has1 ? 64 : 0);
-        st.ksc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(s0, soff));
-        st.ksc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(s1, soff));
-        st.vsc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(t0, soff));
-        st.vsc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(t1, soff));
+        const Rsrc ks0 = make_rsrc(hb.ks + (uint64_t)u0 * a.ks_sblk + 64u * s0, has0 ? 64 : 0);
+        const Rsrc ks1 = make_rsrc(hb.ks + (uint64_t)u1 * a.ks_sblk + 64u * s1, has1 ? 64 : 0);
+        const Rsrc vs0 = make_rsrc(hb.vs + (uint64_t)u0 * a.vs_sblk + 64u * s0, has0 ? 64 : 0);
+        const Rsrc vs1 = make_rsrc(hb.vs + (uint64_t)u1 * a.vs_sblk + 64u * s1, has1 ? 64 : 0);
+        st.ksc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(ks0, soff));
+        st.ksc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(ks1, soff));
+        st.vsc[0] = __builtin_bit_cast(f32x4, bload<u32x4>(vs0, soff));
+        st.vsc[1] = __builtin_bit_cast(f32x4, bload<u32x4>(vs1, soff));
     }
 }
 
@@ -341,20 +368,21 @@ __device__ __forceinline__ void build_kf(const Step<D, FP8>& st, bf16x8 (&kf)[2]
 // more than kRescaleLog2 (any row of the wave: the branch is uniform);
 // otherwise p <= 2^kRescaleLog2 and l and the accumulators keep their scale.
 // The result is the same: m, l and O all refer to one m.
-template <int D, bool FP8, int NT, bool MASK>
+template <int D, bool FP8, int NT, bool MASK, bool GEN>
 __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>& s, const u32x4 (&qf)[NT][D / 32],
-                                             const PartArgs& a, int cbase, int L, int nq, int lane) {
+                                             const PartArgs& a, int cbase, int L, int nq, int vlo, int lane) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
     if constexpr (kQuadV<D, FP8>) unpack_quad<D, FP8>(st, lane);
 
     if constexpr (MASK) {
-        // zero V rows (and scales) of positions >= L so that p = 0 never
-        // meets NaN or garbage from unwritten slots
+        // zero V rows (and scales) of positions >= L or below every row's
+        // window (vlo) so that p = 0 never meets NaN or garbage from
+        // unwritten or recycled slots
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int tok = cbase + 16 * (i >> 2) + 4 * grp + (i & 3);
-            if (tok >= L) {
+            if (tok >= L || (GEN && tok < vlo)) {
                 st.v[i] = typename VLoad<D, FP8>::T{};
                 if constexpr (FP8) {
                     st.vsc[i >> 2][i & 3] = 0.f;
@@ -392,13 +420,16 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
         }
         bool hidden[8];
         if constexpr (MASK) {
+            // row t sees keys lo .. lim: its causal limit and, with a
+            // sliding window, the window's first position
             const int row = 16 * nt + n16;
             const int t = row / a.G;
             const int lim = (row < a.rows && t < nq) ? L - nq + t : L - 1;
+            const int lo = GEN && a.window > 0 ? lim - a.window + 1 : 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int tok = cbase + 16 * (i >> 2) + 4 * grp + (i & 3);
-                hidden[i] = tok > lim;
+                hidden[i] = tok > lim || (GEN && tok < lo);
                 y[i] = hidden[i] ? -__builtin_inff() : y[i];
             }
         }
@@ -446,22 +477,37 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
     }
 }
 
-// Block-table window of a piece: entry 2*pc + lane of sequence b (clamped to
-// the table), its block id clamped into the pool.
-__device__ __forceinline__ int load_window(const PartArgs& a, int b, int pc, int lane) {
-    const int idx = min(2 * pc + lane, a.W - 1);
-    const int v = a.bt[(int64_t)b * a.bt_sb + idx];
-    return min(max(v, 0), a.NB - 1);
+// Block-table window of a piece: sub-block 2*pc + lane of sequence b
+// (clamped to the table's reach), its block id clamped into the pool.
+template <bool GEN>
+__device__ __forceinline__ BlockRef load_window(const PartArgs& a, int b, int pc, int lane) {
+    const int idx = min(2 * pc + lane, a.wsub - 1);
+    const int e = GEN && a.bsub > 1 ? idx / a.bsub : idx;
+    const int v = a.bt[(int64_t)b * a.bt_sb + e];
+    return BlockRef{min(max(v, 0), a.NB - 1), idx - e * (GEN ? a.bsub : 1)};
 }
 
-// One segment = chunks [c0, c1) of the cb chunks (32 tokens each) of
-// sequence b for kv head g, run by one wave of workgroup w.  The segment's
+// First 32-token chunk of sequence b that a query row can see: 0, or with
+// a sliding window the chunk of the earliest row's first key.
+template <bool GEN>
+__device__ __forceinline__ int first_chunk(const PartArgs& a, int L, int nq) {
+    return GEN && a.window > 0 ? max(0, L - nq - a.window + 1) / kChunkTokens : 0;
+}
+
+// Query head h's sink logit in log2 units (log2(e) * sink), or -inf.
+__device__ __forceinline__ float sink_log2(const float* sinks, int64_t stride, int h) {
+    return sinks ? sinks[(int64_t)h * stride] * kLog2e : -__builtin_inff();
+}
+
+// One segment = chunks [c0, c1) of the cb chunks (32 tokens each) that
+// sequence b's rows see, for kv head g, run by one wave of workgroup w
+// (chunk c is the sequence's chunk first_chunk + c).  The segment's
 // online-softmax state ends as the output row when the segment is the whole
 // sequence, otherwise as a normalised fp32 partial output and its base-2
 // log-sum-exp in the workgroup's partial slot `slot` (0: the first segment
 // of its share, 1: the last) for the merge kernel.  Chunks are processed in
 // pieces of up to 32 (one 64-entry block-table window per piece).
-template <int D, bool FP8, int NT>
+template <int D, bool FP8, int NT, bool GEN>
 __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g, int wave, int c0, int c1, int cb,
                                                 int w, int slot, int lane) {
     constexpr int J = D / 16;
@@ -472,8 +518,17 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
 
     // Start-up loads issued together: the first block-table window, the
     // query fragments and the lengths do not depend on each other, so the
-    // first K/V loads wait for one round trip only.
-    int bid_lane = load_window(a, b, c0, lane);
+    // first K/V loads wait for one round trip only (with a sliding window the
+    // window's first chunk waits for the lengths).
+    const bool direct = c0 == 0 && c1 == cb;
+    if (GEN && a.window > 0) {
+        const int L0 = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
+        const int nq0 = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+        const int cs = first_chunk<GEN>(a, L0, nq0);
+        c0 += cs;
+        c1 += cs;
+    }
+    BlockRef br = load_window<GEN>(a, b, c0, lane);
     // query fragments: row r = 16*nt + n16 -> (t, h_local) = (r / G, r % G);
     // rows t < Qmax are in bounds, rows past query_len are zeroed below
     u32x4 qf[NT][D / 32];
@@ -488,8 +543,10 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
             qf[nt][kk] = row < a.rows ? *reinterpret_cast<const u32x4*>(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
         }
     }
-    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
+    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
     const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+    // keys below vlo are outside every row's window
+    const int vlo = GEN && a.window > 0 ? L - nq - a.window + 1 : 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int row = 16 * nt + n16;
@@ -524,12 +581,14 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
     }
 
     for (int pc = c0; pc < c1; pc += kWindowChunks) {
-        if (pc != c0) bid_lane = load_window(a, b, pc, lane);
+        if (pc != c0) br = load_window<GEN>(a, b, pc, lane);
         const int tok0 = kChunkTokens * pc;
         const int nsteps = min(c1, pc + kWindowChunks) - pc;
-        // steps [0, nclean) hold only keys below L that every query row sees
-        const int nclean = min(nsteps, max(0, L - nq + 1 - tok0) / kChunkTokens);
-        // last block of the sequence, relative to the window
+        // steps [0, nclean) hold only keys below L that every query row
+        // sees; with a sliding window every step takes the masked variant
+        // (a window's range is short, and its first steps are masked anyway)
+        const int nclean = GEN && a.window > 0 ? 0 : min(nsteps, max(0, L - nq + 1 - tok0) / kChunkTokens);
+        // last 16-token sub-block of the sequence, relative to the window
         const int last_blk = (L + 15) / 16 - 1 - 2 * pc;
         // A ring of R register buffers: while a step computes, the loads of
         // the next R-1 steps are in flight.  Loads are issued on every path
@@ -538,7 +597,7 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         // the last steps of the piece take the masked variant.
         Step<D, FP8> buf[R];
 #pragma unroll
-        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8>(buf[i], a, hb, bid_lane, i, nsteps, last_blk, koff, voff, soff);
+        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8, GEN>(buf[i], a, hb, br, i, nsteps, last_blk, koff, voff, soff);
         // Every kLockstep steps the workgroup's waves meet at a barrier.  Two
         // waves share each SIMD, and the older one otherwise wins the issue
         // and memory arbitration until it is done, leaving the younger to
@@ -549,23 +608,22 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         for (; st + R <= nclean; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_step<D, FP8>(buf[(i + R - 1) % R], a, hb, bid_lane, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
                 if (((st + i) & (kLockstep - 1)) == 0) __syncthreads();
-                compute_step<D, FP8, NT, false>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, lane);
+                compute_step<D, FP8, NT, false, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
             }
         }
         for (; st < nsteps; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_step<D, FP8>(buf[(i + R - 1) % R], a, hb, bid_lane, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
                 if (st + i < nsteps)
-                    compute_step<D, FP8, NT, true>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, lane);
+                    compute_step<D, FP8, NT, true, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
             }
         }
     }
 
     // epilogue: lane holds d = (D/16)*(4*grp + i) + j, j < D/16, of row 16*nt + n16
-    const bool direct = c0 == 0 && c1 == cb;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float lt = s.l[nt];
@@ -574,8 +632,13 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         const int row = 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         if (!(row < a.rows && t < nq)) continue;
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const int h = g * a.G + hl;
+        if (GEN && direct && a.sinks) {
+            // the sink joins the normaliser: l += 2^(sink - m), m in log2 units
+            const float sk = sink_log2(a.sinks, a.sinks_s, h);
+            if (sk > -__builtin_inff()) lt += __builtin_amdgcn_exp2f(sk - s.m[nt]);
+        }
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (direct) {
             char* orow = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
@@ -638,22 +701,33 @@ __device__ __forceinline__ int share_owner(int64_t c, int64_t C, int n) {
 // per-sequence chunk counts into LDS (workgroup 0 also stores the scan for
 // the merge kernel); every wave finds a chunk's sequence with a 64-wide
 // ballot over that prefix (a share's chunks only increase).
-template <int D, bool FP8, int NT>
+template <int D, bool FP8, int NT, bool GEN>
 __global__ __launch_bounds__(NT == 1 ? 512 : 256)
 __attribute__((amdgpu_waves_per_eu(NT == 1 ? (FP8 && D == 64 ? 3 : 2) : 1)))
 void partition_kernel(PartArgs a) {
     extern __shared__ int s_pre[];               // inclusive prefix of chunks per sequence
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (GEN && a.whole) {
+        // one workgroup per (sequence, kv-head group) segment, run whole:
+        // no scan, no partials, no merge
+        const int ngrp = a.Hkv / a.HG;
+        const int b = blockIdx.x / ngrp, gg = blockIdx.x - b * ngrp;
+        const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
+        const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
+        const int cb = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens - first_chunk<GEN>(a, L, nq) : 0;
+        if (cb > 0) process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, 0, cb, cb, blockIdx.x, 0, lane);
+        return;
+    }
     if (wave == 0) {
         int carry = 0;
         for (int b0 = 0; b0 < a.B; b0 += 64) {
             const int b = b0 + lane;
             int nc = 0;
             if (b < a.B) {
-                const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.W);
+                const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
                 const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
-                nc = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens : 0;
+                nc = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens - first_chunk<GEN>(a, L, nq) : 0;
             }
             int x = nc;
 #pragma unroll
@@ -693,7 +767,7 @@ void partition_kernel(PartArgs a) {
         const int gg = within / cb;
         const int c0 = within - gg * cb;
         const int c1 = (int)min<int64_t>(cb, c0 + (hi - pos));
-        process_segment<D, FP8, NT>(a, b, gg * a.HG + wave, wave, c0, c1, cb, w, pos == lo ? 0 : 1, lane);
+        process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, c0, c1, cb, w, pos == lo ? 0 : 1, lane);
         pos += c1 - c0;
     }
 }
@@ -785,11 +859,14 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
     __syncthreads();
     if (active && pl == 0) {
         const int stride = CB * RG;
-        float M = m;
+        const int h = g * a.G + hl;
+        // a sink is one more partial: log-sum-exp = the sink, output 0
+        const float sk = sink_log2(a.sinks, a.sinks_s, h);
+        float M = fmaxf(m, sk);
         for (int q = 1; q < PL; ++q) M = fmaxf(M, sm[tid + q * stride]);
         const float Mu = M == ninf ? 0.f : M;
         f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-        float wt = 0.f;
+        float wt = sk > ninf ? __builtin_amdgcn_exp2f(sk - Mu) : 0.f;
         for (int q = 0; q < PL; ++q) {
             const float sc = __builtin_amdgcn_exp2f(sm[tid + q * stride] - Mu);
             tot += sc * sacc[tid + q * stride];
@@ -799,7 +876,6 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
         u32x2 wv;
         wv[0] = pack_bf16_rne(tot[0] * inv, tot[1] * inv);
         wv[1] = pack_bf16_rne(tot[2] * inv, tot[3] * inv);
-        const int h = g * a.G + hl;
         char* orow = a.out + (int64_t)b * a.o_sb + (int64_t)t * a.o_st + (int64_t)h * a.o_sh;
         *reinterpret_cast<u32x2*>(orow + 2 * col) = wv;
     }
@@ -866,20 +942,23 @@ int get_workspace(int dev, void* stream, size_t need, void** out) {
     return PA_OK;
 }
 
-template <int D, bool FP8, int NT>
-const void* kernel_of() { return reinterpret_cast<const void*>(&partition_kernel<D, FP8, NT>); }
+template <int D, bool FP8, bool GEN>
+const void* kernel_of(int nt) {
+    return nt == 1 ? reinterpret_cast<const void*>(&partition_kernel<D, FP8, 1, GEN>)
+         : nt == 2 ? reinterpret_cast<const void*>(&partition_kernel<D, FP8, 2, GEN>)
+         : nt == 3 ? reinterpret_cast<const void*>(&partition_kernel<D, FP8, 3, GEN>)
+                   : reinterpret_cast<const void*>(&partition_kernel<D, FP8, 4, GEN>);
+}
 
-const void* partition_kernel_of(int D, bool fp8, int nt) {
-    if (D == 128) {
-        if (fp8) return nt == 1 ? kernel_of<128, true, 1>() : nt == 2 ? kernel_of<128, true, 2>()
-                      : nt == 3 ? kernel_of<128, true, 3>() : kernel_of<128, true, 4>();
-        return nt == 1 ? kernel_of<128, false, 1>() : nt == 2 ? kernel_of<128, false, 2>()
-             : nt == 3 ? kernel_of<128, false, 3>() : kernel_of<128, false, 4>();
-    }
-    if (fp8) return nt == 1 ? kernel_of<64, true, 1>() : nt == 2 ? kernel_of<64, true, 2>()
-                  : nt == 3 ? kernel_of<64, true, 3>() : kernel_of<64, true, 4>();
-    return nt == 1 ? kernel_of<64, false, 1>() : nt == 2 ? kernel_of<64, false, 2>()
-         : nt == 3 ? kernel_of<64, false, 3>() : kernel_of<64, false, 4>();
+// gen: the general variant (blocks of more than 16 tokens, window, sinks)
+template <int D>
+const void* kernel_of(bool fp8, int nt, bool gen) {
+    if (fp8) return gen ? kernel_of<D, true, true>(nt) : kernel_of<D, true, false>(nt);
+    return gen ? kernel_of<D, false, true>(nt) : kernel_of<D, false, false>(nt);
+}
+
+const void* partition_kernel_of(int D, bool fp8, int nt, bool gen) {
+    return D == 128 ? kernel_of<128>(fp8, nt, gen) : kernel_of<64>(fp8, nt, gen);
 }
 
 }  // namespace
@@ -887,28 +966,31 @@ const void* partition_kernel_of(int D, bool fp8, int nt) {
 
 extern "C" {
 
-int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
-                      const pa_tensor* block_tables, const pa_tensor* context_lens,
-                      const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
-                      const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                          const pa_tensor* block_tables, const pa_tensor* context_lens,
+                          const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                          const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
+                          pa_tensor* out, void* stream) {
     using namespace pa;
     Problem pr;
     int st = validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
-                      out, &pr);
+                      sliding_window, sinks, out, &pr);
     if (st) return st;
     if (pr.B == 0) return PA_OK;
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
     pa_plan plan;
-    if ((st = make_plan(pr.B, pr.Hq, pr.Hkv, pr.D, pr.Qmax, pr.W, pr.fp8, device_cus(dev), &plan))) return st;
+    const int64_t max_ctx = max_context_tokens(pr.BS, pr.W, pr.window, pr.Qmax);
+    if ((st = make_plan(pr.B, pr.Hq, pr.Hkv, pr.D, pr.Qmax, max_ctx, pr.fp8, device_cus(dev), &plan))) return st;
     void* ws = nullptr;
     if (plan.workspace_bytes > 0 &&
         (st = get_workspace(dev, stream, (size_t)plan.workspace_bytes, &ws)))
         return st;
 
-    const size_t lds = (size_t)pr.B * sizeof(int);
-    const void* fn = partition_kernel_of((int)pr.D, pr.fp8, plan.row_tiles);
+    const size_t lds = plan.whole_segments ? 0 : (size_t)pr.B * sizeof(int);
+    const bool general = pr.BS > PA_BLOCK_SIZE || pr.window > 0 || pr.sinks != nullptr || plan.whole_segments;
+    const void* fn = partition_kernel_of((int)pr.D, pr.fp8, plan.row_tiles, general);
     const int HG = plan.heads_per_group;
     const int64_t grid = plan.workgroups;
     const int64_t nslot = 2 * grid * HG * plan.rows;      // partial slots (see PartArgs)
@@ -920,9 +1002,11 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
     a.vs = pr.vs; a.vs_sh = pr.vs_sh;
     a.k_sblk = (uint32_t)pr.k_sblk; a.v_sblk = (uint32_t)pr.v_sblk;
     a.ks_sblk = (uint32_t)(pr.ks_sblk * 4); a.vs_sblk = (uint32_t)(pr.vs_sblk * 4);
+    a.k_ssub = (uint32_t)(PA_BLOCK_SIZE * pr.k_stok); a.v_ssub = (uint32_t)(PA_BLOCK_SIZE * pr.v_stok);
     a.bt = pr.bt; a.bt_sb = pr.bt_sb;
     a.ctx = pr.ctx; a.ctx_s = pr.ctx_s;
     a.ql = pr.ql; a.ql_s = pr.ql_s;
+    a.sinks = pr.sinks; a.sinks_s = pr.sinks_s;
     a.out = static_cast<char*>(pr.out); a.o_sb = pr.o_sb * 2; a.o_st = pr.o_st * 2; a.o_sh = pr.o_sh * 2;
     a.ws_o = static_cast<float*>(ws);
     a.ws_lse = ws ? a.ws_o + nslot * pr.D : nullptr;
@@ -932,7 +1016,11 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
     a.k_span = (int32_t)(15 * pr.k_stok + pr.D * (pr.fp8 ? 1 : 2));
     a.v_span = (int32_t)(15 * pr.v_stok + pr.D * (pr.fp8 ? 1 : 2));
     a.B = (int32_t)pr.B; a.Hq = (int32_t)pr.Hq; a.Hkv = (int32_t)pr.Hkv; a.G = (int32_t)pr.G; a.Qmax = (int32_t)pr.Qmax;
-    a.W = (int32_t)pr.W; a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
+    a.bsub = (int32_t)(pr.BS / PA_BLOCK_SIZE);
+    a.wsub = (int32_t)(pr.W * a.bsub);
+    a.window = pr.window;
+    a.whole = plan.whole_segments;
+    a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
     a.rows = plan.rows; a.HG = HG; a.min_share = plan.min_share_chunks;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -956,6 +1044,7 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
         RedArgs r;
         r.ws_o = a.ws_o; r.ws_lse = a.ws_lse; r.ws_pre = a.ws_pre;
         r.ql = a.ql; r.ql_s = a.ql_s;
+        r.sinks = a.sinks; r.sinks_s = a.sinks_s;
         r.out = a.out; r.o_sb = a.o_sb; r.o_st = a.o_st; r.o_sh = a.o_sh;
         r.B = a.B; r.Hq = a.Hq; r.Hkv = a.Hkv; r.G = a.G; r.Qmax = a.Qmax; r.rows = a.rows; r.HG = HG;
         r.grid = (int32_t)grid; r.min_share = a.min_share;
@@ -968,6 +1057,14 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return PA_OK;
+}
+
+int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* block_tables, const pa_tensor* context_lens,
+                      const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                      const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+    return paged_attn_decode_ext(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
+                                 v_scale, 0, nullptr, out, stream);
 }
 
 int paged_attn_reserve(int64_t bytes, void* stream) {

@@ -83,7 +83,8 @@ int fail(int status, const char* fmt, ...) {
 
 int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* bt,
              const pa_tensor* ctx, const pa_tensor* ql, float scale, const pa_tensor* ks,
-             const pa_tensor* vs, const pa_tensor* out, Problem* pr) {
+             const pa_tensor* vs, int32_t window, const pa_tensor* sinks, const pa_tensor* out,
+             Problem* pr) {
     int st;
     if ((st = check_desc(q, "q", PA_DTYPE_BF16, 3, 4, true))) return st;
     if ((st = check_desc(out, "out", PA_DTYPE_BF16, 3, 4, true))) return st;
@@ -106,6 +107,7 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
         return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
     }
     if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "scale is not finite");
+    if (sinks && (st = check_desc(sinks, "sinks", PA_DTYPE_FP32, 1, 1, true))) return st;
 
     // ---- sizes
     const bool q3 = q->ndim == 3;
@@ -123,10 +125,10 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
         if (kc->shape[i] != vc->shape[i])
             return fail(PA_ERR_SHAPE, "v_cache: size %lld in dim %d, k_cache has %lld",
                         (long long)vc->shape[i], i, (long long)kc->shape[i]);
-    const int64_t NB = kc->shape[0], Hkv = kc->shape[2];
-    if (kc->shape[1] != PA_BLOCK_SIZE)
-        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, only 16 is supported",
-                    (long long)kc->shape[1]);
+    const int64_t NB = kc->shape[0], BS = kc->shape[1], Hkv = kc->shape[2];
+    if (BS < PA_BLOCK_SIZE || BS % PA_BLOCK_SIZE || BS > kMaxBlockSize)
+        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, expected a multiple of 16 up to %d",
+                    (long long)BS, kMaxBlockSize);
     if (kc->shape[3] != D)
         return fail(PA_ERR_SHAPE, "k_cache: head_dim %lld, q has %lld", (long long)kc->shape[3], (long long)D);
     if (D != 64 && D != 128)
@@ -152,18 +154,23 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     if (fp8) {
         for (const pa_tensor* s : {ks, vs}) {
             const char* nm = s == ks ? "k_scale" : "v_scale";
-            if (s->shape[0] != NB || s->shape[1] != PA_BLOCK_SIZE || s->shape[2] != Hkv)
-                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, 16, kv_heads]", nm);
+            if (s->shape[0] != NB || s->shape[1] != BS || s->shape[2] != Hkv)
+                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, block_size, kv_heads]", nm);
             if (s->stride[1] != 1)
                 return fail(PA_ERR_LAYOUT, "%s: the slot dimension must be contiguous", nm);
             if (s->stride[0] % 4 || s->stride[2] % 4 || !aligned(s->data, 16))
                 return fail(PA_ERR_LAYOUT, "%s: strides of dims 0 and 2 must be multiples of 4 and data 16-byte aligned", nm);
         }
     }
+    if (sinks) {
+        if (sinks->shape[0] != Hq)
+            return fail(PA_ERR_SHAPE, "sinks: %lld entries, q has %lld heads", (long long)sinks->shape[0], (long long)Hq);
+        if (!aligned(sinks->data, 4)) return fail(PA_ERR_LAYOUT, "sinks: data is not 4-byte aligned");
+    }
     if (B > 0) {
         if (W < 1) return fail(PA_ERR_SHAPE, "block_tables: width must be >= 1");
         if (NB < 1) return fail(PA_ERR_SHAPE, "k_cache: the pool has no blocks");
-        if (W > (int64_t(1) << 26)) return fail(PA_ERR_UNSUPPORTED, "block_tables: width too large");
+        if (W > kMaxContext / BS) return fail(PA_ERR_UNSUPPORTED, "block_tables: width x block size too large");
     }
 
     // ---- layouts
@@ -177,7 +184,7 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     const int64_t eb = fp8 ? 1 : 2;
     // in-block byte offsets of the kernels are 32-bit
     for (const pa_tensor* c : {kc, vc}) {
-        const int64_t span = (PA_BLOCK_SIZE - 1) * c->stride[1] * eb + (Hkv - 1) * c->stride[2] * eb + D * eb;
+        const int64_t span = (BS - 1) * c->stride[1] * eb + (Hkv - 1) * c->stride[2] * eb + D * eb;
         if (span >= (int64_t(1) << 31))
             return fail(PA_ERR_LAYOUT, "%s: one block spans more than 2 GiB", c == kc ? "k_cache" : "v_cache");
         // block strides are 32-bit byte counts in the kernels
@@ -191,8 +198,11 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
 
     if (pr) {
         Problem& p = *pr;
-        p.B = B; p.Qmax = Qmax; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.D = D; p.NB = NB; p.W = W;
+        p.B = B; p.Qmax = Qmax; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.D = D; p.NB = NB; p.W = W; p.BS = BS;
         p.fp8 = fp8; p.scale = scale;
+        p.window = window > 0 ? window : 0;
+        p.sinks = sinks ? static_cast<const float*>(sinks->data) : nullptr;
+        p.sinks_s = sinks ? sinks->stride[0] : 0;
         p.q = q->data;
         p.q_sb = q->stride[0]; p.q_st = q3 ? 0 : q->stride[1]; p.q_sh = q->stride[q3 ? 1 : 2];
         p.out = out->data;
@@ -242,23 +252,25 @@ int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm
         if (kc->shape[i] != vc->shape[i])
             return fail(PA_ERR_SHAPE, "v_cache: size %lld in dim %d, k_cache has %lld", (long long)vc->shape[i], i,
                         (long long)kc->shape[i]);
-    const int64_t NB = kc->shape[0];
-    if (kc->shape[1] != PA_BLOCK_SIZE)
-        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, only 16 is supported", (long long)kc->shape[1]);
+    const int64_t NB = kc->shape[0], BS = kc->shape[1];
+    if (BS < PA_BLOCK_SIZE || BS % PA_BLOCK_SIZE || BS > kMaxBlockSize)
+        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, expected a multiple of 16 up to %d",
+                    (long long)BS, kMaxBlockSize);
     if (kc->shape[2] != Hkv || kc->shape[3] != D)
-        return fail(PA_ERR_SHAPE, "k_cache: [%lld, 16, %lld, %lld], new tokens are [T, %lld, %lld]",
-                    (long long)NB, (long long)kc->shape[2], (long long)kc->shape[3], (long long)Hkv, (long long)D);
+        return fail(PA_ERR_SHAPE, "k_cache: [%lld, %lld, %lld, %lld], new tokens are [T, %lld, %lld]",
+                    (long long)NB, (long long)BS, (long long)kc->shape[2], (long long)kc->shape[3], (long long)Hkv,
+                    (long long)D);
     if (D != 64 && D != 128)
         return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64 and 128 are supported", (long long)D);
     if (Hkv < 1) return fail(PA_ERR_SHAPE, "no kv heads");
-    if (NB * PA_BLOCK_SIZE >= (int64_t(1) << 31))
+    if (NB * BS >= (int64_t(1) << 31))
         return fail(PA_ERR_UNSUPPORTED, "pool of %lld blocks: slots do not fit int32", (long long)NB);
     if (T * Hkv * (D / 8) >= (int64_t(1) << 40)) return fail(PA_ERR_UNSUPPORTED, "too many new tokens");
     if (fp8) {
         for (const pa_tensor* s : {ks, vs}) {
             const char* nm = s == ks ? "k_scale" : "v_scale";
-            if (s->shape[0] != NB || s->shape[1] != PA_BLOCK_SIZE || s->shape[2] != Hkv)
-                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, 16, kv_heads]", nm);
+            if (s->shape[0] != NB || s->shape[1] != BS || s->shape[2] != Hkv)
+                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, block_size, kv_heads]", nm);
             if (s->stride[1] != 1) return fail(PA_ERR_LAYOUT, "%s: the slot dimension must be contiguous", nm);
             if (!aligned(s->data, 4)) return fail(PA_ERR_LAYOUT, "%s: data is not 4-byte aligned", nm);
         }
@@ -271,7 +283,7 @@ int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm
     if (pr) {
         WriteProblem& p = *pr;
         const int64_t eb = fp8 ? 1 : 2;
-        p.T = T; p.Hkv = Hkv; p.D = D; p.NB = NB; p.fp8 = fp8;
+        p.T = T; p.Hkv = Hkv; p.D = D; p.NB = NB; p.BS = BS; p.fp8 = fp8;
         p.k_new = kn->data; p.kn_st = kn->stride[0] * 2; p.kn_sh = kn->stride[1] * 2;
         p.v_new = vn->data; p.vn_st = vn->stride[0] * 2; p.vn_sh = vn->stride[1] * 2;
         p.slots = static_cast<const int32_t*>(sm->data); p.slot_s = sm->stride[0];
@@ -285,10 +297,20 @@ int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm
     return PA_OK;
 }
 
-int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W, bool fp8,
+int64_t max_context_tokens(int64_t block_size, int64_t table_width, int32_t window, int64_t Qmax) {
+    const int64_t reach = block_size * table_width;
+    if (window <= 0) return reach;
+    // rows t < Qmax read keys from L - Qmax - window + 1 to L - 1: at most
+    // window + Qmax - 1 tokens, over one more chunk when not aligned
+    const int64_t span = int64_t(window) + Qmax - 1;
+    return std::min<int64_t>(reach, ((span + kChunkTokens - 1) / kChunkTokens + 1) * kChunkTokens);
+}
+
+int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t max_context, bool fp8,
               int32_t num_cus, pa_plan* plan) {
     if (!plan) return fail(PA_ERR_NULL, "plan: NULL");
-    if (B < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Qmax < 1 || W < 1 || num_cus < 1 || D < 1)
+    if (B < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Qmax < 1 || max_context < 1 || max_context > kMaxContext ||
+        num_cus < 1 || D < 1)
         return fail(PA_ERR_ARG, "plan: invalid sizes");
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
@@ -298,7 +320,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     const int64_t hg_cap = row_tiles == 1 ? 8 : 4;
     // chunk space: 32-token chunks of every (sequence, head group) segment;
     // only its upper bound is known here (lengths live on the device)
-    const int64_t seq_chunks = (int64_t(PA_BLOCK_SIZE) * W + kChunkTokens - 1) / kChunkTokens;
+    const int64_t seq_chunks = (max_context + kChunkTokens - 1) / kChunkTokens;
     // Waves: about kStepsPerWave chunks each for the (kv head, chunk) pairs
     // the shapes suggest (the whole table for one sequence, half of it per
     // sequence of a ragged batch), at least a quarter of the CUs, at most
@@ -325,6 +347,29 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
     const int64_t max_chunks = B * (Hkv / HG) * seq_chunks;
     if (max_chunks >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "batch x context too large for the chunk index");
+    // Whole segments: every segment is short and there is one for every CU
+    // (the head group chosen so), so splitting would only add partials and
+    // a merge.  Overrides of the grid or the share keep the split.
+    if (seq_chunks <= kWholeSegmentChunks && g_grid_override.load() <= 0 && g_share_override.load() <= 0) {
+        int64_t hg = hg_over > 0 ? HG : 1;
+        if (hg_over <= 0)
+            for (int64_t h = hg_cap; h >= 1; --h)
+                if (Hkv % h == 0 && h <= cu_waves && B * (Hkv / h) >= num_cus) { hg = h; break; }
+        if (B * (Hkv / hg) >= num_cus) {
+            plan->rows = int32_t(rows);
+            plan->row_tiles = int32_t(row_tiles);
+            plan->heads_per_group = int32_t(hg);
+            plan->min_share_chunks = int32_t(seq_chunks);
+            plan->reduce_rows = plan->reduce_col4 = plan->reduce_lanes = 1;
+            plan->expected_partials = 0;
+            plan->whole_segments = 1;
+            plan->reserved = 0;
+            plan->workgroups = B * (Hkv / hg);
+            plan->reduce_groups = 0;
+            plan->workspace_bytes = 0;
+            return PA_OK;
+        }
+    }
     const int64_t share_over = g_share_override.load();
     const int64_t min_share = share_over > 0 ? share_over : kDefaultMinShare;
     const int64_t slots = int64_t(num_cus) * std::max<int64_t>(1, cu_waves / HG);
@@ -355,6 +400,8 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     plan->reduce_col4 = int32_t(CB);
     plan->reduce_lanes = int32_t(PL);
     plan->expected_partials = int32_t(std::min<int64_t>(expected, INT32_MAX));
+    plan->whole_segments = 0;
+    plan->reserved = 0;
     plan->workgroups = n;
     plan->reduce_groups = n > 1 ? B * Qmax * Hkv * (G / RG) * (col4 / CB) : 0;
     plan->workspace_bytes = n > 1 ? 2 * n * HG * rows * (D + 1) * int64_t(sizeof(float)) + B * int64_t(sizeof(int32_t)) : 0;
@@ -371,7 +418,16 @@ int paged_attn_check(const pa_tensor* q, const pa_tensor* k_cache, const pa_tens
                      const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
                      const pa_tensor* v_scale, const pa_tensor* out) {
     return pa::validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
-                        v_scale, out, nullptr);
+                        v_scale, 0, nullptr, out, nullptr);
+}
+
+int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                         const pa_tensor* block_tables, const pa_tensor* context_lens,
+                         const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                         const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
+                         const pa_tensor* out) {
+    return pa::validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
+                        v_scale, sliding_window, sinks, out, nullptr);
 }
 
 int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,
@@ -382,11 +438,11 @@ int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* 
 }
 
 int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
-                    int64_t query_len, int64_t table_width, int32_t kv_dtype, int32_t num_cus,
+                    int64_t query_len, int64_t max_context, int32_t kv_dtype, int32_t num_cus,
                     pa_plan* plan) {
     if (kv_dtype != PA_DTYPE_BF16 && kv_dtype != PA_DTYPE_FP8_E4M3FN)
         return pa::fail(PA_ERR_DTYPE, "plan: kv dtype must be BF16 or FP8_E4M3FN");
-    return pa::make_plan(batch, q_heads, kv_heads, head_dim, query_len, table_width,
+    return pa::make_plan(batch, q_heads, kv_heads, head_dim, query_len, max_context,
                          kv_dtype == PA_DTYPE_FP8_E4M3FN, num_cus, plan);
 }
 
@@ -410,8 +466,10 @@ int paged_attn_set_heads_per_group(int32_t heads) {
 
 int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_lens,
                               const int32_t* block_tables, int64_t batch, int64_t table_width,
-                              int64_t table_row_stride, int64_t query_len, int64_t num_blocks) {
-    if (batch < 0 || table_width < 0 || query_len < 1 || num_blocks < 0 || table_row_stride < table_width)
+                              int64_t table_row_stride, int64_t query_len, int64_t num_blocks,
+                              int64_t block_size, int32_t sliding_window) {
+    if (batch < 0 || table_width < 0 || query_len < 1 || num_blocks < 0 || table_row_stride < table_width ||
+        block_size < 1)
         return pa::fail(PA_ERR_ARG, "check_metadata: invalid sizes");
     if (batch > 0 && (!context_lens || !block_tables))
         return pa::fail(PA_ERR_NULL, "check_metadata: NULL metadata");
@@ -421,11 +479,14 @@ int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_
         if (n < 0 || n > query_len)
             return pa::fail(PA_ERR_ARG, "sequence %lld: query_len %lld outside [0, %lld]", (long long)b,
                             (long long)n, (long long)query_len);
-        if (L < n || L > PA_BLOCK_SIZE * table_width)
+        if (L < n || L > block_size * table_width)
             return pa::fail(PA_ERR_ARG, "sequence %lld: context_len %lld outside [%lld, %lld]", (long long)b,
-                            (long long)L, (long long)n, (long long)(PA_BLOCK_SIZE * table_width));
-        const int64_t used = (L + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
-        for (int64_t i = 0; i < used; ++i) {
+                            (long long)L, (long long)n, (long long)(block_size * table_width));
+        if (n == 0) continue;
+        // the entries the kernels read: blocks holding keys some row sees
+        const int64_t lo = sliding_window > 0 ? std::max<int64_t>(0, L - n - sliding_window + 1) : 0;
+        const int64_t used = (L + block_size - 1) / block_size;
+        for (int64_t i = lo / block_size; i < used; ++i) {
             const int64_t blk = block_tables[b * table_row_stride + i];
             if (blk < 0 || blk >= num_blocks)
                 return pa::fail(PA_ERR_ARG, "sequence %lld: block_tables[%lld] = %lld outside [0, %lld)",

@@ -12,8 +12,11 @@ namespace pa {
 // kernels use.  Element strides unless the name says bytes.
 struct Problem {
     int64_t B, Qmax, Hq, Hkv, G, D, NB, W;
+    int64_t BS;                                        // tokens per block (a multiple of 16)
     bool fp8;
     float scale;
+    int32_t window;                                    // sliding window in tokens, 0 = none
+    const float* sinks; int64_t sinks_s;               // fp32 per query head, may be null
 
     const void* q;  int64_t q_sb, q_st, q_sh;          // bf16 elements
     void* out;      int64_t o_sb, o_st, o_sh;          // bf16 elements
@@ -28,7 +31,7 @@ struct Problem {
 
 // A validated cache write (paged_attn_reshape_and_cache).
 struct WriteProblem {
-    int64_t T, Hkv, D, NB;
+    int64_t T, Hkv, D, NB, BS;
     bool fp8;
     const void* k_new; int64_t kn_st, kn_sh;           // bytes
     const void* v_new; int64_t vn_st, vn_sh;           // bytes
@@ -43,22 +46,30 @@ int validate_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tens
                    const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* k_scale,
                    const pa_tensor* v_scale, WriteProblem* p);
 
-// Host-only validation shared by paged_attn_check and paged_attn_decode.
+// Host-only validation shared by the check and decode entry points.
 int validate(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
              const pa_tensor* block_tables, const pa_tensor* context_lens,
              const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
-             const pa_tensor* v_scale, const pa_tensor* out, Problem* pr);
+             const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
+             const pa_tensor* out, Problem* pr);
+
+// The most cache tokens one sequence's rows can read: the table's reach,
+// or the window plus the query rows when a window is set.
+int64_t max_context_tokens(int64_t block_size, int64_t table_width, int32_t window, int64_t Qmax);
 
 // The split-context plan (see pa_plan in paged_attn.h).
-int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t W,
+int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t max_context,
               bool fp8, int32_t num_cus, pa_plan* plan);
 
 // Records a failure description for paged_attn_last_error() and returns `status`.
 int fail(int status, const char* fmt, ...);
 
 constexpr int kChunkTokens = 32;            // tokens per chunk: the unit of work splitting
+constexpr int kMaxBlockSize = 4096;         // largest tokens-per-block (a multiple of 16)
+constexpr int64_t kMaxContext = int64_t(1) << 30;   // tokens a block-table row may reach
 constexpr int kDefaultMinShare = 1;         // smallest share of chunks per workgroup
 constexpr int kStepsPerWave = 8;            // planner's target chunks per wave
+constexpr int kWholeSegmentChunks = 2 * kStepsPerWave;   // longest segment run whole
 constexpr int kMaxBatch = 16384;            // per-sequence chunk counts live in LDS
 constexpr int kRedThreads = 256;            // merge workgroup size (reduce_kernel)
 constexpr int kRedUnroll = 8;               // partial loads in flight per merge lane

@@ -25,14 +25,18 @@ Generation order for a spec with seed ``s`` (``torch.Generator('cpu')``):
    (token, kv head) row of D values with scale ``absmax / 448`` (1 if the
    row is all zero) and ``torch``'s round-to-nearest-even cast to
    ``float8_e4m3fn``;
-5. block tables: sequence ``b`` takes the next ``ceil(L_b / 16)`` entries of
+5. block tables: sequence ``b`` takes the next ``ceil(L_b / BS)`` entries of
    the permutation; unused table columns hold block 0 (or, with
-   ``poison=True``, an unused block filled with NaN).
+   ``poison=True``, an unused block filled with NaN);
+6. for specs with ``sinks``, one sink logit per query head, uniform in
+   ``[-2, 8]`` (from about no effect to dominating a 128-token window's
+   log-sum-exp).
 
 Unused pool blocks hold zeros (NaN with ``poison=True``; the tail slots past
 ``L_b`` of each sequence's last block are NaN then as well).  Scales are
-stored physically ``[NB, Hkv, 16]`` so that one (block, kv head) reads 64
-contiguous bytes, and handed out as the logical ``[NB, 16, Hkv]`` view.
+stored physically ``[NB, Hkv, BS]`` so that one (block, kv head) reads its
+slots' scales contiguously, and handed out as the logical ``[NB, BS, Hkv]``
+view.  ``BS`` is the spec's block size (16 unless stated).
 """
 from __future__ import annotations
 
@@ -65,6 +69,9 @@ class WorkloadSpec:
     seed: int
     scale: Optional[float] = None   # None: 1 / sqrt(head_dim)
     qlen_lo: Optional[int] = None   # ragged query lengths, uniform in [qlen_lo, qlen]
+    block_size: int = BLOCK         # tokens per cache block
+    sliding_window: int = 0         # 0: none
+    sinks: bool = False             # per-query-head sink logits
 
     @property
     def softmax_scale(self) -> float:
@@ -72,7 +79,7 @@ class WorkloadSpec:
 
     @property
     def table_width(self) -> int:
-        return (self.ctx_hi + BLOCK - 1) // BLOCK
+        return (self.ctx_hi + self.block_size - 1) // self.block_size
 
     def replace(self, **kw) -> "WorkloadSpec":
         return dataclasses.replace(self, **kw)
@@ -111,7 +118,28 @@ CONFIGS.update({
                                       qlen=4, hq=64, hkv=8, head_dim=128, kv_dtype="bf16", ctx_lo=256,
                                       ctx_hi=16384, pool_blocks=65536, seed=7, qlen_lo=1),
 })
-NEXT_CONFIG_ORDER = ["mtp_verify_q4", "mtp_verify_ragged"]
+# Shape variants that the pages' decode dispatch and model table name: a
+# larger cache block (the persistent decode kernel's block size 256), a
+# multi-head (q_heads == kv_heads) model, and GPT-OSS-style sliding-window
+# layers with attention sinks (the landing page's model table; 64 query /
+# 8 kv heads of dimension 64 and a 128-token window are GPT-OSS's published
+# attention shape) next to its full-attention layers with sinks.
+CONFIGS.update({
+    "long_ctx_bs256": WorkloadSpec("long_ctx_b1_q64kv8_d128_ctx131072_bf16_block256", batch=1, qlen=1,
+                                   hq=64, hkv=8, head_dim=128, kv_dtype="bf16", ctx_lo=131072,
+                                   ctx_hi=131072, pool_blocks=1024, seed=8, block_size=256),
+    "mha": WorkloadSpec("mha_b8_q32kv32_d128_ctx1k-8k_bf16", batch=8, qlen=1, hq=32, hkv=32,
+                        head_dim=128, kv_dtype="bf16", ctx_lo=1024, ctx_hi=8192, pool_blocks=4096,
+                        seed=9),
+    "swa_sinks": WorkloadSpec("swa128_sinks_b64_q64kv8_d64_ctx1k-16k_bf16", batch=64, qlen=1, hq=64,
+                              hkv=8, head_dim=64, kv_dtype="bf16", ctx_lo=1024, ctx_hi=16384,
+                              pool_blocks=70000, seed=10, sliding_window=128, sinks=True),
+    "full_sinks": WorkloadSpec("sinks_b16_q64kv8_d64_ctx1k-32k_bf16", batch=16, qlen=1, hq=64, hkv=8,
+                               head_dim=64, kv_dtype="bf16", ctx_lo=1024, ctx_hi=32768,
+                               pool_blocks=34000, seed=11, sinks=True),
+})
+NEXT_CONFIG_ORDER = ["mtp_verify_q4", "mtp_verify_ragged", "long_ctx_bs256", "mha", "swa_sinks",
+                     "full_sinks"]
 
 
 @dataclass
@@ -126,13 +154,18 @@ class Workload:
     context_lens: torch.Tensor   # int32 [B]
     query_lens: torch.Tensor     # int32 [B]
     scale: float
+    sinks: Optional[torch.Tensor] = None   # fp32 [Hq] or None
+
+    @property
+    def sliding_window(self) -> int:
+        return self.spec.sliding_window
 
     def to(self, device) -> "Workload":
         def mv(t):
             return None if t is None else _move(t, device)
         return Workload(self.spec, mv(self.q), mv(self.k_cache), mv(self.v_cache),
                         mv(self.k_scale), mv(self.v_scale), mv(self.block_tables),
-                        mv(self.context_lens), mv(self.query_lens), self.scale)
+                        mv(self.context_lens), mv(self.query_lens), self.scale, mv(self.sinks))
 
     def numpy_inputs(self) -> dict:
         """The same bytes as NumPy arrays (bf16 as uint16 bit patterns,
@@ -146,7 +179,9 @@ class Workload:
                  block_tables=self.block_tables.cpu().numpy(),
                  context_lens=self.context_lens.cpu().numpy(),
                  query_lens=self.query_lens.cpu().numpy(), scale=self.scale,
-                 kv_dtype=self.spec.kv_dtype, k_scale=None, v_scale=None)
+                 kv_dtype=self.spec.kv_dtype, k_scale=None, v_scale=None,
+                 sliding_window=self.spec.sliding_window or None,
+                 sinks=None if self.sinks is None else self.sinks.cpu().numpy())
         if self.k_scale is not None:
             d["k_scale"] = self.k_scale.cpu().numpy()
             d["v_scale"] = self.v_scale.cpu().numpy()
@@ -158,16 +193,23 @@ def _move(t: torch.Tensor, device) -> torch.Tensor:
     of a contiguous physical tensor)."""
     if t.is_contiguous():
         return t.to(device)
-    # the scale tensors: logical [NB, 16, Hkv] view of physical [NB, Hkv, 16]
+    # the scale tensors: logical [NB, BS, Hkv] view of physical [NB, Hkv, BS]
     phys = t.permute(0, 2, 1)
     assert phys.is_contiguous()
     return phys.to(device).permute(0, 2, 1)
 
 
-def kv_bytes(context_lens, hkv: int, head_dim: int, kv_dtype: str) -> int:
+def kv_bytes(context_lens, hkv: int, head_dim: int, kv_dtype: str, query_lens=None,
+             sliding_window: int = 0) -> int:
     """Algorithmic KV bytes of one call: K and V rows of every attended
-    token, plus the fp32 per-token scales of an fp8 cache."""
-    tokens = int(torch.as_tensor(context_lens).to(torch.int64).sum())
+    token, plus the fp32 per-token scales of an fp8 cache.  With a sliding
+    window a sequence's rows attend to at most window + query_len - 1
+    tokens."""
+    ctx = torch.as_tensor(context_lens).to(torch.int64)
+    if sliding_window > 0:
+        ql = torch.ones_like(ctx) if query_lens is None else torch.as_tensor(query_lens).to(torch.int64)
+        ctx = torch.where(ql > 0, torch.minimum(ctx, sliding_window + ql - 1), torch.zeros_like(ctx))
+    tokens = int(ctx.sum())
     elem = 1 if kv_dtype == "fp8_e4m3fn" else 2
     per_token = 2 * hkv * head_dim * elem
     if kv_dtype == "fp8_e4m3fn":
@@ -181,18 +223,18 @@ def _nan_pattern(kv_dtype: str):
 
 def _fill_cache(cache, scales, block_ids, gen, spec, chunk_blocks):
     """Draw N(0, 1) rows for ``block_ids`` (in order) and store them."""
-    H, D = spec.hkv, spec.head_dim
+    H, D, BS = spec.hkv, spec.head_dim, spec.block_size
     for start in range(0, block_ids.numel(), chunk_blocks):
         ids = block_ids[start:start + chunk_blocks]
-        x = torch.randn(ids.numel(), BLOCK, H, D, generator=gen, dtype=torch.float32)
+        x = torch.randn(ids.numel(), BS, H, D, generator=gen, dtype=torch.float32)
         if spec.kv_dtype == "bf16":
             cache[ids] = x.to(torch.bfloat16)
         else:
-            amax = x.abs().amax(dim=-1)                              # [n, 16, H]
+            amax = x.abs().amax(dim=-1)                              # [n, BS, H]
             s = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
             y = (x / s[..., None]).clamp(-FP8_MAX, FP8_MAX)
             cache[ids] = y.to(torch.float8_e4m3fn).view(torch.uint8)
-            scales[ids] = s.permute(0, 2, 1).contiguous()            # physical [n, H, 16]
+            scales[ids] = s.permute(0, 2, 1).contiguous()            # physical [n, H, BS]
 
 
 def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = False,
@@ -205,7 +247,9 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
     B, Qn, Hq, H, D = spec.batch, spec.qlen, spec.hq, spec.hkv, spec.head_dim
     if Hq % H:
         raise ValueError("q heads must be a multiple of kv heads")
-    NB, W = spec.pool_blocks, spec.table_width
+    NB, W, BS = spec.pool_blocks, spec.table_width, spec.block_size
+    if BS < 1:
+        raise ValueError("block size must be positive")
 
     # 1. context lengths
     if context_lens is not None:
@@ -216,7 +260,7 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
         ctx = torch.full((B,), spec.ctx_lo, dtype=torch.int64)
     else:
         ctx = torch.randint(spec.ctx_lo, spec.ctx_hi + 1, (B,), generator=gen, dtype=torch.int64)
-    if ctx.numel() and int(ctx.max()) > BLOCK * W:
+    if ctx.numel() and int(ctx.max()) > BS * W:
         raise ValueError("a context is longer than the block table")
     if ctx.numel() and int(ctx.min()) < 0:
         raise ValueError("negative context length")
@@ -230,7 +274,7 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
             raise ValueError("query_lens must be in [0, qlen], one per sequence")
     if bool((qls.to(torch.int64) > ctx).any()):
         raise ValueError("a sequence has more query rows than context tokens")
-    nblk = (ctx + BLOCK - 1) // BLOCK
+    nblk = (ctx + BS - 1) // BS
     used = int(nblk.sum())
     if used + (1 if poison else 0) > NB:
         raise ValueError(f"pool of {NB} blocks cannot hold {used} used blocks")
@@ -246,10 +290,10 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
     if spec.kv_dtype not in ("bf16", "fp8_e4m3fn"):
         raise ValueError(spec.kv_dtype)
     cdtype = torch.uint8 if fp8 else torch.bfloat16
-    k_cache = torch.zeros(NB, BLOCK, H, D, dtype=cdtype)
-    v_cache = torch.zeros(NB, BLOCK, H, D, dtype=cdtype)
-    k_sc = torch.ones(NB, H, BLOCK, dtype=torch.float32) if fp8 else None
-    v_sc = torch.ones(NB, H, BLOCK, dtype=torch.float32) if fp8 else None
+    k_cache = torch.zeros(NB, BS, H, D, dtype=cdtype)
+    v_cache = torch.zeros(NB, BS, H, D, dtype=cdtype)
+    k_sc = torch.ones(NB, H, BS, dtype=torch.float32) if fp8 else None
+    v_sc = torch.ones(NB, H, BS, dtype=torch.float32) if fp8 else None
     used_ids = perm[:used]
     if poison:
         pat, vdt = _nan_pattern(spec.kv_dtype)
@@ -258,7 +302,7 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
         for s in (k_sc, v_sc):
             if s is not None:
                 s.fill_(float("nan"))
-    chunk = max(1, (64 << 20) // (BLOCK * H * D * 4))
+    chunk = max(1, (64 << 20) // (BS * H * D * 4))
     _fill_cache(k_cache, k_sc, used_ids, gen, spec, chunk)
     _fill_cache(v_cache, v_sc, used_ids, gen, spec, chunk)
 
@@ -271,8 +315,8 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
         tables[b, :n] = perm[off:off + n].to(torch.int32)
         off += n
         if poison and n:
-            tail = int(ctx[b]) - (n - 1) * BLOCK          # valid slots in the last block
-            if tail < BLOCK:
+            tail = int(ctx[b]) - (n - 1) * BS             # valid slots in the last block
+            if tail < BS:
                 last = int(tables[b, n - 1])
                 pat, vdt = _nan_pattern(spec.kv_dtype)
                 k_cache[last, tail:].view(vdt).fill_(pat)
@@ -281,12 +325,17 @@ def generate(spec: WorkloadSpec, *, seed: Optional[int] = None, poison: bool = F
                     k_sc[last, :, tail:] = float("nan")
                     v_sc[last, :, tail:] = float("nan")
 
+    # 6. sinks
+    sinks = None
+    if spec.sinks:
+        sinks = torch.rand(Hq, generator=gen, dtype=torch.float32) * 10.0 - 2.0
+
     return Workload(
         spec=spec, q=q, k_cache=k_cache, v_cache=v_cache,
         k_scale=None if k_sc is None else k_sc.permute(0, 2, 1),
         v_scale=None if v_sc is None else v_sc.permute(0, 2, 1),
         block_tables=tables, context_lens=ctx.to(torch.int32),
-        query_lens=qls, scale=spec.softmax_scale)
+        query_lens=qls, scale=spec.softmax_scale, sinks=sinks)
 
 
 @dataclass
@@ -318,11 +367,12 @@ def generate_cache_write(spec: WorkloadSpec, *, bulk_tokens: Optional[int] = Non
         slots = []
         for b in range(spec.batch):
             L, n = int(base.context_lens[b]), int(base.query_lens[b])
+            bs = spec.block_size
             for pos in range(L - n, L):
-                slots.append(int(base.block_tables[b, pos // BLOCK]) * BLOCK + pos % BLOCK)
+                slots.append(int(base.block_tables[b, pos // bs]) * bs + pos % bs)
         slots = torch.tensor(slots, dtype=torch.int64)
     else:
-        total = spec.pool_blocks * BLOCK
+        total = spec.pool_blocks * spec.block_size
         if bulk_tokens > total:
             raise ValueError("more tokens than pool slots")
         slots = torch.randperm(total, generator=gen)[:bulk_tokens]
@@ -336,12 +386,13 @@ def generate_cache_write(spec: WorkloadSpec, *, bulk_tokens: Optional[int] = Non
     return CacheWrite(base, k_new, v_new, slots.to(torch.int32))
 
 
-def write_bytes(slot_mapping, hkv: int, head_dim: int, kv_dtype: str, num_blocks: int) -> int:
+def write_bytes(slot_mapping, hkv: int, head_dim: int, kv_dtype: str, num_blocks: int,
+                block_size: int = BLOCK) -> int:
     """Algorithmic bytes of one cache write: the bf16 K and V rows read, the
     cache rows written (and the fp32 scales for an fp8 cache), for the
     tokens whose slot lies in the pool."""
     s = torch.as_tensor(slot_mapping).to(torch.int64)
-    n = int(((s >= 0) & (s < num_blocks * BLOCK)).sum())
+    n = int(((s >= 0) & (s < num_blocks * block_size)).sum())
     per_token = 2 * hkv * head_dim * 2
     if kv_dtype == "fp8_e4m3fn":
         per_token += 2 * hkv * head_dim + 2 * hkv * 4

@@ -41,8 +41,13 @@ def run_gpu(w, workgroups: int = 0, out=None, heads_per_group: int = 0, min_shar
     B.paged_attn_set_heads_per_group(heads_per_group)
     B.paged_attn_set_min_share(min_share)
     try:
-        B.paged_attn_decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
-                            dev.query_lens, dev.scale, dev.k_scale, dev.v_scale, out)
+        if dev.sinks is not None or dev.sliding_window > 0:
+            B.paged_attn_decode_ext(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                                    dev.query_lens, dev.scale, dev.k_scale, dev.v_scale, dev.sliding_window,
+                                    dev.sinks, out)
+        else:
+            B.paged_attn_decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                                dev.query_lens, dev.scale, dev.k_scale, dev.v_scale, out)
         torch.cuda.synchronize()
     finally:
         B.paged_attn_set_workgroups(0)
@@ -94,6 +99,7 @@ def compare(gpu_out, ref, query_lens, batch_subset=None, label=""):
 def check(w, workgroups: int = 0, batch_subset=None, label="", heads_per_group: int = 0,
           min_share: int = 0):
     note(f"[gpu] {label or w.spec.name}: B={w.spec.batch} ctx={w.context_lens.tolist()[:8]} "
+         f"bs={w.spec.block_size} window={w.spec.sliding_window} sinks={w.sinks is not None} "
          f"groups={workgroups or 'auto'} HG={heads_per_group or 'auto'} share={min_share or 'auto'}")
     out = run_gpu(w, workgroups, heads_per_group=heads_per_group, min_share=min_share)
     ref = oracle_out(w, batch_subset)

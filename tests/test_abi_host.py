@@ -21,8 +21,8 @@ def _tensors(kv="bf16", d=D, hq=HQ, hkv=HKV, qmax=QMAX, block=16):
     ql = torch.ones(BQ, dtype=torch.int32)
     ks = vs = None
     if kv == "fp8":
-        ks = torch.ones(NB, hkv, 16).permute(0, 2, 1)
-        vs = torch.ones(NB, hkv, 16).permute(0, 2, 1)
+        ks = torch.ones(NB, hkv, block).permute(0, 2, 1)
+        vs = torch.ones(NB, hkv, block).permute(0, 2, 1)
     out = torch.empty_like(q)
     return dict(q=q, k_cache=kc, v_cache=vc, block_tables=bt, context_lens=ctx, query_lens=ql,
                 scale=0.125, k_scale=ks, v_scale=vs, out=out)
@@ -102,6 +102,46 @@ def test_unsupported_configurations(kw, expect):
     assert _check(**_tensors(**kw)) == _status(expect)
 
 
+@pytest.mark.parametrize("block", [32, 48, 64, 256, 4096])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_block_sizes_that_are_multiples_of_16_are_accepted(block, kv):
+    assert _check(**_tensors(kv, block=block)) == B.PA_OK
+
+
+@pytest.mark.parametrize("block", [1, 8, 24, 40, 4112, 8192])
+def test_other_block_sizes_are_unsupported(block):
+    assert _check(**_tensors(block=block)) == _status("PA_ERR_UNSUPPORTED")
+
+
+def test_fp8_scales_follow_the_block_size():
+    t = _tensors("fp8", block=64)
+    t["k_scale"] = torch.ones(NB, HKV, 16).permute(0, 2, 1)          # 16 slots, blocks of 64
+    assert _check(**t) == _status("PA_ERR_SHAPE")
+
+
+def test_block_table_reach_limit():
+    t = _tensors(block=4096)
+    t["block_tables"] = torch.zeros(BQ, (1 << 30) // 4096 + 1, dtype=torch.int32)
+    assert _check(**t) == _status("PA_ERR_UNSUPPORTED")
+    t["block_tables"] = torch.zeros(BQ, (1 << 30) // 4096, dtype=torch.int32)
+    assert _check(**t) == B.PA_OK
+
+
+def test_check_ext_window_and_sinks():
+    t = _tensors()
+    sinks = torch.zeros(HQ, dtype=torch.float32)
+    for window in (-1, 0, 1, 128, 1 << 30):
+        assert B.paged_attn_check_ext(**t, sliding_window=window, sinks=sinks) == B.PA_OK
+        assert B.paged_attn_check_ext(**t, sliding_window=window) == B.PA_OK
+    assert B.paged_attn_check_ext(**t, sinks=torch.zeros(2 * HQ)[::2]) == B.PA_OK     # strided
+    assert B.paged_attn_check_ext(**t, sinks=sinks[:-1]) == _status("PA_ERR_SHAPE")
+    assert B.paged_attn_check_ext(**t, sinks=sinks[None]) == _status("PA_ERR_SHAPE")
+    assert B.paged_attn_check_ext(**t, sinks=sinks.to(torch.bfloat16)) == _status("PA_ERR_DTYPE")
+    t2 = _tensors()
+    t2["scale"] = float("nan")                                     # the other rules still apply
+    assert B.paged_attn_check_ext(**t2, sinks=sinks) == _status("PA_ERR_ARG")
+
+
 def test_rows_limit_is_inclusive():
     assert _check(**_tensors(hq=32, hkv=1, qmax=2)) == B.PA_OK      # exactly 64 rows
 
@@ -148,11 +188,11 @@ def test_empty_batch_is_valid():
 @pytest.mark.parametrize("shape", [
     (1, 32, 8, 128, 1, 32), (4, 32, 8, 128, 1, 512), (1, 64, 8, 128, 1, 8192),
     (16, 64, 8, 64, 1, 2048), (64, 64, 8, 128, 2, 1024), (3, 8, 8, 64, 4, 1),
-    (1, 4, 1, 128, 1, 1 << 16), (0, 8, 2, 128, 1, 4),
+    (1, 4, 1, 128, 1, 1 << 16), (0, 8, 2, 128, 1, 4), (64, 64, 8, 64, 1, 10), (256, 32, 8, 128, 2, 32),
 ])
 def test_plan_properties(shape):
     b, hq, hkv, d, ql, w = shape
-    p = B.paged_attn_plan(b, hq, hkv, d, ql, w)
+    p = B.paged_attn_plan(b, hq, hkv, d, ql, 16 * w)
     assert p["rows"] == hq // hkv * ql and p["row_tiles"] == (p["rows"] + 15) // 16
     hg = p["heads_per_group"]
     assert hkv % hg == 0 and 1 <= hg <= (8 if p["row_tiles"] == 1 else 4)
@@ -164,36 +204,39 @@ def test_plan_properties(shape):
     rg, cb, pl = p["reduce_rows"], p["reduce_col4"], p["reduce_lanes"]
     assert rg * cb * pl <= 256 and (hq // hkv) % rg == 0 and (d // 4) % cb == 0
     assert pl * 8 >= min(p["expected_partials"], 256)      # one round of loads (up to 32 lanes)
-    assert (p["reduce_groups"] > 0) == (n > 1)
-    if n > 1:
+    if p["whole_segments"]:
+        # one workgroup per short segment: no partials, no merge
+        assert n == b * (hkv // hg) and n >= 256 and 16 * w <= 512
+        assert p["reduce_groups"] == 0 and p["workspace_bytes"] == 0
+    elif n > 1:
         assert p["reduce_groups"] == b * ql * hkv * (hq // hkv // rg) * (d // 4 // cb)
         assert p["workspace_bytes"] == 2 * n * hg * p["rows"] * (d + 1) * 4 + 4 * b
     else:
-        assert p["workspace_bytes"] == 0
-    assert p == B.paged_attn_plan(b, hq, hkv, d, ql, w)      # deterministic
+        assert p["reduce_groups"] == 0 and p["workspace_bytes"] == 0
+    assert p == B.paged_attn_plan(b, hq, hkv, d, ql, 16 * w)      # deterministic
 
 
 def test_plan_fills_the_device_for_long_single_sequence():
-    p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=256)
+    p = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192, num_cus=256)
     assert p["workgroups"] * p["heads_per_group"] >= 1024          # at least one wave per SIMD
-    small = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=8)
+    small = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192, num_cus=8)
     assert small["workgroups"] < p["workgroups"]
 
 
 def test_workgroup_and_share_overrides_and_reset():
     try:
         B.paged_attn_set_workgroups(5)
-        p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)
+        p = B.paged_attn_plan(4, 32, 8, 128, 1, 16 * 512)
         assert p["workgroups"] == 5
         B.paged_attn_set_workgroups(1)
-        p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)
+        p = B.paged_attn_plan(4, 32, 8, 128, 1, 16 * 512)
         assert p["workgroups"] == 1 and p["reduce_groups"] == 0 and p["workspace_bytes"] == 0
         B.paged_attn_set_workgroups(1 << 30)                      # capped by the chunk count
-        p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
+        p = B.paged_attn_plan(1, 32, 8, 128, 1, 16 * 32)
         assert p["workgroups"] == 16 // p["min_share_chunks"] * (8 // p["heads_per_group"])
         B.paged_attn_set_workgroups(0)
         B.paged_attn_set_min_share(4)
-        p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)
+        p = B.paged_attn_plan(1, 32, 8, 128, 1, 16 * 32)
         assert p["min_share_chunks"] == 4 and p["workgroups"] * 4 <= 16 * (8 // p["heads_per_group"])
         with pytest.raises(B.PagedAttnError):
             B.paged_attn_set_workgroups(-1)
@@ -202,19 +245,19 @@ def test_workgroup_and_share_overrides_and_reset():
     finally:
         B.paged_attn_set_workgroups(0)
         B.paged_attn_set_min_share(0)
-    assert B.paged_attn_plan(1, 32, 8, 128, 1, 32)["min_share_chunks"] == 1
+    assert B.paged_attn_plan(1, 32, 8, 128, 1, 16 * 32)["min_share_chunks"] == 1
 
 
 def test_heads_per_group_override():
     try:
         B.paged_attn_set_heads_per_group(2)
-        assert B.paged_attn_plan(1, 64, 8, 128, 1, 8192)["heads_per_group"] == 2
+        assert B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192)["heads_per_group"] == 2
         B.paged_attn_set_heads_per_group(3)                     # does not divide 8 kv heads
         with pytest.raises(B.PagedAttnError):
-            B.paged_attn_plan(1, 64, 8, 128, 1, 8192)
+            B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192)
         B.paged_attn_set_heads_per_group(8)                     # 64 rows: at most 4 heads
         with pytest.raises(B.PagedAttnError):
-            B.paged_attn_plan(1, 64, 1, 128, 1, 8192)
+            B.paged_attn_plan(1, 64, 1, 128, 1, 16 * 8192)
         with pytest.raises(B.PagedAttnError):
             B.paged_attn_set_heads_per_group(9)
     finally:
@@ -224,32 +267,50 @@ def test_heads_per_group_override():
 def test_plan_grids():
     # about 8 chunks per wave, at least a quarter of the CUs, at most the
     # chip; the largest head group that still gives every CU a workgroup
-    p = B.paged_attn_plan(1, 32, 8, 128, 1, 32)                  # one 512-token sequence
+    p = B.paged_attn_plan(1, 32, 8, 128, 1, 16 * 32)                  # one 512-token sequence
     assert p["heads_per_group"] == 1 and p["workgroups"] == 64    # latency bound: spread out
-    p = B.paged_attn_plan(4, 32, 8, 128, 1, 512)                 # 4 x <= 8192 tokens
+    p = B.paged_attn_plan(4, 32, 8, 128, 1, 16 * 512)                 # 4 x <= 8192 tokens
     assert p["heads_per_group"] == 2 and p["workgroups"] == 256
-    p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192)                # 131072 tokens, batch 1
+    p = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192)                # 131072 tokens, batch 1
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256
-    p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048)                # fp8-sized rows, bf16 cache
+    p = B.paged_attn_plan(16, 64, 8, 64, 1, 16 * 2048)                # fp8-sized rows, bf16 cache
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256
-    p = B.paged_attn_plan(16, 64, 8, 64, 1, 2048, kv_dtype="fp8_e4m3fn")
+    p = B.paged_attn_plan(16, 64, 8, 64, 1, 16 * 2048, kv_dtype="fp8_e4m3fn")
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256   # whole token rows per workgroup
-    p = B.paged_attn_plan(64, 64, 8, 128, 2, 1024)               # MTP verify
+    p = B.paged_attn_plan(64, 64, 8, 128, 2, 16 * 1024)               # MTP verify
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256
-    p = B.paged_attn_plan(1, 64, 8, 128, 1, 8192, num_cus=8)     # a small device
+    p = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192, num_cus=8)     # a small device
     assert p["workgroups"] == 8
+
+
+def test_plan_takes_whole_segments_when_short_and_many():
+    # a 128-token window (at most 160 tokens read): 64 x 8 segments
+    p = B.paged_attn_plan(64, 64, 8, 64, 1, 160)
+    assert p["whole_segments"] == 1 and p["heads_per_group"] == 2 and p["workgroups"] == 256
+    assert p["reduce_groups"] == 0 and p["workspace_bytes"] == 0
+    # too few segments for the device, or segments too long: shares
+    assert B.paged_attn_plan(64, 64, 8, 64, 1, 160, num_cus=1024)["whole_segments"] == 0
+    assert B.paged_attn_plan(4, 64, 8, 64, 1, 160)["whole_segments"] == 0
+    assert B.paged_attn_plan(64, 64, 8, 64, 1, 16 * 33)["whole_segments"] == 0
+    assert B.paged_attn_plan(64, 64, 8, 64, 1, 16 * 32)["whole_segments"] == 1
+    # a grid or share override keeps the split
+    try:
+        B.paged_attn_set_workgroups(7)
+        assert B.paged_attn_plan(64, 64, 8, 64, 1, 160)["whole_segments"] == 0
+    finally:
+        B.paged_attn_set_workgroups(0)
 
 
 def test_plan_rejects_chunk_index_overflow():
     with pytest.raises(B.PagedAttnError):
-        B.paged_attn_plan(16384, 8, 8, 128, 1, 1 << 20)
+        B.paged_attn_plan(16384, 8, 8, 128, 1, 16 * 1 << 20)
 
 
 def test_plan_rejects_bad_sizes():
     with pytest.raises(B.PagedAttnError):
-        B.paged_attn_plan(1, 6, 4, 128, 1, 4)
+        B.paged_attn_plan(1, 6, 4, 128, 1, 16 * 4)
     with pytest.raises(B.PagedAttnError):
-        B.paged_attn_plan(1, 8, 8, 128, 1, 0)
+        B.paged_attn_plan(1, 8, 8, 128, 1, 16 * 0)
 
 
 def test_check_metadata():
@@ -272,23 +333,40 @@ def test_check_metadata():
     B.paged_attn_check_metadata(ctx, ql, torch.tensor([[3, -7, 99], [0, 1, 2]], dtype=torch.int32), 2, 10)
 
 
+def test_check_metadata_block_size_and_window():
+    ctx = torch.tensor([100, 64], dtype=torch.int32)
+    ql = torch.tensor([1, 1], dtype=torch.int32)
+    bt = torch.tensor([[-5, 3], [1, -1]], dtype=torch.int32)
+    with pytest.raises(B.PagedAttnError):                          # entry 0 of row 0 holds keys
+        B.paged_attn_check_metadata(ctx, ql, bt, 1, 4, block_size=64)
+    # a 30-token window: row 0 sees keys 70..99 (entry 1 only), row 1 keys
+    # 34..63 (entry 0 only)
+    B.paged_attn_check_metadata(ctx, ql, bt, 1, 4, block_size=64, sliding_window=30)
+    with pytest.raises(B.PagedAttnError):                          # row 1 sees entry 0 = -1
+        B.paged_attn_check_metadata(ctx, ql, torch.tensor([[-5, 3], [-1, 2]], dtype=torch.int32), 1, 4,
+                                    block_size=64, sliding_window=30)
+    with pytest.raises(B.PagedAttnError):                          # L > block_size * W
+        B.paged_attn_check_metadata(torch.tensor([129, 1], dtype=torch.int32), ql, bt, 1, 4, block_size=64,
+                                    sliding_window=30)
+
+
 def test_strerror_covers_every_status():
     for code in B.STATUS_NAMES:
         assert B.paged_attn_strerror(code) != "unknown status"
     assert B.paged_attn_strerror(12345) == "unknown status"
 
 
-def _write_tensors(kv="bf16", T=5, hkv=HKV, d=D):
+def _write_tensors(kv="bf16", T=5, hkv=HKV, d=D, block=16):
     kn = torch.zeros(T, hkv, d, dtype=torch.bfloat16)
     vn = torch.zeros(T, hkv, d, dtype=torch.bfloat16)
     sm = torch.zeros(T, dtype=torch.int32)
     cdt = torch.uint8 if kv == "fp8" else torch.bfloat16
-    kc = torch.zeros(NB, 16, hkv, d, dtype=cdt)
-    vc = torch.zeros(NB, 16, hkv, d, dtype=cdt)
+    kc = torch.zeros(NB, block, hkv, d, dtype=cdt)
+    vc = torch.zeros(NB, block, hkv, d, dtype=cdt)
     ks = vs = None
     if kv == "fp8":
-        ks = torch.ones(NB, hkv, 16).permute(0, 2, 1)
-        vs = torch.ones(NB, hkv, 16).permute(0, 2, 1)
+        ks = torch.ones(NB, hkv, block).permute(0, 2, 1)
+        vs = torch.ones(NB, hkv, block).permute(0, 2, 1)
     return dict(k_new=kn, v_new=vn, slot_mapping=sm, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs)
 
 
@@ -297,6 +375,11 @@ def test_cache_write_validation_accepts_good_arguments(kv):
     assert B.paged_attn_check_reshape_and_cache(**_write_tensors(kv)) == B.PA_OK
     t = _write_tensors(kv, T=0)                                   # nothing to write
     assert B.paged_attn_check_reshape_and_cache(**t) == B.PA_OK
+    for block in (32, 64, 256, 4096):
+        assert B.paged_attn_check_reshape_and_cache(**_write_tensors(kv, block=block)) == B.PA_OK
+    for block in (8, 24, 8192):
+        assert B.paged_attn_check_reshape_and_cache(**_write_tensors(kv, block=block)) == \
+            _status("PA_ERR_UNSUPPORTED")
 
 
 def test_cache_write_validation_rejects_bad_arguments():

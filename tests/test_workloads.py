@@ -26,7 +26,7 @@ def test_five_configs_have_the_stated_shapes():
     m = CONFIGS["mtp_verify"]
     assert (m.batch, m.qlen, m.ctx_lo, m.ctx_hi) == (64, 2, 256, 16384)
     for s in CONFIGS.values():
-        assert s.table_width * 16 >= s.ctx_hi
+        assert s.table_width * s.block_size >= s.ctx_hi and s.block_size % 16 == 0
         assert s.pool_blocks >= s.batch * s.table_width or s.name.startswith("tiny")
 
 
@@ -104,3 +104,22 @@ def test_ragged_query_lengths_are_drawn_in_range_and_reproducibly():
     assert torch.equal(ql, b.query_lens) and torch.equal(a.k_cache, b.k_cache)
     # specs without qlen_lo draw nothing extra: the five workloads are unchanged
     assert CONFIGS["mtp_verify"].qlen_lo is None
+
+
+def test_block_size_window_and_sinks_in_the_generator():
+    from paged_attention_decode_attn_amd.workloads import kv_bytes
+    spec = CONFIGS["mtp_verify"].replace(batch=3, ctx_lo=2, ctx_hi=300, pool_blocks=20, block_size=64,
+                                         sliding_window=50, sinks=True)
+    w = generate(spec)
+    assert w.k_cache.shape[1] == 64 and w.block_tables.shape[1] == 5
+    assert w.sinks.shape == (spec.hq,) and float(w.sinks.min()) >= -2 and float(w.sinks.max()) <= 8
+    # the draws before the sinks are those of the same spec without sinks
+    w0 = generate(spec.replace(sinks=False))
+    assert torch.equal(w.k_cache.view(torch.int16), w0.k_cache.view(torch.int16)) and w0.sinks is None
+    ins = w.numpy_inputs()
+    assert ins["sliding_window"] == 50 and ins["sinks"].shape == (spec.hq,)
+    # a window bounds the attended tokens: min(L, window + n - 1) per sequence
+    ctx, ql = torch.tensor([10, 100, 60]), torch.tensor([2, 2, 0])
+    per = 2 * spec.hkv * spec.head_dim * 2
+    assert kv_bytes(ctx, spec.hkv, spec.head_dim, "bf16", ql, 50) == (10 + 51 + 0) * per
+    assert kv_bytes(ctx, spec.hkv, spec.head_dim, "bf16") == 170 * per
