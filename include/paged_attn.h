@@ -48,6 +48,7 @@ extern "C" {
 #define PA_BLOCK_SIZE 16      /* default tokens per KV-cache block; a block
                                  holds any multiple of 16 up to 4096 tokens  */
 #define PA_MAX_ROWS   64      /* max (q_heads / kv_heads) * query_len       */
+#define PA_MAX_ROWS_D256 16   /* the same limit for head_dim 256            */
 
 typedef enum pa_dtype {
     PA_DTYPE_BF16        = 1,  /* bfloat16                                  */
@@ -62,7 +63,7 @@ typedef enum pa_status {
     PA_ERR_DTYPE       = -2,  /* a tensor has the wrong dtype                */
     PA_ERR_SHAPE       = -3,  /* ranks or sizes disagree between tensors     */
     PA_ERR_UNSUPPORTED = -4,  /* block size not a multiple of 16, head_dim
-                                 not 64/128,
+                                 not 64/128/256,
                                  q_heads % kv_heads != 0, rows > 64, ...     */
     PA_ERR_LAYOUT      = -5,  /* inner stride != 1, misaligned base/stride   */
     PA_ERR_CAPTURE     = -6,  /* workspace would have to grow while the
@@ -113,8 +114,8 @@ typedef struct pa_tensor {
  *                 receive the attention output rounded to nearest even.
  *   stream        hipStream_t as void*, NULL = default stream.
  *
- * Query head h reads KV head h / (Hq / Hkv).  D must be 64 or 128,
- * (Hq / Hkv) * Qmax <= 64.  Inner strides of q, out, caches and block_tables
+ * Query head h reads KV head h / (Hq / Hkv).  D must be 64, 128 or 256,
+ * (Hq / Hkv) * Qmax <= 64 (<= 16 for D 256).  Inner strides of q, out, caches and block_tables
  * must be 1, the other strides of q/out/caches multiples of 16 bytes, data
  * pointers 16-byte aligned; k_scale/v_scale strides of dims 0 and 2
  * multiples of 4 and data 16-byte aligned.
@@ -198,7 +199,7 @@ int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_
  * High-Interactivity Inference", "Attention Input Fusion" (fp8 scales are
  * calculated as K/V are written into the paged cache).
  *
- *   k_new, v_new  bf16 [T, Hkv, D]: the new tokens' rows (D 64 or 128).
+ *   k_new, v_new  bf16 [T, Hkv, D]: the new tokens' rows (D 64, 128 or 256).
  *   slot_mapping  int32 [T]: slot s of token t is position s % BS of block
  *                 s / BS.  Entries < 0 (padding tokens) and >= NB * BS are
  *                 skipped; the others must be distinct (two tokens on one
@@ -304,7 +305,8 @@ int paged_attn_set_min_share(int32_t chunks);
 /*
  * paged_attn_set_heads_per_group -- override the planner's kv heads per
  * partition workgroup for every later call in the process (1..8; it must
- * divide kv_heads, and be at most 4 when (Hq / Hkv) * Qmax > 16, or the call
+ * divide kv_heads, and be at most 4 when (Hq / Hkv) * Qmax > 16 or head_dim is
+ * 256, or the call
  * fails with PA_ERR_ARG), or 0 for the automatic choice.  A tuning hook;
  * not synchronised with concurrent calls.
  */

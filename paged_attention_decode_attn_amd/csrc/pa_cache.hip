@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
 
 template <bool FP8>
 const void* write_kernel_of(int D) {
-    return D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 16>)
+    return D == 256 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 32>)
+         : D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 16>)
                     : reinterpret_cast<const void*>(&cache_write_kernel<FP8, 8>);
 }
 

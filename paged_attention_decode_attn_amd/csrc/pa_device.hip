@@ -61,6 +61,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr unsigned kSelLo = 0x05040100u;   // v_perm: (src1.lo16, src0.lo16)
@@ -124,6 +125,8 @@ __device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
 // Per-step register tiles.  KL: 16-byte K loads per lane and block;
 // V: one load of D/16 elements per lane and token slot.
 template <int D, bool FP8> struct VLoad;
+template <> struct VLoad<256, false> { typedef u32x8 T; };
+template <> struct VLoad<256, true>  { typedef u32x4 T; };
 template <> struct VLoad<128, false> { typedef u32x4 T; };
 template <> struct VLoad<64, false>  { typedef u32x2 T; };
 template <> struct VLoad<128, true>  { typedef u32x2 T; };
@@ -159,6 +162,11 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
 template <typename T> __device__ __forceinline__ T bload(Rsrc r, unsigned off);
 template <> __device__ __forceinline__ u32x4 bload<u32x4>(Rsrc r, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ u32x8 bload<u32x8>(Rsrc r, unsigned off) {
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u, 0, 0);
+    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 template <> __device__ __forceinline__ u32x2 bload<u32x2>(Rsrc r, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
@@ -513,7 +521,10 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
     constexpr int J = D / 16;
     constexpr int KL = Step<D, FP8>::KL;
     constexpr int E = FP8 ? 1 : 2;
-    constexpr int R = NT > 2 ? 1 : 2;    // register buffers: loads of R-1 steps ahead in flight
+    // register buffers: loads of R-1 steps ahead in flight (head_dim 256:
+    // one buffer, its bf16 step alone is 128 registers; the CU's other
+    // waves keep the loads flowing)
+    constexpr int R = (NT > 2 || D > 128) ? 1 : 2;
     const int n16 = lane & 15, grp = lane >> 4;
 
     // Start-up loads issued together: the first block-table window, the
@@ -644,12 +655,16 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = J * (4 * grp + i);
-                if constexpr (J == 8) {
-                    u32x4 wv;
+                if constexpr (J >= 8) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        wv[e] = pack_bf16_rne(s.acc[nt][2 * e][i] * inv, s.acc[nt][2 * e + 1][i] * inv);
-                    *reinterpret_cast<u32x4*>(orow + 2 * d0) = wv;
+                    for (int h = 0; h < J / 8; ++h) {
+                        u32x4 wv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            wv[e] = pack_bf16_rne(s.acc[nt][8 * h + 2 * e][i] * inv,
+                                                  s.acc[nt][8 * h + 2 * e + 1][i] * inv);
+                        *reinterpret_cast<u32x4*>(orow + 2 * (d0 + 8 * h)) = wv;
+                    }
                 } else {
                     u32x2 wv;
 #pragma unroll
@@ -702,8 +717,8 @@ __device__ __forceinline__ int share_owner(int64_t c, int64_t C, int n) {
 // the merge kernel); every wave finds a chunk's sequence with a 64-wide
 // ballot over that prefix (a share's chunks only increase).
 template <int D, bool FP8, int NT, bool GEN>
-__global__ __launch_bounds__(NT == 1 ? 512 : 256)
-__attribute__((amdgpu_waves_per_eu(NT == 1 ? (FP8 && D == 64 ? 3 : 2) : 1)))
+__global__ __launch_bounds__(NT == 1 && D <= 128 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(NT == 1 && D <= 128 ? (FP8 && D == 64 ? 3 : 2) : 1)))
 void partition_kernel(PartArgs a) {
     extern __shared__ int s_pre[];               // inclusive prefix of chunks per sequence
     const int lane = threadIdx.x & 63;
@@ -957,7 +972,18 @@ const void* kernel_of(bool fp8, int nt, bool gen) {
     return gen ? kernel_of<D, false, true>(nt) : kernel_of<D, false, false>(nt);
 }
 
+// head_dim 256 serves at most 16 rows (one tile: with two, the step, the
+// query fragments and the accumulators no longer fit the register file)
+template <bool FP8, bool GEN>
+const void* kernel256_of(int) {
+    return reinterpret_cast<const void*>(&partition_kernel<256, FP8, 1, GEN>);
+}
+
 const void* partition_kernel_of(int D, bool fp8, int nt, bool gen) {
+    if (D == 256) {
+        if (fp8) return gen ? kernel256_of<true, true>(nt) : kernel256_of<true, false>(nt);
+        return gen ? kernel256_of<false, true>(nt) : kernel256_of<false, false>(nt);
+    }
     return D == 128 ? kernel_of<128>(fp8, nt, gen) : kernel_of<64>(fp8, nt, gen);
 }
 
@@ -1050,7 +1076,8 @@ int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa
         r.grid = (int32_t)grid; r.min_share = a.min_share;
         r.red_rows = plan.reduce_rows; r.red_col4 = plan.reduce_col4; r.red_lanes = plan.reduce_lanes;
         const dim3 rgrid((unsigned)plan.reduce_groups), rblock((unsigned)kRedThreads);
-        if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, rgrid, rblock, 0, s, r);
+        if (pr.D == 256) hipLaunchKernelGGL(reduce_kernel<256>, rgrid, rblock, 0, s, r);
+        else if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, rgrid, rblock, 0, s, r);
         else hipLaunchKernelGGL(reduce_kernel<64>, rgrid, rblock, 0, s, r);
     }
     if (e2) (void)hipEventRecord(e2, s);

@@ -131,8 +131,8 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
                     (long long)BS, kMaxBlockSize);
     if (kc->shape[3] != D)
         return fail(PA_ERR_SHAPE, "k_cache: head_dim %lld, q has %lld", (long long)kc->shape[3], (long long)D);
-    if (D != 64 && D != 128)
-        return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64 and 128 are supported", (long long)D);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64, 128 and 256 are supported", (long long)D);
     if (Hkv < 1) return fail(PA_ERR_SHAPE, "k_cache: no kv heads");
     if (Hq % Hkv != 0 || Hq == 0)
         return fail(PA_ERR_UNSUPPORTED, "q_heads %lld is not a positive multiple of kv_heads %lld",
@@ -142,6 +142,9 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     if (G * Qmax > PA_MAX_ROWS)
         return fail(PA_ERR_UNSUPPORTED, "(q_heads / kv_heads) * query_len = %lld exceeds %d",
                     (long long)(G * Qmax), PA_MAX_ROWS);
+    if (D == 256 && G * Qmax > PA_MAX_ROWS_D256)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim 256: (q_heads / kv_heads) * query_len = %lld exceeds %d",
+                    (long long)(G * Qmax), PA_MAX_ROWS_D256);
     if (bt->shape[0] != B)
         return fail(PA_ERR_SHAPE, "block_tables: %lld rows, batch is %lld", (long long)bt->shape[0], (long long)B);
     if (B > kMaxBatch)
@@ -260,8 +263,8 @@ int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm
         return fail(PA_ERR_SHAPE, "k_cache: [%lld, %lld, %lld, %lld], new tokens are [T, %lld, %lld]",
                     (long long)NB, (long long)BS, (long long)kc->shape[2], (long long)kc->shape[3], (long long)Hkv,
                     (long long)D);
-    if (D != 64 && D != 128)
-        return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64 and 128 are supported", (long long)D);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64, 128 and 256 are supported", (long long)D);
     if (Hkv < 1) return fail(PA_ERR_SHAPE, "no kv heads");
     if (NB * BS >= (int64_t(1) << 31))
         return fail(PA_ERR_UNSUPPORTED, "pool of %lld blocks: slots do not fit int32", (long long)NB);
@@ -314,10 +317,13 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
         return fail(PA_ERR_ARG, "plan: invalid sizes");
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
+    if (D == 256 && rows > PA_MAX_ROWS_D256)
+        return fail(PA_ERR_UNSUPPORTED, "plan: head_dim 256 serves at most %d rows", PA_MAX_ROWS_D256);
     // waves one CU holds for the kernel variant (register budget) and the
     // largest kv-head group (one wave per head) a workgroup may carry
-    const int64_t cu_waves = row_tiles == 1 ? (fp8 && D == 64 ? 12 : 8) : 4;
-    const int64_t hg_cap = row_tiles == 1 ? 8 : 4;
+    const bool one_tile = row_tiles == 1 && D <= 128;
+    const int64_t cu_waves = one_tile ? (fp8 && D == 64 ? 12 : 8) : 4;
+    const int64_t hg_cap = one_tile ? 8 : 4;
     // chunk space: 32-token chunks of every (sequence, head group) segment;
     // only its upper bound is known here (lengths live on the device)
     const int64_t seq_chunks = (max_context + kChunkTokens - 1) / kChunkTokens;

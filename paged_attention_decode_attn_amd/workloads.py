@@ -138,8 +138,12 @@ CONFIGS.update({
                                head_dim=64, kv_dtype="bf16", ctx_lo=1024, ctx_hi=32768,
                                pool_blocks=34000, seed=11, sinks=True),
 })
+# head_dim 256 (the model operations guide routes head_dim != 128 to another
+# decode kernel): a Gemma-2-9B-shaped layer, 16 query / 8 kv heads.
+CONFIGS["d256"] = WorkloadSpec("d256_b8_q16kv8_ctx1k-8k_bf16", batch=8, qlen=1, hq=16, hkv=8, head_dim=256,
+                               kv_dtype="bf16", ctx_lo=1024, ctx_hi=8192, pool_blocks=4096, seed=12)
 NEXT_CONFIG_ORDER = ["mtp_verify_q4", "mtp_verify_ragged", "long_ctx_bs256", "mha", "swa_sinks",
-                     "full_sinks"]
+                     "full_sinks", "d256"]
 
 
 @dataclass

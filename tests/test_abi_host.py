@@ -94,7 +94,8 @@ def test_validation_errors(mutate, expect):
 @pytest.mark.parametrize("kw,expect", [
     (dict(block=8), "PA_ERR_UNSUPPORTED"),
     (dict(d=96), "PA_ERR_UNSUPPORTED"),
-    (dict(d=256), "PA_ERR_UNSUPPORTED"),
+    (dict(d=512), "PA_ERR_UNSUPPORTED"),
+    (dict(d=256, hq=32, hkv=2, qmax=2), "PA_ERR_UNSUPPORTED"),  # 32 rows at head_dim 256
     (dict(hq=6, hkv=4), "PA_ERR_UNSUPPORTED"),
     (dict(hq=40, hkv=1, qmax=2), "PA_ERR_UNSUPPORTED"),      # 80 rows per kv head
 ])
@@ -144,6 +145,15 @@ def test_check_ext_window_and_sinks():
 
 def test_rows_limit_is_inclusive():
     assert _check(**_tensors(hq=32, hkv=1, qmax=2)) == B.PA_OK      # exactly 64 rows
+    assert _check(**_tensors(d=256, hq=16, hkv=2, qmax=2)) == B.PA_OK          # 16 rows at head_dim 256
+    assert _check(**_tensors("fp8", d=256, hq=8, hkv=8, qmax=1)) == B.PA_OK
+
+
+def test_head_dim_256_plans_one_tile_and_small_groups():
+    p = B.paged_attn_plan(8, 16, 8, 256, 1, 8192)
+    assert p["row_tiles"] == 1 and p["heads_per_group"] <= 4
+    with pytest.raises(B.PagedAttnError):
+        B.paged_attn_plan(8, 32, 2, 256, 2, 8192)                  # 32 rows
 
 
 def test_fp8_scale_rules():

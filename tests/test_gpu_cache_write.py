@@ -67,7 +67,7 @@ def test_decode_step_write_matches_oracle(name, kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
-@pytest.mark.parametrize("hkv,d", [(1, 64), (2, 128), (8, 64), (8, 128), (3, 128)])
+@pytest.mark.parametrize("hkv,d", [(1, 64), (2, 128), (8, 64), (8, 128), (3, 128), (2, 256), (8, 256)])
 def test_bulk_write_with_padding_and_out_of_pool_slots(kv, hkv, d):
     spec = CONFIGS["llama3_8b"].replace(batch=2, hq=hkv, hkv=hkv, head_dim=d, kv_dtype=kv, ctx_lo=16,
                                         ctx_hi=64, pool_blocks=90)

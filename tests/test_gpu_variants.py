@@ -147,6 +147,30 @@ def test_whole_segments_with_short_tables(kv, bs):
     check(w, 5, label=f"whole/short/{kv}/bs{bs}/split")          # an override keeps the split
 
 
+# --------------------------------------------------------------------------
+# head_dim 256
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("hq,hkv,qlen,qlen_lo", [(16, 8, 1, None), (16, 2, 2, None), (8, 1, 2, 1), (4, 4, 4, None),
+                                                 (16, 1, 1, None)])
+def test_head_dim_256(kv, hq, hkv, qlen, qlen_lo):
+    w = generate(_ragged(kv=kv, qlen=qlen, qlen_lo=qlen_lo, hq=hq, hkv=hkv, d=256, batch=4, ctx_hi=1200,
+                         seed=50 + hq + qlen))
+    for groups in (0, 1, 7, 100000):
+        check(w, groups, label=f"d256/{hq}/{hkv}/q{qlen}/{kv}/g{groups}")
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_head_dim_256_window_sinks_and_whole_segments(bs):
+    w = generate(_ragged(bs, qlen=2, hq=16, hkv=2, d=256, window=50, sinks=True, batch=4, ctx_hi=900, seed=60))
+    for groups in (0, 3, 100000):
+        check(w, groups, label=f"d256/window/bs{bs}/g{groups}")
+    spec = _ragged(bs, qlen=1, hq=16, hkv=8, d=256, window=64, sinks=True, batch=64, ctx_hi=600, seed=61)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B.paged_attn_plan(64, 16, 8, 256, 1, 128, "bf16", cus)["whole_segments"] == 1
+    check(generate(spec), 0, label=f"d256/whole/bs{bs}")
+
+
 def test_ext_without_window_or_sinks_equals_decode_bitwise():
     w = generate(_ragged(qlen=2, seed=35)).to("cuda")
     a = torch.empty_like(w.q)
