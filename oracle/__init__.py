@@ -14,6 +14,7 @@ paged_attention  dense softmax attention gathered through the block table
 split_merge      split-context partial states and their log-sum-exp merge
 cache_write      new tokens' K/V into the paged cache through a slot mapping,
                  bf16 bit copies or per-token absmax fp8 e4m3fn quantisation
+prefill          packed variable-length prefill chunks over the paged cache
 
 Every function is pinned by ``-m "not gpu"`` tests against closed forms,
 invariants, brute force and independent library routines; no function here
@@ -23,10 +24,11 @@ from .formats import bf16_bits_to_f64, e4m3fn_bytes_to_f64, e4m3fn_table, e4m3fn
 from .paged_attention import BLOCK_SIZE, gather_sequence_kv, paged_decode_attention
 from .split_merge import merge_states, partial_state
 from .cache_write import e4m3fn_encode, quantize_rows_e4m3fn, reshape_and_cache
+from .prefill import paged_prefill_attention
 
 __all__ = [
     "BLOCK_SIZE", "bf16_bits_to_f64", "e4m3fn_bytes_to_f64", "e4m3fn_table",
     "e4m3fn_value", "gather_sequence_kv", "paged_decode_attention",
     "merge_states", "partial_state", "e4m3fn_encode", "quantize_rows_e4m3fn",
-    "reshape_and_cache",
+    "reshape_and_cache", "paged_prefill_attention",
 ]

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 from test_oracle import _bf16_bits, _case, _page, _sdpa_reference
+from test_oracle_prefill import prefill_battery
 from test_oracle_variants import variant_battery
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
@@ -39,6 +40,9 @@ MUTANTS = {
     "sink_not_in_max": ("paged_attention.py", "mx = np.maximum(mx, sk)", "mx = mx + 0 * sk"),
     "sink_dropped": ("paged_attention.py", "+ np.exp(sk - mx)", "+ 0 * np.exp(sk - mx)"),
     "block_size_fixed": ("paged_attention.py", "bs = np.asarray(cache).shape[1]", "bs = 16"),
+    "prefill_prefix_dropped": ("prefill.py", "[int(ctx[b])], [n], scale", "[n], [n], scale"),
+    "prefill_row_position": ("prefill.py", "Lt = int(ctx[b]) - n + int(t) + 1", "Lt = int(ctx[b]) - n + int(t)"),
+    "prefill_rows_reversed": ("prefill.py", "q_bits[cu[b]:cu[b + 1]][None]", "q_bits[cu[b]:cu[b + 1]][::-1][None]"),
     "e4m3_subnormal": ("formats.py", "man_field * 2.0 ** -9", "man_field * 2.0 ** -10"),
     "e4m3_bias": ("formats.py", "2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
     "e4m3_mantissa": ("formats.py", "(1.0 + man_field / 8.0)", "(1.0 + man_field / 16.0)"),
@@ -132,6 +136,9 @@ def _battery(orc) -> bool:
             return False
         # block sizes, sliding window, sinks
         if not variant_battery(orc):
+            return False
+        # packed prefill chunks
+        if not prefill_battery(orc):
             return False
     except Exception:
         return False

@@ -1,0 +1,138 @@
+"""Pins of the prefill oracle (oracle/prefill.py), CPU only: packed
+variable-length chunks over the paged cache against torch's float64
+attention with a causal mask, a pure-Python brute force, the chunking
+invariance of causal attention, and the agreement of its whole-sequence and
+single-row evaluations."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bf16_bits_to_f64, paged_prefill_attention
+from test_oracle import _bf16_bits
+from test_oracle_variants import _paged, _seqs
+
+
+def _pack(rng, lens, chunks, hq, d):
+    """q rows of the last chunks[b] positions of each sequence, packed."""
+    q = [_bf16_bits(rng.standard_normal((n, hq, d))) for n in chunks]
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return np.concatenate(q, axis=0) if sum(chunks) else np.zeros((0, hq, d), np.uint16), cu
+
+
+def _sdpa_packed(qp, cu, ks, vs, lens, scale, hq, hkv):
+    """torch float64 SDPA per sequence with an offset-causal boolean mask
+    (is_causal for chunks that are the whole sequence)."""
+    G = hq // hkv
+    out = np.full(qp.shape, np.nan)
+    for b in range(len(lens)):
+        n, L = int(cu[b + 1] - cu[b]), int(lens[b])
+        if n == 0:
+            continue
+        q = torch.from_numpy(bf16_bits_to_f64(qp[cu[b]:cu[b + 1]])).permute(1, 0, 2)     # [Hq, n, D]
+        k = torch.from_numpy(bf16_bits_to_f64(ks[b])).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        v = torch.from_numpy(bf16_bits_to_f64(vs[b])).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        if n == L:
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+        else:
+            mask = torch.arange(L)[None, :] <= (torch.arange(n)[:, None] + (L - n))
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+        out[cu[b]:cu[b + 1]] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 1)])
+def test_whole_and_chunked_prefill_match_torch_sdpa(hq, hkv):
+    rng = np.random.default_rng(hq * 10 + hkv)
+    d = 32
+    lens = (1, 17, 64, 150, 300)
+    chunks = (1, 17, 30, 150, 77)          # whole prompts and chunks after cached prefixes
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 3)
+    scale = np.float32(0.2)
+    out = paged_prefill_attention(qp, kp, vp, t, lens, cu, scale)
+    ref = _sdpa_packed(qp, cu, ks, vs, lens, float(scale), hq, hkv)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_matches_brute_force_tiny():
+    rng = np.random.default_rng(5)
+    hq, hkv, d = 4, 2, 8
+    lens, chunks = (3, 20), (3, 6)
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 32, 4)
+    out = paged_prefill_attention(qp, kp, vp, t, lens, cu, 0.5)
+    qf = bf16_bits_to_f64(qp)
+    for b, (L, n) in enumerate(zip(lens, chunks)):
+        kf, vf = bf16_bits_to_f64(ks[b]), bf16_bits_to_f64(vs[b])
+        for r in range(n):
+            p = L - n + r
+            for h in range(hq):
+                xs = [0.5 * sum(qf[cu[b] + r, h, e] * kf[j, h // 2, e] for e in range(d)) for j in range(p + 1)]
+                m = max(xs)
+                w = [math.exp(x - m) for x in xs]
+                ref = [sum(w[j] * vf[j, h // 2, e] for j in range(p + 1)) / sum(w) for e in range(d)]
+                np.testing.assert_allclose(out[cu[b] + r, h], ref, rtol=0, atol=1e-12)
+
+
+def test_chunking_a_prompt_does_not_change_its_rows():
+    """Causal attention of a prompt done in one piece equals the same prompt
+    done as two chunks, the second seeing the first through the cache."""
+    rng = np.random.default_rng(6)
+    hq, hkv, d, L = 8, 2, 32, 200
+    ks, vs = _seqs(rng, (L,), hkv, d)
+    q = _bf16_bits(rng.standard_normal((L, hq, d)))
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 5)
+    whole = paged_prefill_attention(q, kp, vp, t, [L], [0, L], 0.3)
+    first = paged_prefill_attention(q[:120], kp, vp, t, [120], [0, 120], 0.3)
+    second = paged_prefill_attention(q[120:], kp, vp, t, [L], [0, L - 120], 0.3)
+    np.testing.assert_allclose(np.concatenate([first, second]), whole, rtol=0, atol=1e-12)
+
+
+def test_single_row_evaluation_equals_whole_sequence_evaluation():
+    rng = np.random.default_rng(7)
+    hq, hkv, d = 4, 1, 16
+    lens, chunks = (90, 40), (60, 40)
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 6)
+    whole = paged_prefill_attention(qp, kp, vp, t, lens, cu, 0.25)
+    rows = [0, 13, 59]
+    part = paged_prefill_attention(qp, kp, vp, t, lens, cu, 0.25, batch_subset=[0], row_subset=rows)
+    np.testing.assert_allclose(part[rows], whole[rows], rtol=0, atol=1e-12)
+    assert np.isnan(part[60:]).all() and np.isnan(np.delete(part[:60], rows, axis=0)).all()
+
+
+def test_empty_chunks_and_bad_offsets():
+    rng = np.random.default_rng(8)
+    hq, hkv, d = 4, 2, 8
+    lens, chunks = (5, 30, 9), (0, 4, 0)
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 7)
+    out = paged_prefill_attention(qp, kp, vp, t, lens, cu, 0.5)
+    assert out.shape == (4, hq, d) and np.isfinite(out).all()
+    with pytest.raises(ValueError):
+        paged_prefill_attention(qp, kp, vp, t, lens, np.array([0, 4, 3, 4]), 0.5)
+    with pytest.raises(ValueError):
+        paged_prefill_attention(qp, kp, vp, t, lens, np.array([0, 1, 2, 3]), 0.5)
+
+
+def prefill_battery(orc) -> bool:
+    """The pins above in brief, against a (possibly mutated) oracle copy."""
+    rng = np.random.default_rng(9)
+    hq, hkv, d = 4, 2, 16
+    lens, chunks = (40, 70, 5), (40, 25, 5)
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 8)
+    scale = np.float32(0.3)
+    out = orc.paged_prefill_attention(qp, kp, vp, t, lens, cu, scale)
+    ref = _sdpa_packed(qp, cu, ks, vs, lens, float(scale), hq, hkv)
+    if not np.allclose(out, ref, rtol=0, atol=1e-12):
+        return False
+    part = orc.paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, batch_subset=[1], row_subset=[0, 24])
+    return bool(np.allclose(part[[cu[1], cu[1] + 24]], ref[[cu[1], cu[1] + 24]], rtol=0, atol=1e-12))
