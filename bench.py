@@ -27,22 +27,25 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: KV GB/s (% of HBM peak) and µs/call at batch 1"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the kernels and the planner that sets their launch shape
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", f)
-                  for f in ("pa_device.hip", "pa_cache.hip", "pa_host.cpp", "pa_internal.h")]
+                  for f in ("pa_device.hip", "pa_cache.hip", "pa_prefill.hip", "pa_host.cpp", "pa_internal.h")]
 
 
 def parse_args():
-    from paged_attention_decode_attn_amd.workloads import CONFIG_ORDER, NEXT_CONFIG_ORDER
+    from paged_attention_decode_attn_amd.workloads import CONFIG_ORDER, NEXT_CONFIG_ORDER, PREFILL_CONFIGS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER + NEXT_CONFIG_ORDER)
-    ap.add_argument("--op", default="decode", choices=["decode", "cache_write"],
+    ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER + NEXT_CONFIG_ORDER + list(PREFILL_CONFIGS))
+    ap.add_argument("--op", default="decode", choices=["decode", "cache_write", "prefill"],
                     help="decode: the attention call (default); cache_write: the paged KV-cache "
-                         "write before it, on --config's decode step or a bulk write (--bulk)")
+                         "write before it, on --config's decode step or a bulk write (--bulk); "
+                         "prefill: packed prefill chunks over the paged cache (--config prefill_8k or "
+                         "chunked_prefill)")
     ap.add_argument("--bulk", type=int, default=0,
                     help="with --op cache_write: write this many tokens to distinct random slots "
                          "of a large pool instead of the config's decode step")
@@ -112,7 +115,17 @@ def summarize(args):
     """Kernel-trace statistics and calibrated HBM traffic of one workload."""
     from paged_attention_decode_attn_amd.workloads import CONFIGS, generate, kv_bytes
     trace, fetch, write, cfetch, cwrite = args.summarize
-    if args.op == "cache_write":
+    flops = None
+    if args.op == "prefill":
+        from paged_attention_decode_attn_amd.workloads import PREFILL_CONFIGS, generate_prefill, prefill_flops
+        pspec = PREFILL_CONFIGS[args.config]
+        pf = generate_prefill(pspec)
+        spec, wname = pspec, pspec.name
+        flops = prefill_flops(pf.cache.context_lens, pf.chunk_lens, pspec.hq, pspec.head_dim)
+        kvb = prefill_bytes(pf)
+        kname, title, unit = "prefill_kernel", "paged prefill attention", "bytes (q, K/V once, out)"
+        kernels = (("%prefill_kernel%", "prefill_kernel"),)
+    elif args.op == "cache_write":
         spec, _, wname, kvb = cache_write_workload(args)
         kname, title, unit = "cache_write_kernel", "paged KV-cache write", "bytes (rows read + cache written)"
         kernels = (("%cache_write_kernel%", "cache_write_kernel"),)
@@ -157,7 +170,14 @@ def summarize(args):
         lines.append(f"| {label} | {fk:.0f} | {wk:.0f} | {hbm:.0f} |")
         record[label] = hbm
     part = [r for r in stats if kname in r[0]]
-    if part:
+    if part and flops is not None:
+        avg_ns = part[0][2]
+        lines += ["", f"Algorithmic flops per call: {flops}", "",
+                  f"{kname}: {flops / avg_ns / 1e3:.1f} TFLOP/s algorithmic "
+                  f"({100 * flops / avg_ns / 1e3 / MFMA_BF16_PEAK_TFLOPS:.1f}% of the 2.5 PFLOP/s dense bf16 "
+                  f"peak) at the traced average duration; HBM traffic {record.get(kname, 0) / kvb:.3f} x the "
+                  f"bytes that must move once (q, the chunks' K/V, out)."]
+    elif part:
         avg_ns = part[0][2]
         lines += ["", f"{kname}: {kvb / avg_ns:.1f} GB/s algorithmic "
                       f"({100 * kvb / avg_ns / HBM_PEAK_GBS:.1f}% of 8 TB/s) at the traced average "
@@ -177,6 +197,8 @@ def summarize(args):
                              "hbm_bytes_per_launch": round(record[kname]),
                              "algorithmic_bytes": kvb,
                              "calibration": {"fetch": round(cf, 4), "write": round(cw, 4)}}
+        if flops is not None:
+            allrec[wname]["algorithmic_flops"] = flops
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(allrec, f, indent=1, sort_keys=True)
     print("\n".join(lines))
@@ -225,6 +247,111 @@ def cpu_baseline(w, seconds: float):
 
 
 WRITE_METRIC = "paged KV-cache write: GB/s (% of HBM peak) and µs/call"
+PREFILL_METRIC = "paged prefill attention: TFLOP/s (% of dense bf16 MFMA peak) and ms/call"
+
+
+def prefill_bytes(pf) -> int:
+    """Bytes a prefill call must move at least once: the packed q rows and
+    outputs, and the K/V rows of every attended token (each sequence's
+    whole context) for every kv head."""
+    s = pf.spec
+    tokens = sum(int(x) for x in pf.cache.context_lens)
+    return 2 * pf.q.numel() * 2 + tokens * s.hkv * s.head_dim * 2 * 2
+
+
+def bench_prefill(args):
+    """Packed prefill chunks over the paged cache: one call per step, timed
+    eagerly and as a replayed HIP graph; the roofline is the matrix peak."""
+    import torch
+
+    from paged_attention_decode_attn_amd import binding as B
+    from paged_attention_decode_attn_amd.workloads import PREFILL_CONFIGS, generate_prefill, prefill_flops
+
+    spec = PREFILL_CONFIGS[args.config]
+    print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
+    pf = generate_prefill(spec)
+    flops = prefill_flops(pf.cache.context_lens, pf.chunk_lens, spec.hq, spec.head_dim)
+    nbytes = prefill_bytes(pf)
+    d = pf.to("cuda")
+    c = d.cache
+    out = torch.empty_like(d.q)
+
+    def call():
+        B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
+                             pf.max_query_len, pf.scale, out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    gs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gs):
+        for _ in range(args.steps):
+            B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
+                                 pf.max_query_len, pf.scale, out, stream=gs)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
+    del graph
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (min(ms, ms_graph) * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.hq, "kv_heads": spec.hkv,
+                   "head_dim": spec.head_dim, "kv_dtype": "bf16", "block_size": spec.block_size,
+                   "context_lens": [int(x) for x in pf.cache.context_lens],
+                   "chunk_lens": [int(x) for x in pf.chunk_lens]},
+        "ms_per_call_graph": round(ms_graph, 6), "flops_per_call": flops, "bytes_per_call": nbytes,
+        "wall_s_timed_region": round(t_wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(spec.name), "algorithmic_flops": flops,
+                     "kernel": "prefill_kernel",
+                     "timing": "faster of the eager and graph-replayed timed steps (one kernel per call)"},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import paged_prefill_attention
+        h = pf.cache
+
+        def bits(t):
+            return t.view(torch.int16).numpy().view("uint16") if t.dtype == torch.bfloat16 else t.numpy()
+        qb, kb, vb = bits(pf.q), bits(h.k_cache), bits(h.v_cache)
+        tables, ctx, cu = h.block_tables.numpy(), h.context_lens.numpy(), pf.cu_seqlens.numpy()
+        done, rows_done, t, r = 0, 0, 0.0, 0
+        b = spec.batch - 1
+        n = int(pf.chunk_lens[b])
+        with threadpool_limits(limits=1):
+            while t < args.cpu_seconds and rows_done < n:
+                rows = list(range(n - 1 - r, max(n - 1 - r - 8, -1), -1))    # the longest rows first
+                t0 = time.perf_counter()
+                paged_prefill_attention(qb, kb, vb, tables, ctx, cu, pf.scale, batch_subset=[b], row_subset=rows)
+                t += time.perf_counter() - t0
+                L = int(ctx[b])
+                done += sum(4 * spec.head_dim * spec.hq * (L - n + x + 1) for x in rows)
+                rows_done += len(rows)
+                r += len(rows)
+        res["cpu_baseline"] = {"value": done / t / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{rows_done} rows of sequence {b} evaluated one by one by the oracle "
+                                         f"({done} flops, {t:.1f} s, 1 thread)"}
+    print(json.dumps(res), flush=True)
 
 
 def bench_cache_write(args):
@@ -344,6 +471,9 @@ def main():
         return
     if args.op == "cache_write":
         bench_cache_write(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     spec = CONFIGS[args.config]

@@ -190,6 +190,49 @@ int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          const pa_tensor* out);
 
 /*
+ * paged_attn_prefill -- causal attention of packed prefill chunks over the
+ * paged KV cache (prefill and chunked prefill).  Sources: ATOM model
+ * operations guide, "Attention operations" (prefill always runs a
+ * variable-length flash-attention call; a unified paged prefill kernel is
+ * also listed), "Backend abstraction" (block tables and cumulative
+ * sequence lengths prepared for every prefill step) and its source-file
+ * list (a ragged prefill chunk's tokens placed in their own sequences).
+ *
+ *   q, out        bf16 [T, Hq, D] (D 64 or 128): the new tokens of all
+ *                 sequences packed row after row.
+ *   cu_seqlens_q  int32 [B + 1]: sequence b owns rows cu[b] .. cu[b+1]-1
+ *                 (n_b = cu[b+1] - cu[b] rows; cu[0] = 0, non-decreasing).
+ *                 They are the last n_b of its L_b = context_lens[b] tokens,
+ *                 whose K/V are already in the cache (the chunk's own rows
+ *                 written before the call; earlier chunks or a cached
+ *                 prefix make up the rest).  Row t sits at position
+ *                 L_b - n_b + t and attends to keys 0 .. L_b - n_b + t.
+ *   max_query_len the largest n_b (a bound is enough; it sizes the grid).
+ *   k_cache, v_cache, block_tables, context_lens, scale: as for
+ *                 paged_attn_decode (bf16 caches only; k_scale and v_scale
+ *                 must be NULL — an fp8 cache returns PA_ERR_UNSUPPORTED).
+ *   stream        hipStream_t as void*, NULL = default stream.
+ *
+ * Device-side preconditions, not checked: cu non-decreasing with
+ * cu[B] <= T, n_b <= L_b <= BS * W, max_query_len >= every n_b, table
+ * entries holding keys in [0, NB).  Rows t < n_b of every sequence are
+ * written; a row count clamped by these bounds leaves the rest unwritten,
+ * and no access leaves the tensors' extents.  No workspace; nothing is
+ * allocated.  Layout rules and errors as for paged_attn_decode; (Hq / Hkv)
+ * <= 64.
+ */
+int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                       const pa_tensor* block_tables, const pa_tensor* context_lens,
+                       const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                       const pa_tensor* k_scale, const pa_tensor* v_scale, pa_tensor* out, void* stream);
+
+/* paged_attn_check_prefill -- the host-side validation of paged_attn_prefill. */
+int paged_attn_check_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                             const pa_tensor* block_tables, const pa_tensor* context_lens,
+                             const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                             const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out);
+
+/*
  * paged_attn_reshape_and_cache -- write the new tokens' K and V rows into
  * the paged cache (the step that precedes paged_attn_decode in a decode
  * step).  Sources: ATOM model operations guide, "KV cache operations" (the

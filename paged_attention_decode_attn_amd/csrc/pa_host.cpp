@@ -223,6 +223,91 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     return PA_OK;
 }
 
+int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* bt,
+                     const pa_tensor* ctx, const pa_tensor* cu, int32_t max_query_len, float scale,
+                     const pa_tensor* ks, const pa_tensor* vs, const pa_tensor* out, PrefillProblem* pr) {
+    int st;
+    if ((st = check_desc(q, "q", PA_DTYPE_BF16, 3, 3, true))) return st;
+    if ((st = check_desc(out, "out", PA_DTYPE_BF16, 3, 3, true))) return st;
+    if (!kc) return fail(PA_ERR_NULL, "k_cache: descriptor is NULL");
+    if (!vc) return fail(PA_ERR_NULL, "v_cache: descriptor is NULL");
+    if (kc->dtype == PA_DTYPE_FP8_E4M3FN || (vc && vc->dtype == PA_DTYPE_FP8_E4M3FN))
+        return fail(PA_ERR_UNSUPPORTED, "prefill: an fp8 cache is not supported (bf16 only)");
+    if ((st = check_desc(kc, "k_cache", PA_DTYPE_BF16, 4, 4, true))) return st;
+    if ((st = check_desc(vc, "v_cache", PA_DTYPE_BF16, 4, 4, true))) return st;
+    if ((st = check_desc(bt, "block_tables", PA_DTYPE_INT32, 2, 2, true))) return st;
+    if ((st = check_desc(ctx, "context_lens", PA_DTYPE_INT32, 1, 1, true))) return st;
+    if ((st = check_desc(cu, "cu_seqlens_q", PA_DTYPE_INT32, 1, 1, true))) return st;
+    if (ks || vs) return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
+    if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "scale is not finite");
+    if (max_query_len < 0) return fail(PA_ERR_ARG, "max_query_len is negative");
+
+    const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i])
+            return fail(PA_ERR_SHAPE, "out: size %lld in dim %d, q has %lld", (long long)out->shape[i], i,
+                        (long long)q->shape[i]);
+    for (int i = 0; i < 4; ++i)
+        if (kc->shape[i] != vc->shape[i])
+            return fail(PA_ERR_SHAPE, "v_cache: size %lld in dim %d, k_cache has %lld", (long long)vc->shape[i], i,
+                        (long long)kc->shape[i]);
+    const int64_t NB = kc->shape[0], BS = kc->shape[1], Hkv = kc->shape[2];
+    if (BS < PA_BLOCK_SIZE || BS % PA_BLOCK_SIZE || BS > kMaxBlockSize)
+        return fail(PA_ERR_UNSUPPORTED, "k_cache: block size %lld, expected a multiple of 16 up to %d",
+                    (long long)BS, kMaxBlockSize);
+    if (kc->shape[3] != D)
+        return fail(PA_ERR_SHAPE, "k_cache: head_dim %lld, q has %lld", (long long)kc->shape[3], (long long)D);
+    if (D != 64 && D != 128)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: head_dim %lld, only 64 and 128 are supported", (long long)D);
+    if (Hkv < 1) return fail(PA_ERR_SHAPE, "k_cache: no kv heads");
+    if (Hq % Hkv != 0 || Hq == 0)
+        return fail(PA_ERR_UNSUPPORTED, "q_heads %lld is not a positive multiple of kv_heads %lld",
+                    (long long)Hq, (long long)Hkv);
+    const int64_t G = Hq / Hkv;
+    if (G > PA_MAX_ROWS)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: q_heads / kv_heads = %lld exceeds %d", (long long)G, PA_MAX_ROWS);
+    const int64_t B = bt->shape[0], W = bt->shape[1];
+    if (ctx->shape[0] != B)
+        return fail(PA_ERR_SHAPE, "context_lens: %lld entries, block_tables has %lld rows", (long long)ctx->shape[0],
+                    (long long)B);
+    if (cu->shape[0] != B + 1)
+        return fail(PA_ERR_SHAPE, "cu_seqlens_q: %lld entries, expected batch + 1 = %lld", (long long)cu->shape[0],
+                    (long long)(B + 1));
+    if (T >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: too many query rows");
+    if (B > 0 && T > 0) {
+        if (W < 1) return fail(PA_ERR_SHAPE, "block_tables: width must be >= 1");
+        if (NB < 1) return fail(PA_ERR_SHAPE, "k_cache: the pool has no blocks");
+        if (W > kMaxContext / BS) return fail(PA_ERR_UNSUPPORTED, "block_tables: width x block size too large");
+    }
+    if ((st = check_rows16(q, "q"))) return st;
+    if ((st = check_rows16(out, "out"))) return st;
+    if ((st = check_rows16(kc, "k_cache"))) return st;
+    if ((st = check_rows16(vc, "v_cache"))) return st;
+    if (bt->stride[1] != 1 && W > 1) return fail(PA_ERR_LAYOUT, "block_tables: innermost stride must be 1");
+    if (!aligned(bt->data, 4) || !aligned(ctx->data, 4) || !aligned(cu->data, 4))
+        return fail(PA_ERR_LAYOUT, "int32 metadata must be 4-byte aligned");
+    for (const pa_tensor* c : {kc, vc}) {
+        const int64_t span = (BS - 1) * c->stride[1] * 2 + (Hkv - 1) * c->stride[2] * 2 + D * 2;
+        if (span >= (int64_t(1) << 31))
+            return fail(PA_ERR_LAYOUT, "%s: one block spans more than 2 GiB", c == kc ? "k_cache" : "v_cache");
+        if (c->stride[0] * 2 >= (int64_t(1) << 32))
+            return fail(PA_ERR_LAYOUT, "%s: block stride of 4 GiB or more", c == kc ? "k_cache" : "v_cache");
+    }
+    if (pr) {
+        PrefillProblem& p = *pr;
+        p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.D = D; p.NB = NB; p.W = W; p.BS = BS;
+        p.scale = scale;
+        p.q = q->data; p.q_st = q->stride[0] * 2; p.q_sh = q->stride[1] * 2;
+        p.out = out->data; p.o_st = out->stride[0] * 2; p.o_sh = out->stride[1] * 2;
+        p.k = kc->data; p.k_sblk = kc->stride[0] * 2; p.k_stok = kc->stride[1] * 2; p.k_sh = kc->stride[2] * 2;
+        p.v = vc->data; p.v_sblk = vc->stride[0] * 2; p.v_stok = vc->stride[1] * 2; p.v_sh = vc->stride[2] * 2;
+        p.bt = static_cast<const int32_t*>(bt->data); p.bt_sb = bt->stride[0];
+        p.ctx = static_cast<const int32_t*>(ctx->data); p.ctx_s = ctx->stride[0];
+        p.cu = static_cast<const int32_t*>(cu->data); p.cu_s = cu->stride[0];
+    }
+    return PA_OK;
+}
+
 int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm, const pa_tensor* kc,
                    const pa_tensor* vc, const pa_tensor* ks, const pa_tensor* vs, WriteProblem* pr) {
     int st;
@@ -434,6 +519,14 @@ int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_
                          const pa_tensor* out) {
     return pa::validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
                         v_scale, sliding_window, sinks, out, nullptr);
+}
+
+int paged_attn_check_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                             const pa_tensor* block_tables, const pa_tensor* context_lens,
+                             const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                             const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out) {
+    return pa::validate_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len,
+                                scale, k_scale, v_scale, out, nullptr);
 }
 
 int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,

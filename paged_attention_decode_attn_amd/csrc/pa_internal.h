@@ -42,6 +42,25 @@ struct WriteProblem {
     float* vs; int64_t vs_sblk, vs_sh;
 };
 
+// A validated prefill call (paged_attn_prefill).
+struct PrefillProblem {
+    int64_t B, T, Hq, Hkv, G, D, NB, W, BS;
+    float scale;
+    const void* q;  int64_t q_st, q_sh;                // bytes
+    void* out;      int64_t o_st, o_sh;                // bytes
+    const void* k;  int64_t k_sblk, k_stok, k_sh;      // bytes
+    const void* v;  int64_t v_sblk, v_stok, v_sh;      // bytes
+    const int32_t* bt; int64_t bt_sb;                  // int32 elements
+    const int32_t* ctx; int64_t ctx_s;
+    const int32_t* cu;  int64_t cu_s;
+};
+
+int validate_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                     const pa_tensor* block_tables, const pa_tensor* context_lens,
+                     const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                     const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out,
+                     PrefillProblem* p);
+
 int validate_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
                    const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* k_scale,
                    const pa_tensor* v_scale, WriteProblem* p);

@@ -1,0 +1,413 @@
+// Paged prefill attention for gfx950: packed variable-length query chunks
+// (sequence b owns rows cu[b] .. cu[b+1]-1, the last n_b of its L_b cached
+// tokens) attend causally to their sequence's keys through the block table.
+//
+// The operation: ATOM model operations guide, "Attention operations"
+// (prefill always runs a variable-length flash-attention call; the kernel
+// table also lists a unified paged prefill kernel) and "Backend
+// abstraction" (block tables and cumulative sequence lengths prepared for
+// every prefill step); its source-file list places a ragged prefill chunk's
+// tokens in their own sequences.
+//
+// Workgroup = 4 waves on one (sequence, kv head, block of 4P positions).
+// Wave w owns positions p0 + wP .. p0 + wP + P - 1 of the chunk for all G
+// query heads of the kv head: 64 rows (row r = position r / G, head r % G,
+// P = 64 / G), the N side of 16x16 MFMA tiles as in the decode kernel.  The
+// workgroup walks the keys in 32-token tiles: all 256 threads load the
+// tile's K and V rows (16-byte buffer loads, sub-block addressing through a
+// per-wave block-table window) into one of two padded LDS buffers while the
+// waves compute on the other, so every K/V byte read from L2 serves 256
+// rows.  Per tile and wave: S^T = K Q^T and O^T += V^T P^T with
+// v_mfma_f32_16x16x32_bf16, online softmax in base 2 with a lazy rescale.
+// A wave skips the tiles past its last position; tiles that reach past its
+// first position's causal limit take the masked step.  Keys past L_b are
+// zero-filled in LDS, so unwritten cache slots never reach the output.
+// Workgroups are ordered longest first (the highest position blocks).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr unsigned kSelLo = 0x05040100u;   // v_perm: (src1.lo16, src0.lo16)
+constexpr unsigned kSelHi = 0x07060302u;   // v_perm: (src1.hi16, src0.hi16)
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
+constexpr float kRescaleLog2 = 8.0f;       // lazy rescale threshold (log2 units)
+constexpr int kTile = 32;                  // keys per tile (two 16-token sub-blocks)
+constexpr int kWaves = 4;                  // waves per workgroup
+constexpr int kRows = 64;                  // query rows per wave (four 16-row tiles)
+constexpr int kNT = kRows / 16;
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+struct PrefillArgs {
+    const char* q;   int64_t q_st, q_sh;              // bytes
+    char* out;       int64_t o_st, o_sh;              // bytes
+    const char* k;   int64_t k_stok, k_sh;            // bytes
+    const char* v;   int64_t v_stok, v_sh;
+    uint32_t k_sblk, v_sblk, k_ssub, v_ssub;          // block / 16-token sub-block strides, bytes
+    const int32_t* bt; int64_t bt_sb;
+    const int32_t* ctx; int64_t ctx_s;
+    const int32_t* cu;  int64_t cu_s;
+    float scale_log2;                                 // |scale| * log2(e)
+    int32_t q_neg;                                    // scale < 0: negate q
+    int32_t k_span, v_span;                           // bytes of one (sub-block, head) slice
+    int32_t B, Hkv, G, P, qblocks, bsub, wsub, NB, T;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
+    f32x2 f = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// LDS row stride of a K or V tile: a 16-byte pad per row spreads the rows
+// that 16 lanes read at one column over the banks.
+template <int D> constexpr int kRowBytes = 2 * D + 16;
+template <int D> constexpr int kTileBytes = kTile * kRowBytes<D>;
+// 16-byte pieces of one row, and per thread of a tile
+template <int D> constexpr int kPieces = D / 8;
+template <int D> constexpr int kPerThread = kTile * kPieces<D> / (64 * kWaves);
+
+// The block-table window: lane l holds sub-block 2*t0 + l of sequence b.
+struct BlockRef {
+    int blk, sub;
+};
+
+__device__ __forceinline__ BlockRef load_window(const PrefillArgs& a, int b, int t0, int lane) {
+    const int idx = min(2 * t0 + lane, a.wsub - 1);
+    const int e = a.bsub > 1 ? idx / a.bsub : idx;
+    const int v = a.bt[(int64_t)b * a.bt_sb + e];
+    return BlockRef{min(max(v, 0), a.NB - 1), idx - e * a.bsub};
+}
+
+// Global K/V pieces of tile `tile` for this thread: piece i is token
+// (tid + 256 i) / kPieces of the tile, 16-byte column (tid + 256 i) %
+// kPieces; every piece of one load instruction lies in one sub-block per
+// wave, so its block id is a wave-uniform readlane of the window.
+template <int D>
+struct Pieces {
+    u32x4 k[kPerThread<D>], v[kPerThread<D>];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(Pieces<D>& pc, const PrefillArgs& a, const char* kh, const char* vh,
+                                          const BlockRef& br, int tile, int wbase, int L, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPerThread<D>; ++i) {
+        const int piece = tid + 64 * kWaves * i;
+        const int tok = piece / kPieces<D>, col = piece % kPieces<D>;
+        const int sb = __builtin_amdgcn_readfirstlane(tok >> 4);   // uniform per wave
+        const int rel = 2 * tile + sb - wbase;                     // window lane of the sub-block
+        const uint32_t blk = (uint32_t)__builtin_amdgcn_readlane(br.blk, rel);
+        const uint32_t sub = (uint32_t)__builtin_amdgcn_readlane(br.sub, rel);
+        const int tok0 = kTile * tile + 16 * sb;                   // first token of the sub-block
+        const bool live = tok0 < L;
+        const Rsrc rk = make_rsrc(kh + (uint64_t)blk * a.k_sblk + sub * a.k_ssub, live ? a.k_span : 0);
+        const Rsrc rv = make_rsrc(vh + (uint64_t)blk * a.v_sblk + sub * a.v_ssub, live ? a.v_span : 0);
+        const unsigned ko = (unsigned)((tok & 15) * a.k_stok) + 16u * col;
+        const unsigned vo = (unsigned)((tok & 15) * a.v_stok) + 16u * col;
+        pc.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
+        pc.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0);
+    }
+}
+
+// Store the pieces into an LDS tile buffer; keys at or past L become zeros
+// (their slots may hold anything).
+template <int D>
+__device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Pieces<D>& pc, int tile, int L, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPerThread<D>; ++i) {
+        const int piece = tid + 64 * kWaves * i;
+        const int tok = piece / kPieces<D>, col = piece % kPieces<D>;
+        const bool keep = kTile * tile + tok < L;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(lds_k + tok * kRowBytes<D> + 16 * col) = keep ? pc.k[i] : z;
+        *reinterpret_cast<u32x4*>(lds_v + tok * kRowBytes<D> + 16 * col) = keep ? pc.v[i] : z;
+    }
+}
+
+template <int D>
+struct Acc {
+    float m[kNT], l[kNT];
+    f32x4 o[kNT][D / 16];
+};
+
+// One 32-key tile of one wave: K fragments (A operand, token = lane % 16,
+// head_dim 8 * (lane / 16) ... of each 32-wide step) and V rows (token slot
+// 4 * (lane / 16) + i of each sub-block, head_dim (D/16) * (lane % 16) ...)
+// read from LDS, then the decode kernel's step: S^T = K Q^T, base-2 online
+// softmax with a lazy rescale, O^T += V^T P^T.  masked (wave-uniform): some
+// key of the tile lies past some row's causal limit.  One copy of the step
+// serves both cases: two inlined copies would not fit the register file.
+template <int D>
+__device__ __forceinline__ void tile_step(Acc<D>& s, const u32x4 (&qf)[kNT][D / 32], const char* lds_k,
+                                          const char* lds_v, const int (&lim)[kNT], int kbase, float c, int lane,
+                                          bool masked) {
+    constexpr int J = D / 16;
+    const int n16 = lane & 15, grp = lane >> 4;
+    bf16x8 kf[2][D / 32];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            kf[mt][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                lds_k + (16 * mt + n16) * kRowBytes<D> + 2 * (32 * kk + 8 * grp)));
+    typedef typename std::conditional<D == 128, u32x4, u32x2>::type VT;
+    VT v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const VT*>(lds_v + (16 * (i >> 2) + 4 * grp + (i & 3)) * kRowBytes<D> +
+                                            2 * (D / 16) * n16);
+
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        // one row tile at a time: interleaving the four tiles' score and
+        // softmax work would not fit the register file next to the
+        // accumulators and query fragments
+        if (nt > 0) __builtin_amdgcn_sched_barrier(0);
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const bf16x8 qb = as_bf16x8(qf[nt][kk]);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qb, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qb, s1, 0, 0, 0);
+        }
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[i] = s0[i];
+            y[4 + i] = s1[i];
+        }
+        if (masked) {
+            // keys past the row's causal limit: -inf, whose exponent below
+            // is 0 (c > 0, so c * -inf stays -inf)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int tok = kbase + 16 * (i >> 2) + 4 * grp + (i & 3);
+                y[i] = tok > lim[nt] ? -__builtin_inff() : y[i];
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mxs = c * mx;
+        if (__any(mxs > s.m[nt] + kRescaleLog2)) {
+            const float m_new = fmaxf(s.m[nt], mxs);
+            const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(s.m[nt] - m_new);
+            s.l[nt] *= alpha;
+#pragma unroll
+            for (int j = 0; j < J; ++j) s.o[nt][j] *= alpha;
+            s.m[nt] = m_new;
+        }
+        const float neg_m = s.m[nt] == -__builtin_inff() ? 0.f : -s.m[nt];
+        float p[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c, neg_m));
+            psum += p[i];
+        }
+        s.l[nt] += psum;
+        u32x4 pw;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pw[w] = pack_bf16_rne(p[2 * w], p[2 * w + 1]);
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            u32x4 x;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                x[q] = __builtin_amdgcn_perm(v[2 * q + 1][j / 2], v[2 * q][j / 2], (j & 1) ? kSelHi : kSelLo);
+            s.o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x), pb, s.o[nt][j], 0, 0, 0);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
+    constexpr int J = D / 16;
+    extern __shared__ __align__(16) char lds[];            // [2 buffers][K tile, V tile]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, grp = lane >> 4;
+    // longest first: the highest position blocks of every (sequence, kv head)
+    const int pairs = a.B * a.Hkv;
+    const int qb = a.qblocks - 1 - (int)(blockIdx.x / pairs);
+    const int pr = blockIdx.x % pairs;
+    const int b = pr / a.Hkv, g = pr - b * a.Hkv;
+    // the chunk's rows, clamped to the packed rows and to the sequence
+    const int c0 = min(max(a.cu[(int64_t)b * a.cu_s], 0), a.T);
+    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
+    const int n = min(min(a.cu[(int64_t)(b + 1) * a.cu_s], a.T) - c0, L);
+    const int p0 = qb * kWaves * a.P;                      // first position (in the chunk) of the workgroup
+    if (n <= 0 || p0 >= n) return;
+    const int pw = p0 + wave * a.P;                        // first position of this wave
+    // keys the workgroup needs: below L - n + min(p0 + 4P, n); this wave's
+    // rows need keys below L - n + min(pw + P, n) (none if pw >= n)
+    const int kend = L - n + min(p0 + kWaves * a.P, n);
+    const int wend = pw < n ? L - n + min(pw + a.P, n) : 0;
+    const int ntiles = (kend + kTile - 1) / kTile;
+    const int wtiles = (wend + kTile - 1) / kTile;
+    // tiles wholly at or below every row's causal limit: the first row's
+    // limit is L - n + pw
+    const int wclean = pw < n ? (L - n + pw + 1) / kTile : 0;
+
+    // query fragments and per-row causal limits
+    u32x4 qf[kNT][D / 32];
+    int lim[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int row = 16 * nt + n16;
+        const int t = row / a.G, hl = row - t * a.G;
+        const int pos = pw + t;
+        const bool live = t < a.P && pos < n;
+        lim[nt] = live ? L - n + pos : L - 1;
+        const char* qrow = a.q + (int64_t)(c0 + (live ? pos : 0)) * a.q_st + (int64_t)(g * a.G + hl) * a.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            u32x4 x = live ? *reinterpret_cast<const u32x4*>(qrow + 2 * (32 * kk + 8 * grp)) : u32x4{0u, 0u, 0u, 0u};
+            qf[nt][kk] = a.q_neg ? x ^ 0x80008000u : x;
+        }
+    }
+
+    const char* kh = a.k + (int64_t)g * a.k_sh;
+    const char* vh = a.v + (int64_t)g * a.v_sh;
+    // buffer i: K tile at lds + 2i * TB, V tile at lds + (2i + 1) * TB (plain
+    // arithmetic on the shared array keeps the accesses in LDS instructions)
+    constexpr int TB = kTileBytes<D>;
+
+    Acc<D> s;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        s.m[nt] = -__builtin_inff();
+        s.l[nt] = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) s.o[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float c = a.scale_log2;
+
+    // tile 0 into buffer 0
+    BlockRef br = load_window(a, b, 0, lane);
+    int wbase = 0;                                         // first sub-block of the window
+    Pieces<D> pc;
+    load_tile<D>(pc, a, kh, vh, br, 0, wbase, L, tid);
+    store_tile<D>(lds, lds + TB, pc, 0, L, tid);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const bool more = j + 1 < ntiles;
+        if (more) {
+            // a window holds 64 sub-blocks = 32 tiles
+            if (((j + 1) & 31) == 0) {
+                br = load_window(a, b, j + 1, lane);
+                wbase = 2 * (j + 1);
+            }
+            load_tile<D>(pc, a, kh, vh, br, j + 1, wbase, L, tid);
+        }
+        const int cur = (j & 1) * 2 * TB, nxt = 2 * TB - cur;
+        if (j < wtiles) tile_step<D>(s, qf, lds + cur, lds + cur + TB, lim, kTile * j, c, lane, j >= wclean);
+        if (more) store_tile<D>(lds + nxt, lds + nxt + TB, pc, j + 1, L, tid);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds d = J * (4 * grp + i) + jj of row 16 * nt + n16
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        float lt = s.l[nt];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const int row = 16 * nt + n16;
+        const int t = row / a.G, hl = row - t * a.G;
+        const int pos = pw + t;
+        if (!(t < a.P && pos < n)) continue;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        char* orow = a.out + (int64_t)(c0 + pos) * a.o_st + (int64_t)(g * a.G + hl) * a.o_sh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = J * (4 * grp + i);
+            if constexpr (J == 8) {
+                u32x4 wv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wv[e] = pack_bf16_rne(s.o[nt][2 * e][i] * inv, s.o[nt][2 * e + 1][i] * inv);
+                *reinterpret_cast<u32x4*>(orow + 2 * d0) = wv;
+            } else {
+                u32x2 wv;
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    wv[e] = pack_bf16_rne(s.o[nt][2 * e][i] * inv, s.o[nt][2 * e + 1][i] * inv);
+                *reinterpret_cast<u32x2*>(orow + 2 * d0) = wv;
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                       const pa_tensor* block_tables, const pa_tensor* context_lens,
+                       const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                       const pa_tensor* k_scale, const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+    using namespace pa;
+    PrefillProblem p;
+    int st = validate_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len, scale,
+                              k_scale, v_scale, out, &p);
+    if (st) return st;
+    if (p.B == 0 || p.T == 0 || max_query_len == 0) return PA_OK;
+    PrefillArgs a;
+    a.q = static_cast<const char*>(p.q); a.q_st = p.q_st; a.q_sh = p.q_sh;
+    a.out = static_cast<char*>(p.out); a.o_st = p.o_st; a.o_sh = p.o_sh;
+    a.k = static_cast<const char*>(p.k); a.k_stok = p.k_stok; a.k_sh = p.k_sh;
+    a.v = static_cast<const char*>(p.v); a.v_stok = p.v_stok; a.v_sh = p.v_sh;
+    a.k_sblk = (uint32_t)p.k_sblk; a.v_sblk = (uint32_t)p.v_sblk;
+    a.k_ssub = (uint32_t)(PA_BLOCK_SIZE * p.k_stok); a.v_ssub = (uint32_t)(PA_BLOCK_SIZE * p.v_stok);
+    a.bt = p.bt; a.bt_sb = p.bt_sb;
+    a.ctx = p.ctx; a.ctx_s = p.ctx_s;
+    a.cu = p.cu; a.cu_s = p.cu_s;
+    // kept positive so that a masked score's -inf times it stays -inf (a zero
+    // scale becomes a negligible one: every score then weighs the same)
+    a.scale_log2 = std::max(std::fabs(p.scale) * kLog2e, 1e-30f);
+    a.q_neg = p.scale < 0.f;
+    a.k_span = (int32_t)(15 * p.k_stok + 2 * p.D);
+    a.v_span = (int32_t)(15 * p.v_stok + 2 * p.D);
+    a.B = (int32_t)p.B; a.Hkv = (int32_t)p.Hkv; a.G = (int32_t)p.G;
+    a.P = (int32_t)(kRows / p.G);
+    a.qblocks = (int32_t)((max_query_len + kWaves * a.P - 1) / (kWaves * a.P));
+    a.bsub = (int32_t)(p.BS / PA_BLOCK_SIZE);
+    a.wsub = (int32_t)(p.W * a.bsub);
+    a.NB = (int32_t)std::min<int64_t>(p.NB, INT32_MAX);
+    a.T = (int32_t)p.T;
+    const int64_t grid = (int64_t)a.qblocks * p.B * p.Hkv;
+    if (grid >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: grid too large");
+    const void* fn = p.D == 128 ? reinterpret_cast<const void*>(&prefill_kernel<128>)
+                                : reinterpret_cast<const void*>(&prefill_kernel<64>);
+    const size_t lds = 4 * (size_t)(p.D == 128 ? kTileBytes<128> : kTileBytes<64>);
+    void* args[] = {&a};
+    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kWaves), args, lds,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PA_OK;
+}
+
+}  // extern "C"

@@ -51,7 +51,8 @@ BLOCK = 16
 FP8_MAX = 448.0
 
 __all__ = ["WorkloadSpec", "Workload", "CONFIGS", "CONFIG_ORDER", "NEXT_CONFIG_ORDER", "generate", "kv_bytes",
-           "CacheWrite", "generate_cache_write", "write_bytes"]
+           "CacheWrite", "generate_cache_write", "write_bytes", "PrefillSpec", "Prefill", "PREFILL_CONFIGS",
+           "generate_prefill", "prefill_flops"]
 
 
 @dataclass(frozen=True)
@@ -403,3 +404,101 @@ def write_bytes(slot_mapping, hkv: int, head_dim: int, kv_dtype: str, num_blocks
     else:
         per_token += 2 * hkv * head_dim * 2
     return n * per_token
+
+
+# ----------------------------------------------------------------------------
+# prefill (chunked prefill) inputs
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PrefillSpec:
+    """Packed prefill chunks over a paged cache.  Sequence b's chunk holds
+    the last n_b of its L_b tokens: L_b uniform in [ctx_lo, ctx_hi]; n_b =
+    L_b for whole prompts (chunk_lo = chunk_hi = 0), else uniform in
+    [chunk_lo, chunk_hi] clamped to L_b."""
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    head_dim: int
+    ctx_lo: int
+    ctx_hi: int
+    chunk_lo: int
+    chunk_hi: int
+    pool_blocks: int
+    seed: int
+    block_size: int = BLOCK
+
+    def cache_spec(self) -> WorkloadSpec:
+        return WorkloadSpec(self.name, batch=self.batch, qlen=1, hq=self.hq, hkv=self.hkv,
+                            head_dim=self.head_dim, kv_dtype="bf16", ctx_lo=self.ctx_lo, ctx_hi=self.ctx_hi,
+                            pool_blocks=self.pool_blocks, seed=self.seed, block_size=self.block_size)
+
+    def replace(self, **kw) -> "PrefillSpec":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclass
+class Prefill:
+    spec: PrefillSpec
+    cache: Workload              # its caches, tables and context lengths (its q is unused)
+    q: torch.Tensor              # bf16 [T, Hq, D], packed
+    cu_seqlens: torch.Tensor     # int32 [B + 1]
+    max_query_len: int
+    scale: float
+
+    def to(self, device) -> "Prefill":
+        return Prefill(self.spec, self.cache.to(device), self.q.to(device), self.cu_seqlens.to(device),
+                       self.max_query_len, self.scale)
+
+    @property
+    def chunk_lens(self) -> torch.Tensor:
+        return (self.cu_seqlens[1:] - self.cu_seqlens[:-1]).cpu()
+
+
+# A Llama-3-8B-shaped whole 8192-token prompt, and chunked prefill of four
+# sequences (2048-token chunks after cached prefixes, up to 16k tokens),
+# 64 query / 8 kv heads: the prefill shapes of the pages' engine (a
+# variable-length prefill call over the paged cache).
+PREFILL_CONFIGS = {
+    "prefill_8k": PrefillSpec("prefill_b1_q32kv8_d128_prompt8192_bf16", batch=1, hq=32, hkv=8, head_dim=128,
+                              ctx_lo=8192, ctx_hi=8192, chunk_lo=0, chunk_hi=0, pool_blocks=600, seed=21),
+    "chunked_prefill": PrefillSpec("chunked_prefill_b4_q64kv8_d128_chunk2048_ctx2k-16k_bf16", batch=4, hq=64,
+                                   hkv=8, head_dim=128, ctx_lo=2048, ctx_hi=16384, chunk_lo=2048,
+                                   chunk_hi=2048, pool_blocks=4200, seed=22),
+}
+
+
+def generate_prefill(spec: PrefillSpec, *, context_lens=None, chunk_lens=None) -> Prefill:
+    """The cache as ``generate`` draws it for ``spec.cache_spec()`` (steps 1-5),
+    then from a generator seeded with ``seed + 2000``: the chunk lengths
+    (unless whole prompts or given) and the packed q rows (N(0, 1) -> bf16)."""
+    cache = generate(spec.cache_spec(), context_lens=context_lens)
+    gen = torch.Generator("cpu").manual_seed(spec.seed + 2000)
+    L = cache.context_lens.to(torch.int64)
+    if chunk_lens is not None:
+        n = torch.as_tensor(chunk_lens, dtype=torch.int64).clone()
+    elif spec.chunk_hi == 0:
+        n = L.clone()
+    else:
+        n = torch.randint(spec.chunk_lo, spec.chunk_hi + 1, (spec.batch,), generator=gen, dtype=torch.int64)
+    n = torch.minimum(n, L)
+    if bool((n < 0).any()):
+        raise ValueError("negative chunk length")
+    cu = torch.zeros(spec.batch + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(n, 0)
+    T = int(cu[-1])
+    q = torch.randn(T, spec.hq, spec.head_dim, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    return Prefill(spec, cache, q, cu.to(torch.int32), int(n.max()) if spec.batch else 0,
+                   1.0 / math.sqrt(spec.head_dim))
+
+
+def prefill_flops(context_lens, chunk_lens, hq: int, head_dim: int) -> int:
+    """Algorithmic flops of one prefill call: every (row, visible key, query
+    head) pair costs 2 * D for the score and 2 * D for the value update; row
+    t of a chunk of n rows in a sequence of L tokens sees L - n + t + 1 keys."""
+    total = 0
+    for L, n in zip(torch.as_tensor(context_lens).tolist(), torch.as_tensor(chunk_lens).tolist()):
+        n = min(int(n), int(L))
+        # sum over t < n of (L - n + t + 1)
+        total += n * (L - n) + n * (n + 1) // 2
+    return 4 * head_dim * hq * total

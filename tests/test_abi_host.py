@@ -408,3 +408,50 @@ def test_cache_write_validation_rejects_bad_arguments():
     assert status(kv="fp8", k_scale=torch.ones(NB, 16, HKV)) == "PA_ERR_LAYOUT"       # slot dim not contiguous
     assert status(k_new=torch.zeros(5, HKV, 2 * D, dtype=torch.bfloat16)[:, :, 1:D + 1]) == "PA_ERR_LAYOUT"
     assert status(k_new=None) == "PA_ERR_NULL"
+
+
+def _prefill_tensors(T=20, hq=8, hkv=2, d=128, block=16, B_=3):
+    q = torch.zeros(T, hq, d, dtype=torch.bfloat16)
+    kc = torch.zeros(NB, block, hkv, d, dtype=torch.bfloat16)
+    vc = torch.zeros(NB, block, hkv, d, dtype=torch.bfloat16)
+    bt = torch.zeros(B_, W, dtype=torch.int32)
+    ctx = torch.full((B_,), 30, dtype=torch.int32)
+    cu = torch.tensor([0, 5, 12, T][:B_ + 1], dtype=torch.int32)
+    return dict(q=q, k_cache=kc, v_cache=vc, block_tables=bt, context_lens=ctx, cu_seqlens_q=cu,
+                max_query_len=8, scale=0.1, out=torch.empty_like(q))
+
+
+def test_prefill_validation():
+    def status(**over):
+        t = _prefill_tensors()
+        t.update(over)
+        return B.STATUS_NAMES[B.paged_attn_check_prefill(**t)]
+    assert status() == "PA_OK"
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**_prefill_tensors(d=64, hq=64, hkv=1))] == "PA_OK"
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**_prefill_tensors(block=64))] == "PA_OK"
+    assert status(cu_seqlens_q=torch.tensor([0, 5, 20], dtype=torch.int32)) == "PA_ERR_SHAPE"     # B + 1 entries
+    assert status(cu_seqlens_q=torch.tensor([0, 5, 12, 20], dtype=torch.int64)) == "PA_ERR_DTYPE"
+    assert status(max_query_len=-1) == "PA_ERR_ARG"
+    assert status(scale=float("nan")) == "PA_ERR_ARG"
+    assert status(out=torch.zeros(19, 8, 128, dtype=torch.bfloat16)) == "PA_ERR_SHAPE"
+    assert status(k_cache=torch.zeros(NB, 16, 2, 128, dtype=torch.uint8)) == "PA_ERR_UNSUPPORTED"   # fp8
+    assert status(k_scale=torch.ones(NB, 16, 2)) == "PA_ERR_ARG"
+    t = _prefill_tensors(d=256)
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"
+    t = _prefill_tensors(hq=6, hkv=4)
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"
+    t = _prefill_tensors(hq=130, hkv=1)
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"                 # ratio > 64
+    t = _prefill_tensors()
+    t["q"] = t["q"].transpose(1, 2).contiguous().transpose(1, 2)
+    t["out"] = torch.empty_like(t["q"])
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_LAYOUT"
+
+
+def test_prefill_flops_closed_form():
+    from paged_attention_decode_attn_amd.workloads import prefill_flops
+    # a whole prompt of n tokens: n (n + 1) / 2 (row, key) pairs
+    assert prefill_flops([100], [100], 8, 64) == 4 * 64 * 8 * 5050
+    # a chunk of 10 after 90 cached tokens: rows see 91 .. 100 keys
+    assert prefill_flops([100], [10], 1, 1) == 4 * sum(range(91, 101))
+    assert prefill_flops([5, 7], [0, 7], 2, 2) == 4 * 2 * 2 * 28

@@ -1,0 +1,204 @@
+"""GPU parity of paged prefill (paged_attn_prefill) against the CPU oracle:
+packed variable-length chunks after cached prefixes, every q/kv head ratio,
+head_dim 64 and 128, block sizes, chunk-length edges around the 32-key tile
+and the 4-wave position block, NaN in unread memory.  Tolerance as for
+decode: |gpu - ref| <= 1e-2 + 1e-2 |ref| on every produced element,
+relative L2 <= 1e-2; rows outside every chunk keep a canary."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from _parity import ATOL, CANARY, REL_L2_MAX, RTOL, note
+from oracle import paged_prefill_attention
+from paged_attention_decode_attn_amd import binding as B
+from paged_attention_decode_attn_amd.workloads import PREFILL_CONFIGS, generate_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    t = t.detach().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _oracle(p, batch_subset=None, row_subset=None):
+    c = p.cache
+    return paged_prefill_attention(_bits(p.q), _bits(c.k_cache), _bits(c.v_cache), c.block_tables.numpy(),
+                                   c.context_lens.numpy(), p.cu_seqlens.numpy(), p.scale,
+                                   batch_subset=batch_subset, row_subset=row_subset)
+
+
+def _run(p, max_query_len=None, extra_rows=0):
+    d = p.to("cuda")
+    T, H, D = d.q.shape
+    q = d.q
+    if extra_rows:
+        q = torch.cat([q, torch.zeros(extra_rows, H, D, dtype=q.dtype, device=q.device)])
+    out = torch.empty_like(q)
+    out.view(torch.int16).fill_(CANARY)
+    B.paged_attn_prefill(q, d.cache.k_cache, d.cache.v_cache, d.cache.block_tables, d.cache.context_lens,
+                         d.cu_seqlens, p.max_query_len if max_query_len is None else max_query_len, p.scale,
+                         out)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def _compare(out, ref, label, rows=None):
+    g = out.float().numpy().astype(np.float64)
+    sel = np.arange(ref.shape[0]) if rows is None else np.asarray(rows)
+    gb, rb = g[sel], ref[sel]
+    assert np.all(np.isfinite(rb)), f"{label}: oracle rows not finite"
+    err = np.abs(gb - rb)
+    bad = ~(err <= ATOL + RTOL * np.abs(rb))
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{label}: {bad.sum()} elements out of tolerance, first at row/head/d {tuple(i)}: "
+                             f"gpu {gb[tuple(i)]!r} ref {rb[tuple(i)]!r}")
+    rel = math.sqrt(float((err ** 2).sum()) / max(float((rb ** 2).sum()), 1e-300))
+    assert rel <= REL_L2_MAX, f"{label}: relative L2 {rel:.3e}"
+
+
+def _check(p, label, **kw):
+    note(f"[gpu] prefill {label}: ctx={p.cache.context_lens.tolist()[:6]} chunks={p.chunk_lens.tolist()[:6]} "
+         f"heads={p.spec.hq}/{p.spec.hkv} d={p.spec.head_dim} bs={p.spec.block_size}")
+    out = _run(p, **kw)
+    _compare(out, _oracle(p), label)
+    return out
+
+
+SMALL = PREFILL_CONFIGS["chunked_prefill"].replace(batch=3, ctx_lo=1, ctx_hi=400, chunk_lo=1, chunk_hi=300,
+                                                   pool_blocks=100)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (16, 1), (64, 1), (12, 4), (40, 8)])
+def test_head_ratios(d, hq, hkv):
+    p = generate_prefill(SMALL.replace(hq=hq, hkv=hkv, head_dim=d, seed=hq + hkv + d))
+    _check(p, f"heads{hq}/{hkv}/d{d}")
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+def test_block_sizes(bs):
+    p = generate_prefill(SMALL.replace(block_size=bs, pool_blocks=3 * (-(-400 // bs)) + 2, seed=30 + bs))
+    _check(p, f"bs{bs}")
+
+
+def test_whole_prompts():
+    p = generate_prefill(SMALL.replace(chunk_lo=0, chunk_hi=0, seed=40))
+    assert torch.equal(p.chunk_lens, p.cache.context_lens.to(torch.int32))
+    _check(p, "whole prompts")
+
+
+EDGE_CHUNKS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (64, 8)])
+def test_chunk_length_edges(hq, hkv):
+    ctx = [max(c, 1) + 37 * i for i, c in enumerate(EDGE_CHUNKS)]
+    spec = SMALL.replace(batch=len(ctx), hq=hq, hkv=hkv, ctx_lo=1, ctx_hi=max(ctx), pool_blocks=400, seed=41)
+    p = generate_prefill(spec, context_lens=ctx, chunk_lens=EDGE_CHUNKS)
+    _check(p, f"edges/{hq}/{hkv}")
+
+
+def test_larger_max_query_len_and_rows_outside_every_chunk():
+    p = generate_prefill(SMALL.replace(seed=42))
+    out = _run(p, max_query_len=p.max_query_len + 300, extra_rows=7)
+    T = p.q.shape[0]
+    _compare(out[:T], _oracle(p), "bigger max_query_len")
+    assert torch.all(out[T:].view(torch.int16) == CANARY)
+
+
+def test_nan_in_unread_memory_never_reaches_output():
+    spec = SMALL.replace(seed=43)
+    p = generate_prefill(spec)
+    c = p.cache
+    # poison every slot past each sequence's length in its last block, and
+    # every unused block
+    used = set()
+    for b in range(spec.batch):
+        L = int(c.context_lens[b])
+        nb = -(-L // 16)
+        used.update(int(x) for x in c.block_tables[b, :nb])
+        last = int(c.block_tables[b, nb - 1])
+        tail = L - (nb - 1) * 16
+        c.k_cache[last, tail:].view(torch.int16).fill_(0x7FC0)
+        c.v_cache[last, tail:].view(torch.int16).fill_(0x7FC0)
+    for blk in range(spec.pool_blocks):
+        if blk not in used:
+            c.k_cache[blk].view(torch.int16).fill_(0x7FC0)
+            c.v_cache[blk].view(torch.int16).fill_(0x7FC0)
+    _check(p, "poison")
+
+
+@pytest.mark.parametrize("factor", [4.0, 8.0])
+def test_sharpened_queries(factor):
+    p = generate_prefill(SMALL.replace(seed=44))
+    p.q = (p.q.float() * factor).to(torch.bfloat16)
+    _check(p, f"sharp{factor}")
+
+
+def test_repeat_calls_are_bitwise_identical():
+    p = generate_prefill(SMALL.replace(seed=45))
+    a = _run(p)
+    b = _run(p)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_graph_capture_replays_match_eager():
+    p = generate_prefill(SMALL.replace(seed=46)).to("cuda")
+    c = p.cache
+    eager = torch.empty_like(p.q)
+    note("[gpu] prefill graph capture")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        B.paged_attn_prefill(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                             p.max_query_len, p.scale, eager, stream=s)
+    s.synchronize()
+    out = torch.empty_like(p.q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.paged_attn_prefill(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                             p.max_query_len, p.scale, out, stream=s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.view(torch.int16).fill_(CANARY)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
+
+
+def test_argument_errors_launch_nothing():
+    p = generate_prefill(SMALL.replace(seed=47)).to("cuda")
+    c = p.cache
+    out = torch.full_like(p.q, 3.0)
+    note("[gpu] prefill argument errors")
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_prefill(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens[:-1],
+                             p.max_query_len, p.scale, out)
+    assert e.value.name == "PA_ERR_SHAPE"
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_prefill(p.q, c.k_cache.view(torch.uint8)[..., :p.spec.head_dim], c.v_cache, c.block_tables,
+                             c.context_lens, p.cu_seqlens, p.max_query_len, p.scale, out)
+    assert e.value.name in ("PA_ERR_UNSUPPORTED", "PA_ERR_DTYPE")
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+# --------------------------------------------------------------------------
+# the full-size workloads, in the benchmark's launch, checked on sampled rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name,seq,rows", [
+    ("prefill_8k", 0, [0, 1, 31, 32, 255, 256, 4095, 4096, 8190, 8191]),
+    ("chunked_prefill", 1, [0, 1, 63, 64, 1000, 2047]),
+    ("chunked_prefill", 3, [0, 511, 2047]),
+])
+def test_full_size_sampled_rows(name, seq, rows):
+    p = generate_prefill(PREFILL_CONFIGS[name])
+    note(f"[gpu] prefill full {name}: seq {seq} rows {rows}")
+    out = _run(p)
+    ref = _oracle(p, batch_subset=[seq], row_subset=rows)
+    base = int(p.cu_seqlens[seq])
+    _compare(out, ref, f"full/{name}/{seq}", rows=[base + r for r in rows])
