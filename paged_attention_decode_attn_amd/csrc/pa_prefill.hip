@@ -47,9 +47,6 @@ constexpr unsigned kSelHi = 0x07060302u;   // v_perm: (src1.hi16, src0.hi16)
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
 constexpr float kRescaleLog2 = 8.0f;       // lazy rescale threshold (log2 units)
 constexpr int kTile = 32;                  // keys per tile (two 16-token sub-blocks)
-constexpr int kWaves = 4;                  // waves per workgroup
-constexpr int kRows = 64;                  // query rows per wave (four 16-row tiles)
-constexpr int kNT = kRows / 16;
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
@@ -75,17 +72,46 @@ __device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (one query row's
+// partial results) with the cross-row swaps: v_permlane16_swap_b32 (and
+// v_permlane32_swap_b32) on a value and a copy of it leaves each lane with
+// its own value in one register and its partner's (lane l^16, l^32) in the
+// other, so combining the two gives the pair's result on every lane.  The
+// swap is written as one instruction: the compiler's builtin for it folds a
+// combination of its two results into the first.
+__device__ __forceinline__ void swap_pair(float x, bool rows32, float& r0, float& r1) {
+    r0 = x;
+    r1 = x;
+    if (rows32) asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(r0), "+v"(r1));
+    else asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(r0), "+v"(r1));
+}
+__device__ __forceinline__ float pair_max(float x, bool rows32) {
+    float a, b;
+    swap_pair(x, rows32, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x, bool rows32) {
+    float a, b;
+    swap_pair(x, rows32, a, b);
+    return a + b;
+}
+__device__ __forceinline__ float row_max(float x) { return pair_max(pair_max(x, false), true); }
+__device__ __forceinline__ float row_sum(float x) { return pair_sum(pair_sum(x, false), true); }
+
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
-// LDS row stride of a K or V tile: a 16-byte pad per row spreads the rows
-// that 16 lanes read at one column over the banks.
-template <int D> constexpr int kRowBytes = 2 * D + 16;
+// LDS row stride of a K or V tile: a pad per row spreads the rows that 16
+// lanes read at one column over the banks (32 bytes measured best of 16, 32
+// and 48).
+constexpr int kRowPad = 32;
+template <int D> constexpr int kRowBytes = 2 * D + kRowPad;
 template <int D> constexpr int kTileBytes = kTile * kRowBytes<D>;
 // 16-byte pieces of one row, and per thread of a tile
 template <int D> constexpr int kPieces = D / 8;
-template <int D> constexpr int kPerThread = kTile * kPieces<D> / (64 * kWaves);
+// (rounded up: with head_dim 64 and 8 waves half the threads load nothing)
+template <int D, int W> constexpr int kPerThread = (kTile * kPieces<D> + 64 * W - 1) / (64 * W);
 
 // The block-table window: lane l holds sub-block 2*t0 + l of sequence b.
 struct BlockRef {
@@ -103,17 +129,18 @@ __device__ __forceinline__ BlockRef load_window(const PrefillArgs& a, int b, int
 // (tid + 256 i) / kPieces of the tile, 16-byte column (tid + 256 i) %
 // kPieces; every piece of one load instruction lies in one sub-block per
 // wave, so its block id is a wave-uniform readlane of the window.
-template <int D>
+template <int D, int W>
 struct Pieces {
-    u32x4 k[kPerThread<D>], v[kPerThread<D>];
+    u32x4 k[kPerThread<D, W>], v[kPerThread<D, W>];
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile(Pieces<D>& pc, const PrefillArgs& a, const char* kh, const char* vh,
+template <int D, int W>
+__device__ __forceinline__ void load_tile(Pieces<D, W>& pc, const PrefillArgs& a, const char* kh, const char* vh,
                                           const BlockRef& br, int tile, int wbase, int L, int tid) {
 #pragma unroll
-    for (int i = 0; i < kPerThread<D>; ++i) {
-        const int piece = tid + 64 * kWaves * i;
+    for (int i = 0; i < kPerThread<D, W>; ++i) {
+        const int piece = tid + 64 * W * i;
+        if (kTile * kPieces<D> % (64 * W) != 0 && piece >= kTile * kPieces<D>) break;   // wave-uniform
         const int tok = piece / kPieces<D>, col = piece % kPieces<D>;
         const int sb = __builtin_amdgcn_readfirstlane(tok >> 4);   // uniform per wave
         const int rel = 2 * tile + sb - wbase;                     // window lane of the sub-block
@@ -132,11 +159,13 @@ __device__ __forceinline__ void load_tile(Pieces<D>& pc, const PrefillArgs& a, c
 
 // Store the pieces into an LDS tile buffer; keys at or past L become zeros
 // (their slots may hold anything).
-template <int D>
-__device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Pieces<D>& pc, int tile, int L, int tid) {
+template <int D, int W>
+__device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Pieces<D, W>& pc, int tile, int L,
+                                           int tid) {
 #pragma unroll
-    for (int i = 0; i < kPerThread<D>; ++i) {
-        const int piece = tid + 64 * kWaves * i;
+    for (int i = 0; i < kPerThread<D, W>; ++i) {
+        const int piece = tid + 64 * W * i;
+        if (kTile * kPieces<D> % (64 * W) != 0 && piece >= kTile * kPieces<D>) break;   // wave-uniform
         const int tok = piece / kPieces<D>, col = piece % kPieces<D>;
         const bool keep = kTile * tile + tok < L;
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -145,10 +174,10 @@ __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Piece
     }
 }
 
-template <int D>
+template <int D, int NT>
 struct Acc {
-    float m[kNT], l[kNT];
-    f32x4 o[kNT][D / 16];
+    float m[NT], l[NT];
+    f32x4 o[NT][D / 16];
 };
 
 // One 32-key tile of one wave: K fragments (A operand, token = lane % 16,
@@ -158,9 +187,9 @@ struct Acc {
 // softmax with a lazy rescale, O^T += V^T P^T.  masked (wave-uniform): some
 // key of the tile lies past some row's causal limit.  One copy of the step
 // serves both cases: two inlined copies would not fit the register file.
-template <int D>
-__device__ __forceinline__ void tile_step(Acc<D>& s, const u32x4 (&qf)[kNT][D / 32], const char* lds_k,
-                                          const char* lds_v, const int (&lim)[kNT], int kbase, float c, int lane,
+template <int D, int NT>
+__device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D / 32], const char* lds_k,
+                                          const char* lds_v, const int (&lim)[NT], int kbase, float c, int lane,
                                           bool masked) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
@@ -179,7 +208,7 @@ __device__ __forceinline__ void tile_step(Acc<D>& s, const u32x4 (&qf)[kNT][D / 
                                             2 * (D / 16) * n16);
 
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         // one row tile at a time: interleaving the four tiles' score and
         // softmax work would not fit the register file next to the
         // accumulators and query fragments
@@ -207,8 +236,7 @@ __device__ __forceinline__ void tile_step(Acc<D>& s, const u32x4 (&qf)[kNT][D / 
             }
         }
         float mx = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row_max(mx);
         const float mxs = c * mx;
         if (__any(mxs > s.m[nt] + kRescaleLog2)) {
             const float m_new = fmaxf(s.m[nt], mxs);
@@ -242,8 +270,10 @@ __device__ __forceinline__ void tile_step(Acc<D>& s, const u32x4 (&qf)[kNT][D / 
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
+// NT: 16-row tiles per wave (rows = 16 NT = positions P x query heads G);
+// W: waves per workgroup.
+template <int D, int NT, int W>
+__global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     constexpr int J = D / 16;
     extern __shared__ __align__(16) char lds[];            // [2 buffers][K tile, V tile]
     const int tid = threadIdx.x, lane = tid & 63;
@@ -258,12 +288,12 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
     const int c0 = min(max(a.cu[(int64_t)b * a.cu_s], 0), a.T);
     const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
     const int n = min(min(a.cu[(int64_t)(b + 1) * a.cu_s], a.T) - c0, L);
-    const int p0 = qb * kWaves * a.P;                      // first position (in the chunk) of the workgroup
+    const int p0 = qb * W * a.P;                      // first position (in the chunk) of the workgroup
     if (n <= 0 || p0 >= n) return;
     const int pw = p0 + wave * a.P;                        // first position of this wave
     // keys the workgroup needs: below L - n + min(p0 + 4P, n); this wave's
     // rows need keys below L - n + min(pw + P, n) (none if pw >= n)
-    const int kend = L - n + min(p0 + kWaves * a.P, n);
+    const int kend = L - n + min(p0 + W * a.P, n);
     const int wend = pw < n ? L - n + min(pw + a.P, n) : 0;
     const int ntiles = (kend + kTile - 1) / kTile;
     const int wtiles = (wend + kTile - 1) / kTile;
@@ -272,10 +302,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
     const int wclean = pw < n ? (L - n + pw + 1) / kTile : 0;
 
     // query fragments and per-row causal limits
-    u32x4 qf[kNT][D / 32];
-    int lim[kNT];
+    u32x4 qf[NT][D / 32];
+    int lim[NT];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const int row = 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         const int pos = pw + t;
@@ -295,9 +325,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
     // arithmetic on the shared array keeps the accesses in LDS instructions)
     constexpr int TB = kTileBytes<D>;
 
-    Acc<D> s;
+    Acc<D, NT> s;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         s.m[nt] = -__builtin_inff();
         s.l[nt] = 0.f;
 #pragma unroll
@@ -308,9 +338,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
     // tile 0 into buffer 0
     BlockRef br = load_window(a, b, 0, lane);
     int wbase = 0;                                         // first sub-block of the window
-    Pieces<D> pc;
-    load_tile<D>(pc, a, kh, vh, br, 0, wbase, L, tid);
-    store_tile<D>(lds, lds + TB, pc, 0, L, tid);
+    Pieces<D, W> pc;
+    load_tile<D, W>(pc, a, kh, vh, br, 0, wbase, L, tid);
+    store_tile<D, W>(lds, lds + TB, pc, 0, L, tid);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         const bool more = j + 1 < ntiles;
@@ -320,20 +350,18 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
                 br = load_window(a, b, j + 1, lane);
                 wbase = 2 * (j + 1);
             }
-            load_tile<D>(pc, a, kh, vh, br, j + 1, wbase, L, tid);
+            load_tile<D, W>(pc, a, kh, vh, br, j + 1, wbase, L, tid);
         }
         const int cur = (j & 1) * 2 * TB, nxt = 2 * TB - cur;
-        if (j < wtiles) tile_step<D>(s, qf, lds + cur, lds + cur + TB, lim, kTile * j, c, lane, j >= wclean);
-        if (more) store_tile<D>(lds + nxt, lds + nxt + TB, pc, j + 1, L, tid);
+        if (j < wtiles) tile_step<D, NT>(s, qf, lds + cur, lds + cur + TB, lim, kTile * j, c, lane, j >= wclean);
+        if (more) store_tile<D, W>(lds + nxt, lds + nxt + TB, pc, j + 1, L, tid);
         __syncthreads();
     }
 
     // epilogue: lane holds d = J * (4 * grp + i) + jj of row 16 * nt + n16
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-        float lt = s.l[nt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+    for (int nt = 0; nt < NT; ++nt) {
+        const float lt = row_sum(s.l[nt]);
         const int row = 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         const int pos = pw + t;
@@ -358,6 +386,30 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillArgs a) {
             }
         }
     }
+}
+
+struct PrefillShape {
+    int nt, waves;
+};
+
+// 32 rows per wave in 8-wave workgroups (246 registers: two waves per SIMD,
+// so one wave's softmax arithmetic overlaps the other's matrix work; 64
+// rows in 4-wave workgroups measured 1.4x slower, the accumulators pushing
+// other values into spill moves).  Ratios G > 32 need 64-row waves.
+PrefillShape prefill_shape(int D, int G) {
+    (void)D;
+    if (G > 32) return {4, 4};
+    return {2, 8};
+}
+
+template <int D>
+const void* prefill_kernel_of_d(PrefillShape sh) {
+    if (sh.nt == 4) return reinterpret_cast<const void*>(&prefill_kernel<D, 4, 4>);
+    return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8>);
+}
+
+const void* prefill_kernel_of(int D, PrefillShape sh) {
+    return D == 128 ? prefill_kernel_of_d<128>(sh) : prefill_kernel_of_d<64>(sh);
 }
 
 }  // namespace
@@ -392,19 +444,20 @@ int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_te
     a.k_span = (int32_t)(15 * p.k_stok + 2 * p.D);
     a.v_span = (int32_t)(15 * p.v_stok + 2 * p.D);
     a.B = (int32_t)p.B; a.Hkv = (int32_t)p.Hkv; a.G = (int32_t)p.G;
-    a.P = (int32_t)(kRows / p.G);
-    a.qblocks = (int32_t)((max_query_len + kWaves * a.P - 1) / (kWaves * a.P));
+    // rows per wave and waves per workgroup (see prefill_shape)
+    const PrefillShape sh = prefill_shape((int)p.D, (int)p.G);
+    a.P = (int32_t)(16 * sh.nt / p.G);
+    a.qblocks = (int32_t)((max_query_len + sh.waves * a.P - 1) / (sh.waves * a.P));
     a.bsub = (int32_t)(p.BS / PA_BLOCK_SIZE);
     a.wsub = (int32_t)(p.W * a.bsub);
     a.NB = (int32_t)std::min<int64_t>(p.NB, INT32_MAX);
     a.T = (int32_t)p.T;
     const int64_t grid = (int64_t)a.qblocks * p.B * p.Hkv;
     if (grid >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: grid too large");
-    const void* fn = p.D == 128 ? reinterpret_cast<const void*>(&prefill_kernel<128>)
-                                : reinterpret_cast<const void*>(&prefill_kernel<64>);
+    const void* fn = prefill_kernel_of((int)p.D, sh);
     const size_t lds = 4 * (size_t)(p.D == 128 ? kTileBytes<128> : kTileBytes<64>);
     void* args[] = {&a};
-    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kWaves), args, lds,
+    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * sh.waves), args, lds,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
         return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(hipGetLastError()));
     return PA_OK;
