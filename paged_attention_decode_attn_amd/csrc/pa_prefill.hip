@@ -177,6 +177,7 @@ __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Piece
 template <int D, int NT>
 struct Acc {
     float m[NT], l[NT];
+    float t[NT];                 // score above which m must rise: (m + kRescaleLog2) / c
     f32x4 o[NT][D / 16];
 };
 
@@ -209,10 +210,10 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        // one row tile at a time: interleaving the four tiles' score and
-        // softmax work would not fit the register file next to the
-        // accumulators and query fragments
-        if (nt > 0) __builtin_amdgcn_sched_barrier(0);
+        // four tiles: one at a time (interleaving their score and softmax
+        // work would not fit the register file next to the accumulators and
+        // query fragments); two tiles interleave freely
+        if (NT > 2 && nt > 0) __builtin_amdgcn_sched_barrier(0);
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
@@ -235,16 +236,22 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
                 y[i] = tok > lim[nt] ? -__builtin_inff() : y[i];
             }
         }
-        float mx = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-        mx = row_max(mx);
-        const float mxs = c * mx;
-        if (__any(mxs > s.m[nt] + kRescaleLog2)) {
-            const float m_new = fmaxf(s.m[nt], mxs);
+        // the running max m (log2 units) only has to rise when some score
+        // exceeds it by more than kRescaleLog2: a compare per score against
+        // the row's threshold, the row max itself only when it does
+        bool over = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) over |= y[i] > s.t[nt];
+        if (__any(over)) {
+            float mx = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+            mx = row_max(mx);
+            const float m_new = fmaxf(s.m[nt], c * mx);
             const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(s.m[nt] - m_new);
             s.l[nt] *= alpha;
 #pragma unroll
             for (int j = 0; j < J; ++j) s.o[nt][j] *= alpha;
             s.m[nt] = m_new;
+            s.t[nt] = (m_new + kRescaleLog2) / c;
         }
         const float neg_m = s.m[nt] == -__builtin_inff() ? 0.f : -s.m[nt];
         float p[8];
@@ -329,6 +336,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         s.m[nt] = -__builtin_inff();
+        s.t[nt] = -__builtin_inff();
         s.l[nt] = 0.f;
 #pragma unroll
         for (int j = 0; j < J; ++j) s.o[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
