@@ -29,9 +29,13 @@ METRIC = "paged decode attention: KV GB/s (% of HBM peak) and µs/call at batch 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# the kernels and the planner that sets their launch shape
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc", f)
-                  for f in ("pa_device.hip", "pa_cache.hip", "pa_prefill.hip", "pa_host.cpp", "pa_internal.h")]
+# per operation: the kernel source and the host code that validates and
+# plans its launch; a counter record is valid only for the digest it was
+# taken under
+_CSRC = os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc")
+KERNEL_SOURCES = {op: [os.path.join(_CSRC, f) for f in (k, "pa_host.cpp", "pa_internal.h")]
+                  for op, k in (("decode", "pa_device.hip"), ("cache_write", "pa_cache.hip"),
+                                ("prefill", "pa_prefill.hip"))}
 
 
 def parse_args():
@@ -63,23 +67,23 @@ def parse_args():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+def source_digest(op: str) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES[op]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per partition-kernel launch from the committed rocprofv3
-    counter summary, or None when the kernel source changed since."""
+def measured_traffic(workload: str, op: str = "decode"):
+    """HBM bytes per launch of the operation's main kernel from the committed
+    rocprofv3 counter summary, or None when its sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha256_16") != source_digest():
+    if not rec or rec.get("kernel_source_sha256_16") != source_digest(op):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -193,7 +197,7 @@ def summarize(args):
     except (OSError, ValueError):
         allrec = {}
     if kname in record:
-        allrec[wname] = {"kernel_source_sha256_16": source_digest(),
+        allrec[wname] = {"kernel_source_sha256_16": source_digest(args.op),
                              "hbm_bytes_per_launch": round(record[kname]),
                              "algorithmic_bytes": kvb,
                              "calibration": {"fetch": round(cf, 4), "write": round(cw, 4)}}
@@ -321,7 +325,7 @@ def bench_prefill(args):
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(spec.name), "algorithmic_flops": flops,
+                     "traffic": measured_traffic(spec.name, "prefill"), "algorithmic_flops": flops,
                      "kernel": "prefill_kernel",
                      "timing": "faster of the eager and graph-replayed timed steps (one kernel per call)"},
     }
@@ -416,7 +420,7 @@ def bench_cache_write(args):
         "us_per_call": round(ms * 1e3, 3), "us_per_call_graph": round(ms_graph * 1e3, 3),
         "bytes_per_call": wb,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, "cache_write"),
                      "algorithmic_bytes": wb,
                      "kernel": "cache_write_kernel",
                      "timing": "faster of the eager and graph-replayed timed steps"},
