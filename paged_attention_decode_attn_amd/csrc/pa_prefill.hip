@@ -22,7 +22,9 @@
 // A wave skips the tiles past its last position; tiles that reach past its
 // first position's causal limit take the masked step.  Keys past L_b are
 // zero-filled in LDS, so unwritten cache slots never reach the output.
-// Workgroups are ordered longest first (the highest position blocks).
+// Workgroups are ordered longest first (work_order), which also keeps the
+// workgroups running together on the same sequences' keys, so that they
+// share the L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -277,6 +279,68 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
     }
 }
 
+// Longest work first.  Workgroup (b, qb, g) reads the keys below
+// K(b, qb) = (L_b - n_b) + min((qb + 1) WP, n_b) (WP positions per
+// workgroup), so its work grows with K; launched in order of decreasing K
+// (ties: lower b first; the kv heads of one (b, qb) consecutive), the
+// longest workgroups start first and the short ones fill the tail, whatever
+// the mix of prefix and chunk lengths.  Rank r = blockIdx.x maps to its item
+// by a binary search over K: lane b of the wave holds sequence b (B <= 64)
+// and counts its items with K >= x in closed form.  Every wave computes the
+// same answer; false: the rank is past the last item.
+struct SeqWork {
+    int A, n, nb;        // prefix length L - n, chunk rows, position blocks
+};
+__device__ __forceinline__ int count_ge(const SeqWork& s, int x, int WP) {
+    // items qb < nb with A + min((qb + 1) WP, n) >= x
+    const int y = x - s.A;
+    if (y <= 0) return s.nb;
+    if (y > s.n) return 0;
+    return s.nb - ((y + WP - 1) / WP - 1);
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ bool work_order(const PrefillArgs& a, int rank, int lane, int WP, int& b, int& qb,
+                                           int& g) {
+    SeqWork s = {0, 0, 0};
+    int Lmax = 0;
+    if (lane < a.B) {
+        const int c0 = min(max(a.cu[(int64_t)lane * a.cu_s], 0), a.T);
+        const int L = min(a.ctx[(int64_t)lane * a.ctx_s], 16 * a.wsub);
+        const int n = min(min(a.cu[(int64_t)(lane + 1) * a.cu_s], a.T) - c0, L);
+        if (n > 0) {
+            s.A = L - n;
+            s.n = n;
+            s.nb = (n + WP - 1) / WP;
+            Lmax = L;
+        }
+    }
+    const int item = rank / a.Hkv;
+    g = rank - item * a.Hkv;
+    if (item >= wave_sum(s.nb)) return false;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) Lmax = max(Lmax, __shfl_xor(Lmax, o));
+    // the largest x with more than `item` items of key >= x: the item's key
+    int lo = 1, hi = Lmax + 1;                       // count(lo) > item >= count(hi)
+    while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (wave_sum(count_ge(s, mid, WP)) > item) lo = mid;
+        else hi = mid;
+    }
+    // among the sequences with an item of key lo, the j-th (by b)
+    const int j = item - wave_sum(count_ge(s, lo + 1, WP));
+    const bool has = count_ge(s, lo, WP) > count_ge(s, lo + 1, WP);
+    uint64_t m = __ballot(has);
+    for (int k = 0; k < j; ++k) m &= m - 1;
+    b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+    // the item of key lo is sequence b's lowest position block with key >= lo
+    qb = __builtin_amdgcn_readfirstlane(__shfl(s.nb - count_ge(s, lo, WP), b));
+    return true;
+}
+
 // NT: 16-row tiles per wave (rows = 16 NT = positions P x query heads G);
 // W: waves per workgroup.
 template <int D, int NT, int W>
@@ -286,11 +350,18 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, grp = lane >> 4;
-    // longest first: the highest position blocks of every (sequence, kv head)
-    const int pairs = a.B * a.Hkv;
-    const int qb = a.qblocks - 1 - (int)(blockIdx.x / pairs);
-    const int pr = blockIdx.x % pairs;
-    const int b = pr / a.Hkv, g = pr - b * a.Hkv;
+    int b, qb, g;
+    if (a.B > 1 && a.B <= 64) {
+        if (!work_order(a, (int)blockIdx.x, lane, W * a.P, b, qb, g)) return;
+    } else {
+        // one sequence (the same order) or many: the highest position blocks
+        // of every (sequence, kv head) first
+        const int pairs = a.B * a.Hkv;
+        qb = a.qblocks - 1 - (int)(blockIdx.x / pairs);
+        const int pr = blockIdx.x % pairs;
+        b = pr / a.Hkv;
+        g = pr - b * a.Hkv;
+    }
     // the chunk's rows, clamped to the packed rows and to the sequence
     const int c0 = min(max(a.cu[(int64_t)b * a.cu_s], 0), a.T);
     const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);

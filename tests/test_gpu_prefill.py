@@ -102,6 +102,20 @@ def test_chunk_length_edges(hq, hkv):
     _check(p, f"edges/{hq}/{hkv}")
 
 
+@pytest.mark.parametrize("batch", [2, 64, 70])
+def test_launch_order_covers_every_row(batch):
+    """Up to 64 sequences run in order of decreasing work (a per-workgroup
+    search over the sequences), more in the plain order: mixed prefix and
+    chunk lengths, empty chunks and whole prompts, every row produced once."""
+    rng = np.random.default_rng(batch)
+    ctx = rng.integers(1, 260, batch)
+    chunks = [int(rng.integers(0, c + 1)) if i % 5 else (0 if i % 10 == 0 else int(c)) for i, c in enumerate(ctx)]
+    spec = SMALL.replace(batch=batch, hq=16, hkv=4, head_dim=64, ctx_lo=1, ctx_hi=int(ctx.max()),
+                         pool_blocks=int(sum(-(-int(c) // 16) for c in ctx)) + 8, seed=48 + batch)
+    p = generate_prefill(spec, context_lens=[int(c) for c in ctx], chunk_lens=chunks)
+    _check(p, f"order/B{batch}")
+
+
 def test_larger_max_query_len_and_rows_outside_every_chunk():
     p = generate_prefill(SMALL.replace(seed=42))
     out = _run(p, max_query_len=p.max_query_len + 300, extra_rows=7)
