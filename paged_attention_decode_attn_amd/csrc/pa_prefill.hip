@@ -29,7 +29,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -42,10 +41,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr unsigned kSelLo = 0x05040100u;   // v_perm: (src1.lo16, src0.lo16)
-constexpr unsigned kSelHi = 0x07060302u;   // v_perm: (src1.hi16, src0.hi16)
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
 constexpr float kRescaleLog2 = 8.0f;       // lazy rescale threshold (log2 units)
 constexpr int kTile = 32;                  // keys per tile (two 16-token sub-blocks)
@@ -183,10 +182,20 @@ struct Acc {
     f32x4 o[NT][D / 16];
 };
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces that lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group address.  With
+// lane s of the group at head_dim 4 (s % 4) .. + 3 of key row s / 4, lane i
+// gets head_dim i of those four keys: a column of V, the V^T operand.
+__device__ __forceinline__ u32x2 read_vt(const char* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
 // One 32-key tile of one wave: K fragments (A operand, token = lane % 16,
-// head_dim 8 * (lane / 16) ... of each 32-wide step) and V rows (token slot
-// 4 * (lane / 16) + i of each sub-block, head_dim (D/16) * (lane % 16) ...)
-// read from LDS, then the decode kernel's step: S^T = K Q^T, base-2 online
+// head_dim 8 * (lane / 16) ... of each 32-wide step) and V^T fragments
+// (A operand, head_dim 16 j + lane % 16, the eight keys 4 (lane / 16) + i
+// and 16 + 4 (lane / 16) + i of the lane's score fragments, by transposing
+// reads of the key-major V tile) read from LDS, then the decode kernel's step: S^T = K Q^T, base-2 online
 // softmax with a lazy rescale, O^T += V^T P^T.  masked (wave-uniform): some
 // key of the tile lies past some row's causal limit.  One copy of the step
 // serves both cases: two inlined copies would not fit the register file.
@@ -203,12 +212,16 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         for (int kk = 0; kk < D / 32; ++kk)
             kf[mt][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
                 lds_k + (16 * mt + n16) * kRowBytes<D> + 2 * (32 * kk + 8 * grp)));
-    typedef typename std::conditional<D == 128, u32x4, u32x2>::type VT;
-    VT v[8];
+    // lane (n16, grp) addresses key 4 grp + n16 / 4 (and 16 more), head_dim
+    // 16 j + 4 (n16 % 4)
+    const char* vrow = lds_v + (4 * grp + (n16 >> 2)) * kRowBytes<D> + 8 * (n16 & 3);
+    u32x4 vt[J];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        v[i] = *reinterpret_cast<const VT*>(lds_v + (16 * (i >> 2) + 4 * grp + (i & 3)) * kRowBytes<D> +
-                                            2 * (D / 16) * n16);
+    for (int j = 0; j < J; ++j) {
+        const u32x2 lo = read_vt(vrow + 32 * j);
+        const u32x2 hi = read_vt(vrow + 16 * kRowBytes<D> + 32 * j);
+        vt[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -269,13 +282,8 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         for (int w = 0; w < 4; ++w) pw[w] = pack_bf16_rne(p[2 * w], p[2 * w + 1]);
         const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            u32x4 x;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                x[q] = __builtin_amdgcn_perm(v[2 * q + 1][j / 2], v[2 * q][j / 2], (j & 1) ? kSelHi : kSelLo);
-            s.o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x), pb, s.o[nt][j], 0, 0, 0);
-        }
+        for (int j = 0; j < J; ++j)
+            s.o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[j]), pb, s.o[nt][j], 0, 0, 0);
     }
 }
 
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    // epilogue: lane holds d = J * (4 * grp + i) + jj of row 16 * nt + n16
+    // epilogue: lane holds d = 16 j + 4 grp + i of row 16 nt + n16
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const float lt = row_sum(s.l[nt]);
@@ -448,21 +456,10 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         char* orow = a.out + (int64_t)(c0 + pos) * a.o_st + (int64_t)(g * a.G + hl) * a.o_sh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = J * (4 * grp + i);
-            if constexpr (J == 8) {
-                u32x4 wv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    wv[e] = pack_bf16_rne(s.o[nt][2 * e][i] * inv, s.o[nt][2 * e + 1][i] * inv);
-                *reinterpret_cast<u32x4*>(orow + 2 * d0) = wv;
-            } else {
-                u32x2 wv;
-#pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    wv[e] = pack_bf16_rne(s.o[nt][2 * e][i] * inv, s.o[nt][2 * e + 1][i] * inv);
-                *reinterpret_cast<u32x2*>(orow + 2 * d0) = wv;
-            }
+        for (int j = 0; j < J; ++j) {
+            const u32x2 wv = {pack_bf16_rne(s.o[nt][j][0] * inv, s.o[nt][j][1] * inv),
+                              pack_bf16_rne(s.o[nt][j][2] * inv, s.o[nt][j][3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + 2 * (16 * j + 4 * grp)) = wv;
         }
     }
 }
