@@ -48,6 +48,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit data format
 constexpr float kRescaleLog2 = 8.0f;       // lazy rescale threshold (log2 units)
 constexpr int kTile = 32;                  // keys per tile (two 16-token sub-blocks)
+constexpr unsigned kOnes = 0x3F803F80u;    // two bf16 ones
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
@@ -73,7 +74,7 @@ __device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 (one query row's
+// Row maxima over the four lanes l, l^16, l^32, l^48 (one query row's
 // partial results) with the cross-row swaps: v_permlane16_swap_b32 (and
 // v_permlane32_swap_b32) on a value and a copy of it leaves each lane with
 // its own value in one register and its partner's (lane l^16, l^32) in the
@@ -91,13 +92,7 @@ __device__ __forceinline__ float pair_max(float x, bool rows32) {
     swap_pair(x, rows32, a, b);
     return fmaxf(a, b);
 }
-__device__ __forceinline__ float pair_sum(float x, bool rows32) {
-    float a, b;
-    swap_pair(x, rows32, a, b);
-    return a + b;
-}
 __device__ __forceinline__ float row_max(float x) { return pair_max(pair_max(x, false), true); }
-__device__ __forceinline__ float row_sum(float x) { return pair_sum(pair_sum(x, false), true); }
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -177,7 +172,8 @@ __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Piece
 
 template <int D, int NT>
 struct Acc {
-    float m[NT], l[NT];
+    float m[NT];
+    f32x4 l[NT];                 // row sums: every element holds the lane's row's sum
     float t[NT];                 // score above which m must rise: (m + kRescaleLog2) / c
     f32x4 o[NT][D / 16];
 };
@@ -262,7 +258,7 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
             mx = row_max(mx);
             const float m_new = fmaxf(s.m[nt], c * mx);
             const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(s.m[nt] - m_new);
-            s.l[nt] *= alpha;
+            s.l[nt] *= alpha;               // (all four elements)
 #pragma unroll
             for (int j = 0; j < J; ++j) s.o[nt][j] *= alpha;
             s.m[nt] = m_new;
@@ -270,13 +266,8 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         }
         const float neg_m = s.m[nt] == -__builtin_inff() ? 0.f : -s.m[nt];
         float p[8];
-        float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c, neg_m));
-            psum += p[i];
-        }
-        s.l[nt] += psum;
+        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c, neg_m));
         u32x4 pw;
 #pragma unroll
         for (int w = 0; w < 4; ++w) pw[w] = pack_bf16_rne(p[2 * w], p[2 * w + 1]);
@@ -284,6 +275,11 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
 #pragma unroll
         for (int j = 0; j < J; ++j)
             s.o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[j]), pb, s.o[nt][j], 0, 0, 0);
+        // row sums by the matrix unit: an all-ones A operand sums the 32 keys
+        // of P for every row, already across the lanes holding the row, and
+        // from the same bf16 P as the accumulators
+        s.l[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{kOnes, kOnes, kOnes, kOnes}), pb, s.l[nt],
+                                                         0, 0, 0);
     }
 }
 
@@ -416,7 +412,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
         s.m[nt] = -__builtin_inff();
         s.t[nt] = -__builtin_inff();
-        s.l[nt] = 0.f;
+        s.l[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < J; ++j) s.o[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -448,7 +444,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     // epilogue: lane holds d = 16 j + 4 grp + i of row 16 nt + n16
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const float lt = row_sum(s.l[nt]);
+        const float lt = s.l[nt][0];
         const int row = 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         const int pos = pw + t;
