@@ -9,22 +9,24 @@
 // every prefill step); its source-file list places a ragged prefill chunk's
 // tokens in their own sequences.
 //
-// Workgroup = 4 waves on one (sequence, kv head, block of 4P positions).
-// Wave w owns positions p0 + wP .. p0 + wP + P - 1 of the chunk for all G
-// query heads of the kv head: 64 rows (row r = position r / G, head r % G,
-// P = 64 / G), the N side of 16x16 MFMA tiles as in the decode kernel.  The
-// workgroup walks the keys in 32-token tiles: all 256 threads load the
+// Workgroup = W waves on one (sequence, kv head, block of W*P positions);
+// W = 8 waves of 32 rows, or 4 waves of 64 rows when q_heads / kv_heads >
+// 32 (prefill_shape).  Wave w owns positions p0 + wP .. p0 + wP + P - 1 of
+// the chunk for all G query heads of the kv head (row r = position r / G,
+// head r % G), the N side of 16x16 MFMA tiles as in the decode kernel.  The
+// workgroup walks the keys in 32-token tiles: all threads load the next
 // tile's K and V rows (16-byte buffer loads, sub-block addressing through a
 // per-wave block-table window) into one of two padded LDS buffers while the
-// waves compute on the other, so every K/V byte read from L2 serves 256
-// rows.  Per tile and wave: S^T = K Q^T and O^T += V^T P^T with
-// v_mfma_f32_16x16x32_bf16, online softmax in base 2 with a lazy rescale.
-// A wave skips the tiles past its last position; tiles that reach past its
-// first position's causal limit take the masked step.  Keys past L_b are
-// zero-filled in LDS, so unwritten cache slots never reach the output.
-// Workgroups are ordered longest first (work_order), which also keeps the
-// workgroups running together on the same sequences' keys, so that they
-// share the L2.
+// waves compute on the other, so every K/V byte read from L2 serves every
+// row of the workgroup.  Per tile and wave: S^T = K Q^T and O^T += V^T P^T
+// with v_mfma_f32_16x16x32_bf16 (the V^T operand by transposing LDS reads),
+// online softmax in base 2 with a lazy rescale, row sums by the matrix
+// unit.  A wave skips the tiles past its last position; tiles that reach
+// past its first position's causal limit take the masked step.  Keys past
+// L_b are zero-filled in LDS, so unwritten cache slots never reach the
+// output.  Workgroups are ordered longest first (work_order), which also
+// keeps the workgroups running together on the same sequences' keys, so
+// that they share the L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -464,10 +466,10 @@ struct PrefillShape {
     int nt, waves;
 };
 
-// 32 rows per wave in 8-wave workgroups (246 registers: two waves per SIMD,
-// so one wave's softmax arithmetic overlaps the other's matrix work; 64
-// rows in 4-wave workgroups measured 1.4x slower, the accumulators pushing
-// other values into spill moves).  Ratios G > 32 need 64-row waves.
+// 32 rows per wave in 8-wave workgroups (under 256 registers: two waves per
+// SIMD, so one wave's softmax arithmetic can overlap the other's matrix
+// work; 64 rows in 4-wave workgroups measured 1.4x slower, one wave per
+// SIMD with its accumulators in AGPRs).  Ratios G > 32 need 64-row waves.
 PrefillShape prefill_shape(int D, int G) {
     (void)D;
     if (G > 32) return {4, 4};
