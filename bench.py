@@ -125,7 +125,7 @@ def summarize(args):
         pspec = PREFILL_CONFIGS[args.config]
         pf = generate_prefill(pspec)
         spec, wname = pspec, pspec.name
-        flops = prefill_flops(pf.cache.context_lens, pf.chunk_lens, pspec.hq, pspec.head_dim)
+        flops = prefill_flops(pf.cache.context_lens, pf.chunk_lens, pspec.hq, pspec.head_dim, pspec.sliding_window)
         kvb = prefill_bytes(pf)
         kname, title, unit = "prefill_kernel", "paged prefill attention", "bytes (q, K/V once, out)"
         kernels = (("%prefill_kernel%", "prefill_kernel"),)
@@ -257,9 +257,12 @@ PREFILL_METRIC = "paged prefill attention: TFLOP/s (% of dense bf16 MFMA peak) a
 def prefill_bytes(pf) -> int:
     """Bytes a prefill call must move at least once: the packed q rows and
     outputs, and the K/V rows of every attended token (each sequence's
-    whole context) for every kv head."""
+    whole context, or from its first row's window on) for every kv head."""
     s = pf.spec
-    tokens = sum(int(x) for x in pf.cache.context_lens)
+    w = s.sliding_window
+    tokens = 0
+    for L, n in zip(pf.cache.context_lens.tolist(), pf.chunk_lens.tolist()):
+        tokens += L - (max(0, L - n - w + 1) if w > 0 and n > 0 else 0)
     return 2 * pf.q.numel() * 2 + tokens * s.hkv * s.head_dim * 2 * 2
 
 
@@ -274,15 +277,20 @@ def bench_prefill(args):
     spec = PREFILL_CONFIGS[args.config]
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
     pf = generate_prefill(spec)
-    flops = prefill_flops(pf.cache.context_lens, pf.chunk_lens, spec.hq, spec.head_dim)
+    flops = prefill_flops(pf.cache.context_lens, pf.chunk_lens, spec.hq, spec.head_dim, spec.sliding_window)
     nbytes = prefill_bytes(pf)
     d = pf.to("cuda")
     c = d.cache
     out = torch.empty_like(d.q)
+    ext = spec.sliding_window > 0 or c.sinks is not None
 
-    def call():
-        B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
-                             pf.max_query_len, pf.scale, out)
+    def call(stream=None):
+        if ext:
+            B.paged_attn_prefill_ext(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
+                                     pf.max_query_len, pf.scale, spec.sliding_window, c.sinks, out, stream=stream)
+        else:
+            B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
+                                 pf.max_query_len, pf.scale, out, stream=stream)
 
     for _ in range(args.warmup):
         call()
@@ -300,8 +308,7 @@ def bench_prefill(args):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=gs):
         for _ in range(args.steps):
-            B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
-                                 pf.max_query_len, pf.scale, out, stream=gs)
+            call(stream=gs)
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
@@ -319,6 +326,7 @@ def bench_prefill(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.hq, "kv_heads": spec.hkv,
                    "head_dim": spec.head_dim, "kv_dtype": "bf16", "block_size": spec.block_size,
+                   "sliding_window": spec.sliding_window or None, "sinks": spec.sinks,
                    "context_lens": [int(x) for x in pf.cache.context_lens],
                    "chunk_lens": [int(x) for x in pf.chunk_lens]},
         "ms_per_call_graph": round(ms_graph, 6), "flops_per_call": flops, "bytes_per_call": nbytes,
@@ -339,6 +347,8 @@ def bench_prefill(args):
             return t.view(torch.int16).numpy().view("uint16") if t.dtype == torch.bfloat16 else t.numpy()
         qb, kb, vb = bits(pf.q), bits(h.k_cache), bits(h.v_cache)
         tables, ctx, cu = h.block_tables.numpy(), h.context_lens.numpy(), pf.cu_seqlens.numpy()
+        sinks = None if h.sinks is None else h.sinks.numpy()
+        w = spec.sliding_window
         done, rows_done, t, r = 0, 0, 0.0, 0
         b = spec.batch - 1
         n = int(pf.chunk_lens[b])
@@ -346,10 +356,12 @@ def bench_prefill(args):
             while t < args.cpu_seconds and rows_done < n:
                 rows = list(range(n - 1 - r, max(n - 1 - r - 8, -1), -1))    # the longest rows first
                 t0 = time.perf_counter()
-                paged_prefill_attention(qb, kb, vb, tables, ctx, cu, pf.scale, batch_subset=[b], row_subset=rows)
+                paged_prefill_attention(qb, kb, vb, tables, ctx, cu, pf.scale, batch_subset=[b], row_subset=rows,
+                                        sliding_window=w, sinks=sinks)
                 t += time.perf_counter() - t0
                 L = int(ctx[b])
-                done += sum(4 * spec.head_dim * spec.hq * (L - n + x + 1) for x in rows)
+                done += sum(4 * spec.head_dim * spec.hq * (min(L - n + x + 1, w) if w > 0 else L - n + x + 1)
+                            for x in rows)
                 rows_done += len(rows)
                 r += len(rows)
         res["cpu_baseline"] = {"value": done / t / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",

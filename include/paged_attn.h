@@ -233,6 +233,39 @@ int paged_attn_check_prefill(const pa_tensor* q, const pa_tensor* k_cache, const
                              const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out);
 
 /*
+ * paged_attn_prefill_ext -- paged_attn_prefill with a sliding window and
+ * attention sinks, as paged_attn_decode_ext adds them to the decode call
+ * (ATOM model operations guide, "Attention operations": the attention
+ * dispatch takes a sliding window; ATOM README model table: GPT-OSS uses
+ * a sliding window and attention sinks).
+ *
+ *   sliding_window  w > 0: the row at position a sees keys max(0, a - w + 1)
+ *                   .. a only; w <= 0: no window.  Blocks wholly below every
+ *                   row's window may be freed (their table entries are not
+ *                   dereferenced past the pool: ids are clamped into it, and
+ *                   their keys are never read into a result).
+ *   sinks           NULL or fp32 [Hq], any stride: one logit s_h per query
+ *                   head, in the units of scale * q.k, added to the softmax
+ *                   normaliser only: out = sum e^{x_j} v_j / (e^{s_h} +
+ *                   sum e^{x_j}); -inf disables a head's sink.
+ *
+ * Everything else, and the error behaviour, as paged_attn_prefill, which is
+ * this call with sliding_window = 0 and sinks = NULL.
+ */
+int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                           const pa_tensor* block_tables, const pa_tensor* context_lens,
+                           const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                           const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t sliding_window,
+                           const pa_tensor* sinks, pa_tensor* out, void* stream);
+
+/* paged_attn_check_prefill_ext -- the host-side validation of paged_attn_prefill_ext. */
+int paged_attn_check_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                                 const pa_tensor* block_tables, const pa_tensor* context_lens,
+                                 const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                                 const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t sliding_window,
+                                 const pa_tensor* sinks, const pa_tensor* out);
+
+/*
  * paged_attn_reshape_and_cache -- write the new tokens' K and V rows into
  * the paged cache (the step that precedes paged_attn_decode in a decode
  * step).  Sources: ATOM model operations guide, "KV cache operations" (the

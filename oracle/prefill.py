@@ -24,7 +24,12 @@ sequences (``token_layout/prefill.py``).  The reading taken here:
   causally to keys ``0 .. L_b - n_b + t`` through the block table — the same
   definition as decode attention with ``n_b`` query rows, so this oracle
   lays the packed rows out per sequence and evaluates that definition
-  (``paged_decode_attention``).
+  (``paged_decode_attention``), with the same sliding window and attention
+  sinks as the decode call when they are given (the model operations
+  guide's attention dispatch takes a sliding window; the README's model
+  table gives GPT-OSS a sliding window and sinks): the row at position
+  ``a`` sees keys ``max(0, a - w + 1) .. a``, and a head's sink logit joins
+  the softmax normaliser only.
 """
 from __future__ import annotations
 
@@ -37,7 +42,7 @@ __all__ = ["paged_prefill_attention"]
 
 def paged_prefill_attention(q_bits, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q,
                             scale, k_scale=None, v_scale=None, kv_dtype: str = "bf16",
-                            batch_subset=None, row_subset=None):
+                            batch_subset=None, row_subset=None, sliding_window=None, sinks=None):
     """Reference output, float64 ``[T, Hq, D]`` for packed bf16 bits ``q_bits``
     ``[T, Hq, D]``; rows of sequences left out by ``batch_subset`` are NaN.
     ``row_subset`` (optional, with one sequence in ``batch_subset``): only
@@ -59,7 +64,8 @@ def paged_prefill_attention(q_bits, k_cache, v_cache, block_tables, context_lens
         if row_subset is None:
             # the sequence's n rows as the query rows of one decode call
             one = paged_decode_attention(q_bits[cu[b]:cu[b + 1]][None], k_cache, v_cache, tables[b:b + 1],
-                                         [int(ctx[b])], [n], scale, k_scale, v_scale, kv_dtype)
+                                         [int(ctx[b])], [n], scale, k_scale, v_scale, kv_dtype,
+                                         sliding_window=sliding_window, sinks=sinks)
             out[cu[b]:cu[b + 1]] = one[0]
             continue
         # a chosen row t alone: the one query row of a sequence whose cache
@@ -67,6 +73,7 @@ def paged_prefill_attention(q_bits, k_cache, v_cache, block_tables, context_lens
         for t in np.asarray(row_subset, dtype=np.int64):
             Lt = int(ctx[b]) - n + int(t) + 1
             one = paged_decode_attention(q_bits[cu[b] + t][None, None], k_cache, v_cache, tables[b:b + 1],
-                                         [Lt], [1], scale, k_scale, v_scale, kv_dtype)
+                                         [Lt], [1], scale, k_scale, v_scale, kv_dtype,
+                                         sliding_window=sliding_window, sinks=sinks)
             out[cu[b] + t] = one[0, 0]
     return out

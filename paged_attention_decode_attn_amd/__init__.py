@@ -11,7 +11,7 @@ from . import workloads  # noqa: F401  (inputs only; no GPU, no library)
 
 _BINDING_NAMES = (
     "paged_attn_decode", "paged_attn_check", "paged_attn_decode_ext", "paged_attn_check_ext",
-    "paged_attn_prefill", "paged_attn_check_prefill",
+    "paged_attn_prefill", "paged_attn_check_prefill", "paged_attn_prefill_ext", "paged_attn_check_prefill_ext",
     "paged_attn_check_descriptors", "paged_attn_plan",
     "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
     "paged_attn_set_workgroups", "paged_attn_set_min_share", "paged_attn_set_heads_per_group",

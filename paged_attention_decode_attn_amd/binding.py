@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
                 args_pf = [_P] * 6 + [ctypes.c_int32, ctypes.c_float, _P, _P, _P]
                 L.paged_attn_prefill.argtypes = args_pf + [ctypes.c_void_p]
                 L.paged_attn_check_prefill.argtypes = args_pf
+                L.paged_attn_prefill_ext.argtypes = args_pf[:-1] + [ctypes.c_int32, _P, _P, ctypes.c_void_p]
+                L.paged_attn_check_prefill_ext.argtypes = args_pf[:-1] + [ctypes.c_int32, _P, _P]
                 L.paged_attn_reshape_and_cache.argtypes = [_P] * 7 + [ctypes.c_void_p]
                 L.paged_attn_check_reshape_and_cache.argtypes = [_P] * 7
                 L.paged_attn_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, ctypes.c_int32,
@@ -101,6 +103,7 @@ def lib() -> ctypes.CDLL:
                 for name in ("paged_attn_decode", "paged_attn_check", "paged_attn_plan",
                              "paged_attn_decode_ext", "paged_attn_check_ext",
                              "paged_attn_prefill", "paged_attn_check_prefill",
+                             "paged_attn_prefill_ext", "paged_attn_check_prefill_ext",
                              "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
                              "paged_attn_set_workgroups", "paged_attn_set_min_share",
                              "paged_attn_set_heads_per_group",
@@ -231,6 +234,32 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqle
                                   _stream_handle(q, stream))
     _raise(st, "paged_attn_prefill")
     return out
+
+
+def paged_attn_prefill_ext(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len, scale,
+                           sliding_window=0, sinks=None, out=None, stream=None):
+    """``paged_attn_prefill`` with a sliding window (``> 0``: a row sees its
+    ``sliding_window`` most recent positions) and per-query-head sink logits
+    (fp32 ``[Hq]`` or None); returns ``out``."""
+    if out is None:
+        out = torch.empty_like(q)
+    descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q)]
+    st = lib().paged_attn_prefill_ext(*[_ref(d) for d in descs], ctypes.c_int32(int(max_query_len)),
+                                      ctypes.c_float(scale), None, None, ctypes.c_int32(int(sliding_window)),
+                                      _ref(describe(sinks)), _ref(describe(out)), _stream_handle(q, stream))
+    _raise(st, "paged_attn_prefill_ext")
+    return out
+
+
+def paged_attn_check_prefill_ext(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len,
+                                 scale, k_scale=None, v_scale=None, sliding_window=0, sinks=None,
+                                 out=None) -> int:
+    """Status of the host-side validation of ``paged_attn_prefill_ext``."""
+    descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q)]
+    return lib().paged_attn_check_prefill_ext(*[_ref(d) for d in descs], ctypes.c_int32(int(max_query_len)),
+                                              ctypes.c_float(scale), _ref(describe(k_scale)),
+                                              _ref(describe(v_scale)), ctypes.c_int32(int(sliding_window)),
+                                              _ref(describe(sinks)), _ref(describe(out)))
 
 
 def paged_attn_check_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len, scale,

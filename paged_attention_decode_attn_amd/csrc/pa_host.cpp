@@ -225,7 +225,8 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
 
 int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const pa_tensor* bt,
                      const pa_tensor* ctx, const pa_tensor* cu, int32_t max_query_len, float scale,
-                     const pa_tensor* ks, const pa_tensor* vs, const pa_tensor* out, PrefillProblem* pr) {
+                     const pa_tensor* ks, const pa_tensor* vs, int32_t window, const pa_tensor* sinks,
+                     const pa_tensor* out, PrefillProblem* pr) {
     int st;
     if ((st = check_desc(q, "q", PA_DTYPE_BF16, 3, 3, true))) return st;
     if ((st = check_desc(out, "out", PA_DTYPE_BF16, 3, 3, true))) return st;
@@ -241,6 +242,7 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
     if (ks || vs) return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
     if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "scale is not finite");
     if (max_query_len < 0) return fail(PA_ERR_ARG, "max_query_len is negative");
+    if (sinks && (st = check_desc(sinks, "sinks", PA_DTYPE_FP32, 1, 1, true))) return st;
 
     const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
     for (int i = 0; i < 3; ++i)
@@ -274,6 +276,11 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
         return fail(PA_ERR_SHAPE, "cu_seqlens_q: %lld entries, expected batch + 1 = %lld", (long long)cu->shape[0],
                     (long long)(B + 1));
     if (T >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: too many query rows");
+    if (sinks) {
+        if (sinks->shape[0] != Hq)
+            return fail(PA_ERR_SHAPE, "sinks: %lld entries, q has %lld heads", (long long)sinks->shape[0], (long long)Hq);
+        if (!aligned(sinks->data, 4)) return fail(PA_ERR_LAYOUT, "sinks: data is not 4-byte aligned");
+    }
     if (B > 0 && T > 0) {
         if (W < 1) return fail(PA_ERR_SHAPE, "block_tables: width must be >= 1");
         if (NB < 1) return fail(PA_ERR_SHAPE, "k_cache: the pool has no blocks");
@@ -304,6 +311,9 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
         p.bt = static_cast<const int32_t*>(bt->data); p.bt_sb = bt->stride[0];
         p.ctx = static_cast<const int32_t*>(ctx->data); p.ctx_s = ctx->stride[0];
         p.cu = static_cast<const int32_t*>(cu->data); p.cu_s = cu->stride[0];
+        p.window = window > 0 ? window : 0;
+        p.sinks = sinks ? static_cast<const float*>(sinks->data) : nullptr;
+        p.sinks_s = sinks ? sinks->stride[0] : 0;
     }
     return PA_OK;
 }
@@ -526,7 +536,16 @@ int paged_attn_check_prefill(const pa_tensor* q, const pa_tensor* k_cache, const
                              const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
                              const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out) {
     return pa::validate_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len,
-                                scale, k_scale, v_scale, out, nullptr);
+                                scale, k_scale, v_scale, 0, nullptr, out, nullptr);
+}
+
+int paged_attn_check_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                                 const pa_tensor* block_tables, const pa_tensor* context_lens,
+                                 const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                                 const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t sliding_window,
+                                 const pa_tensor* sinks, const pa_tensor* out) {
+    return pa::validate_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len,
+                                scale, k_scale, v_scale, sliding_window, sinks, out, nullptr);
 }
 
 int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* v_new,

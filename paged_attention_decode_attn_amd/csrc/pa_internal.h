@@ -53,13 +53,15 @@ struct PrefillProblem {
     const int32_t* bt; int64_t bt_sb;                  // int32 elements
     const int32_t* ctx; int64_t ctx_s;
     const int32_t* cu;  int64_t cu_s;
+    int32_t window;                                    // sliding window in tokens, 0 = none
+    const float* sinks; int64_t sinks_s;               // per query head, may be null
 };
 
 int validate_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
                      const pa_tensor* block_tables, const pa_tensor* context_lens,
                      const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
-                     const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out,
-                     PrefillProblem* p);
+                     const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t window,
+                     const pa_tensor* sinks, const pa_tensor* out, PrefillProblem* p);
 
 int validate_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
                    const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* k_scale,

@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 
 #include "pa_internal.h"
@@ -67,6 +68,8 @@ struct PrefillArgs {
     int32_t q_neg;                                    // scale < 0: negate q
     int32_t k_span, v_span;                           // bytes of one (sub-block, head) slice
     int32_t B, Hkv, G, P, qblocks, bsub, wsub, NB, T;
+    int32_t window;                                   // sliding window in tokens, 0 = none
+    const float* sinks; int64_t sinks_s;              // per query head, may be null
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -155,17 +158,18 @@ __device__ __forceinline__ void load_tile(Pieces<D, W>& pc, const PrefillArgs& a
     }
 }
 
-// Store the pieces into an LDS tile buffer; keys at or past L become zeros
-// (their slots may hold anything).
+// Store the pieces into an LDS tile buffer; keys at or past L, and with a
+// sliding window keys below vlo (outside every row's window: their blocks
+// may have been freed), become zeros (their slots may hold anything).
 template <int D, int W>
 __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Pieces<D, W>& pc, int tile, int L,
-                                           int tid) {
+                                           int vlo, int tid) {
 #pragma unroll
     for (int i = 0; i < kPerThread<D, W>; ++i) {
         const int piece = tid + 64 * W * i;
         if (kTile * kPieces<D> % (64 * W) != 0 && piece >= kTile * kPieces<D>) break;   // wave-uniform
         const int tok = piece / kPieces<D>, col = piece % kPieces<D>;
-        const bool keep = kTile * tile + tok < L;
+        const bool keep = kTile * tile + tok < L && kTile * tile + tok >= vlo;
         const u32x4 z = {0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(lds_k + tok * kRowBytes<D> + 16 * col) = keep ? pc.k[i] : z;
         *reinterpret_cast<u32x4*>(lds_v + tok * kRowBytes<D> + 16 * col) = keep ? pc.v[i] : z;
@@ -199,8 +203,8 @@ __device__ __forceinline__ u32x2 read_vt(const char* p) {
 // serves both cases: two inlined copies would not fit the register file.
 template <int D, int NT>
 __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D / 32], const char* lds_k,
-                                          const char* lds_v, const int (&lim)[NT], int kbase, float c, int lane,
-                                          bool masked) {
+                                          const char* lds_v, const int (&lim)[NT], const int (&low)[NT], int kbase,
+                                          float c, int lane, bool masked) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
     bf16x8 kf[2][D / 32];
@@ -241,12 +245,12 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
             y[4 + i] = s1[i];
         }
         if (masked) {
-            // keys past the row's causal limit: -inf, whose exponent below
-            // is 0 (c > 0, so c * -inf stays -inf)
+            // keys past the row's causal limit or below its window: -inf,
+            // whose exponent below is 0 (c > 0, so c * -inf stays -inf)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int tok = kbase + 16 * (i >> 2) + 4 * grp + (i & 3);
-                y[i] = tok > lim[nt] ? -__builtin_inff() : y[i];
+                y[i] = (tok > lim[nt] || tok < low[nt]) ? -__builtin_inff() : y[i];
             }
         }
         // the running max m (log2 units) only has to rise when some score
@@ -297,17 +301,36 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
 struct SeqWork {
     int A, n, nb;        // prefix length L - n, chunk rows, position blocks
 };
-__device__ __forceinline__ int count_ge(const SeqWork& s, int x, int WP) {
-    // items qb < nb with A + min((qb + 1) WP, n) >= x
+__device__ __forceinline__ int count_ge(const SeqWork& s, int x, int WP, double inv_wp) {
+    // items qb < nb with A + min((qb + 1) WP, n) >= x: nb - (ceil(y / WP) - 1)
+    // for y = x - A in (0, n].  The quotient in double: z / WP for z < 2^32
+    // is within 2^-20 of the exact value, and a non-integer quotient is at
+    // least 1 / WP >= 2^-8 above its floor, so adding 2^-12 and truncating
+    // is exact.
     const int y = x - s.A;
     if (y <= 0) return s.nb;
     if (y > s.n) return 0;
-    return s.nb - ((y + WP - 1) / WP - 1);
+    const int q = (int)__builtin_fma((double)y + (double)(WP - 1), inv_wp, 0x1p-12);
+    return s.nb - (q - 1);
 }
+// Sum (max) over the wave: inclusive scans within each row of 16 lanes by
+// DPP row shifts (lanes shifted in from outside the row contribute 0), then
+// the four rows' last lanes.
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    return v;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);      // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);      // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);      // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);      // row_shr:8
+    return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
+           __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+    return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+               max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
 }
 __device__ __forceinline__ bool work_order(const PrefillArgs& a, int rank, int lane, int WP, int& b, int& qb,
                                            int& g) {
@@ -327,23 +350,23 @@ __device__ __forceinline__ bool work_order(const PrefillArgs& a, int rank, int l
     const int item = rank / a.Hkv;
     g = rank - item * a.Hkv;
     if (item >= wave_sum(s.nb)) return false;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) Lmax = max(Lmax, __shfl_xor(Lmax, o));
+    Lmax = wave_max_nonneg(Lmax);
+    const double inv_wp = 1.0 / (double)WP;
     // the largest x with more than `item` items of key >= x: the item's key
     int lo = 1, hi = Lmax + 1;                       // count(lo) > item >= count(hi)
     while (hi - lo > 1) {
         const int mid = lo + (hi - lo) / 2;
-        if (wave_sum(count_ge(s, mid, WP)) > item) lo = mid;
+        if (wave_sum(count_ge(s, mid, WP, inv_wp)) > item) lo = mid;
         else hi = mid;
     }
     // among the sequences with an item of key lo, the j-th (by b)
-    const int j = item - wave_sum(count_ge(s, lo + 1, WP));
-    const bool has = count_ge(s, lo, WP) > count_ge(s, lo + 1, WP);
+    const int j = item - wave_sum(count_ge(s, lo + 1, WP, inv_wp));
+    const bool has = count_ge(s, lo, WP, inv_wp) > count_ge(s, lo + 1, WP, inv_wp);
     uint64_t m = __ballot(has);
     for (int k = 0; k < j; ++k) m &= m - 1;
     b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
     // the item of key lo is sequence b's lowest position block with key >= lo
-    qb = __builtin_amdgcn_readfirstlane(__shfl(s.nb - count_ge(s, lo, WP), b));
+    qb = __builtin_amdgcn_readfirstlane(__shfl(s.nb - count_ge(s, lo, WP, inv_wp), b));
     return true;
 }
 
@@ -357,11 +380,12 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, grp = lane >> 4;
     int b, qb, g;
-    if (a.B > 1 && a.B <= 64) {
+    if (a.B > 1 && a.B <= 64 && a.window <= 0) {
         if (!work_order(a, (int)blockIdx.x, lane, W * a.P, b, qb, g)) return;
     } else {
-        // one sequence (the same order) or many: the highest position blocks
-        // of every (sequence, kv head) first
+        // one sequence (the same order), many, or a sliding window (every
+        // workgroup then has about the same work): the highest position
+        // blocks of every (sequence, kv head) first
         const int pairs = a.B * a.Hkv;
         qb = a.qblocks - 1 - (int)(blockIdx.x / pairs);
         const int pr = blockIdx.x % pairs;
@@ -375,19 +399,29 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     const int p0 = qb * W * a.P;                      // first position (in the chunk) of the workgroup
     if (n <= 0 || p0 >= n) return;
     const int pw = p0 + wave * a.P;                        // first position of this wave
-    // keys the workgroup needs: below L - n + min(p0 + 4P, n); this wave's
-    // rows need keys below L - n + min(pw + P, n) (none if pw >= n)
+    // keys the workgroup needs: below L - n + min(p0 + W P, n); this wave's
+    // rows need keys below L - n + min(pw + P, n) (none if pw >= n).  With
+    // a sliding window w the row at position a sees keys a - w + 1 .. a, so
+    // the workgroup starts at its first row's window (jstart, keys below
+    // vlo are outside every row's window) and a wave at its own (wstart).
+    const int w = a.window;
     const int kend = L - n + min(p0 + W * a.P, n);
     const int wend = pw < n ? L - n + min(pw + a.P, n) : 0;
     const int ntiles = (kend + kTile - 1) / kTile;
     const int wtiles = (wend + kTile - 1) / kTile;
-    // tiles wholly at or below every row's causal limit: the first row's
-    // limit is L - n + pw
+    const int vlo = w > 0 ? max(0, L - n + p0 - w + 1) : 0;
+    const int jstart = vlo / kTile;
+    const int wstart = w > 0 && pw < n ? max(0, L - n + pw - w + 1) / kTile : 0;
+    // tiles wholly at or below every row's causal limit (the first row's
+    // limit is L - n + pw) and, with a window, wholly at or above every
+    // row's lower limit (the last row's is L - n + min(pw + P, n) - w) take
+    // the step without masks
     const int wclean = pw < n ? (L - n + pw + 1) / kTile : 0;
+    const int wlow = w > 0 && pw < n ? L - n + min(pw + a.P, n) - w : 0;
 
-    // query fragments and per-row causal limits
+    // query fragments and per-row causal limits (and lower limits)
     u32x4 qf[NT][D / 32];
-    int lim[NT];
+    int lim[NT], low[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int row = 16 * nt + n16;
@@ -395,6 +429,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
         const int pos = pw + t;
         const bool live = t < a.P && pos < n;
         lim[nt] = live ? L - n + pos : L - 1;
+        low[nt] = w > 0 && live ? L - n + pos - w + 1 : INT_MIN;
         const char* qrow = a.q + (int64_t)(c0 + (live ? pos : 0)) * a.q_st + (int64_t)(g * a.G + hl) * a.q_sh;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
@@ -420,39 +455,50 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     }
     const float c = a.scale_log2;
 
-    // tile 0 into buffer 0
-    BlockRef br = load_window(a, b, 0, lane);
-    int wbase = 0;                                         // first sub-block of the window
+    // tile jstart into its buffer (tile j lives in buffer j & 1)
+    BlockRef br = load_window(a, b, jstart, lane);
+    int wbase = 2 * jstart;                                // first sub-block of the block-table window
     Pieces<D, W> pc;
-    load_tile<D, W>(pc, a, kh, vh, br, 0, wbase, L, tid);
-    store_tile<D, W>(lds, lds + TB, pc, 0, L, tid);
+    load_tile<D, W>(pc, a, kh, vh, br, jstart, wbase, L, tid);
+    {
+        const int first = (jstart & 1) * 2 * TB;
+        store_tile<D, W>(lds + first, lds + first + TB, pc, jstart, L, vlo, tid);
+    }
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
+    for (int j = jstart; j < ntiles; ++j) {
         const bool more = j + 1 < ntiles;
         if (more) {
-            // a window holds 64 sub-blocks = 32 tiles
-            if (((j + 1) & 31) == 0) {
+            // a block-table window holds 64 sub-blocks = 32 tiles
+            if (((j + 1 - jstart) & 31) == 0) {
                 br = load_window(a, b, j + 1, lane);
                 wbase = 2 * (j + 1);
             }
             load_tile<D, W>(pc, a, kh, vh, br, j + 1, wbase, L, tid);
         }
         const int cur = (j & 1) * 2 * TB, nxt = 2 * TB - cur;
-        if (j < wtiles) tile_step<D, NT>(s, qf, lds + cur, lds + cur + TB, lim, kTile * j, c, lane, j >= wclean);
-        if (more) store_tile<D, W>(lds + nxt, lds + nxt + TB, pc, j + 1, L, tid);
+        if (j >= wstart && j < wtiles)
+            tile_step<D, NT>(s, qf, lds + cur, lds + cur + TB, lim, low, kTile * j, c, lane,
+                             j >= wclean || kTile * j < wlow);
+        if (more) store_tile<D, W>(lds + nxt, lds + nxt + TB, pc, j + 1, L, vlo, tid);
         __syncthreads();
     }
 
     // epilogue: lane holds d = 16 j + 4 grp + i of row 16 nt + n16
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const float lt = s.l[nt][0];
+        float lt = s.l[nt][0];
         const int row = 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         const int pos = pw + t;
         if (!(t < a.P && pos < n)) continue;
+        const int h = g * a.G + hl;
+        if (a.sinks) {
+            // the sink logit joins the normaliser: l += 2^(sink log2(e) - m)
+            const float sk = a.sinks[(int64_t)h * a.sinks_s] * kLog2e;
+            if (sk > -__builtin_inff()) lt += __builtin_amdgcn_exp2f(sk - s.m[nt]);
+        }
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        char* orow = a.out + (int64_t)(c0 + pos) * a.o_st + (int64_t)(g * a.G + hl) * a.o_sh;
+        char* orow = a.out + (int64_t)(c0 + pos) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const u32x2 wv = {pack_bf16_rne(s.o[nt][j][0] * inv, s.o[nt][j][1] * inv),
@@ -491,14 +537,15 @@ const void* prefill_kernel_of(int D, PrefillShape sh) {
 
 extern "C" {
 
-int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
-                       const pa_tensor* block_tables, const pa_tensor* context_lens,
-                       const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
-                       const pa_tensor* k_scale, const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                           const pa_tensor* block_tables, const pa_tensor* context_lens,
+                           const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                           const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t sliding_window,
+                           const pa_tensor* sinks, pa_tensor* out, void* stream) {
     using namespace pa;
     PrefillProblem p;
     int st = validate_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len, scale,
-                              k_scale, v_scale, out, &p);
+                              k_scale, v_scale, sliding_window, sinks, out, &p);
     if (st) return st;
     if (p.B == 0 || p.T == 0 || max_query_len == 0) return PA_OK;
     PrefillArgs a;
@@ -526,6 +573,8 @@ int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_te
     a.wsub = (int32_t)(p.W * a.bsub);
     a.NB = (int32_t)std::min<int64_t>(p.NB, INT32_MAX);
     a.T = (int32_t)p.T;
+    a.window = p.window;
+    a.sinks = p.sinks; a.sinks_s = p.sinks_s;
     const int64_t grid = (int64_t)a.qblocks * p.B * p.Hkv;
     if (grid >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: grid too large");
     const void* fn = prefill_kernel_of((int)p.D, sh);
@@ -535,6 +584,14 @@ int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_te
                         static_cast<hipStream_t>(stream)) != hipSuccess)
         return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(hipGetLastError()));
     return PA_OK;
+}
+
+int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                       const pa_tensor* block_tables, const pa_tensor* context_lens,
+                       const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
+                       const pa_tensor* k_scale, const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+    return paged_attn_prefill_ext(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len,
+                                  scale, k_scale, v_scale, 0, nullptr, out, stream);
 }
 
 }  // extern "C"

@@ -427,11 +427,14 @@ class PrefillSpec:
     pool_blocks: int
     seed: int
     block_size: int = BLOCK
+    sliding_window: int = 0         # 0: none
+    sinks: bool = False             # per-query-head sink logits (drawn as for decode)
 
     def cache_spec(self) -> WorkloadSpec:
         return WorkloadSpec(self.name, batch=self.batch, qlen=1, hq=self.hq, hkv=self.hkv,
                             head_dim=self.head_dim, kv_dtype="bf16", ctx_lo=self.ctx_lo, ctx_hi=self.ctx_hi,
-                            pool_blocks=self.pool_blocks, seed=self.seed, block_size=self.block_size)
+                            pool_blocks=self.pool_blocks, seed=self.seed, block_size=self.block_size,
+                            sliding_window=self.sliding_window, sinks=self.sinks)
 
     def replace(self, **kw) -> "PrefillSpec":
         return dataclasses.replace(self, **kw)
@@ -454,6 +457,14 @@ class Prefill:
     def chunk_lens(self) -> torch.Tensor:
         return (self.cu_seqlens[1:] - self.cu_seqlens[:-1]).cpu()
 
+    @property
+    def sinks(self) -> Optional[torch.Tensor]:
+        return self.cache.sinks
+
+    @property
+    def sliding_window(self) -> int:
+        return self.spec.sliding_window
+
 
 # A Llama-3-8B-shaped whole 8192-token prompt, and chunked prefill of four
 # sequences (2048-token chunks after cached prefixes, up to 16k tokens),
@@ -465,6 +476,11 @@ PREFILL_CONFIGS = {
     "chunked_prefill": PrefillSpec("chunked_prefill_b4_q64kv8_d128_chunk2048_ctx2k-16k_bf16", batch=4, hq=64,
                                    hkv=8, head_dim=128, ctx_lo=2048, ctx_hi=16384, chunk_lo=2048,
                                    chunk_hi=2048, pool_blocks=4200, seed=22),
+    # GPT-OSS-shaped sliding-window layers (64 query / 8 kv heads of 64, a
+    # 128-token window and sink logits): four whole 8192-token prompts
+    "prefill_swa_sinks": PrefillSpec("prefill_swa128_sinks_b4_q64kv8_d64_prompt8192_bf16", batch=4, hq=64, hkv=8,
+                                     head_dim=64, ctx_lo=8192, ctx_hi=8192, chunk_lo=0, chunk_hi=0,
+                                     pool_blocks=2100, seed=23, sliding_window=128, sinks=True),
 }
 
 
@@ -492,13 +508,24 @@ def generate_prefill(spec: PrefillSpec, *, context_lens=None, chunk_lens=None) -
                    1.0 / math.sqrt(spec.head_dim))
 
 
-def prefill_flops(context_lens, chunk_lens, hq: int, head_dim: int) -> int:
+def prefill_flops(context_lens, chunk_lens, hq: int, head_dim: int, sliding_window: int = 0) -> int:
     """Algorithmic flops of one prefill call: every (row, visible key, query
     head) pair costs 2 * D for the score and 2 * D for the value update; row
-    t of a chunk of n rows in a sequence of L tokens sees L - n + t + 1 keys."""
+    t of a chunk of n rows in a sequence of L tokens sees a + 1 keys, a =
+    L - n + t its position, or min(a + 1, w) with a sliding window w."""
     total = 0
+    w = int(sliding_window)
     for L, n in zip(torch.as_tensor(context_lens).tolist(), torch.as_tensor(chunk_lens).tolist()):
         n = min(int(n), int(L))
-        # sum over t < n of (L - n + t + 1)
-        total += n * (L - n) + n * (n + 1) // 2
+        if n <= 0:
+            continue
+        a0, a1 = L - n, L - 1                    # first and last row position
+        if w <= 0:
+            total += n * (L - n) + n * (n + 1) // 2          # sum of a + 1 over the rows
+            continue
+        # rows below w - 1 see a + 1 keys, the rest w
+        lo_end = min(a1, w - 2)
+        if lo_end >= a0:
+            total += (lo_end + 1) * (lo_end + 2) // 2 - a0 * (a0 + 1) // 2
+        total += w * (a1 - max(a0, w - 1) + 1) if a1 >= max(a0, w - 1) else 0
     return 4 * head_dim * hq * total

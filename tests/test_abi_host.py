@@ -448,6 +448,23 @@ def test_prefill_validation():
     assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_LAYOUT"
 
 
+def test_prefill_ext_validation():
+    """paged_attn_check_prefill_ext: the window is free (<= 0 is none);
+    sinks are fp32 [Hq], 4-byte aligned."""
+    def status(**over):
+        t = _prefill_tensors()
+        t.update(over)
+        return B.STATUS_NAMES[B.paged_attn_check_prefill_ext(**t)]
+    hq = _prefill_tensors()["q"].shape[1]
+    assert status() == "PA_OK"
+    assert status(sliding_window=128, sinks=torch.zeros(hq)) == "PA_OK"
+    assert status(sliding_window=-1) == "PA_OK"
+    assert status(sinks=torch.zeros(hq + 1)) == "PA_ERR_SHAPE"
+    assert status(sinks=torch.zeros(hq, dtype=torch.bfloat16)) == "PA_ERR_DTYPE"
+    assert status(sinks=torch.zeros(hq, 1)) == "PA_ERR_SHAPE"
+    assert status(sinks=torch.zeros(2 * hq)[1::2]) == "PA_OK"                 # any stride
+
+
 def test_prefill_flops_closed_form():
     from paged_attention_decode_attn_amd.workloads import prefill_flops
     # a whole prompt of n tokens: n (n + 1) / 2 (row, key) pairs
@@ -455,3 +472,17 @@ def test_prefill_flops_closed_form():
     # a chunk of 10 after 90 cached tokens: rows see 91 .. 100 keys
     assert prefill_flops([100], [10], 1, 1) == 4 * sum(range(91, 101))
     assert prefill_flops([5, 7], [0, 7], 2, 2) == 4 * 2 * 2 * 28
+
+
+def test_prefill_flops_with_a_window_matches_counting():
+    """With a sliding window w the row at position a sees min(a + 1, w) keys:
+    the closed form against a plain count over the rows."""
+    import random
+    from paged_attention_decode_attn_amd.workloads import prefill_flops
+    rng = random.Random(0)
+    for _ in range(500):
+        L = rng.randint(0, 300)
+        n = rng.randint(0, L)
+        w = rng.choice([0, -1, 1, 2, 3, 7, 50, 400])
+        count = sum((a + 1) if w <= 0 else min(a + 1, w) for a in range(L - n, L))
+        assert prefill_flops([L], [n], 1, 1, w) == 4 * count, (L, n, w)

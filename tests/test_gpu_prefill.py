@@ -27,10 +27,14 @@ def _oracle(p, batch_subset=None, row_subset=None):
     c = p.cache
     return paged_prefill_attention(_bits(p.q), _bits(c.k_cache), _bits(c.v_cache), c.block_tables.numpy(),
                                    c.context_lens.numpy(), p.cu_seqlens.numpy(), p.scale,
-                                   batch_subset=batch_subset, row_subset=row_subset)
+                                   batch_subset=batch_subset, row_subset=row_subset,
+                                   sliding_window=p.sliding_window or None,
+                                   sinks=None if c.sinks is None else c.sinks.numpy())
 
 
-def _run(p, max_query_len=None, extra_rows=0):
+def _run(p, max_query_len=None, extra_rows=0, ext=None):
+    """The plain call, or (ext: True, or None with a window or sinks in the
+    workload) paged_attn_prefill_ext with the workload's window and sinks."""
     d = p.to("cuda")
     T, H, D = d.q.shape
     q = d.q
@@ -38,9 +42,14 @@ def _run(p, max_query_len=None, extra_rows=0):
         q = torch.cat([q, torch.zeros(extra_rows, H, D, dtype=q.dtype, device=q.device)])
     out = torch.empty_like(q)
     out.view(torch.int16).fill_(CANARY)
-    B.paged_attn_prefill(q, d.cache.k_cache, d.cache.v_cache, d.cache.block_tables, d.cache.context_lens,
-                         d.cu_seqlens, p.max_query_len if max_query_len is None else max_query_len, p.scale,
-                         out)
+    mql = p.max_query_len if max_query_len is None else max_query_len
+    c = d.cache
+    if ext or (ext is None and (p.sliding_window or c.sinks is not None)):
+        B.paged_attn_prefill_ext(q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens, mql,
+                                 p.scale, p.sliding_window, c.sinks, out)
+    else:
+        B.paged_attn_prefill(q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens, mql, p.scale,
+                             out)
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -62,7 +71,8 @@ def _compare(out, ref, label, rows=None):
 
 def _check(p, label, **kw):
     note(f"[gpu] prefill {label}: ctx={p.cache.context_lens.tolist()[:6]} chunks={p.chunk_lens.tolist()[:6]} "
-         f"heads={p.spec.hq}/{p.spec.hkv} d={p.spec.head_dim} bs={p.spec.block_size}")
+         f"heads={p.spec.hq}/{p.spec.hkv} d={p.spec.head_dim} bs={p.spec.block_size} "
+         f"window={p.sliding_window} sinks={p.sinks is not None}")
     out = _run(p, **kw)
     _compare(out, _oracle(p), label)
     return out
@@ -202,12 +212,91 @@ def test_argument_errors_launch_nothing():
 
 
 # --------------------------------------------------------------------------
+# sliding window and attention sinks (paged_attn_prefill_ext)
+# --------------------------------------------------------------------------
+SWA = SMALL.replace(hq=64, hkv=8, head_dim=64, ctx_hi=700, chunk_hi=300, pool_blocks=180)
+
+
+@pytest.mark.parametrize("window", [1, 2, 31, 32, 33, 100, 128, 1000])
+@pytest.mark.parametrize("with_sinks", [False, True])
+def test_window_and_sinks(window, with_sinks):
+    p = generate_prefill(SWA.replace(sliding_window=window, sinks=with_sinks, seed=60 + window + with_sinks))
+    _check(p, f"window{window}/sinks{with_sinks}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 8, 128), (64, 1, 64), (8, 8, 128)])
+def test_window_and_sinks_head_ratios(hq, hkv, d):
+    p = generate_prefill(SWA.replace(hq=hq, hkv=hkv, head_dim=d, sliding_window=77, sinks=True, seed=70 + hq))
+    _check(p, f"window77/heads{hq}/{hkv}/d{d}")
+
+
+def test_sinks_alone_and_chunk_edges_with_a_window():
+    p = generate_prefill(SWA.replace(sinks=True, seed=74))
+    _check(p, "sinks, no window")
+    ctx = [max(c, 1) + 37 * i for i, c in enumerate(EDGE_CHUNKS)]
+    spec = SWA.replace(batch=len(ctx), ctx_hi=max(ctx), pool_blocks=400, sliding_window=40, sinks=True, seed=75)
+    p = generate_prefill(spec, context_lens=ctx, chunk_lens=EDGE_CHUNKS)
+    _check(p, "window40 edges")
+
+
+def test_blocks_freed_below_every_window_never_reach_output():
+    """Blocks wholly below each sequence's first row's window hold NaN and
+    their table entries point outside the pool; the output is that of the
+    intact cache."""
+    w = 48
+    p = generate_prefill(SWA.replace(sliding_window=w, sinks=True, ctx_lo=200, seed=76))
+    ref = _oracle(p)
+    c = p.cache
+    NB = c.k_cache.shape[0]
+    freed = 0
+    for b in range(p.spec.batch):
+        L, n = int(c.context_lens[b]), int(p.chunk_lens[b])
+        lo = max(0, L - n - w + 1)
+        for i in range(lo // 16):
+            blk = int(c.block_tables[b, i])
+            c.k_cache[blk].view(torch.int16).fill_(0x7FC0)
+            c.v_cache[blk].view(torch.int16).fill_(0x7FC0)
+            c.block_tables[b, i] = NB + 5 if i % 2 else -7
+            freed += 1
+    assert freed > 0
+    note(f"[gpu] prefill freed-below-window: {freed} blocks")
+    _compare(_run(p), ref, "freed below window")
+
+
+def test_ext_without_a_window_or_sinks_is_the_plain_call():
+    p = generate_prefill(SMALL.replace(seed=77))
+    plain = _run(p, ext=False)
+    assert torch.equal(_run(p, ext=True).view(torch.int16), plain.view(torch.int16))
+    # a window no row can exceed changes nothing either
+    wide = generate_prefill(SMALL.replace(seed=77, sliding_window=1 << 20))
+    assert torch.equal(_run(wide).view(torch.int16), plain.view(torch.int16))
+
+
+def test_ext_argument_errors():
+    p = generate_prefill(SWA.replace(sinks=True, seed=78)).to("cuda")
+    c = p.cache
+    out = torch.full_like(p.q, 3.0)
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_prefill_ext(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                                 p.max_query_len, p.scale, 32, c.sinks[:-1], out)
+    assert e.value.name == "PA_ERR_SHAPE"
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_prefill_ext(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                                 p.max_query_len, p.scale, 32, c.sinks.to(torch.bfloat16), out)
+    assert e.value.name == "PA_ERR_DTYPE"
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+# --------------------------------------------------------------------------
 # the full-size workloads, in the benchmark's launch, checked on sampled rows
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("name,seq,rows", [
     ("prefill_8k", 0, [0, 1, 31, 32, 255, 256, 4095, 4096, 8190, 8191]),
     ("chunked_prefill", 1, [0, 1, 63, 64, 1000, 2047]),
     ("chunked_prefill", 3, [0, 511, 2047]),
+    ("prefill_swa_sinks", 0, [0, 1, 126, 127, 128, 129, 4095, 8191]),
+    ("prefill_swa_sinks", 3, [0, 200, 8191]),
 ])
 def test_full_size_sampled_rows(name, seq, rows):
     p = generate_prefill(PREFILL_CONFIGS[name])

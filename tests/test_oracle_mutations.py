@@ -43,6 +43,10 @@ MUTANTS = {
     "prefill_prefix_dropped": ("prefill.py", "[int(ctx[b])], [n], scale", "[n], [n], scale"),
     "prefill_row_position": ("prefill.py", "Lt = int(ctx[b]) - n + int(t) + 1", "Lt = int(ctx[b]) - n + int(t)"),
     "prefill_rows_reversed": ("prefill.py", "q_bits[cu[b]:cu[b + 1]][None]", "q_bits[cu[b]:cu[b + 1]][::-1][None]"),
+    "prefill_window_dropped": ("prefill.py", "sliding_window=sliding_window, sinks=sinks)",
+                               "sliding_window=None, sinks=sinks)"),
+    "prefill_sinks_dropped": ("prefill.py", "sliding_window=sliding_window, sinks=sinks)",
+                              "sliding_window=sliding_window, sinks=None)"),
     "e4m3_subnormal": ("formats.py", "man_field * 2.0 ** -9", "man_field * 2.0 ** -10"),
     "e4m3_bias": ("formats.py", "2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
     "e4m3_mantissa": ("formats.py", "(1.0 + man_field / 8.0)", "(1.0 + man_field / 16.0)"),

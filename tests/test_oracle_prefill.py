@@ -11,7 +11,7 @@ import torch
 
 from oracle import bf16_bits_to_f64, paged_prefill_attention
 from test_oracle import _bf16_bits
-from test_oracle_variants import _paged, _seqs
+from test_oracle_variants import _paged, _sdpa_masked, _seqs
 
 
 def _pack(rng, lens, chunks, hq, d):
@@ -121,6 +121,52 @@ def test_empty_chunks_and_bad_offsets():
         paged_prefill_attention(qp, kp, vp, t, lens, np.array([0, 1, 2, 3]), 0.5)
 
 
+def _padded(qp, cu, chunks, hq, d):
+    """Packed rows as a padded [B, max chunk, Hq, D] batch of query rows."""
+    q = np.zeros((len(chunks), max(max(chunks), 1), hq, d), np.uint16)
+    for b, n in enumerate(chunks):
+        q[b, :n] = qp[cu[b]:cu[b + 1]]
+    return q
+
+
+@pytest.mark.parametrize("window", [1, 5, 16, 40, 1000])
+def test_window_and_sinks_match_torch_sdpa(window):
+    """A sliding window and sink logits on packed chunks: torch float64 SDPA
+    with an additive mask (-inf outside each row's causal window) and one
+    extra zero key/value column biased by the head's sink."""
+    rng = np.random.default_rng(300 + window)
+    hq, hkv, d = 8, 2, 16
+    lens, chunks = (1, 37, 90, 150), (1, 37, 20, 64)
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 11)
+    sinks = rng.uniform(-4, 4, hq).astype(np.float32)
+    sinks[2] = -np.inf                                      # this head has no sink
+    scale = np.float32(0.3)
+    out = paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, sliding_window=window, sinks=sinks)
+    ref = _sdpa_masked(_padded(qp, cu, chunks, hq, d), ks, vs, lens, chunks, float(scale), hq, hkv, window, sinks)
+    for b, n in enumerate(chunks):
+        np.testing.assert_allclose(out[cu[b]:cu[b + 1]], ref[b, :n], rtol=0, atol=1e-12)
+    # chosen rows alone agree with the whole-sequence evaluation
+    part = paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, sliding_window=window, sinks=sinks,
+                                   batch_subset=[3], row_subset=[0, 31, 63])
+    rows = [cu[3] + r for r in (0, 31, 63)]
+    np.testing.assert_allclose(part[rows], out[rows], rtol=0, atol=1e-12)
+
+
+def test_window_of_one_returns_the_rows_own_value():
+    rng = np.random.default_rng(12)
+    hq, hkv, d = 4, 1, 8
+    lens, chunks = (20, 9), (7, 9)
+    ks, vs = _seqs(rng, lens, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    kp, vp, t = _paged(ks, vs, hkv, d, 16, 12)
+    out = paged_prefill_attention(qp, kp, vp, t, lens, cu, 0.7, sliding_window=1)
+    for b, (L, n) in enumerate(zip(lens, chunks)):
+        for r in range(n):
+            np.testing.assert_array_equal(out[cu[b] + r], np.repeat(bf16_bits_to_f64(vs[b][L - n + r]), hq, axis=0))
+
+
 def prefill_battery(orc) -> bool:
     """The pins above in brief, against a (possibly mutated) oracle copy."""
     rng = np.random.default_rng(9)
@@ -135,4 +181,15 @@ def prefill_battery(orc) -> bool:
     if not np.allclose(out, ref, rtol=0, atol=1e-12):
         return False
     part = orc.paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, batch_subset=[1], row_subset=[0, 24])
-    return bool(np.allclose(part[[cu[1], cu[1] + 24]], ref[[cu[1], cu[1] + 24]], rtol=0, atol=1e-12))
+    if not np.allclose(part[[cu[1], cu[1] + 24]], ref[[cu[1], cu[1] + 24]], rtol=0, atol=1e-12):
+        return False
+    # a sliding window with sinks, whole sequences and a chosen row
+    sinks = np.array([1.5, -1.0, 0.5, 3.0], np.float32)
+    outw = orc.paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, sliding_window=9, sinks=sinks)
+    refw = _sdpa_masked(_padded(qp, cu, chunks, hq, d), ks, vs, lens, chunks, float(scale), hq, hkv, 9, sinks)
+    for b, n in enumerate(chunks):
+        if not np.allclose(outw[cu[b]:cu[b + 1]], refw[b, :n], rtol=0, atol=1e-12):
+            return False
+    partw = orc.paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, batch_subset=[1], row_subset=[20],
+                                        sliding_window=9, sinks=sinks)
+    return bool(np.allclose(partw[cu[1] + 20], refw[1, 20], rtol=0, atol=1e-12))
