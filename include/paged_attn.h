@@ -208,9 +208,12 @@ int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_
  *                 prefix make up the rest).  Row t sits at position
  *                 L_b - n_b + t and attends to keys 0 .. L_b - n_b + t.
  *   max_query_len the largest n_b (a bound is enough; it sizes the grid).
- *   k_cache, v_cache, block_tables, context_lens, scale: as for
- *                 paged_attn_decode (bf16 caches only; k_scale and v_scale
- *                 must be NULL — an fp8 cache returns PA_ERR_UNSUPPORTED).
+ *   k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale:
+ *                 as for paged_attn_decode: bf16 caches (scales NULL), or
+ *                 e4m3fn caches with fp32 per-(token, kv head) scales
+ *                 [NB, BS, Hkv] (slot dimension contiguous, 4-byte aligned).
+ *                 With fp8, K enters the scores exactly (its scale multiplies
+ *                 the score) and V is scaled and rounded to bf16 once.
  *   stream        hipStream_t as void*, NULL = default stream.
  *
  * Device-side preconditions, not checked: cu non-decreasing with

@@ -222,22 +222,23 @@ def paged_attn_check_ext(q, k_cache, v_cache, block_tables, context_lens, query_
 
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len, scale,
-                       out=None, stream=None):
+                       out=None, stream=None, k_scale=None, v_scale=None):
     """Causal attention of packed prefill chunks (bf16 ``[T, Hq, D]``; sequence
     ``b`` owns rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1``, the last of
-    its ``context_lens[b]`` cached tokens); returns ``out``."""
+    its ``context_lens[b]`` cached tokens); an fp8 cache takes ``k_scale`` and
+    ``v_scale``.  Returns ``out``."""
     if out is None:
         out = torch.empty_like(q)
     descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q)]
     st = lib().paged_attn_prefill(*[_ref(d) for d in descs], ctypes.c_int32(int(max_query_len)),
-                                  ctypes.c_float(scale), None, None, _ref(describe(out)),
-                                  _stream_handle(q, stream))
+                                  ctypes.c_float(scale), _ref(describe(k_scale)), _ref(describe(v_scale)),
+                                  _ref(describe(out)), _stream_handle(q, stream))
     _raise(st, "paged_attn_prefill")
     return out
 
 
 def paged_attn_prefill_ext(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q, max_query_len, scale,
-                           sliding_window=0, sinks=None, out=None, stream=None):
+                           sliding_window=0, sinks=None, out=None, stream=None, k_scale=None, v_scale=None):
     """``paged_attn_prefill`` with a sliding window (``> 0``: a row sees its
     ``sliding_window`` most recent positions) and per-query-head sink logits
     (fp32 ``[Hq]`` or None); returns ``out``."""
@@ -245,7 +246,8 @@ def paged_attn_prefill_ext(q, k_cache, v_cache, block_tables, context_lens, cu_s
         out = torch.empty_like(q)
     descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, cu_seqlens_q)]
     st = lib().paged_attn_prefill_ext(*[_ref(d) for d in descs], ctypes.c_int32(int(max_query_len)),
-                                      ctypes.c_float(scale), None, None, ctypes.c_int32(int(sliding_window)),
+                                      ctypes.c_float(scale), _ref(describe(k_scale)), _ref(describe(v_scale)),
+                                      ctypes.c_int32(int(sliding_window)),
                                       _ref(describe(sinks)), _ref(describe(out)), _stream_handle(q, stream))
     _raise(st, "paged_attn_prefill_ext")
     return out

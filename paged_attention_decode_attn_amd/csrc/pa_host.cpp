@@ -232,14 +232,22 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
     if ((st = check_desc(out, "out", PA_DTYPE_BF16, 3, 3, true))) return st;
     if (!kc) return fail(PA_ERR_NULL, "k_cache: descriptor is NULL");
     if (!vc) return fail(PA_ERR_NULL, "v_cache: descriptor is NULL");
-    if (kc->dtype == PA_DTYPE_FP8_E4M3FN || (vc && vc->dtype == PA_DTYPE_FP8_E4M3FN))
-        return fail(PA_ERR_UNSUPPORTED, "prefill: an fp8 cache is not supported (bf16 only)");
-    if ((st = check_desc(kc, "k_cache", PA_DTYPE_BF16, 4, 4, true))) return st;
-    if ((st = check_desc(vc, "v_cache", PA_DTYPE_BF16, 4, 4, true))) return st;
+    const int32_t kvt = kc->dtype;
+    if (kvt != PA_DTYPE_BF16 && kvt != PA_DTYPE_FP8_E4M3FN)
+        return fail(PA_ERR_DTYPE, "k_cache: dtype %s, expected BF16 or FP8_E4M3FN", dtype_name(kvt));
+    if ((st = check_desc(kc, "k_cache", kvt, 4, 4, true))) return st;
+    if ((st = check_desc(vc, "v_cache", kvt, 4, 4, true))) return st;
     if ((st = check_desc(bt, "block_tables", PA_DTYPE_INT32, 2, 2, true))) return st;
     if ((st = check_desc(ctx, "context_lens", PA_DTYPE_INT32, 1, 1, true))) return st;
     if ((st = check_desc(cu, "cu_seqlens_q", PA_DTYPE_INT32, 1, 1, true))) return st;
-    if (ks || vs) return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
+    const bool fp8 = kvt == PA_DTYPE_FP8_E4M3FN;
+    if (fp8) {
+        if (!ks || !vs) return fail(PA_ERR_NULL, "fp8 cache needs k_scale and v_scale");
+        if ((st = check_desc(ks, "k_scale", PA_DTYPE_FP32, 3, 3, true))) return st;
+        if ((st = check_desc(vs, "v_scale", PA_DTYPE_FP32, 3, 3, true))) return st;
+    } else if (ks || vs) {
+        return fail(PA_ERR_ARG, "k_scale/v_scale are only accepted with an fp8 cache");
+    }
     if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "scale is not finite");
     if (max_query_len < 0) return fail(PA_ERR_ARG, "max_query_len is negative");
     if (sinks && (st = check_desc(sinks, "sinks", PA_DTYPE_FP32, 1, 1, true))) return st;
@@ -276,6 +284,17 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
         return fail(PA_ERR_SHAPE, "cu_seqlens_q: %lld entries, expected batch + 1 = %lld", (long long)cu->shape[0],
                     (long long)(B + 1));
     if (T >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: too many query rows");
+    if (fp8) {
+        for (const pa_tensor* s : {ks, vs}) {
+            const char* nm = s == ks ? "k_scale" : "v_scale";
+            if (s->shape[0] != NB || s->shape[1] != BS || s->shape[2] != Hkv)
+                return fail(PA_ERR_SHAPE, "%s: shape must be [num_blocks, block_size, kv_heads]", nm);
+            if (s->stride[1] != 1) return fail(PA_ERR_LAYOUT, "%s: the slot dimension must be contiguous", nm);
+            if (!aligned(s->data, 4)) return fail(PA_ERR_LAYOUT, "%s: data is not 4-byte aligned", nm);
+            if (s->stride[0] * 4 >= (int64_t(1) << 32) || s->stride[2] * 4 >= (int64_t(1) << 32))
+                return fail(PA_ERR_LAYOUT, "%s: block or head stride of 4 GiB or more", nm);
+        }
+    }
     if (sinks) {
         if (sinks->shape[0] != Hq)
             return fail(PA_ERR_SHAPE, "sinks: %lld entries, q has %lld heads", (long long)sinks->shape[0], (long long)Hq);
@@ -293,11 +312,12 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
     if (bt->stride[1] != 1 && W > 1) return fail(PA_ERR_LAYOUT, "block_tables: innermost stride must be 1");
     if (!aligned(bt->data, 4) || !aligned(ctx->data, 4) || !aligned(cu->data, 4))
         return fail(PA_ERR_LAYOUT, "int32 metadata must be 4-byte aligned");
+    const int64_t eb = fp8 ? 1 : 2;
     for (const pa_tensor* c : {kc, vc}) {
-        const int64_t span = (BS - 1) * c->stride[1] * 2 + (Hkv - 1) * c->stride[2] * 2 + D * 2;
+        const int64_t span = (BS - 1) * c->stride[1] * eb + (Hkv - 1) * c->stride[2] * eb + D * eb;
         if (span >= (int64_t(1) << 31))
             return fail(PA_ERR_LAYOUT, "%s: one block spans more than 2 GiB", c == kc ? "k_cache" : "v_cache");
-        if (c->stride[0] * 2 >= (int64_t(1) << 32))
+        if (c->stride[0] * eb >= (int64_t(1) << 32))
             return fail(PA_ERR_LAYOUT, "%s: block stride of 4 GiB or more", c == kc ? "k_cache" : "v_cache");
     }
     if (pr) {
@@ -306,8 +326,13 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
         p.scale = scale;
         p.q = q->data; p.q_st = q->stride[0] * 2; p.q_sh = q->stride[1] * 2;
         p.out = out->data; p.o_st = out->stride[0] * 2; p.o_sh = out->stride[1] * 2;
-        p.k = kc->data; p.k_sblk = kc->stride[0] * 2; p.k_stok = kc->stride[1] * 2; p.k_sh = kc->stride[2] * 2;
-        p.v = vc->data; p.v_sblk = vc->stride[0] * 2; p.v_stok = vc->stride[1] * 2; p.v_sh = vc->stride[2] * 2;
+        p.k = kc->data; p.k_sblk = kc->stride[0] * eb; p.k_stok = kc->stride[1] * eb; p.k_sh = kc->stride[2] * eb;
+        p.v = vc->data; p.v_sblk = vc->stride[0] * eb; p.v_stok = vc->stride[1] * eb; p.v_sh = vc->stride[2] * eb;
+        p.fp8 = fp8;
+        p.ks = fp8 ? static_cast<const float*>(ks->data) : nullptr;
+        p.vs = fp8 ? static_cast<const float*>(vs->data) : nullptr;
+        p.ks_sblk = fp8 ? ks->stride[0] : 0; p.ks_sh = fp8 ? ks->stride[2] : 0;
+        p.vs_sblk = fp8 ? vs->stride[0] : 0; p.vs_sh = fp8 ? vs->stride[2] : 0;
         p.bt = static_cast<const int32_t*>(bt->data); p.bt_sb = bt->stride[0];
         p.ctx = static_cast<const int32_t*>(ctx->data); p.ctx_s = ctx->stride[0];
         p.cu = static_cast<const int32_t*>(cu->data); p.cu_s = cu->stride[0];

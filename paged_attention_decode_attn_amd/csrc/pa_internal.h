@@ -55,6 +55,9 @@ struct PrefillProblem {
     const int32_t* cu;  int64_t cu_s;
     int32_t window;                                    // sliding window in tokens, 0 = none
     const float* sinks; int64_t sinks_s;               // per query head, may be null
+    bool fp8;                                          // e4m3fn cache with per-token scales
+    const float* ks; int64_t ks_sblk, ks_sh;           // floats
+    const float* vs; int64_t vs_sblk, vs_sh;
 };
 
 int validate_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,

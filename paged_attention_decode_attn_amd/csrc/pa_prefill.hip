@@ -31,6 +31,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 #include <cmath>
 
 #include "pa_internal.h"
@@ -70,6 +71,10 @@ struct PrefillArgs {
     int32_t B, Hkv, G, P, qblocks, bsub, wsub, NB, T;
     int32_t window;                                   // sliding window in tokens, 0 = none
     const float* sinks; int64_t sinks_s;              // per query head, may be null
+    // fp8 cache: per (token, kv head) scales, logical [NB, BS, Hkv] with the
+    // slot dimension contiguous; block and head strides in bytes
+    const char* ks; const char* vs;
+    uint32_t ks_sblk, vs_sblk, ks_sh, vs_sh;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -113,6 +118,12 @@ template <int D> constexpr int kTileBytes = kTile * kRowBytes<D>;
 template <int D> constexpr int kPieces = D / 8;
 // (rounded up: with head_dim 64 and 8 waves half the threads load nothing)
 template <int D, int W> constexpr int kPerThread = (kTile * kPieces<D> + 64 * W - 1) / (64 * W);
+// fp8: 8-byte pieces (8 elements, 16 bytes once in bf16) of one row, per
+// thread of a tile
+template <int D> constexpr int kPieces8 = D / 8;
+template <int D, int W> constexpr int kPerThread8 = (kTile * kPieces8<D> + 64 * W - 1) / (64 * W);
+// one LDS buffer: K tile, V tile, and with fp8 the tile's 32 K scales
+template <int D, bool FP8> constexpr int kBufBytes = 2 * kTileBytes<D> + (FP8 ? 4 * kTile : 0);
 
 // The block-table window: lane l holds sub-block 2*t0 + l of sequence b.
 struct BlockRef {
@@ -127,17 +138,28 @@ __device__ __forceinline__ BlockRef load_window(const PrefillArgs& a, int b, int
 }
 
 // Global K/V pieces of tile `tile` for this thread: piece i is token
-// (tid + 256 i) / kPieces of the tile, 16-byte column (tid + 256 i) %
-// kPieces; every piece of one load instruction lies in one sub-block per
-// wave, so its block id is a wave-uniform readlane of the window.
-template <int D, int W>
+// u / kPieces of the tile, column u % kPieces (u = tid + 64 W i), 16 bytes
+// of bf16 or 8 bytes of fp8 (the same 8 elements), plus with fp8 the
+// token's K and V scales; every piece of one load instruction lies in one
+// sub-block per wave, so its block id is a wave-uniform readlane of the
+// window.
+template <int D, int W, bool FP8>
 struct Pieces {
-    u32x4 k[kPerThread<D, W>], v[kPerThread<D, W>];
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type PT;
+    PT k[kPerThread<D, W>], v[kPerThread<D, W>];
+    float ks[FP8 ? kPerThread<D, W> : 1], vs[FP8 ? kPerThread<D, W> : 1];
 };
 
-template <int D, int W>
-__device__ __forceinline__ void load_tile(Pieces<D, W>& pc, const PrefillArgs& a, const char* kh, const char* vh,
-                                          const BlockRef& br, int tile, int wbase, int L, int tid) {
+// head-h slices of the scale arrays (fp8)
+struct ScaleBase {
+    const char* k; const char* v;
+};
+
+template <int D, int W, bool FP8>
+__device__ __forceinline__ void load_tile(Pieces<D, W, FP8>& pc, const PrefillArgs& a, const char* kh,
+                                          const char* vh, const ScaleBase& sc, const BlockRef& br, int tile,
+                                          int wbase, int L, int tid) {
+    constexpr unsigned EB = FP8 ? 8u : 16u;                        // bytes of a piece in the cache
 #pragma unroll
     for (int i = 0; i < kPerThread<D, W>; ++i) {
         const int piece = tid + 64 * W * i;
@@ -151,19 +173,45 @@ __device__ __forceinline__ void load_tile(Pieces<D, W>& pc, const PrefillArgs& a
         const bool live = tok0 < L;
         const Rsrc rk = make_rsrc(kh + (uint64_t)blk * a.k_sblk + sub * a.k_ssub, live ? a.k_span : 0);
         const Rsrc rv = make_rsrc(vh + (uint64_t)blk * a.v_sblk + sub * a.v_ssub, live ? a.v_span : 0);
-        const unsigned ko = (unsigned)((tok & 15) * a.k_stok) + 16u * col;
-        const unsigned vo = (unsigned)((tok & 15) * a.v_stok) + 16u * col;
-        pc.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
-        pc.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0);
+        const unsigned ko = (unsigned)((tok & 15) * a.k_stok) + EB * col;
+        const unsigned vo = (unsigned)((tok & 15) * a.v_stok) + EB * col;
+        if constexpr (FP8) {
+            pc.k[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, ko, 0, 0);
+            pc.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo, 0, 0);
+            // the 16 slots' scales of the sub-block: 64 contiguous bytes
+            const Rsrc rks = make_rsrc(sc.k + (uint64_t)blk * a.ks_sblk + 64u * sub, live ? 64 : 0);
+            const Rsrc rvs = make_rsrc(sc.v + (uint64_t)blk * a.vs_sblk + 64u * sub, live ? 64 : 0);
+            pc.ks[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4u * (tok & 15), 0, 0));
+            pc.vs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, 4u * (tok & 15), 0, 0));
+        } else {
+            pc.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
+            pc.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0);
+        }
     }
+}
+
+// Two e4m3fn bytes (bytes 0-1, or 2-3 with HI, of w) -> a bf16 pair, exact:
+// every e4m3fn value, subnormals included, is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ unsigned fp8x2_bf16x2(unsigned w) {
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Two e4m3fn bytes times a scale -> a bf16 pair (round to nearest even).
+template <bool HI>
+__device__ __forceinline__ unsigned fp8x2_scaled_bf16x2(unsigned w, float s) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    return pack_bf16_rne(f[0] * s, f[1] * s);
 }
 
 // Store the pieces into an LDS tile buffer; keys at or past L, and with a
 // sliding window keys below vlo (outside every row's window: their blocks
-// may have been freed), become zeros (their slots may hold anything).
-template <int D, int W>
-__device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Pieces<D, W>& pc, int tile, int L,
-                                           int vlo, int tid) {
+// may have been freed), become zeros (their slots may hold anything).  fp8:
+// K becomes bf16 exactly and its scales go to lds_ks (applied to the
+// scores, so K stays exact); V is scaled and rounded to bf16 (one rounding,
+// as a bf16 cache has).
+template <int D, int W, bool FP8>
+__device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, float* lds_ks, const Pieces<D, W, FP8>& pc,
+                                           int tile, int L, int vlo, int tid) {
 #pragma unroll
     for (int i = 0; i < kPerThread<D, W>; ++i) {
         const int piece = tid + 64 * W * i;
@@ -171,8 +219,20 @@ __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, const Piece
         const int tok = piece / kPieces<D>, col = piece % kPieces<D>;
         const bool keep = kTile * tile + tok < L && kTile * tile + tok >= vlo;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(lds_k + tok * kRowBytes<D> + 16 * col) = keep ? pc.k[i] : z;
-        *reinterpret_cast<u32x4*>(lds_v + tok * kRowBytes<D> + 16 * col) = keep ? pc.v[i] : z;
+        u32x4 k, v;
+        if constexpr (FP8) {
+            k = u32x4{fp8x2_bf16x2<false>(pc.k[i][0]), fp8x2_bf16x2<true>(pc.k[i][0]),
+                      fp8x2_bf16x2<false>(pc.k[i][1]), fp8x2_bf16x2<true>(pc.k[i][1])};
+            const float s = pc.vs[i];
+            v = u32x4{fp8x2_scaled_bf16x2<false>(pc.v[i][0], s), fp8x2_scaled_bf16x2<true>(pc.v[i][0], s),
+                      fp8x2_scaled_bf16x2<false>(pc.v[i][1], s), fp8x2_scaled_bf16x2<true>(pc.v[i][1], s)};
+            if (col == 0) lds_ks[tok] = keep ? pc.ks[i] : 0.f;
+        } else {
+            k = pc.k[i];
+            v = pc.v[i];
+        }
+        *reinterpret_cast<u32x4*>(lds_k + tok * kRowBytes<D> + 16 * col) = keep ? k : z;
+        *reinterpret_cast<u32x4*>(lds_v + tok * kRowBytes<D> + 16 * col) = keep ? v : z;
     }
 }
 
@@ -201,10 +261,11 @@ __device__ __forceinline__ u32x2 read_vt(const char* p) {
 // softmax with a lazy rescale, O^T += V^T P^T.  masked (wave-uniform): some
 // key of the tile lies past some row's causal limit.  One copy of the step
 // serves both cases: two inlined copies would not fit the register file.
-template <int D, int NT>
+// fp8 (lds_ks non-null): the scores of key k are multiplied by its K scale.
+template <int D, int NT, bool FP8>
 __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D / 32], const char* lds_k,
-                                          const char* lds_v, const int (&lim)[NT], const int (&low)[NT], int kbase,
-                                          float c, int lane, bool masked) {
+                                          const char* lds_v, const float* lds_ks, const int (&lim)[NT],
+                                          const int (&low)[NT], int kbase, float c, int lane, bool masked) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
     bf16x8 kf[2][D / 32];
@@ -224,6 +285,12 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         const u32x2 hi = read_vt(vrow + 16 * kRowBytes<D> + 32 * j);
         vt[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
+    // fp8: the K scales of the lane's keys 4 grp + i and 16 + 4 grp + i
+    f32x4 ksc0 = {1.f, 1.f, 1.f, 1.f}, ksc1 = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (FP8) {
+        ksc0 = *reinterpret_cast<const f32x4*>(lds_ks + 4 * grp);
+        ksc1 = *reinterpret_cast<const f32x4*>(lds_ks + 16 + 4 * grp);
+    }
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -241,8 +308,8 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         float y[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            y[i] = s0[i];
-            y[4 + i] = s1[i];
+            y[i] = FP8 ? s0[i] * ksc0[i] : s0[i];
+            y[4 + i] = FP8 ? s1[i] * ksc1[i] : s1[i];
         }
         if (masked) {
             // keys past the row's causal limit or below its window: -inf,
@@ -372,10 +439,10 @@ __device__ __forceinline__ bool work_order(const PrefillArgs& a, int rank, int l
 
 // NT: 16-row tiles per wave (rows = 16 NT = positions P x query heads G);
 // W: waves per workgroup.
-template <int D, int NT, int W>
+template <int D, int NT, int W, bool FP8>
 __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     constexpr int J = D / 16;
-    extern __shared__ __align__(16) char lds[];            // [2 buffers][K tile, V tile]
+    extern __shared__ __align__(16) char lds[];            // [2 buffers][K tile, V tile (, K scales)]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, grp = lane >> 4;
@@ -440,9 +507,12 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
 
     const char* kh = a.k + (int64_t)g * a.k_sh;
     const char* vh = a.v + (int64_t)g * a.v_sh;
-    // buffer i: K tile at lds + 2i * TB, V tile at lds + (2i + 1) * TB (plain
-    // arithmetic on the shared array keeps the accesses in LDS instructions)
-    constexpr int TB = kTileBytes<D>;
+    // buffer i at lds + i * BB: K tile, V tile at + TB, with fp8 the K scales
+    // at + 2 TB (plain arithmetic on the shared array keeps the accesses in
+    // LDS instructions)
+    constexpr int TB = kTileBytes<D>, BB = kBufBytes<D, FP8>;
+    ScaleBase sc = {nullptr, nullptr};
+    if constexpr (FP8) sc = ScaleBase{a.ks + (int64_t)g * a.ks_sh, a.vs + (int64_t)g * a.vs_sh};
 
     Acc<D, NT> s;
 #pragma unroll
@@ -458,11 +528,12 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     // tile jstart into its buffer (tile j lives in buffer j & 1)
     BlockRef br = load_window(a, b, jstart, lane);
     int wbase = 2 * jstart;                                // first sub-block of the block-table window
-    Pieces<D, W> pc;
-    load_tile<D, W>(pc, a, kh, vh, br, jstart, wbase, L, tid);
+    Pieces<D, W, FP8> pc;
+    load_tile<D, W, FP8>(pc, a, kh, vh, sc, br, jstart, wbase, L, tid);
     {
-        const int first = (jstart & 1) * 2 * TB;
-        store_tile<D, W>(lds + first, lds + first + TB, pc, jstart, L, vlo, tid);
+        const int first = (jstart & 1) * BB;
+        store_tile<D, W, FP8>(lds + first, lds + first + TB, reinterpret_cast<float*>(lds + first + 2 * TB), pc,
+                              jstart, L, vlo, tid);
     }
     __syncthreads();
     for (int j = jstart; j < ntiles; ++j) {
@@ -473,13 +544,15 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
                 br = load_window(a, b, j + 1, lane);
                 wbase = 2 * (j + 1);
             }
-            load_tile<D, W>(pc, a, kh, vh, br, j + 1, wbase, L, tid);
+            load_tile<D, W, FP8>(pc, a, kh, vh, sc, br, j + 1, wbase, L, tid);
         }
-        const int cur = (j & 1) * 2 * TB, nxt = 2 * TB - cur;
+        const int cur = (j & 1) * BB, nxt = BB - cur;
         if (j >= wstart && j < wtiles)
-            tile_step<D, NT>(s, qf, lds + cur, lds + cur + TB, lim, low, kTile * j, c, lane,
-                             j >= wclean || kTile * j < wlow);
-        if (more) store_tile<D, W>(lds + nxt, lds + nxt + TB, pc, j + 1, L, vlo, tid);
+            tile_step<D, NT, FP8>(s, qf, lds + cur, lds + cur + TB, reinterpret_cast<const float*>(lds + cur + 2 * TB),
+                                  lim, low, kTile * j, c, lane, j >= wclean || kTile * j < wlow);
+        if (more)
+            store_tile<D, W, FP8>(lds + nxt, lds + nxt + TB, reinterpret_cast<float*>(lds + nxt + 2 * TB), pc, j + 1,
+                                  L, vlo, tid);
         __syncthreads();
     }
 
@@ -522,14 +595,15 @@ PrefillShape prefill_shape(int D, int G) {
     return {2, 8};
 }
 
-template <int D>
+template <int D, bool FP8>
 const void* prefill_kernel_of_d(PrefillShape sh) {
-    if (sh.nt == 4) return reinterpret_cast<const void*>(&prefill_kernel<D, 4, 4>);
-    return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8>);
+    if (sh.nt == 4) return reinterpret_cast<const void*>(&prefill_kernel<D, 4, 4, FP8>);
+    return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8, FP8>);
 }
 
-const void* prefill_kernel_of(int D, PrefillShape sh) {
-    return D == 128 ? prefill_kernel_of_d<128>(sh) : prefill_kernel_of_d<64>(sh);
+const void* prefill_kernel_of(int D, bool fp8, PrefillShape sh) {
+    if (fp8) return D == 128 ? prefill_kernel_of_d<128, true>(sh) : prefill_kernel_of_d<64, true>(sh);
+    return D == 128 ? prefill_kernel_of_d<128, false>(sh) : prefill_kernel_of_d<64, false>(sh);
 }
 
 }  // namespace
@@ -562,8 +636,13 @@ int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const p
     // scale becomes a negligible one: every score then weighs the same)
     a.scale_log2 = std::max(std::fabs(p.scale) * kLog2e, 1e-30f);
     a.q_neg = p.scale < 0.f;
-    a.k_span = (int32_t)(15 * p.k_stok + 2 * p.D);
-    a.v_span = (int32_t)(15 * p.v_stok + 2 * p.D);
+    const int64_t eb = p.fp8 ? 1 : 2;                 // bytes per cache element
+    a.k_span = (int32_t)(15 * p.k_stok + eb * p.D);
+    a.v_span = (int32_t)(15 * p.v_stok + eb * p.D);
+    a.ks = reinterpret_cast<const char*>(p.ks);
+    a.vs = reinterpret_cast<const char*>(p.vs);
+    a.ks_sblk = (uint32_t)(4 * p.ks_sblk); a.vs_sblk = (uint32_t)(4 * p.vs_sblk);
+    a.ks_sh = (uint32_t)(4 * p.ks_sh); a.vs_sh = (uint32_t)(4 * p.vs_sh);
     a.B = (int32_t)p.B; a.Hkv = (int32_t)p.Hkv; a.G = (int32_t)p.G;
     // rows per wave and waves per workgroup (see prefill_shape)
     const PrefillShape sh = prefill_shape((int)p.D, (int)p.G);
@@ -577,8 +656,9 @@ int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const p
     a.sinks = p.sinks; a.sinks_s = p.sinks_s;
     const int64_t grid = (int64_t)a.qblocks * p.B * p.Hkv;
     if (grid >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: grid too large");
-    const void* fn = prefill_kernel_of((int)p.D, sh);
-    const size_t lds = 4 * (size_t)(p.D == 128 ? kTileBytes<128> : kTileBytes<64>);
+    const void* fn = prefill_kernel_of((int)p.D, p.fp8, sh);
+    const size_t lds = 2 * (size_t)(p.fp8 ? (p.D == 128 ? kBufBytes<128, true> : kBufBytes<64, true>)
+                                          : (p.D == 128 ? kBufBytes<128, false> : kBufBytes<64, false>));
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * sh.waves), args, lds,
                         static_cast<hipStream_t>(stream)) != hipSuccess)

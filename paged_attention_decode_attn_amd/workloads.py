@@ -429,10 +429,11 @@ class PrefillSpec:
     block_size: int = BLOCK
     sliding_window: int = 0         # 0: none
     sinks: bool = False             # per-query-head sink logits (drawn as for decode)
+    kv_dtype: str = "bf16"          # or "fp8_e4m3fn" (per-token scales, drawn as for decode)
 
     def cache_spec(self) -> WorkloadSpec:
         return WorkloadSpec(self.name, batch=self.batch, qlen=1, hq=self.hq, hkv=self.hkv,
-                            head_dim=self.head_dim, kv_dtype="bf16", ctx_lo=self.ctx_lo, ctx_hi=self.ctx_hi,
+                            head_dim=self.head_dim, kv_dtype=self.kv_dtype, ctx_lo=self.ctx_lo, ctx_hi=self.ctx_hi,
                             pool_blocks=self.pool_blocks, seed=self.seed, block_size=self.block_size,
                             sliding_window=self.sliding_window, sinks=self.sinks)
 

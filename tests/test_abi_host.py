@@ -434,7 +434,14 @@ def test_prefill_validation():
     assert status(max_query_len=-1) == "PA_ERR_ARG"
     assert status(scale=float("nan")) == "PA_ERR_ARG"
     assert status(out=torch.zeros(19, 8, 128, dtype=torch.bfloat16)) == "PA_ERR_SHAPE"
-    assert status(k_cache=torch.zeros(NB, 16, 2, 128, dtype=torch.uint8)) == "PA_ERR_UNSUPPORTED"   # fp8
+    # fp8: both caches e4m3fn, with fp32 scales [NB, 16, Hkv] whose slot dimension is contiguous
+    k8, v8 = (torch.zeros(NB, 16, 2, 128, dtype=torch.uint8) for _ in range(2))
+    sc = torch.ones(NB, 2, 16).permute(0, 2, 1)
+    assert status(k_cache=k8) == "PA_ERR_DTYPE"                                  # v_cache still bf16
+    assert status(k_cache=k8, v_cache=v8) == "PA_ERR_NULL"                       # no scales
+    assert status(k_cache=k8, v_cache=v8, k_scale=sc, v_scale=sc) == "PA_OK"
+    assert status(k_cache=k8, v_cache=v8, k_scale=sc[:, :8], v_scale=sc) == "PA_ERR_SHAPE"
+    assert status(k_cache=k8, v_cache=v8, k_scale=torch.ones(NB, 16, 2), v_scale=sc) == "PA_ERR_LAYOUT"   # slots strided
     assert status(k_scale=torch.ones(NB, 16, 2)) == "PA_ERR_ARG"
     t = _prefill_tensors(d=256)
     assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"

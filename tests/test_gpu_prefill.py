@@ -25,8 +25,12 @@ def _bits(t):
 
 def _oracle(p, batch_subset=None, row_subset=None):
     c = p.cache
+    fp8 = c.k_scale is not None
     return paged_prefill_attention(_bits(p.q), _bits(c.k_cache), _bits(c.v_cache), c.block_tables.numpy(),
                                    c.context_lens.numpy(), p.cu_seqlens.numpy(), p.scale,
+                                   k_scale=c.k_scale.numpy() if fp8 else None,
+                                   v_scale=c.v_scale.numpy() if fp8 else None,
+                                   kv_dtype="fp8_e4m3fn" if fp8 else "bf16",
                                    batch_subset=batch_subset, row_subset=row_subset,
                                    sliding_window=p.sliding_window or None,
                                    sinks=None if c.sinks is None else c.sinks.numpy())
@@ -46,10 +50,10 @@ def _run(p, max_query_len=None, extra_rows=0, ext=None):
     c = d.cache
     if ext or (ext is None and (p.sliding_window or c.sinks is not None)):
         B.paged_attn_prefill_ext(q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens, mql,
-                                 p.scale, p.sliding_window, c.sinks, out)
+                                 p.scale, p.sliding_window, c.sinks, out, k_scale=c.k_scale, v_scale=c.v_scale)
     else:
         B.paged_attn_prefill(q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens, mql, p.scale,
-                             out)
+                             out, k_scale=c.k_scale, v_scale=c.v_scale)
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -72,7 +76,7 @@ def _compare(out, ref, label, rows=None):
 def _check(p, label, **kw):
     note(f"[gpu] prefill {label}: ctx={p.cache.context_lens.tolist()[:6]} chunks={p.chunk_lens.tolist()[:6]} "
          f"heads={p.spec.hq}/{p.spec.hkv} d={p.spec.head_dim} bs={p.spec.block_size} "
-         f"window={p.sliding_window} sinks={p.sinks is not None}")
+         f"window={p.sliding_window} sinks={p.sinks is not None} kv={p.spec.kv_dtype}")
     out = _run(p, **kw)
     _compare(out, _oracle(p), label)
     return out
@@ -284,6 +288,75 @@ def test_ext_argument_errors():
         B.paged_attn_prefill_ext(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
                                  p.max_query_len, p.scale, 32, c.sinks.to(torch.bfloat16), out)
     assert e.value.name == "PA_ERR_DTYPE"
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+# --------------------------------------------------------------------------
+# fp8 e4m3fn cache with per-token scales
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 8), (64, 1)])
+def test_fp8_cache(d, hq, hkv):
+    p = generate_prefill(SMALL.replace(kv_dtype="fp8_e4m3fn", hq=hq, hkv=hkv, head_dim=d, seed=80 + hq + hkv + d))
+    _check(p, f"fp8/heads{hq}/{hkv}/d{d}")
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_fp8_block_sizes_window_and_sinks(bs):
+    p = generate_prefill(SWA.replace(kv_dtype="fp8_e4m3fn", block_size=bs, pool_blocks=3 * (-(-700 // bs)) + 2,
+                                     sliding_window=50, sinks=True, seed=90 + bs))
+    _check(p, f"fp8/bs{bs}/window50/sinks")
+
+
+def test_fp8_sharpened_queries_and_chunk_edges():
+    p = generate_prefill(SMALL.replace(kv_dtype="fp8_e4m3fn", seed=95))
+    p.q = (p.q.float() * 8.0).to(torch.bfloat16)
+    _check(p, "fp8 sharp8")
+    ctx = [max(c, 1) + 37 * i for i, c in enumerate(EDGE_CHUNKS)]
+    spec = SMALL.replace(kv_dtype="fp8_e4m3fn", batch=len(ctx), ctx_hi=max(ctx), pool_blocks=400, seed=96)
+    _check(generate_prefill(spec, context_lens=ctx, chunk_lens=EDGE_CHUNKS), "fp8 edges")
+
+
+def test_fp8_nan_scales_and_codes_in_unread_slots():
+    """NaN codes (0x7F) and NaN scales past each sequence's length, and in
+    unused blocks, never reach the output."""
+    p = generate_prefill(SMALL.replace(kv_dtype="fp8_e4m3fn", seed=97))
+    c = p.cache
+    ref = _oracle(p)
+    used = set()
+    for b in range(p.spec.batch):
+        L = int(c.context_lens[b])
+        nb = -(-L // 16)
+        used.update(int(x) for x in c.block_tables[b, :nb])
+        last = int(c.block_tables[b, nb - 1])
+        tail = L - (nb - 1) * 16
+        c.k_cache[last, tail:] = 0x7F
+        c.v_cache[last, tail:] = 0x7F
+        c.k_scale[last, tail:] = float("nan")
+        c.v_scale[last, tail:] = float("nan")
+    for blk in range(p.spec.pool_blocks):
+        if blk not in used:
+            c.k_cache[blk] = 0x7F
+            c.v_cache[blk] = 0x7F
+            c.k_scale[blk] = float("nan")
+            c.v_scale[blk] = float("nan")
+    note("[gpu] prefill fp8 poison")
+    _compare(_run(p), ref, "fp8 poison")
+
+
+def test_fp8_argument_errors():
+    p = generate_prefill(SMALL.replace(kv_dtype="fp8_e4m3fn", seed=98)).to("cuda")
+    c = p.cache
+    out = torch.full_like(p.q, 3.0)
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_prefill(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                             p.max_query_len, p.scale, out)                      # scales missing
+    assert e.value.name == "PA_ERR_NULL"
+    with pytest.raises(B.PagedAttnError) as e:
+        B.paged_attn_prefill(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                             p.max_query_len, p.scale, out, k_scale=c.k_scale[:, :8], v_scale=c.v_scale)
+    assert e.value.name == "PA_ERR_SHAPE"
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
 

@@ -47,6 +47,8 @@ MUTANTS = {
                                "sliding_window=None, sinks=sinks)"),
     "prefill_sinks_dropped": ("prefill.py", "sliding_window=sliding_window, sinks=sinks)",
                               "sliding_window=sliding_window, sinks=None)"),
+    "prefill_fp8_scales_swapped": ("prefill.py", "scale, k_scale, v_scale, kv_dtype,",
+                                   "scale, v_scale, k_scale, kv_dtype,"),
     "e4m3_subnormal": ("formats.py", "man_field * 2.0 ** -9", "man_field * 2.0 ** -10"),
     "e4m3_bias": ("formats.py", "2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
     "e4m3_mantissa": ("formats.py", "(1.0 + man_field / 8.0)", "(1.0 + man_field / 16.0)"),

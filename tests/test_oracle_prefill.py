@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle import bf16_bits_to_f64, paged_prefill_attention
-from test_oracle import _bf16_bits
+from test_oracle import _bf16_bits, _page, _sdpa_reference
 from test_oracle_variants import _paged, _sdpa_masked, _seqs
 
 
@@ -167,6 +167,42 @@ def test_window_of_one_returns_the_rows_own_value():
             np.testing.assert_array_equal(out[cu[b] + r], np.repeat(bf16_bits_to_f64(vs[b][L - n + r]), hq, axis=0))
 
 
+def _fp8_case(rng, lens, chunks, hq, hkv, d):
+    """Random e4m3fn codes (no NaN) and per-token scales for each sequence,
+    paged into a pool with the scales following their slots."""
+    ks8, vs8, kss, vss = [], [], [], []
+    for L in lens:
+        for store, sc in ((ks8, kss), (vs8, vss)):
+            c = rng.integers(0, 256, (L, hkv, d)).astype(np.uint8)
+            c[(c & 0x7F) == 0x7F] = 0x3A
+            store.append(c)
+            sc.append(rng.uniform(0.001, 0.02, (L, hkv)).astype(np.float32))
+    kp, vp, t = _page(ks8, vs8, hkv, d, rng, dtype=np.uint8)
+    ksc = np.ones((kp.shape[0], 16, hkv), np.float32)
+    vsc = np.ones_like(ksc)
+    for b, L in enumerate(lens):
+        for j in range(L):
+            ksc[t[b, j // 16], j % 16] = kss[b][j]
+            vsc[t[b, j // 16], j % 16] = vss[b][j]
+    return ks8, vs8, kss, vss, kp, vp, t, ksc, vsc
+
+
+def test_fp8_cache_matches_torch_sdpa_on_dequantised_values():
+    """An e4m3fn cache with per-token scales: torch float64 SDPA on the
+    decoded codes times their scales (torch's own e4m3fn decoding)."""
+    rng = np.random.default_rng(13)
+    hq, hkv, d = 8, 2, 16
+    lens, chunks = (3, 40, 90), (3, 15, 50)
+    ks8, vs8, kss, vss, kp, vp, t, ksc, vsc = _fp8_case(rng, lens, chunks, hq, hkv, d)
+    qp, cu = _pack(rng, lens, chunks, hq, d)
+    scale = np.float32(0.25)
+    out = paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, ksc, vsc, kv_dtype="fp8_e4m3fn")
+    ref = _sdpa_reference(_padded(qp, cu, chunks, hq, d), ks8, vs8, lens, chunks, float(scale), hq, hkv, kss, vss,
+                          fp8=True)
+    for b, n in enumerate(chunks):
+        np.testing.assert_allclose(out[cu[b]:cu[b + 1]], ref[b, :n], rtol=0, atol=1e-12)
+
+
 def prefill_battery(orc) -> bool:
     """The pins above in brief, against a (possibly mutated) oracle copy."""
     rng = np.random.default_rng(9)
@@ -192,4 +228,13 @@ def prefill_battery(orc) -> bool:
             return False
     partw = orc.paged_prefill_attention(qp, kp, vp, t, lens, cu, scale, batch_subset=[1], row_subset=[20],
                                         sliding_window=9, sinks=sinks)
-    return bool(np.allclose(partw[cu[1] + 20], refw[1, 20], rtol=0, atol=1e-12))
+    if not np.allclose(partw[cu[1] + 20], refw[1, 20], rtol=0, atol=1e-12):
+        return False
+    # an fp8 cache with per-token scales
+    lens8, chunks8 = (20, 33), (20, 9)
+    ks8, vs8, kss, vss, kp8, vp8, t8, ksc, vsc = _fp8_case(rng, lens8, chunks8, hq, hkv, d)
+    qp8, cu8 = _pack(rng, lens8, chunks8, hq, d)
+    out8 = orc.paged_prefill_attention(qp8, kp8, vp8, t8, lens8, cu8, scale, ksc, vsc, kv_dtype="fp8_e4m3fn")
+    ref8 = _sdpa_reference(_padded(qp8, cu8, chunks8, hq, d), ks8, vs8, lens8, chunks8, float(scale), hq, hkv,
+                           kss, vss, fp8=True)
+    return all(np.allclose(out8[cu8[b]:cu8[b + 1]], ref8[b, :n], rtol=0, atol=1e-12) for b, n in enumerate(chunks8))
