@@ -263,7 +263,9 @@ def prefill_bytes(pf) -> int:
     tokens = 0
     for L, n in zip(pf.cache.context_lens.tolist(), pf.chunk_lens.tolist()):
         tokens += L - (max(0, L - n - w + 1) if w > 0 and n > 0 else 0)
-    return 2 * pf.q.numel() * 2 + tokens * s.hkv * s.head_dim * 2 * 2
+    per_token = s.hkv * (s.head_dim * 2 * (1 if s.kv_dtype == "fp8_e4m3fn" else 2)
+                         + (8 if s.kv_dtype == "fp8_e4m3fn" else 0))
+    return 2 * pf.q.numel() * 2 + tokens * per_token
 
 
 def bench_prefill(args):
@@ -287,10 +289,11 @@ def bench_prefill(args):
     def call(stream=None):
         if ext:
             B.paged_attn_prefill_ext(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
-                                     pf.max_query_len, pf.scale, spec.sliding_window, c.sinks, out, stream=stream)
+                                     pf.max_query_len, pf.scale, spec.sliding_window, c.sinks, out, stream=stream,
+                                     k_scale=c.k_scale, v_scale=c.v_scale)
         else:
             B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, d.cu_seqlens,
-                                 pf.max_query_len, pf.scale, out, stream=stream)
+                                 pf.max_query_len, pf.scale, out, stream=stream, k_scale=c.k_scale, v_scale=c.v_scale)
 
     for _ in range(args.warmup):
         call()
@@ -323,9 +326,10 @@ def bench_prefill(args):
     res = {
         "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3fn-kv/bf16-mfma" if spec.kv_dtype == "fp8_e4m3fn" else "bf16", "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.batch, "q_heads": spec.hq, "kv_heads": spec.hkv,
-                   "head_dim": spec.head_dim, "kv_dtype": "bf16", "block_size": spec.block_size,
+                   "head_dim": spec.head_dim, "kv_dtype": spec.kv_dtype, "block_size": spec.block_size,
                    "sliding_window": spec.sliding_window or None, "sinks": spec.sinks,
                    "context_lens": [int(x) for x in pf.cache.context_lens],
                    "chunk_lens": [int(x) for x in pf.chunk_lens]},
@@ -346,6 +350,9 @@ def bench_prefill(args):
         def bits(t):
             return t.view(torch.int16).numpy().view("uint16") if t.dtype == torch.bfloat16 else t.numpy()
         qb, kb, vb = bits(pf.q), bits(h.k_cache), bits(h.v_cache)
+        fp8 = h.k_scale is not None
+        kscale = h.k_scale.numpy() if fp8 else None
+        vscale = h.v_scale.numpy() if fp8 else None
         tables, ctx, cu = h.block_tables.numpy(), h.context_lens.numpy(), pf.cu_seqlens.numpy()
         sinks = None if h.sinks is None else h.sinks.numpy()
         w = spec.sliding_window
@@ -356,7 +363,8 @@ def bench_prefill(args):
             while t < args.cpu_seconds and rows_done < n:
                 rows = list(range(n - 1 - r, max(n - 1 - r - 8, -1), -1))    # the longest rows first
                 t0 = time.perf_counter()
-                paged_prefill_attention(qb, kb, vb, tables, ctx, cu, pf.scale, batch_subset=[b], row_subset=rows,
+                paged_prefill_attention(qb, kb, vb, tables, ctx, cu, pf.scale, kscale, vscale,
+                                        "fp8_e4m3fn" if fp8 else "bf16", batch_subset=[b], row_subset=rows,
                                         sliding_window=w, sinks=sinks)
                 t += time.perf_counter() - t0
                 L = int(ctx[b])

@@ -477,6 +477,10 @@ PREFILL_CONFIGS = {
     "chunked_prefill": PrefillSpec("chunked_prefill_b4_q64kv8_d128_chunk2048_ctx2k-16k_bf16", batch=4, hq=64,
                                    hkv=8, head_dim=128, ctx_lo=2048, ctx_hi=16384, chunk_lo=2048,
                                    chunk_hi=2048, pool_blocks=4200, seed=22),
+    # the chunked workload over an fp8 e4m3fn cache with per-token scales
+    "chunked_prefill_fp8": PrefillSpec("chunked_prefill_b4_q64kv8_d128_chunk2048_ctx2k-16k_fp8", batch=4, hq=64,
+                                       hkv=8, head_dim=128, ctx_lo=2048, ctx_hi=16384, chunk_lo=2048,
+                                       chunk_hi=2048, pool_blocks=4200, seed=22, kv_dtype="fp8_e4m3fn"),
     # GPT-OSS-shaped sliding-window layers (64 query / 8 kv heads of 64, a
     # 128-token window and sink logits): four whole 8192-token prompts
     "prefill_swa_sinks": PrefillSpec("prefill_swa128_sinks_b4_q64kv8_d64_prompt8192_bf16", batch=4, hq=64, hkv=8,

@@ -368,6 +368,7 @@ def test_fp8_argument_errors():
     ("prefill_8k", 0, [0, 1, 31, 32, 255, 256, 4095, 4096, 8190, 8191]),
     ("chunked_prefill", 1, [0, 1, 63, 64, 1000, 2047]),
     ("chunked_prefill", 3, [0, 511, 2047]),
+    ("chunked_prefill_fp8", 0, [0, 1, 1000, 2047]),
     ("prefill_swa_sinks", 0, [0, 1, 126, 127, 128, 129, 4095, 8191]),
     ("prefill_swa_sinks", 3, [0, 200, 8191]),
 ])
