@@ -43,28 +43,7 @@ struct WriteProblem {
 };
 
 // A validated prefill call (paged_attn_prefill).
-struct PrefillProblem {
-    int64_t B, T, Hq, Hkv, G, D, NB, W, BS;
-    float scale;
-    const void* q;  int64_t q_st, q_sh;                // bytes
-    void* out;      int64_t o_st, o_sh;                // bytes
-    const void* k;  int64_t k_sblk, k_stok, k_sh;      // bytes
-    const void* v;  int64_t v_sblk, v_stok, v_sh;      // bytes
-    const int32_t* bt; int64_t bt_sb;                  // int32 elements
-    const int32_t* ctx; int64_t ctx_s;
-    const int32_t* cu;  int64_t cu_s;
-    int32_t window;                                    // sliding window in tokens, 0 = none
-    const float* sinks; int64_t sinks_s;               // per query head, may be null
-    bool fp8;                                          // e4m3fn cache with per-token scales
-    const float* ks; int64_t ks_sblk, ks_sh;           // floats
-    const float* vs; int64_t vs_sblk, vs_sh;
-};
 
-int validate_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
-                     const pa_tensor* block_tables, const pa_tensor* context_lens,
-                     const pa_tensor* cu_seqlens_q, int32_t max_query_len, float scale,
-                     const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t window,
-                     const pa_tensor* sinks, const pa_tensor* out, PrefillProblem* p);
 
 int validate_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
                    const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* k_scale,
@@ -87,6 +66,16 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
 
 // Records a failure description for paged_attn_last_error() and returns `status`.
 int fail(int status, const char* fmt, ...);
+
+// Descriptor checks shared by the entry points' validation.
+int64_t elem_bytes(int32_t dtype);
+const char* dtype_name(int32_t dtype);
+bool aligned(const void* p, uintptr_t a);
+// rank in [ndim_lo, ndim_hi], the dtype, non-negative sizes and strides, and
+// (need_data) a data pointer when the tensor is not empty
+int check_desc(const pa_tensor* t, const char* name, int32_t dtype, int ndim_lo, int ndim_hi, bool need_data);
+// inner stride 1, other strides multiples of 16 bytes, base 16-byte aligned
+int check_rows16(const pa_tensor* t, const char* name);
 
 constexpr int kChunkTokens = 32;            // tokens per chunk: the unit of work splitting
 constexpr int kMaxBlockSize = 4096;         // largest tokens-per-block (a multiple of 16)
