@@ -107,8 +107,8 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
                     (long long)BS, kMaxBlockSize);
     if (kc->shape[3] != D)
         return fail(PA_ERR_SHAPE, "k_cache: head_dim %lld, q has %lld", (long long)kc->shape[3], (long long)D);
-    if (D != 64 && D != 128)
-        return fail(PA_ERR_UNSUPPORTED, "prefill: head_dim %lld, only 64 and 128 are supported", (long long)D);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: head_dim %lld, only 64, 128 and 256 are supported", (long long)D);
     if (Hkv < 1) return fail(PA_ERR_SHAPE, "k_cache: no kv heads");
     if (Hq % Hkv != 0 || Hq == 0)
         return fail(PA_ERR_UNSUPPORTED, "q_heads %lld is not a positive multiple of kv_heads %lld",
@@ -116,6 +116,9 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* v
     const int64_t G = Hq / Hkv;
     if (G > PA_MAX_ROWS)
         return fail(PA_ERR_UNSUPPORTED, "prefill: q_heads / kv_heads = %lld exceeds %d", (long long)G, PA_MAX_ROWS);
+    if (D == 256 && G > PA_MAX_ROWS_D256)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: head_dim 256 takes q_heads / kv_heads up to %d, not %lld",
+                    PA_MAX_ROWS_D256, (long long)G);
     const int64_t B = bt->shape[0], W = bt->shape[1];
     if (ctx->shape[0] != B)
         return fail(PA_ERR_SHAPE, "context_lens: %lld entries, block_tables has %lld rows", (long long)ctx->shape[0],
@@ -736,7 +739,9 @@ struct PrefillShape {
 // work; 64 rows in 4-wave workgroups measured 1.4x slower, one wave per
 // SIMD with its accumulators in AGPRs).  Ratios G > 32 need 64-row waves.
 PrefillShape prefill_shape(int D, int G) {
-    (void)D;
+    // head_dim 256: one 16-row tile per wave (a 256-wide step's fragments
+    // and accumulators leave no room for a second), G <= 16
+    if (D == 256) return {1, 8};
     if (G > 32) return {4, 4};
     return {2, 8};
 }
@@ -747,9 +752,14 @@ const void* prefill_kernel_of_d(PrefillShape sh) {
     return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8, FP8>);
 }
 
+template <bool FP8>
+const void* prefill_kernel_of_f(int D, PrefillShape sh) {
+    if (D == 256) return reinterpret_cast<const void*>(&prefill_kernel<256, 1, 8, FP8>);
+    return D == 128 ? prefill_kernel_of_d<128, FP8>(sh) : prefill_kernel_of_d<64, FP8>(sh);
+}
+
 const void* prefill_kernel_of(int D, bool fp8, PrefillShape sh) {
-    if (fp8) return D == 128 ? prefill_kernel_of_d<128, true>(sh) : prefill_kernel_of_d<64, true>(sh);
-    return D == 128 ? prefill_kernel_of_d<128, false>(sh) : prefill_kernel_of_d<64, false>(sh);
+    return fp8 ? prefill_kernel_of_f<true>(D, sh) : prefill_kernel_of_f<false>(D, sh);
 }
 
 }  // namespace
@@ -803,8 +813,10 @@ int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const p
     const int64_t grid = (int64_t)a.qblocks * p.B * p.Hkv;
     if (grid >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: grid too large");
     const void* fn = prefill_kernel_of((int)p.D, p.fp8, sh);
-    const size_t lds = 2 * (size_t)(p.fp8 ? (p.D == 128 ? kBufBytes<128, true> : kBufBytes<64, true>)
-                                          : (p.D == 128 ? kBufBytes<128, false> : kBufBytes<64, false>));
+    const size_t buf = p.D == 256 ? (p.fp8 ? kBufBytes<256, true> : kBufBytes<256, false>)
+                       : p.D == 128 ? (p.fp8 ? kBufBytes<128, true> : kBufBytes<128, false>)
+                                    : (p.fp8 ? kBufBytes<64, true> : kBufBytes<64, false>);
+    const size_t lds = 2 * buf;
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * sh.waves), args, lds,
                         static_cast<hipStream_t>(stream)) != hipSuccess)

@@ -477,6 +477,10 @@ PREFILL_CONFIGS = {
     "chunked_prefill": PrefillSpec("chunked_prefill_b4_q64kv8_d128_chunk2048_ctx2k-16k_bf16", batch=4, hq=64,
                                    hkv=8, head_dim=128, ctx_lo=2048, ctx_hi=16384, chunk_lo=2048,
                                    chunk_hi=2048, pool_blocks=4200, seed=22),
+    # Gemma-2-9B-shaped head_dim 256 (16 query / 8 kv heads): one whole
+    # 8192-token prompt
+    "prefill_d256": PrefillSpec("prefill_b1_q16kv8_d256_prompt8192_bf16", batch=1, hq=16, hkv=8, head_dim=256,
+                                ctx_lo=8192, ctx_hi=8192, chunk_lo=0, chunk_hi=0, pool_blocks=600, seed=24),
     # the chunked workload over an fp8 e4m3fn cache with per-token scales
     "chunked_prefill_fp8": PrefillSpec("chunked_prefill_b4_q64kv8_d128_chunk2048_ctx2k-16k_fp8", batch=4, hq=64,
                                        hkv=8, head_dim=128, ctx_lo=2048, ctx_hi=16384, chunk_lo=2048,

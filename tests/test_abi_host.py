@@ -443,7 +443,10 @@ def test_prefill_validation():
     assert status(k_cache=k8, v_cache=v8, k_scale=sc[:, :8], v_scale=sc) == "PA_ERR_SHAPE"
     assert status(k_cache=k8, v_cache=v8, k_scale=torch.ones(NB, 16, 2), v_scale=sc) == "PA_ERR_LAYOUT"   # slots strided
     assert status(k_scale=torch.ones(NB, 16, 2)) == "PA_ERR_ARG"
-    t = _prefill_tensors(d=256)
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**_prefill_tensors(d=256))] == "PA_OK"
+    t = _prefill_tensors(d=256, hq=64, hkv=2)                                         # ratio 32 > 16 at head_dim 256
+    assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"
+    t = _prefill_tensors(d=96)
     assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"
     t = _prefill_tensors(hq=6, hkv=4)
     assert B.STATUS_NAMES[B.paged_attn_check_prefill(**t)] == "PA_ERR_UNSUPPORTED"

@@ -293,6 +293,24 @@ def test_ext_argument_errors():
 
 
 # --------------------------------------------------------------------------
+# head_dim 256 (one 16-row tile per wave: q_heads / kv_heads <= 16)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (8, 8), (32, 2), (16, 1), (12, 4)])
+def test_head_dim_256(hq, hkv):
+    p = generate_prefill(SMALL.replace(hq=hq, hkv=hkv, head_dim=256, seed=100 + hq + hkv))
+    _check(p, f"d256/heads{hq}/{hkv}")
+
+
+def test_head_dim_256_fp8_window_sinks_and_edges():
+    p = generate_prefill(SWA.replace(head_dim=256, hq=16, hkv=8, kv_dtype="fp8_e4m3fn", sliding_window=70,
+                                     sinks=True, seed=106))
+    _check(p, "d256/fp8/window70/sinks")
+    ctx = [max(c, 1) + 37 * i for i, c in enumerate(EDGE_CHUNKS)]
+    spec = SMALL.replace(head_dim=256, hq=16, hkv=8, batch=len(ctx), ctx_hi=max(ctx), pool_blocks=400, seed=107)
+    _check(generate_prefill(spec, context_lens=ctx, chunk_lens=EDGE_CHUNKS), "d256 edges")
+
+
+# --------------------------------------------------------------------------
 # fp8 e4m3fn cache with per-token scales
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("d", [64, 128])
@@ -369,6 +387,7 @@ def test_fp8_argument_errors():
     ("chunked_prefill", 1, [0, 1, 63, 64, 1000, 2047]),
     ("chunked_prefill", 3, [0, 511, 2047]),
     ("chunked_prefill_fp8", 0, [0, 1, 1000, 2047]),
+    ("prefill_d256", 0, [0, 1, 63, 64, 4095, 8191]),
     ("prefill_swa_sinks", 0, [0, 1, 126, 127, 128, 129, 4095, 8191]),
     ("prefill_swa_sinks", 3, [0, 200, 8191]),
 ])

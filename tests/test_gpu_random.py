@@ -42,6 +42,8 @@ def prefill_spec(i):
     d = int(rng.choice([64, 128]))
     hkv = int(rng.choice([1, 2, 4, 8]))
     g = int(rng.choice([1, 2, 3, 4, 8, 16, 64]))
+    if i % 6 == 5:                                  # head_dim 256 takes ratios up to 16
+        d, g = 256, int(rng.choice([1, 2, 4, 16]))
     bs = int(rng.choice([16, 16, 32, 64, 256]))
     batch = int(rng.integers(1, 9))
     ctx_hi = int(rng.integers(1, 600))
