@@ -50,7 +50,28 @@ def build(verbose: bool = False) -> str:
     finally:
         if os.path.exists(tmp):
             os.remove(tmp)
+    build_cli(verbose)
     return LIB_PATH
+
+
+CLI_SOURCE = os.path.join(PKG, "c_example", "pa_decode_cli.c")
+CLI_PATH = os.path.join(PKG, "pa_decode_cli")
+
+
+def build_cli(verbose: bool = False) -> str:
+    """Compile the C caller of the library (plain C: the HIP runtime API for
+    device memory, the library through paged_attn.h)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), CLI_SOURCE, "-o", CLI_PATH,
+           "-L", PKG, "-lpaged_attn", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    return CLI_PATH
 
 
 if __name__ == "__main__":
