@@ -198,6 +198,63 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
 
 
+def test_strided_tensors():
+    """q and out as views into padded buffers, a block table that is a column
+    slice of a wider one, and context lengths and row offsets with stride 2:
+    the same bytes through every stride the kernel takes."""
+    p = generate_prefill(SMALL.replace(kv_dtype="fp8_e4m3fn", sliding_window=90, sinks=True, seed=49))
+    ref = _oracle(p)
+    d = p.to("cuda")
+    c = d.cache
+    T, Hq, D = d.q.shape
+    qbig = torch.zeros(T, Hq + 3, D + 64, dtype=torch.bfloat16, device="cuda")
+    q = qbig[:, 1:1 + Hq, 32:32 + D]
+    q.copy_(d.q)
+    obig = torch.empty(T, Hq, 2 * D, dtype=torch.bfloat16, device="cuda")
+    obig.view(torch.int16).fill_(CANARY)
+    out = obig[:, :, D:]
+    W = c.block_tables.shape[1]
+    tbig = torch.zeros(c.block_tables.shape[0], W + 5, dtype=torch.int32, device="cuda")
+    tbig[:, 2:2 + W] = c.block_tables
+    ctx2 = torch.zeros(2 * len(c.context_lens), dtype=torch.int32, device="cuda")
+    ctx2[::2] = c.context_lens
+    cu2 = torch.zeros(2 * len(d.cu_seqlens), dtype=torch.int32, device="cuda")
+    cu2[::2] = d.cu_seqlens
+    note("[gpu] prefill strided tensors")
+    B.paged_attn_prefill_ext(q, c.k_cache, c.v_cache, tbig[:, 2:2 + W], ctx2[::2], cu2[::2], p.max_query_len,
+                             p.scale, p.sliding_window, c.sinks, out, k_scale=c.k_scale, v_scale=c.v_scale)
+    torch.cuda.synchronize()
+    _compare(out.cpu(), ref, "strided")
+    assert torch.all(obig[:, :, :D].view(torch.int16) == CANARY), "bytes outside the out view written"
+
+
+def test_graph_capture_fp8_window_sinks():
+    p = generate_prefill(SWA.replace(kv_dtype="fp8_e4m3fn", sliding_window=60, sinks=True, seed=50)).to("cuda")
+    c = p.cache
+
+    def call(out, s):
+        B.paged_attn_prefill_ext(p.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, p.cu_seqlens,
+                                 p.max_query_len, p.scale, p.sliding_window, c.sinks, out, stream=s,
+                                 k_scale=c.k_scale, v_scale=c.v_scale)
+    note("[gpu] prefill graph capture fp8/window/sinks")
+    s = torch.cuda.Stream()
+    eager = torch.empty_like(p.q)
+    with torch.cuda.stream(s):
+        call(eager, s)
+    s.synchronize()
+    out = torch.empty_like(p.q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(out, s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.view(torch.int16).fill_(CANARY)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
+
+
 def test_argument_errors_launch_nothing():
     p = generate_prefill(SMALL.replace(seed=47)).to("cuda")
     c = p.cache
