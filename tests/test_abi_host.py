@@ -282,13 +282,13 @@ def test_plan_grids():
     p = B.paged_attn_plan(4, 32, 8, 128, 1, 16 * 512)                 # 4 x <= 8192 tokens
     assert p["heads_per_group"] == 2 and p["workgroups"] == 256
     p = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192)                # 131072 tokens, batch 1
-    assert p["heads_per_group"] == 8 and p["workgroups"] == 256
+    assert p["heads_per_group"] == 4 and p["workgroups"] == 256   # 256-byte rows: one wave per SIMD
     p = B.paged_attn_plan(16, 64, 8, 64, 1, 16 * 2048)                # fp8-sized rows, bf16 cache
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256
     p = B.paged_attn_plan(16, 64, 8, 64, 1, 16 * 2048, kv_dtype="fp8_e4m3fn")
     assert p["heads_per_group"] == 8 and p["workgroups"] == 256   # whole token rows per workgroup
     p = B.paged_attn_plan(64, 64, 8, 128, 2, 16 * 1024)               # MTP verify
-    assert p["heads_per_group"] == 8 and p["workgroups"] == 256
+    assert p["heads_per_group"] == 4 and p["workgroups"] == 256
     p = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * 8192, num_cus=8)     # a small device
     assert p["workgroups"] == 8
 
