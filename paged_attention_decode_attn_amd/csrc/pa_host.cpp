@@ -387,10 +387,14 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     // same grid with half the heads per workgroup, one wave per SIMD, each
     // wave streaming twice as many chunks.  One wave keeps enough bytes in
     // flight at these row sizes and no longer shares its SIMD's issue and
-    // memory arbitration (measured: 131072-token calls 2.7 % faster, with
-    // 256-token blocks 3-7 % faster and no longer placement-sensitive; MTP
-    // verify and MHA unchanged; head_dim 64 rows, 64 or 128 bytes, lose).
-    if (hg_over <= 0 && HG % 2 == 0 && n * HG >= 8 * int64_t(num_cus) && D * (fp8 ? 1 : 2) >= 256) HG /= 2;
+    // memory arbitration (measured: 131072-token calls 3.8 % faster, with
+    // 256-token blocks 10 % faster and no longer placement-sensitive, MTP
+    // verify 2 % faster, MHA unchanged; head_dim-64 rows of 64 or 128 bytes
+    // lose).
+    // (Halving doubles the segments, so the chunk index must still fit.)
+    if (hg_over <= 0 && HG % 2 == 0 && n * HG >= 8 * int64_t(num_cus) && D * (fp8 ? 1 : 2) >= 256 &&
+        2 * max_chunks < (int64_t(1) << 31))
+        HG /= 2;
     // Merge shape.  Expected partials per row: one per workgroup whose share
     // meets the row's segment, about n / (B * groups) + 1 when the lengths are
     // alike (a lopsided batch only takes more rounds of loads), exactly n for

@@ -42,9 +42,6 @@ struct WriteProblem {
     float* vs; int64_t vs_sblk, vs_sh;
 };
 
-// A validated prefill call (paged_attn_prefill).
-
-
 int validate_write(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
                    const pa_tensor* k_cache, const pa_tensor* v_cache, const pa_tensor* k_scale,
                    const pa_tensor* v_scale, WriteProblem* p);

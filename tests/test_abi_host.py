@@ -316,6 +316,16 @@ def test_plan_rejects_chunk_index_overflow():
         B.paged_attn_plan(16384, 8, 8, 128, 1, 16 * 1 << 20)
 
 
+def test_plan_keeps_whole_rows_when_halving_would_overflow_the_chunk_index():
+    # 16384 sequences x 100000 chunks fit the 31-bit chunk index with one
+    # head group but not with two, so the heads per workgroup stay whole;
+    # a quarter of that context takes one wave per SIMD as usual
+    p = B.paged_attn_plan(16384, 64, 8, 128, 1, 32 * 100000)
+    assert p["heads_per_group"] == 8 and p["workgroups"] == 256
+    p = B.paged_attn_plan(16384, 64, 8, 128, 1, 32 * 25000)
+    assert p["heads_per_group"] == 4 and p["workgroups"] == 256
+
+
 def test_plan_rejects_bad_sizes():
     with pytest.raises(B.PagedAttnError):
         B.paged_attn_plan(1, 6, 4, 128, 1, 16 * 4)
