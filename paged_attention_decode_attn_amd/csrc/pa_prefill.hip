@@ -402,6 +402,25 @@ __device__ __forceinline__ u32x2 read_vt(const char* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
+// Wave priority over the phases of a tile (s_setprio).  The two waves of a
+// SIMD run the same phases at about the same time (they meet at every tile's
+// barrier); raising a wave's priority while it reads K/V fragments and issues
+// matrix instructions, and lowering it for the softmax arithmetic, lets the
+// other wave's softmax fill the matrix unit's gaps instead of competing with
+// its issue.  Which phases pay depends on the shape (measured on MI355X,
+// 8k-token prompts and 2k-row chunks): head_dim 128 bf16 fragments + score
+// product and value product, 9 % faster; with an fp8 cache the whole tile,
+// 4 %, leaving the conversion work around the next tile's stores at the base
+// priority; head_dim 256 fragments + score product, 10 % (fp8 2 %), the value
+// product included slower; head_dim 64 bf16 the value product, 1.5 %; fp8
+// head_dim 64 and the 64-row waves none (every variant slower).
+enum TilePrio { kPrioNone, kPrioScores, kPrioMatrix, kPrioTile, kPrioValue };
+template <int D, int NT, bool FP8>
+constexpr TilePrio kTilePrio = NT == 4 ? kPrioNone
+                             : D == 256 ? kPrioScores
+                             : D == 128 ? (FP8 ? kPrioTile : kPrioMatrix)
+                             : (FP8 ? kPrioNone : kPrioValue);
+
 // One 32-key tile of one wave: K fragments (A operand, token = lane % 16,
 // head_dim 8 * (lane / 16) ... of each 32-wide step) and V^T fragments
 // (A operand, head_dim 16 j + lane % 16, the eight keys 4 (lane / 16) + i
@@ -416,7 +435,9 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
                                           const char* lds_v, const float* lds_ks, const int (&lim)[NT],
                                           const int (&low)[NT], int kbase, float c, int lane, bool masked) {
     constexpr int J = D / 16;
+    constexpr TilePrio P = kTilePrio<D, NT, FP8>;
     const int n16 = lane & 15, grp = lane >> 4;
+    if constexpr (P == kPrioScores || P == kPrioMatrix || P == kPrioTile) __builtin_amdgcn_s_setprio(1);
     bf16x8 kf[2][D / 32];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -454,6 +475,7 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qb, s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qb, s1, 0, 0, 0);
         }
+        if constexpr (P == kPrioScores || P == kPrioMatrix) __builtin_amdgcn_s_setprio(0);
         float y[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -494,6 +516,7 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
 #pragma unroll
         for (int w = 0; w < 4; ++w) pw[w] = pack_bf16_rne(p[2 * w], p[2 * w + 1]);
         const bf16x8 pb = as_bf16x8(pw);
+        if constexpr (P == kPrioMatrix || P == kPrioValue) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < J; ++j)
             s.o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vt[j]), pb, s.o[nt][j], 0, 0, 0);
@@ -502,7 +525,9 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         // from the same bf16 P as the accumulators
         s.l[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{kOnes, kOnes, kOnes, kOnes}), pb, s.l[nt],
                                                          0, 0, 0);
+        if constexpr (P == kPrioMatrix || P == kPrioValue) __builtin_amdgcn_s_setprio(0);
     }
+    if constexpr (P == kPrioTile) __builtin_amdgcn_s_setprio(0);
 }
 
 // Longest work first.  Workgroup (b, qb, g) reads the keys below
