@@ -33,9 +33,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # plans its launch; a counter record is valid only for the digest it was
 # taken under
 _CSRC = os.path.join(ROOT, "paged_attention_decode_attn_amd", "csrc")
-KERNEL_SOURCES = {op: [os.path.join(_CSRC, f) for f in (k, "pa_host.cpp", "pa_internal.h")]
-                  for op, k in (("decode", "pa_device.hip"), ("cache_write", "pa_cache.hip"),
-                                ("prefill", "pa_prefill.hip"))}
+KERNEL_SOURCES = {op: [os.path.join(_CSRC, f) for f in (*k, "pa_host.cpp", "pa_internal.h")]
+                  for op, k in (("decode", ("pa_device.hip",)), ("cache_write", ("pa_cache.hip",)),
+                                ("prefill", ("pa_prefill.hip", "pa_prefill_host.cpp", "pa_prefill_internal.h")))}
 
 
 def parse_args():

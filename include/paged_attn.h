@@ -64,7 +64,10 @@ typedef enum pa_status {
     PA_ERR_SHAPE       = -3,  /* ranks or sizes disagree between tensors     */
     PA_ERR_UNSUPPORTED = -4,  /* block size not a multiple of 16, head_dim
                                  not 64/128/256,
-                                 q_heads % kv_heads != 0, rows > 64, ...     */
+                                 q_heads % kv_heads != 0, rows > 64, a size
+                                 or a tensor's byte extent of 2^48 or more,
+                                 more than 65536 kv heads, 2^31 or more
+                                 cache blocks, ...                           */
     PA_ERR_LAYOUT      = -5,  /* inner stride != 1, misaligned base/stride   */
     PA_ERR_CAPTURE     = -6,  /* workspace would have to grow while the
                                  stream is being captured into a graph       */

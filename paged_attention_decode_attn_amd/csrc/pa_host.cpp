@@ -42,7 +42,20 @@ const char* dtype_name(int32_t dtype) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Rank, dtype and non-negative sizes/strides of one descriptor.
+int64_t sat_mul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+int64_t sat_add(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_add_overflow(a, b, &r) ? INT64_MAX : r;
+}
+int64_t used_stride(const pa_tensor* t, int i) { return t->shape[i] > 1 ? t->stride[i] : 0; }
+
+// Rank, dtype, non-negative sizes and strides, sizes and the byte extent
+// (the last element's offset plus one) below 2^48, and a data pointer when
+// the tensor holds elements.  Every later product of a size or a used
+// stride with another bounded size then fits 64 bits.
 int check_desc(const pa_tensor* t, const char* name, int32_t dtype, int ndim_lo, int ndim_hi,
                bool need_data) {
     if (!t) return fail(PA_ERR_NULL, "%s: descriptor is NULL", name);
@@ -51,23 +64,28 @@ int check_desc(const pa_tensor* t, const char* name, int32_t dtype, int ndim_lo,
     if (t->dtype != dtype)
         return fail(PA_ERR_DTYPE, "%s: dtype %s, expected %s", name, dtype_name(t->dtype),
                     dtype_name(dtype));
-    int64_t numel = 1;
+    bool empty = false;
+    int64_t last = 0;                        // element offset of the last element
     for (int i = 0; i < t->ndim; ++i) {
         if (t->shape[i] < 0) return fail(PA_ERR_SHAPE, "%s: negative size in dim %d", name, i);
         if (t->stride[i] < 0) return fail(PA_ERR_LAYOUT, "%s: negative stride in dim %d", name, i);
-        numel *= t->shape[i];
+        if (t->shape[i] >= kMaxSize) return fail(PA_ERR_UNSUPPORTED, "%s: size of dim %d is 2^48 or more", name, i);
+        if (t->shape[i] == 0) empty = true;
+        else last = sat_add(last, sat_mul(t->shape[i] - 1, used_stride(t, i)));
     }
-    if (need_data && numel > 0 && !t->data) return fail(PA_ERR_NULL, "%s: data pointer is NULL", name);
+    if (!empty && sat_mul(sat_add(last, 1), elem_bytes(dtype)) >= kMaxSize)
+        return fail(PA_ERR_UNSUPPORTED, "%s: spans 2^48 bytes or more", name);
+    if (need_data && !empty && !t->data) return fail(PA_ERR_NULL, "%s: data pointer is NULL", name);
     return PA_OK;
 }
 
 // Inner stride 1, other strides multiples of 16 bytes, base 16-byte aligned.
 int check_rows16(const pa_tensor* t, const char* name) {
-    const int64_t eb = elem_bytes(t->dtype);
+    const int64_t eb = elem_bytes(t->dtype);   // 1, 2 or 4: a divisor of 16
     if (t->stride[t->ndim - 1] != 1 && t->shape[t->ndim - 1] > 1)
         return fail(PA_ERR_LAYOUT, "%s: innermost stride must be 1", name);
     for (int i = 0; i + 1 < t->ndim; ++i)
-        if ((t->stride[i] * eb) % 16 != 0 && t->shape[i] > 1)
+        if (t->stride[i] % (16 / eb) != 0 && t->shape[i] > 1)
             return fail(PA_ERR_LAYOUT, "%s: stride of dim %d is not a multiple of 16 bytes", name, i);
     if (!aligned(t->data, 16)) return fail(PA_ERR_LAYOUT, "%s: data is not 16-byte aligned", name);
     return PA_OK;
@@ -135,12 +153,14 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     if (D != 64 && D != 128 && D != 256)
         return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64, 128 and 256 are supported", (long long)D);
     if (Hkv < 1) return fail(PA_ERR_SHAPE, "k_cache: no kv heads");
+    if (Hkv > kMaxHeads) return fail(PA_ERR_UNSUPPORTED, "k_cache: more than %lld kv heads", (long long)kMaxHeads);
+    if (NB > kMaxBlocks) return fail(PA_ERR_UNSUPPORTED, "k_cache: 2^31 blocks or more");
     if (Hq % Hkv != 0 || Hq == 0)
         return fail(PA_ERR_UNSUPPORTED, "q_heads %lld is not a positive multiple of kv_heads %lld",
                     (long long)Hq, (long long)Hkv);
     const int64_t G = Hq / Hkv;
     if (Qmax < 1) return fail(PA_ERR_SHAPE, "q: query length must be >= 1");
-    if (G * Qmax > PA_MAX_ROWS)
+    if (G > PA_MAX_ROWS || Qmax > PA_MAX_ROWS || G * Qmax > PA_MAX_ROWS)
         return fail(PA_ERR_UNSUPPORTED, "(q_heads / kv_heads) * query_len = %lld exceeds %d",
                     (long long)(G * Qmax), PA_MAX_ROWS);
     if (D == 256 && G * Qmax > PA_MAX_ROWS_D256)
@@ -188,16 +208,16 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     const int64_t eb = fp8 ? 1 : 2;
     // in-block byte offsets of the kernels are 32-bit
     for (const pa_tensor* c : {kc, vc}) {
-        const int64_t span = (BS - 1) * c->stride[1] * eb + (Hkv - 1) * c->stride[2] * eb + D * eb;
+        const int64_t span = sat_add(sat_add(sat_mul(BS - 1, used_stride(c, 1)), sat_mul(Hkv - 1, used_stride(c, 2))), D) * eb;
         if (span >= (int64_t(1) << 31))
             return fail(PA_ERR_LAYOUT, "%s: one block spans more than 2 GiB", c == kc ? "k_cache" : "v_cache");
         // block strides are 32-bit byte counts in the kernels
-        if (c->stride[0] * eb >= (int64_t(1) << 32))
+        if (used_stride(c, 0) * eb >= (int64_t(1) << 32))
             return fail(PA_ERR_LAYOUT, "%s: block stride of 4 GiB or more", c == kc ? "k_cache" : "v_cache");
     }
     if (fp8)
         for (const pa_tensor* s : {ks, vs})
-            if (s->stride[0] * 4 >= (int64_t(1) << 32) || s->stride[2] * 4 >= (int64_t(1) << 31))
+            if (used_stride(s, 0) * 4 >= (int64_t(1) << 32) || used_stride(s, 2) * 4 >= (int64_t(1) << 31))
                 return fail(PA_ERR_LAYOUT, "%s: block stride of 4 GiB or more", s == ks ? "k_scale" : "v_scale");
 
     if (pr) {
@@ -206,20 +226,22 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
         p.fp8 = fp8; p.scale = scale;
         p.window = window > 0 ? window : 0;
         p.sinks = sinks ? static_cast<const float*>(sinks->data) : nullptr;
-        p.sinks_s = sinks ? sinks->stride[0] : 0;
+        p.sinks_s = sinks ? used_stride(sinks, 0) : 0;
         p.q = q->data;
-        p.q_sb = q->stride[0]; p.q_st = q3 ? 0 : q->stride[1]; p.q_sh = q->stride[q3 ? 1 : 2];
+        p.q_sb = used_stride(q, 0); p.q_st = q3 ? 0 : used_stride(q, 1); p.q_sh = used_stride(q, q3 ? 1 : 2);
         p.out = out->data;
-        p.o_sb = out->stride[0]; p.o_st = q3 ? 0 : out->stride[1]; p.o_sh = out->stride[q3 ? 1 : 2];
-        p.k = kc->data; p.k_sblk = kc->stride[0] * eb; p.k_stok = kc->stride[1] * eb; p.k_sh = kc->stride[2] * eb;
-        p.v = vc->data; p.v_sblk = vc->stride[0] * eb; p.v_stok = vc->stride[1] * eb; p.v_sh = vc->stride[2] * eb;
+        p.o_sb = used_stride(out, 0); p.o_st = q3 ? 0 : used_stride(out, 1); p.o_sh = used_stride(out, q3 ? 1 : 2);
+        p.k = kc->data;
+        p.k_sblk = used_stride(kc, 0) * eb; p.k_stok = used_stride(kc, 1) * eb; p.k_sh = used_stride(kc, 2) * eb;
+        p.v = vc->data;
+        p.v_sblk = used_stride(vc, 0) * eb; p.v_stok = used_stride(vc, 1) * eb; p.v_sh = used_stride(vc, 2) * eb;
         p.ks = fp8 ? static_cast<const float*>(ks->data) : nullptr;
         p.vs = fp8 ? static_cast<const float*>(vs->data) : nullptr;
-        p.ks_sblk = fp8 ? ks->stride[0] : 0; p.ks_sh = fp8 ? ks->stride[2] : 0;
-        p.vs_sblk = fp8 ? vs->stride[0] : 0; p.vs_sh = fp8 ? vs->stride[2] : 0;
-        p.bt = static_cast<const int32_t*>(bt->data); p.bt_sb = bt->stride[0];
-        p.ctx = static_cast<const int32_t*>(ctx->data); p.ctx_s = ctx->stride[0];
-        p.ql = ql ? static_cast<const int32_t*>(ql->data) : nullptr; p.ql_s = ql ? ql->stride[0] : 0;
+        p.ks_sblk = fp8 ? used_stride(ks, 0) : 0; p.ks_sh = fp8 ? used_stride(ks, 2) : 0;
+        p.vs_sblk = fp8 ? used_stride(vs, 0) : 0; p.vs_sh = fp8 ? used_stride(vs, 2) : 0;
+        p.bt = static_cast<const int32_t*>(bt->data); p.bt_sb = used_stride(bt, 0);
+        p.ctx = static_cast<const int32_t*>(ctx->data); p.ctx_s = used_stride(ctx, 0);
+        p.ql = ql ? static_cast<const int32_t*>(ql->data) : nullptr; p.ql_s = ql ? used_stride(ql, 0) : 0;
     }
     return PA_OK;
 }
@@ -267,9 +289,10 @@ int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm
     if (D != 64 && D != 128 && D != 256)
         return fail(PA_ERR_UNSUPPORTED, "head_dim %lld, only 64, 128 and 256 are supported", (long long)D);
     if (Hkv < 1) return fail(PA_ERR_SHAPE, "no kv heads");
+    if (Hkv > kMaxHeads) return fail(PA_ERR_UNSUPPORTED, "more than %lld kv heads", (long long)kMaxHeads);
     if (NB * BS >= (int64_t(1) << 31))
         return fail(PA_ERR_UNSUPPORTED, "pool of %lld blocks: slots do not fit int32", (long long)NB);
-    if (T * Hkv * (D / 8) >= (int64_t(1) << 40)) return fail(PA_ERR_UNSUPPORTED, "too many new tokens");
+    if (sat_mul(T, Hkv * (D / 8)) >= (int64_t(1) << 40)) return fail(PA_ERR_UNSUPPORTED, "too many new tokens");
     if (fp8) {
         for (const pa_tensor* s : {ks, vs}) {
             const char* nm = s == ks ? "k_scale" : "v_scale";
@@ -288,15 +311,17 @@ int validate_write(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* sm
         WriteProblem& p = *pr;
         const int64_t eb = fp8 ? 1 : 2;
         p.T = T; p.Hkv = Hkv; p.D = D; p.NB = NB; p.BS = BS; p.fp8 = fp8;
-        p.k_new = kn->data; p.kn_st = kn->stride[0] * 2; p.kn_sh = kn->stride[1] * 2;
-        p.v_new = vn->data; p.vn_st = vn->stride[0] * 2; p.vn_sh = vn->stride[1] * 2;
-        p.slots = static_cast<const int32_t*>(sm->data); p.slot_s = sm->stride[0];
-        p.kc = kc->data; p.k_sblk = kc->stride[0] * eb; p.k_stok = kc->stride[1] * eb; p.k_sh = kc->stride[2] * eb;
-        p.vc = vc->data; p.v_sblk = vc->stride[0] * eb; p.v_stok = vc->stride[1] * eb; p.v_sh = vc->stride[2] * eb;
+        p.k_new = kn->data; p.kn_st = used_stride(kn, 0) * 2; p.kn_sh = used_stride(kn, 1) * 2;
+        p.v_new = vn->data; p.vn_st = used_stride(vn, 0) * 2; p.vn_sh = used_stride(vn, 1) * 2;
+        p.slots = static_cast<const int32_t*>(sm->data); p.slot_s = used_stride(sm, 0);
+        p.kc = kc->data;
+        p.k_sblk = used_stride(kc, 0) * eb; p.k_stok = used_stride(kc, 1) * eb; p.k_sh = used_stride(kc, 2) * eb;
+        p.vc = vc->data;
+        p.v_sblk = used_stride(vc, 0) * eb; p.v_stok = used_stride(vc, 1) * eb; p.v_sh = used_stride(vc, 2) * eb;
         p.ks = fp8 ? static_cast<float*>(ks->data) : nullptr;
         p.vs = fp8 ? static_cast<float*>(vs->data) : nullptr;
-        p.ks_sblk = fp8 ? ks->stride[0] : 0; p.ks_sh = fp8 ? ks->stride[2] : 0;
-        p.vs_sblk = fp8 ? vs->stride[0] : 0; p.vs_sh = fp8 ? vs->stride[2] : 0;
+        p.ks_sblk = fp8 ? used_stride(ks, 0) : 0; p.ks_sh = fp8 ? used_stride(ks, 2) : 0;
+        p.vs_sblk = fp8 ? used_stride(vs, 0) : 0; p.vs_sh = fp8 ? used_stride(vs, 2) : 0;
     }
     return PA_OK;
 }
@@ -316,6 +341,9 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     if (B < 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Qmax < 1 || max_context < 1 || max_context > kMaxContext ||
         num_cus < 1 || D < 1)
         return fail(PA_ERR_ARG, "plan: invalid sizes");
+    if (B > kMaxBatch || Hkv > kMaxHeads || Hq / Hkv > PA_MAX_ROWS || Qmax > PA_MAX_ROWS ||
+        (Hq / Hkv) * Qmax > PA_MAX_ROWS || (D != 64 && D != 128 && D != 256))
+        return fail(PA_ERR_UNSUPPORTED, "plan: sizes outside what the kernels serve");
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
     if (D == 256 && rows > PA_MAX_ROWS_D256)
@@ -498,13 +526,14 @@ int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_
         if (n < 0 || n > query_len)
             return pa::fail(PA_ERR_ARG, "sequence %lld: query_len %lld outside [0, %lld]", (long long)b,
                             (long long)n, (long long)query_len);
-        if (L < n || L > block_size * table_width)
+        const int64_t reach = pa::sat_mul(block_size, table_width);
+        if (L < n || L > reach)
             return pa::fail(PA_ERR_ARG, "sequence %lld: context_len %lld outside [%lld, %lld]", (long long)b,
-                            (long long)L, (long long)n, (long long)(block_size * table_width));
+                            (long long)L, (long long)n, (long long)reach);
         if (n == 0) continue;
         // the entries the kernels read: blocks holding keys some row sees
         const int64_t lo = sliding_window > 0 ? std::max<int64_t>(0, L - n - sliding_window + 1) : 0;
-        const int64_t used = (L + block_size - 1) / block_size;
+        const int64_t used = L / block_size + (L % block_size != 0);
         for (int64_t i = lo / block_size; i < used; ++i) {
             const int64_t blk = block_tables[b * table_row_stride + i];
             if (blk < 0 || blk >= num_blocks)

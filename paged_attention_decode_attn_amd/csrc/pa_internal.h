@@ -73,6 +73,13 @@ bool aligned(const void* p, uintptr_t a);
 int check_desc(const pa_tensor* t, const char* name, int32_t dtype, int ndim_lo, int ndim_hi, bool need_data);
 // inner stride 1, other strides multiples of 16 bytes, base 16-byte aligned
 int check_rows16(const pa_tensor* t, const char* name);
+// Saturating arithmetic on non-negative sizes: a result past INT64_MAX reads
+// as INT64_MAX, so a limit check on it rejects the input.
+int64_t sat_mul(int64_t a, int64_t b);
+int64_t sat_add(int64_t a, int64_t b);
+// The stride of dim i as the kernels use it: 0 for a dim of size 1, whose
+// only index is 0 whatever the caller's stride.
+int64_t used_stride(const pa_tensor* t, int i);
 
 constexpr int kChunkTokens = 32;            // tokens per chunk: the unit of work splitting
 constexpr int kMaxBlockSize = 4096;         // largest tokens-per-block (a multiple of 16)
@@ -81,6 +88,9 @@ constexpr int kDefaultMinShare = 1;         // smallest share of chunks per work
 constexpr int kStepsPerWave = 8;            // planner's target chunks per wave
 constexpr int kWholeSegmentChunks = 2 * kStepsPerWave;   // longest segment run whole
 constexpr int kMaxBatch = 16384;            // per-sequence chunk counts live in LDS
+constexpr int64_t kMaxHeads = int64_t(1) << 16;          // kv heads (and query heads per kv head, far fewer)
+constexpr int64_t kMaxSize = int64_t(1) << 48;           // any size, and any tensor's extent in bytes
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;   // int32 block ids
 constexpr int kRedThreads = 256;            // merge workgroup size (reduce_kernel)
 constexpr int kRedUnroll = 8;               // partial loads in flight per merge lane
 

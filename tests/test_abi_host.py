@@ -188,6 +188,34 @@ def test_misaligned_base_pointer():
                                           d[6]) == _status("PA_ERR_NULL")
 
 
+def _check_descs(t, **edit):
+    """paged_attn_check on descriptors of ``t`` with fields replaced:
+    edit = {name: [(field, dim, value), ...]}."""
+    d = {k: B.describe(v) for k, v in t.items() if k != "scale"}
+    for name, changes in edit.items():
+        for field, dim, value in changes:
+            getattr(d[name], field)[dim] = value
+    names = ("q", "k_cache", "v_cache", "block_tables", "context_lens", "query_lens")
+    return B.lib().paged_attn_check(*[B._ref(d[n]) for n in names], ctypes.c_float(0.125),
+                                    B._ref(d["k_scale"]), B._ref(d["v_scale"]), B._ref(d["out"]))
+
+
+def test_descriptor_size_limits():
+    t = _tensors(qmax=1)
+    assert _check_descs(t) == B.PA_OK
+    # a dim of size 1 may carry any stride: only its index 0 is used
+    assert _check_descs(t, q=[("stride", 1, 1 << 62)], out=[("stride", 1, 1 << 62)]) == B.PA_OK
+    # a tensor reaching 2^48 bytes or more, or a size of 2^48, is refused
+    assert _check_descs(t, q=[("stride", 0, 1 << 62)]) == _status("PA_ERR_UNSUPPORTED")
+    assert _check_descs(t, out=[("stride", 0, (1 << 47) // 2)]) == _status("PA_ERR_UNSUPPORTED")
+    assert _check_descs(t, k_cache=[("shape", 0, 1 << 48), ("stride", 0, 0)]) == _status("PA_ERR_UNSUPPORTED")
+    # pools of 2^31 blocks (int32 block ids) and more than 65536 kv heads
+    many = [("shape", 0, 1 << 31), ("stride", 0, 0)]
+    assert _check_descs(t, k_cache=many, v_cache=many) == _status("PA_ERR_UNSUPPORTED")
+    heads = [("shape", 2, 70000), ("stride", 2, 0)]
+    assert _check_descs(t, k_cache=heads, v_cache=heads, q=heads, out=heads) == _status("PA_ERR_UNSUPPORTED")
+
+
 def test_empty_batch_is_valid():
     t = _tensors()
     for k in ("q", "out", "block_tables", "context_lens", "query_lens"):
