@@ -162,6 +162,29 @@ def test_rank3_query_and_strided_output():
     assert torch.all(big[:, 1, :, :32] == 7.0) and torch.all(big[:, 1, :, 32 + w.q.shape[3]:] == 7.0)
 
 
+def test_size_one_dims_may_carry_any_stride():
+    # one sequence, one query row: the batch and query dims of q/out, the
+    # table's row dim and the length vectors have size 1, so their strides
+    # are never used, whatever they are (odd, huge); the output is bitwise
+    # the contiguous call's
+    w = generate(SMALL["tiny"])
+    dev = w.to("cuda")
+    assert dev.q.shape[:2] == (1, 1)
+    ref = run_gpu(w)
+    H, D = dev.q.shape[2], dev.q.shape[3]
+    odd = 999999937
+    q = torch.as_strided(dev.q, dev.q.shape, (odd, 12345, D, 1))
+    out_buf = torch.empty(H * D, dtype=torch.bfloat16, device="cuda")
+    out = torch.as_strided(out_buf, dev.q.shape, (odd, 777, D, 1))
+    bt = torch.as_strided(dev.block_tables, dev.block_tables.shape, (odd, 1))
+    ctx = torch.as_strided(dev.context_lens, (1,), (odd,))
+    ql = torch.as_strided(dev.query_lens, (1,), (12345,))
+    note("[gpu] size-1 dims with odd strides")
+    B.paged_attn_decode(q, dev.k_cache, dev.v_cache, bt, ctx, ql, w.scale, None, None, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.contiguous().view(torch.int16).cpu(), ref.view(torch.int16).cpu())
+
+
 def test_empty_batch_is_a_no_op():
     w = generate(SMALL["tiny"]).to("cuda")
     note("[gpu] empty batch")

@@ -73,6 +73,26 @@ def _compare(out, ref, label, rows=None):
     assert rel <= REL_L2_MAX, f"{label}: relative L2 {rel:.3e}"
 
 
+@pytest.mark.gpu
+def test_size_one_dims_may_carry_any_stride():
+    # one sequence: the table's row dim and the length vector have size 1,
+    # so their strides are never used, whatever they are; the output is
+    # bitwise the contiguous call's
+    spec = PREFILL_CONFIGS["prefill_8k"].replace(ctx_lo=300, ctx_hi=300, pool_blocks=40)
+    p = generate_prefill(spec)
+    ref = _run(p)
+    d = p.to("cuda")
+    c = d.cache
+    bt = torch.as_strided(c.block_tables, c.block_tables.shape, (999999937, 1))
+    ctx = torch.as_strided(c.context_lens, (1,), (12345,))
+    out = torch.empty_like(d.q)
+    note("[gpu] prefill size-1 dims with odd strides")
+    B.paged_attn_prefill(d.q, c.k_cache, c.v_cache, bt, ctx, d.cu_seqlens, p.max_query_len, p.scale, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16).cpu(), ref.view(torch.int16))
+
+
+
 def _check(p, label, **kw):
     note(f"[gpu] prefill {label}: ctx={p.cache.context_lens.tolist()[:6]} chunks={p.chunk_lens.tolist()[:6]} "
          f"heads={p.spec.hq}/{p.spec.hkv} d={p.spec.head_dim} bs={p.spec.block_size} "
