@@ -29,7 +29,7 @@ def test_host_entry_points_under_sanitizers(tmp_path):
              os.path.join(CSRC, "pa_host.cpp"), os.path.join(CSRC, "pa_prefill_host.cpp"), "-o", exe]
     r = subprocess.run(build, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-4000:]
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0", UBSAN_OPTIONS="print_stacktrace=1")
     for seed in (1, 2):
         r = subprocess.run([exe, "200000", str(seed)], capture_output=True, text=True, timeout=300, env=env)
         assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
