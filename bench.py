@@ -7,10 +7,15 @@ input already resident in HBM.  The KV pools are rotated over several
 device copies so that each call reads its K/V from HBM rather than from the
 256 MB Infinity Cache.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config long_ctx]
+    python bench.py [--steps K] [--warmup W] [--config long_ctx] [--only]
 
 Default workload: the batch-1 long-context decode (1 sequence, 131072
-tokens, 64 query / 8 kv heads, head_dim 128, bf16 KV).
+tokens, 64 query / 8 kv heads, head_dim 128, bf16 KV).  Unless --only is
+given, the same line also carries the fp8-KV workload (16 sequences,
+contexts 512..32768, head_dim 64, e4m3fn with per-token scales) measured
+the same way ("fp8_config") and the read rate of a plain streaming kernel
+at both calls' byte counts ("read_ceiling").  --op stream sweeps the
+streaming probe's launch shapes alone.
 """
 from __future__ import annotations
 
@@ -45,11 +50,12 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="long_ctx", choices=CONFIG_ORDER + NEXT_CONFIG_ORDER + list(PREFILL_CONFIGS))
-    ap.add_argument("--op", default="decode", choices=["decode", "cache_write", "prefill"],
+    ap.add_argument("--op", default="decode", choices=["decode", "cache_write", "prefill", "stream"],
                     help="decode: the attention call (default); cache_write: the paged KV-cache "
                          "write before it, on --config's decode step or a bulk write (--bulk); "
                          "prefill: packed prefill chunks over the paged cache (--config prefill_8k or "
-                         "chunked_prefill)")
+                         "chunked_prefill); stream: the streaming-read probe's ceiling over launch "
+                         "shapes")
     ap.add_argument("--bulk", type=int, default=0,
                     help="with --op cache_write: write this many tokens to distinct random slots "
                          "of a large pool instead of the config's decode step")
@@ -57,6 +63,8 @@ def parse_args():
     ap.add_argument("--min-share", type=int, default=0, help="smallest share in 32-token chunks (0 = the planner's)")
     ap.add_argument("--copies", type=int, default=0, help="rotated KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="with the default long_ctx workload: measure it alone (no fp8 config, no read ceiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 1 GiB device copies (HBM counter calibration)")
@@ -469,38 +477,51 @@ def bench_cache_write(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse_args()
-    if args.summarize:
-        summarize(args)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the decode-attention path has no multi-GPU mode here.",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
+def stream_ceiling(nbytes_list=(1 << 30,), steps: int = 20, warmup: int = 3):
+    """The streaming-read probe over launch shapes (workgroups, threads,
+    loads in flight, contiguous or grid-stride ranges) on buffers of the
+    given sizes: the best rate per size is the achievable read ceiling."""
+    import torch
 
+    from paged_attention_decode_attn_amd import binding as B
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    shapes = [(cus * k, t, u, g) for k in (1, 2, 4, 8) for t in (256, 512) for u in (4, 8) for g in (0, 1)
+              if k * t <= 2048]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for nbytes in nbytes_list:
+        bufs = [torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(2)]
+        rows = []
+        for wg, t, u, g in shapes:
+            for i in range(warmup):
+                B.paged_attn_probe_stream_read(bufs[i % 2], wg, t, u, g, sink)
+            torch.cuda.synchronize()
+            start.record()
+            for i in range(steps):
+                B.paged_attn_probe_stream_read(bufs[i % 2], wg, t, u, g, sink)
+            stop.record()
+            torch.cuda.synchronize()
+            us = start.elapsed_time(stop) * 1e3 / steps
+            rows.append({"workgroups": wg, "threads": t, "loads_in_flight": u,
+                         "layout": "grid_stride" if g else "contiguous", "us": round(us, 3),
+                         "GBs": round(nbytes / us / 1e3, 1)})
+        best = max(rows, key=lambda r: r["GBs"])
+        out[str(nbytes)] = {"best_GBs": best["GBs"], "best_frac_of_peak": round(best["GBs"] / HBM_PEAK_GBS, 4),
+                            "best_shape": best, "shapes": rows}
+        del bufs
+    return out
+
+
+def bench_decode(args, config: str, cpu_seconds: float):
+    """One decode workload: eager steps (the value), the same steps with
+    per-kernel HIP events (the roofline's kernel time), and a graph replay."""
     import torch
 
     from paged_attention_decode_attn_amd import binding as B
     from paged_attention_decode_attn_amd.workloads import CONFIGS, generate, kv_bytes
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.op == "cache_write":
-        bench_cache_write(args)
-        return
-    if args.op == "prefill":
-        bench_prefill(args)
-        return
-
-    spec = CONFIGS[args.config]
+    spec = CONFIGS[config]
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
     w = generate(spec)
     kvb = kv_bytes(w.context_lens, spec.hkv, spec.head_dim, spec.kv_dtype, w.query_lens, spec.sliding_window)
@@ -534,7 +555,7 @@ def main():
             B.paged_attn_decode(dev.q, kc, vc, dev.block_tables, dev.context_lens, dev.query_lens,
                                 dev.scale, ks, vs, out)
 
-    print(f"[bench] warmup {args.warmup}, copies {copies}, plan {plan}", file=sys.stderr, flush=True)
+    print(f"[bench] {config}: warmup {args.warmup}, copies {copies}, plan {plan}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -624,9 +645,60 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": kvb,
                      "kernel": "partition_kernel"},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if cpu_seconds > 0:
+        print(f"[bench] {config}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+    del pools, dev
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse_args()
+    if args.summarize:
+        summarize(args)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the decode-attention path has no multi-GPU mode here.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.op == "cache_write":
+        bench_cache_write(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
+        return
+    if args.op == "stream":
+        print("[bench] streaming-read probe", file=sys.stderr, flush=True)
+        print(json.dumps({"op": "stream_read_ceiling", "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                          "sizes": stream_ceiling((1 << 30, 536870912, 266846144), steps=args.steps,
+                                                  warmup=args.warmup)}), flush=True)
+        return
+
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    res = bench_decode(args, args.config, cpu_s)
+    if args.config == "long_ctx" and not args.only:
+        # the second target configuration, measured the same way in the
+        # same run, and the read ceiling of a plain streaming kernel at the
+        # two calls' byte counts
+        res["fp8_config"] = bench_decode(args, "fp8", min(cpu_s, 5.0))
+        print("[bench] streaming-read probe", file=sys.stderr, flush=True)
+        ceil = stream_ceiling((res["kv_bytes_per_call"], res["fp8_config"]["kv_bytes_per_call"]),
+                              steps=max(5, min(args.steps, 20)), warmup=3)
+        res["read_ceiling"] = {k: {"best_GBs": v["best_GBs"], "best_frac_of_peak": v["best_frac_of_peak"],
+                                   "best_shape": v["best_shape"]} for k, v in ceil.items()}
     print(json.dumps(res), flush=True)
 
 

@@ -136,8 +136,12 @@ typedef struct pa_tensor {
  * it grows on demand with hipMalloc outside stream capture.  Capture a
  * call into a graph only after paged_attn_reserve() or an uncaptured call
  * of the same or larger size on that stream; otherwise PA_ERR_CAPTURE.
- * Calls on one stream are ordered; calls on different streams use
- * different workspaces.
+ * Growth never frees a buffer that a call used during capture: graphs
+ * captured earlier keep replaying into their own buffer, which stays
+ * allocated until the process ends (a buffer never used under capture is
+ * freed once the stream has passed the calls that used it).  Calls on one
+ * stream are ordered; calls on different streams use different
+ * workspaces.
  */
 int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
                       const pa_tensor* block_tables, const pa_tensor* context_lens,
@@ -201,8 +205,8 @@ int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_
  * sequence lengths prepared for every prefill step) and its source-file
  * list (a ragged prefill chunk's tokens placed in their own sequences).
  *
- *   q, out        bf16 [T, Hq, D] (D 64 or 128): the new tokens of all
- *                 sequences packed row after row.
+ *   q, out        bf16 [T, Hq, D] (D 64, 128 or 256): the new tokens of
+ *                 all sequences packed row after row.
  *   cu_seqlens_q  int32 [B + 1]: sequence b owns rows cu[b] .. cu[b+1]-1
  *                 (n_b = cu[b+1] - cu[b] rows; cu[0] = 0, non-decreasing).
  *                 They are the last n_b of its L_b = context_lens[b] tokens,
@@ -225,7 +229,7 @@ int paged_attn_check_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_
  * written; a row count clamped by these bounds leaves the rest unwritten,
  * and no access leaves the tensors' extents.  No workspace; nothing is
  * allocated.  Layout rules and errors as for paged_attn_decode; (Hq / Hkv)
- * <= 64.
+ * <= 64 (<= 16 for D 256).
  */
 int paged_attn_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
                        const pa_tensor* block_tables, const pa_tensor* context_lens,
@@ -293,9 +297,9 @@ int paged_attn_check_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, c
  *   v_scale       required iff the cache is fp8, else NULL.  For an fp8
  *                 cache every written (token, kv head) row gets
  *                 scale = max_d |x_d| / 448 (1 for an all-zero row) and
- *                 codes e4m3fn(clamp(x_d * (448 / max_d |x_d|), -448, 448))
- *                 (x_d * 1 for an all-zero row), rounded to nearest, ties
- *                 to even; divisions and products in IEEE float32.
+ *                 codes e4m3fn(clamp(x_d / scale, -448, 448)), rounded to
+ *                 nearest, ties to even; both divisions correctly rounded
+ *                 IEEE float32 (subnormal quotients kept).
  *                 A bf16 cache receives the rows bit for bit.
  *   stream        hipStream_t as void*, NULL = default stream.
  *
@@ -363,36 +367,12 @@ typedef struct pa_plan {
  * pa_dtype of the cache.  max_context is the most cache tokens one
  * sequence's rows can read: block size x table width, or with a sliding
  * window w at most 32 * (ceil((w + query_len - 1) / 32) + 1) of them
- * (1 <= max_context <= 2^30).  Honors the overrides below.
+ * (1 <= max_context <= 2^30).  Honors the overrides of
+ * paged_attn_tuning.h.
  */
 int paged_attn_plan(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t head_dim,
                     int64_t query_len, int64_t max_context, int32_t kv_dtype,
                     int32_t num_cus, pa_plan* plan);
-
-/*
- * paged_attn_set_workgroups -- override the planner's partition-kernel
- * grid for every later call in the process (positive; the min-share rule
- * still lowers it), or 0 for the automatic choice.  A test and tuning
- * hook; not synchronised with concurrent calls.
- */
-int paged_attn_set_workgroups(int32_t workgroups);
-
-/*
- * paged_attn_set_min_share -- override the smallest share of 32-token
- * chunks per workgroup (positive), or 0 for the default of 1.  A tuning
- * hook; not synchronised with concurrent calls.
- */
-int paged_attn_set_min_share(int32_t chunks);
-
-/*
- * paged_attn_set_heads_per_group -- override the planner's kv heads per
- * partition workgroup for every later call in the process (1..8; it must
- * divide kv_heads, and be at most 4 when (Hq / Hkv) * Qmax > 16 or head_dim is
- * 256, or the call
- * fails with PA_ERR_ARG), or 0 for the automatic choice.  A tuning hook;
- * not synchronised with concurrent calls.
- */
-int paged_attn_set_heads_per_group(int32_t heads);
 
 /*
  * paged_attn_reserve -- grow the current device's workspace for `stream`
@@ -417,18 +397,6 @@ int paged_attn_check_metadata(const int32_t* context_lens, const int32_t* query_
                               const int32_t* block_tables, int64_t batch, int64_t table_width,
                               int64_t table_row_stride, int64_t query_len, int64_t num_blocks,
                               int64_t block_size, int32_t sliding_window);
-
-/*
- * Kernel timing for measurement: after paged_attn_profile_begin(n), the
- * next n calls of paged_attn_decode or paged_attn_decode_ext (on any
- * stream) record HIP events
- * before and after each kernel they launch, on the call's stream.
- * paged_attn_profile_end() waits for those events and returns the summed
- * durations in milliseconds of the partition kernel and of the merge
- * kernel and the number of calls recorded, then stops recording.
- */
-int paged_attn_profile_begin(int32_t max_calls);
-int paged_attn_profile_end(double* partition_ms, double* reduce_ms, int32_t* calls);
 
 const char* paged_attn_strerror(int status);
 const char* paged_attn_last_error(void);

@@ -26,16 +26,17 @@ For every new token ``t`` with slot ``s = slot_mapping[t]``:
   head ``h``:
     - bf16 cache: the token's bf16 row, bit for bit;
     - fp8 cache: ``a = max_d |x_d|`` over the row (x widened exactly to
-      float32), ``scale = a / 448`` and ``inv = 448 / a`` (both 1 when
-      ``a == 0``), codes ``e4m3fn(clamp(x_d * inv, -448, 448))`` rounded to
-      nearest, ties to even; ``scale`` goes to ``k_scale`` /
-      ``v_scale[block, pos, h]``.
+      float32), ``scale = a / 448`` (1 when ``a == 0``), codes
+      ``e4m3fn(clamp(x_d / scale, -448, 448))`` rounded to nearest, ties to
+      even; ``scale`` goes to ``k_scale`` / ``v_scale[block, pos, h]``.
 
-The pages give no formula for the per-token scale; the one taken is the
+The pages give no formula for the per-token scale.  The one taken is the
 absmax rule that maps the row's largest magnitude onto the format's largest
-finite value, 448, with the row multiplied by the reciprocal of the scale
-(one division per row).  The divisions and the products are IEEE float32
-operations, the precision the quantised code is decided in on both sides.
+finite value, 448: the scale is the row's absolute maximum over 448, and
+every element is divided by that stored scale, so that dequantisation
+(code times scale) inverts exactly the step the code was taken from.  Both
+divisions are correctly rounded IEEE float32 divisions (gradual underflow
+included), the precision in which the quantised code is decided.
 """
 from __future__ import annotations
 
@@ -80,10 +81,8 @@ def quantize_rows_e4m3fn(x) -> tuple:
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=-1)
     nonzero = amax > 0
-    safe = np.where(nonzero, amax, np.float32(1.0)).astype(np.float32)
     scale = np.where(nonzero, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    inv = np.where(nonzero, np.float32(FP8_MAX) / safe, np.float32(1.0)).astype(np.float32)
-    y = (x * inv[..., None]).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
     y = np.clip(y, np.float32(-FP8_MAX), np.float32(FP8_MAX))
     return e4m3fn_encode(y), scale
 

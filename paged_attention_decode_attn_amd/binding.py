@@ -20,9 +20,9 @@ import torch
 from .build import INCLUDE
 from .build import LIB_PATH as _BUILT_LIB
 
-# PAGED_ATTN_LIB may name another build of the same library (A/B builds of
-# the same sources); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("PAGED_ATTN_LIB", _BUILT_LIB)
+# the in-tree build, and only it
+LIB_PATH = _BUILT_LIB
+HEADERS = ("paged_attn.h", "paged_attn_tuning.h")
 
 PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3FN, PA_DTYPE_FP32, PA_DTYPE_INT32 = 1, 2, 3, 4
 PA_OK = 0
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_set_min_share.argtypes = [ctypes.c_int32]
                 L.paged_attn_set_heads_per_group.argtypes = [ctypes.c_int32]
                 L.paged_attn_reserve.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+                L.paged_attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
+                    ctypes.c_void_p, ctypes.c_void_p]
                 i32p = ctypes.POINTER(ctypes.c_int32)
                 L.paged_attn_check_metadata.argtypes = [i32p, i32p, i32p] + [ctypes.c_int64] * 6 + [ctypes.c_int32]
                 L.paged_attn_profile_begin.argtypes = [ctypes.c_int32]
@@ -107,7 +109,7 @@ def lib() -> ctypes.CDLL:
                              "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
                              "paged_attn_set_workgroups", "paged_attn_set_min_share",
                              "paged_attn_set_heads_per_group",
-                             "paged_attn_reserve",
+                             "paged_attn_reserve", "paged_attn_probe_stream_read",
                              "paged_attn_check_metadata", "paged_attn_profile_begin",
                              "paged_attn_profile_end"):
                     getattr(L, name).restype = ctypes.c_int
@@ -116,10 +118,13 @@ def lib() -> ctypes.CDLL:
 
 
 def header_functions() -> list:
-    """Names of every function that ``include/paged_attn.h`` declares."""
-    text = open(os.path.join(INCLUDE, "paged_attn.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_attn_\w+)\s*\(", text)))
+    """Names of every function that the headers under ``include/`` declare."""
+    names = set()
+    for h in HEADERS:
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(paged_attn_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def _raise(status: int, where: str):
@@ -353,6 +358,15 @@ def paged_attn_profile_end() -> dict:
     _raise(lib().paged_attn_profile_end(ctypes.byref(part), ctypes.byref(red), ctypes.byref(calls)),
            "paged_attn_profile_end")
     return {"partition_ms": part.value, "reduce_ms": red.value, "calls": calls.value}
+
+
+def paged_attn_probe_stream_read(src: torch.Tensor, workgroups: int, threads: int, unroll: int,
+                                 grid_stride: bool, sink: torch.Tensor, stream=None) -> None:
+    """The streaming-read probe over the whole of ``src`` (measurement only)."""
+    st = lib().paged_attn_probe_stream_read(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                            int(workgroups), int(threads), int(unroll), int(bool(grid_stride)),
+                                            ctypes.c_void_p(sink.data_ptr()), _stream_handle(src, stream))
+    _raise(st, "paged_attn_probe_stream_read")
 
 
 def paged_attn_strerror(status: int) -> str:

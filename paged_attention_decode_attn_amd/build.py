@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpaged_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["pa_host.cpp", "pa_prefill_host.cpp", "pa_device.hip", "pa_cache.hip", "pa_prefill.hip"]
+SOURCES = ["pa_host.cpp", "pa_prefill_host.cpp", "pa_device.hip", "pa_cache.hip", "pa_prefill.hip", "pa_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -9,8 +9,10 @@
 // Inference", "Attention Input Fusion" (fp8 scales calculated as K/V are
 // written into the paged cache).  Scale rule: the row's absolute maximum
 // divided by 448, the largest finite e4m3fn value (1 for an all-zero row);
-// the row is multiplied by 448 / absmax (one division per row) and the
-// codes round to nearest, ties to even.
+// every element is divided by that stored scale (correctly rounded float32
+// division, so a code is the rounding of exactly the quotient that
+// dequantisation multiplies back) and the codes round to nearest, ties to
+// even.
 //
 // One thread takes 8 consecutive elements (16 bytes of bf16) of one
 // (token, kv head) row of both K and V, so a wave reads and writes whole
@@ -44,22 +46,22 @@ struct WriteArgs {
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// x * inv clamped to +-448 for the two bf16 values of one dword
-__device__ __forceinline__ float q_lo(unsigned w, float inv) {
-    return fminf(fmaxf(__fmul_rn(bf16_lo(w), inv), -kFp8Max), kFp8Max);
+// x / s clamped to +-448 for the two bf16 values of one dword
+__device__ __forceinline__ float q_lo(unsigned w, float s) {
+    return fminf(fmaxf(__fdiv_rn(bf16_lo(w), s), -kFp8Max), kFp8Max);
 }
-__device__ __forceinline__ float q_hi(unsigned w, float inv) {
-    return fminf(fmaxf(__fmul_rn(bf16_hi(w), inv), -kFp8Max), kFp8Max);
+__device__ __forceinline__ float q_hi(unsigned w, float s) {
+    return fminf(fmaxf(__fdiv_rn(bf16_hi(w), s), -kFp8Max), kFp8Max);
 }
 
-// 8 bf16 values -> 8 e4m3fn bytes of x * inv: each conversion packs two
+// 8 bf16 values -> 8 e4m3fn bytes of x / s: each conversion packs two
 // codes into the low or the high half of a dword.
-__device__ __forceinline__ u32x2 encode8(const u32x4& x, float inv) {
+__device__ __forceinline__ u32x2 encode8(const u32x4& x, float s) {
     u32x2 out;
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[0], inv), q_hi(x[0], inv), 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[1], inv), q_hi(x[1], inv), w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[2], inv), q_hi(x[2], inv), 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[3], inv), q_hi(x[3], inv), w1, true);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[0], s), q_hi(x[0], s), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[1], s), q_hi(x[1], s), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[2], s), q_hi(x[2], s), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[3], s), q_hi(x[3], s), w1, true);
     out[0] = (unsigned)w0;
     out[1] = (unsigned)w1;
     return out;
@@ -104,14 +106,12 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
             mk = fmaxf(mk, __shfl_xor(mk, o));
             mv = fmaxf(mv, __shfl_xor(mv, o));
         }
-        // scale = absmax / 448 (stored), the row multiplied by 448 / absmax
+        // scale = absmax / 448 (stored); every element divided by it
         const float sk = mk > 0.f ? __fdiv_rn(mk, kFp8Max) : 1.f;
         const float sv = mv > 0.f ? __fdiv_rn(mv, kFp8Max) : 1.f;
-        const float ik = mk > 0.f ? __fdiv_rn(kFp8Max, mk) : 1.f;
-        const float iv = mv > 0.f ? __fdiv_rn(kFp8Max, mv) : 1.f;
         if (live) {
-            *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) = encode8(k, ik);
-            *reinterpret_cast<u32x2*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 8 * r) = encode8(v, iv);
+            *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) = encode8(k, sk);
+            *reinterpret_cast<u32x2*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 8 * r) = encode8(v, sv);
             if (r == 0) {
                 a.ks[blk * a.ks_sblk + h * a.ks_sh + pos] = sk;
                 a.vs[blk * a.vs_sblk + h * a.vs_sh + pos] = sv;

@@ -901,6 +901,8 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    bool captured = false;           // a call used it while its stream was capturing
+    std::vector<void*> retired;      // smaller buffers a captured graph may still use
 };
 
 std::mutex g_mu;
@@ -925,26 +927,38 @@ int device_cus(int dev) {
     return g_cus[dev];
 }
 
+// The stream's workspace, grown to `need` bytes when it is smaller.  A
+// buffer that a call used during stream capture may be referenced by a
+// graph that is replayed later, so growth retires it (kept allocated until
+// the process ends) instead of freeing it; a buffer never captured is freed
+// once the stream has passed the calls that used it.
 int get_workspace(int dev, void* stream, size_t need, void** out) {
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace& w = g_ws[{dev, stream}];
-    if (w.bytes >= need) {
-        *out = w.ptr;
-        return PA_OK;
-    }
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess)
         return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
-    if (cs != hipStreamCaptureStatusNone)
+    const bool capturing = cs != hipStreamCaptureStatusNone;
+    if (w.bytes >= need) {
+        w.captured = w.captured || capturing;
+        *out = w.ptr;
+        return PA_OK;
+    }
+    if (capturing)
         return fail(PA_ERR_CAPTURE, "workspace of %zu bytes needed (have %zu) while the stream is capturing",
                     need, w.bytes);
     if (w.ptr) {
-        // earlier calls on this stream may still read it
-        if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
-            return fail(PA_ERR_HIP, "hipStreamSynchronize failed");
-        (void)hipFree(w.ptr);
+        if (w.captured) {
+            w.retired.push_back(w.ptr);
+        } else {
+            // earlier calls on this stream may still read it
+            if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+                return fail(PA_ERR_HIP, "hipStreamSynchronize failed");
+            (void)hipFree(w.ptr);
+        }
         w.ptr = nullptr;
         w.bytes = 0;
+        w.captured = false;
     }
     const size_t bytes = need + need / 4;   // headroom against creeping sizes
     if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
@@ -990,14 +1004,15 @@ const void* partition_kernel_of(int D, bool fp8, int nt, bool gen) {
 }  // namespace
 }  // namespace pa
 
-extern "C" {
+namespace pa {
+namespace {
 
-int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
-                          const pa_tensor* block_tables, const pa_tensor* context_lens,
-                          const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
-                          const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
-                          pa_tensor* out, void* stream) {
-    using namespace pa;
+// Both decode entry points: validation, plan, the stream's workspace, the
+// partition launch and the merge launch.
+int decode_call(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* query_lens,
+                float scale, const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t sliding_window,
+                const pa_tensor* sinks, pa_tensor* out, void* stream) {
     Problem pr;
     int st = validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
                       sliding_window, sinks, out, &pr);
@@ -1086,13 +1101,28 @@ int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa
     return PA_OK;
 }
 
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                          const pa_tensor* block_tables, const pa_tensor* context_lens,
+                          const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                          const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
+                          pa_tensor* out, void* stream) {
+    return pa::decode_call(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
+                           sliding_window, sinks, out, stream);
+}
+
 int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
                       const pa_tensor* block_tables, const pa_tensor* context_lens,
                       const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
                       const pa_tensor* v_scale, pa_tensor* out, void* stream) {
-    return paged_attn_decode_ext(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale,
-                                 v_scale, 0, nullptr, out, stream);
+    return pa::decode_call(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
+                           0, nullptr, out, stream);
 }
+
 
 int paged_attn_reserve(int64_t bytes, void* stream) {
     if (bytes < 0) return pa::fail(PA_ERR_ARG, "reserve: negative size");

@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "paged_attn.h"
+#include "paged_attn_tuning.h"
 
 namespace pa {
 

@@ -121,6 +121,34 @@ def test_fp8_rounding_of_every_code_midpoint_and_subnormal():
     assert np.all(ks[written // 16, written % 16, 0] == 1.0)
 
 
+def test_fp8_quotients_round_as_correctly_rounded_divisions():
+    # rows on which the quotient x / scale and the product x * (448 / absmax)
+    # round to different codes, and rows mixing the largest and smallest bf16
+    # magnitudes (quotients in float32's subnormal range, a subnormal absmax)
+    rng = np.random.default_rng(77)
+    D = 64
+    x = rng.normal(0, 1, (600, D)).astype(np.float32)
+    x[:200] *= np.exp2(rng.integers(-60, 61, (200, 1))).astype(np.float32)
+    tiny = float(torch.tensor(2.0 ** -133, dtype=torch.bfloat16).float())
+    x[590, :8] = [3.0e38, tiny, -tiny, 1e-30, -1e-38, 2.0 ** -126, 1.0, -1.0]
+    x[591] = 0.0
+    x[591, 5] = -7.0
+    x[592] = tiny
+    x[592, 3] = -2 * tiny
+    x[593] = 0.0
+    x[593, :2] = [2.0 ** -120, 2.0 ** -130]
+    x[594, 0], x[594, 1:] = 448.0, -2.0 ** -12
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    T = xb.shape[0]
+    spec = CONFIGS["fp8"].replace(batch=1, hq=1, hkv=1, head_dim=D, ctx_lo=16, ctx_hi=16, pool_blocks=T // 16 + 4)
+    cw = generate_cache_write(spec, bulk_tokens=T)
+    cw.k_new = xb[:, None, :].contiguous()
+    cw.v_new = (-xb)[:, None, :].contiguous()
+    note(f"[gpu] fp8 division sweep: {T} rows")
+    d = _gpu_write(cw)
+    _check_pool(cw, d, "division")
+
+
 def test_all_zero_rows_get_unit_scale():
     spec = CONFIGS["fp8"].replace(batch=1, ctx_lo=32, ctx_hi=32, pool_blocks=40)
     cw = generate_cache_write(spec, bulk_tokens=17)

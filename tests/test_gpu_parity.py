@@ -126,6 +126,18 @@ def test_shared_and_duplicated_blocks():
         check(w, groups, label=f"shared/g{groups}")
 
 
+@pytest.mark.parametrize("name", ["llama3_8b", "fp8", "mtp_verify", "swa_sinks", "d256"])
+@pytest.mark.parametrize("scale", [-0.0883883, -0.5, 0.0])
+def test_negative_and_zero_softmax_scale(name, scale):
+    # a negative scale flips the sign of every logit (the kernels negate q);
+    # zero makes every visible key weigh the same (the mean of V, or with
+    # sinks the mean shrunk by e^s)
+    w = generate(SMALL[name])
+    w.scale = scale
+    for groups in (0, 100000):
+        check(w, groups, label=f"scale{scale}/{name}/g{groups}")
+
+
 @pytest.mark.parametrize("factor", [4.0, 8.0])
 def test_sharpened_queries(factor):
     for name in ("llama3_8b", "fp8", "mtp_verify"):
@@ -325,3 +337,47 @@ def test_capture_without_workspace_is_refused():
                                 w.query_lens, w.scale, None, None, out)
     assert e.value.name == "PA_ERR_CAPTURE"
     torch.cuda.synchronize()
+
+
+def test_workspace_growth_keeps_captured_graphs_valid():
+    # eager warm-up, capture at a small size, then an uncaptured call that
+    # needs a larger workspace on the same stream: the graph keeps replaying
+    # into the buffer it captured, which growth must not free
+    small_w = generate(SMALL["mtp_verify"])
+    big_w = generate(SMALL["long_ctx"].replace(ctx_lo=60001, ctx_hi=60001, pool_blocks=3800))
+    ds, db = small_w.to("cuda"), big_w.to("cuda")
+    s = torch.cuda.Stream()
+    note("[gpu] workspace growth after capture: warm-up and capture at the small size")
+    eager = torch.empty_like(ds.q)
+    with torch.cuda.stream(s):
+        B.paged_attn_decode(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.context_lens,
+                            ds.query_lens, ds.scale, None, None, eager)
+    s.synchronize()
+    out = torch.empty_like(ds.q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.paged_attn_decode(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.context_lens,
+                            ds.query_lens, ds.scale, None, None, out)
+    torch.cuda.synchronize()
+    plan_s = B.paged_attn_plan(6, 64, 8, 128, 2, 16 * ds.block_tables.shape[1], "bf16",
+                               torch.cuda.get_device_properties(0).multi_processor_count)
+    plan_b = B.paged_attn_plan(1, 64, 8, 128, 1, 16 * db.block_tables.shape[1], "bf16",
+                               torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan_b["workspace_bytes"] > 1.25 * plan_s["workspace_bytes"]
+    note("[gpu] workspace growth after capture: the larger uncaptured call")
+    big_out = torch.empty_like(db.q)
+    with torch.cuda.stream(s):
+        B.paged_attn_decode(db.q, db.k_cache, db.v_cache, db.block_tables, db.context_lens,
+                            db.query_lens, db.scale, None, None, big_out)
+    s.synchronize()
+    compare(big_out, oracle_out(big_w), big_w.query_lens, label="growth/big")
+    # fresh device allocations that would land on freed memory
+    filler = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(16)]
+    for r in range(3):
+        note(f"[gpu] workspace growth after capture: replay {r}")
+        out.view(torch.int16).fill_(0x7F7B)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
+    assert all(bool(torch.all(f == 7.0)) for f in filler)

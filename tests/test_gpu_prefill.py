@@ -187,6 +187,20 @@ def test_sharpened_queries(factor):
     _check(p, f"sharp{factor}")
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+def test_negative_and_zero_softmax_scale(scale, kv):
+    p = generate_prefill(SMALL.replace(kv_dtype=kv, seed=51))
+    p.scale = scale
+    _check(p, f"scale{scale}/{kv}")
+    p = generate_prefill(SWA.replace(kv_dtype=kv, sliding_window=60, sinks=True, seed=52))
+    p.scale = scale
+    _check(p, f"scale{scale}/{kv}/window-sinks")
+    p = generate_prefill(SMALL.replace(hq=16, hkv=8, head_dim=256, kv_dtype=kv, seed=53))
+    p.scale = scale
+    _check(p, f"scale{scale}/{kv}/d256")
+
+
 def test_repeat_calls_are_bitwise_identical():
     p = generate_prefill(SMALL.replace(seed=45))
     a = _run(p)

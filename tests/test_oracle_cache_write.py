@@ -64,6 +64,60 @@ def test_row_quantisation_closed_forms():
     assert np.all(c0 == 0) and np.all(s0 == 1.0)
 
 
+def _torch_row_quant(x):
+    """The absmax/448 rule in PyTorch float32 on the CPU: scale = |x|max / 448
+    (1 for an all-zero row), codes = float8_e4m3fn(clamp(x / scale, +-448)).
+    PyTorch's division and its float8 cast, independent of the oracle."""
+    x = torch.from_numpy(np.asarray(x, np.float32))
+    a = x.abs().amax(dim=-1)
+    s = torch.where(a > 0, a / 448.0, torch.ones_like(a))
+    y = (x / s[..., None]).clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), s.numpy()
+
+
+def _bf16_rows(rng, shape, spread=False):
+    """N(0, 1) rows rounded to bf16 (the cache write's input), optionally
+    with per-row magnitudes spread over 2^-40 .. 2^40."""
+    x = rng.normal(0, 1, shape).astype(np.float32)
+    if spread:
+        x *= np.exp2(rng.integers(-40, 41, shape[:-1] + (1,))).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+
+
+def test_row_quantisation_matches_torch_division_and_cast():
+    rng = np.random.default_rng(31)
+    x = np.concatenate([_bf16_rows(rng, (4000, 64)), _bf16_rows(rng, (2000, 128), spread=False)[:, :64],
+                        _bf16_rows(rng, (2000, 64), spread=True)])
+    codes, scale = quantize_rows_e4m3fn(x)
+    tc, ts = _torch_row_quant(x)
+    assert np.array_equal(scale, ts)
+    assert np.array_equal(codes, tc)
+    # the pin separates the division from the reciprocal product
+    # x * (448 / absmax): on these rows the two round to different codes
+    a = np.abs(x).max(-1, keepdims=True)
+    y2 = np.clip(x * (np.float32(448) / a), -448, 448).astype(np.float32)
+    assert np.count_nonzero(e4m3fn_encode(y2) != tc) > 100
+
+
+def test_row_quantisation_of_extreme_rows_matches_torch():
+    # rows mixing the largest and the smallest bf16 magnitudes (quotients in
+    # float32's subnormal range), a single nonzero element, subnormal absmax
+    tiny = np.float32(torch.tensor(2.0 ** -133, dtype=torch.bfloat16).float())
+    rows = np.zeros((6, 64), np.float32)
+    rows[0, 0], rows[0, 1:8] = 3.0e38, [tiny, -tiny, 1e-30, -1e-38, 2.0 ** -126, 1.0, -1.0]
+    rows[1, 5] = -7.0
+    rows[2, :] = tiny
+    rows[2, 3] = -2 * tiny
+    rows[3, 0], rows[3, 1] = 2.0 ** -120, 2.0 ** -130
+    rows[4] = np.linspace(-1, 1, 64)
+    rows[5, 0], rows[5, 1:] = 448.0, -2.0 ** -12
+    rows = torch.from_numpy(rows).to(torch.bfloat16).float().numpy()
+    codes, scale = quantize_rows_e4m3fn(rows)
+    tc, ts = _torch_row_quant(rows)
+    assert np.array_equal(scale, ts) and np.array_equal(codes, tc)
+    assert np.all(scale > 0)
+
+
 def test_quantisation_is_scale_invariant_by_powers_of_two():
     rng = np.random.default_rng(6)
     x = rng.normal(0, 1, (64, 64)).astype(np.float32)
@@ -147,8 +201,12 @@ import sys  # noqa: E402
 _ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 CW_MUTANTS = {
     "scale_max": ("np.where(nonzero, amax / np.float32(FP8_MAX)", "np.where(nonzero, amax / np.float32(224.0)"),
-    "inv_max": ("np.where(nonzero, np.float32(FP8_MAX) / safe", "np.where(nonzero, np.float32(224.0) / safe"),
-    "divide_by_inv": ("y = (x * inv[..., None])", "y = (x / inv[..., None])"),
+    "reciprocal_product": ("y = (x / scale[..., None])",
+                           "y = (x * (np.float32(1.0) / scale[..., None]).astype(np.float32))"),
+    "inverse_of_absmax": ("y = (x / scale[..., None])",
+                          "y = (x * (np.float32(FP8_MAX) / np.where(nonzero, amax, np.float32(1))"
+                          ".astype(np.float32))[..., None])"),
+    "multiply_by_scale": ("y = (x / scale[..., None])", "y = (x * scale[..., None])"),
     "ties_away": ("(_POS_CODES[hi] % 2 == 0)", "(_POS_CODES[hi] >= 0)"),
     "truncate": ("take_hi = (d_hi < d_lo)", "take_hi = (d_hi < 0 * d_lo)"),
     "sign_lost": ("return (code | sign).astype(np.uint8)", "return code.astype(np.uint8)"),
@@ -186,9 +244,10 @@ def _cw_battery(cw, orc) -> bool:
                             [(table[c] + table[c + 1]) / 2 for c in range(0x7E)]]).astype(np.float32)
         if not np.array_equal(cw.e4m3fn_encode(y), _torch_codes(y)):
             return False
-        x = rng.normal(0, 1, (50, 4, 64)).astype(np.float32)
+        x = _bf16_rows(rng, (400, 4, 64))
         codes, scale = cw.quantize_rows_e4m3fn(x)
-        if not np.array_equal(scale, (np.abs(x).max(-1) / np.float32(448)).astype(np.float32)):
+        tc, ts = _torch_row_quant(x)
+        if not (np.array_equal(scale, ts) and np.array_equal(codes, tc)):
             return False
         c0, s0 = cw.quantize_rows_e4m3fn(np.zeros((1, 64), np.float32))
         if not (np.all(c0 == 0) and np.all(s0 == 1.0)):
@@ -212,7 +271,7 @@ def _cw_battery(cw, orc) -> bool:
                         if not np.array_equal(cache[b, p], new[t]):
                             return False
                     else:
-                        c, sref = quantize_rows_e4m3fn(bf16_bits_to_f64(new[t]).astype(np.float32))
+                        c, sref = _torch_row_quant(bf16_bits_to_f64(new[t]).astype(np.float32))
                         if not (np.array_equal(cache[b, p], c) and np.array_equal(sc[b, p], sref)):
                             return False
         # block size 64: slot s is position s % 64 of block s // 64
