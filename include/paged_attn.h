@@ -149,6 +149,29 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
                       const pa_tensor* v_scale, pa_tensor* out, void* stream);
 
 /*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture with no workspace
+ * reserved beforehand, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, semantics, output and errors as
+ * paged_attn_decode (the same kernels run), except for the workspace: the
+ * partial results live in a static array of 48 MiB (50331648 bytes) in the
+ * library's own device memory, one per device, held until the process ends.
+ * A call whose plan needs more (pa_plan.workspace_bytes) returns
+ * PA_ERR_UNSUPPORTED before launching anything.  The call allocates
+ * nothing: no hipMalloc or hipFree, no library allocation; its first call
+ * on a device looks the array's device address up (hipGetSymbolAddress).
+ * Every call on one device shares that device's array (nothing in it has
+ * to start cleared: each call writes every element it reads), so calls
+ * that may overlap on one device (different streams without ordering
+ * between them) race and give unspecified output; calls on one stream are
+ * ordered and safe.
+ */
+int paged_attn_decode_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                              const pa_tensor* block_tables, const pa_tensor* context_lens,
+                              const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                              const pa_tensor* v_scale, pa_tensor* out, void* stream);
+
+/*
  * paged_attn_decode_ext -- paged_attn_decode with a sliding window and
  * attention sinks.  Sources: ATOM model operations guide, "Attention
  * operations" (the decode dispatch takes a sliding_window, -1 for none);

@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
                 L = ctypes.CDLL(LIB_PATH)
                 args11 = [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]
                 L.paged_attn_decode.argtypes = args11 + [_P, ctypes.c_void_p]
+                L.paged_attn_decode_noalloc.argtypes = args11 + [_P, ctypes.c_void_p]
                 L.paged_attn_check.argtypes = args11 + [_P]
                 L.paged_attn_decode_ext.argtypes = args11 + [ctypes.c_int32, _P, _P, ctypes.c_void_p]
                 L.paged_attn_check_ext.argtypes = args11 + [ctypes.c_int32, _P, _P]
@@ -102,7 +103,7 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_strerror.restype = ctypes.c_char_p
                 L.paged_attn_last_error.argtypes = []
                 L.paged_attn_last_error.restype = ctypes.c_char_p
-                for name in ("paged_attn_decode", "paged_attn_check", "paged_attn_plan",
+                for name in ("paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_check", "paged_attn_plan",
                              "paged_attn_decode_ext", "paged_attn_check_ext",
                              "paged_attn_prefill", "paged_attn_check_prefill",
                              "paged_attn_prefill_ext", "paged_attn_check_prefill_ext",
@@ -188,6 +189,21 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, query_len
     st = lib().paged_attn_decode(*[_ref(d) for d in descs], ctypes.c_float(scale), _ref(dks),
                                  _ref(dvs), _ref(dout), _stream_handle(q, stream))
     _raise(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale,
+                              k_scale=None, v_scale=None, out=None, stream=None):
+    """``paged_attn_decode`` through the entry point that allocates nothing
+    (partial results in the library's static per-device scratch array);
+    ``out`` must be given (this call allocates no tensor either)."""
+    if out is None:
+        raise ValueError("paged_attn_decode_noalloc takes a caller-allocated out")
+    descs = [describe(x) for x in (q, k_cache, v_cache, block_tables, context_lens, query_lens)]
+    st = lib().paged_attn_decode_noalloc(*[_ref(d) for d in descs], ctypes.c_float(scale),
+                                         _ref(describe(k_scale)), _ref(describe(v_scale)),
+                                         _ref(describe(out)), _stream_handle(q, stream))
+    _raise(st, "paged_attn_decode_noalloc")
     return out
 
 

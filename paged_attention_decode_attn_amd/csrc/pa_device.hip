@@ -909,6 +909,15 @@ std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
 std::vector<int> g_cus;
 
+// Scratch of the no-allocation entry point: one array per device, in the
+// code object's own device memory (allocated when the runtime loads the
+// library on a device, held until the process ends).  Host code never
+// passes the array's name to a kernel (on the host it only stands for the
+// symbol); it looks the device address up once per device and passes that.
+constexpr size_t kScratchBytes = size_t(48) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::vector<void*> g_scratch;        // per device: scratch's device address (null: not looked up)
+
 struct Profile {
     bool active = false;
     int max_calls = 0, calls = 0;
@@ -971,6 +980,22 @@ int get_workspace(int dev, void* stream, size_t need, void** out) {
     return PA_OK;
 }
 
+// The device address of this device's scratch array, looked up on the
+// device's first no-allocation call (the device is current).
+int scratch_address(int dev, void** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return PA_OK;
+}
+
 template <int D, bool FP8, bool GEN>
 const void* kernel_of(int nt) {
     return nt == 1 ? reinterpret_cast<const void*>(&partition_kernel<D, FP8, 1, GEN>)
@@ -1007,12 +1032,13 @@ const void* partition_kernel_of(int D, bool fp8, int nt, bool gen) {
 namespace pa {
 namespace {
 
-// Both decode entry points: validation, plan, the stream's workspace, the
-// partition launch and the merge launch.
+// Both decode entry points: validation, plan, workspace (the stream's own,
+// or with `noalloc` the device's static scratch array), the partition
+// launch and the merge launch.
 int decode_call(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
                 const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* query_lens,
                 float scale, const pa_tensor* k_scale, const pa_tensor* v_scale, int32_t sliding_window,
-                const pa_tensor* sinks, pa_tensor* out, void* stream) {
+                const pa_tensor* sinks, pa_tensor* out, void* stream, bool noalloc) {
     Problem pr;
     int st = validate(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
                       sliding_window, sinks, out, &pr);
@@ -1025,9 +1051,17 @@ int decode_call(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v
     const int64_t max_ctx = max_context_tokens(pr.BS, pr.W, pr.window, pr.Qmax);
     if ((st = make_plan(pr.B, pr.Hq, pr.Hkv, pr.D, pr.Qmax, max_ctx, pr.fp8, device_cus(dev), &plan))) return st;
     void* ws = nullptr;
-    if (plan.workspace_bytes > 0 &&
-        (st = get_workspace(dev, stream, (size_t)plan.workspace_bytes, &ws)))
-        return st;
+    if (plan.workspace_bytes > 0) {
+        if (noalloc) {
+            if ((size_t)plan.workspace_bytes > kScratchBytes)
+                return fail(PA_ERR_UNSUPPORTED,
+                            "the call needs %lld workspace bytes; the no-allocation entry point's scratch "
+                            "holds %zu", (long long)plan.workspace_bytes, kScratchBytes);
+            if ((st = scratch_address(dev, &ws))) return st;
+        } else if ((st = get_workspace(dev, stream, (size_t)plan.workspace_bytes, &ws))) {
+            return st;
+        }
+    }
 
     const size_t lds = plan.whole_segments ? 0 : (size_t)pr.B * sizeof(int);
     const bool general = pr.BS > PA_BLOCK_SIZE || pr.window > 0 || pr.sinks != nullptr || plan.whole_segments;
@@ -1112,7 +1146,7 @@ int paged_attn_decode_ext(const pa_tensor* q, const pa_tensor* k_cache, const pa
                           const pa_tensor* v_scale, int32_t sliding_window, const pa_tensor* sinks,
                           pa_tensor* out, void* stream) {
     return pa::decode_call(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
-                           sliding_window, sinks, out, stream);
+                           sliding_window, sinks, out, stream, false);
 }
 
 int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
@@ -1120,9 +1154,16 @@ int paged_attn_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_ten
                       const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
                       const pa_tensor* v_scale, pa_tensor* out, void* stream) {
     return pa::decode_call(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
-                           0, nullptr, out, stream);
+                           0, nullptr, out, stream, false);
 }
 
+int paged_attn_decode_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                              const pa_tensor* block_tables, const pa_tensor* context_lens,
+                              const pa_tensor* query_lens, float scale, const pa_tensor* k_scale,
+                              const pa_tensor* v_scale, pa_tensor* out, void* stream) {
+    return pa::decode_call(q, k_cache, v_cache, block_tables, context_lens, query_lens, scale, k_scale, v_scale,
+                           0, nullptr, out, stream, true);
+}
 
 int paged_attn_reserve(int64_t bytes, void* stream) {
     if (bytes < 0) return pa::fail(PA_ERR_ARG, "reserve: negative size");
