@@ -108,6 +108,7 @@ struct RedArgs {
     char* out;       int64_t o_sb, o_st, o_sh;        // bytes
     int32_t B, Hq, Hkv, G, Qmax, rows, HG, grid, min_share;
     int32_t red_rows, red_col4, red_lanes;            // merge workgroup shape (see reduce_kernel)
+    int32_t spec;                                     // 1: one sequence, grid a multiple of the head groups
 };
 
 template <typename T>
@@ -810,46 +811,68 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
     const int g = (int)(id % a.Hkv); id /= a.Hkv;
     const int t = (int)(id % a.Qmax);
     const int b = (int)(id / a.Qmax);
-    const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
-    if (t >= nq) return;
-    const int pre = b > 0 ? a.ws_pre[b - 1] : 0;
-    const int cb = a.ws_pre[b] - pre;
-    if (cb <= 0) return;
-    const int ngrp = a.Hkv / a.HG;
-    const int64_t C = (int64_t)a.ws_pre[a.B - 1] * ngrp;
-    const int n = share_count(a.grid, C, a.min_share);
-    const int gg = g / a.HG, wave = g - gg * a.HG;
-    const int64_t S = (int64_t)pre * ngrp + (int64_t)gg * cb;
-    const int first = share_owner(S, C, n), last = share_owner(S + cb - 1, C, n);
-    if (first == last) return;                  // written by the partition kernel
-    const int np = last - first + 1;
-    const int slot0 = share_begin(first, C, n) == S ? 0 : 1;
-
     // thread = (pl, rg, c): columns fastest, so a wave reads whole partial rows
     const int c = tid % CB, rg = (tid / CB) % RG, pl = tid / (CB * RG);
     const bool active = pl < PL;
     const int hl = rgi * RG + rg;                 // query head within the group
     const int r = t * a.G + hl;                   // row within the kv head's rows
     const int col = 4 * (cbi * CB + c);
+    const int ngrp = a.Hkv / a.HG;
+    const int gg = g / a.HG, wave = g - gg * a.HG;
     const float ninf = -__builtin_inff();
+    float l[U];
+    f32x4 o[U];
+    // one round of partial loads: partials p0, p0 + PL, ... of the row's
+    // list (shares first .. first + np - 1, slot0 for the first)
+    auto load_round = [&](int first, int np, int slot0, int p0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * PL;
+            if (active && p < np) {
+                const int64_t pid = ((int64_t)(2 * (first + p) + (p == 0 ? slot0 : 0)) * a.HG + wave) * a.rows + r;
+                l[u] = a.ws_lse[pid];
+                o[u] = *reinterpret_cast<const f32x4*>(a.ws_o + pid * D + col);
+            } else {
+                l[u] = ninf;
+                o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    // Loads that do not depend on each other go out together: the query
+    // length, the chunk prefix and, for one sequence whose shares split
+    // evenly between the kv-head groups (spec), the row's first round of
+    // partials, whose places then do not depend on the context length (the
+    // shares of group gg are gg*grid/ngrp .. (gg+1)*grid/ngrp - 1, slot 0,
+    // whenever the sequence has at least grid/ngrp chunks per group); the
+    // guess is checked against the prefix and reloaded if it misses.
+    // (every load is unconditional, its address or its value selected, so
+    // that no branch separates them)
+    const int32_t* qlp = a.ql ? a.ql + (int64_t)b * a.ql_s : a.ws_pre + b;
+    const int nq_raw = *qlp;
+    const int pre_raw = a.ws_pre[max(b - 1, 0)];
+    const int end = a.ws_pre[b];
+    const int tot = a.ws_pre[a.B - 1];
+    const int kspec = a.grid / ngrp;
+    if (a.spec) load_round(gg * kspec, kspec, 0, pl);
+    const int nq = min(a.ql ? nq_raw : a.Qmax, a.Qmax);
+    const int pre = b > 0 ? pre_raw : 0;
+    if (t >= nq) return;
+    const int cb = end - pre;
+    if (cb <= 0) return;
+    const int64_t C = (int64_t)tot * ngrp;
+    const int n = share_count(a.grid, C, a.min_share);
+    const int64_t S = (int64_t)pre * ngrp + (int64_t)gg * cb;
+    const int first = share_owner(S, C, n), last = share_owner(S + cb - 1, C, n);
+    if (first == last) return;                  // written by the partition kernel
+    const int np = last - first + 1;
+    const int slot0 = share_begin(first, C, n) == S ? 0 : 1;
+    const bool hit = a.spec && first == gg * kspec && np == kspec && slot0 == 0;
+
     float m = ninf, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (active) {
         for (int p0 = pl; p0 < np; p0 += PL * U) {
-            float l[U];
-            f32x4 o[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = p0 + u * PL;
-                if (p < np) {
-                    const int64_t pid = ((int64_t)(2 * (first + p) + (p == 0 ? slot0 : 0)) * a.HG + wave) * a.rows + r;
-                    l[u] = a.ws_lse[pid];
-                    o[u] = *reinterpret_cast<const f32x4*>(a.ws_o + pid * D + col);
-                } else {
-                    l[u] = ninf;
-                    o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
+            if (!(hit && p0 == pl)) load_round(first, np, slot0, p0);
             float mn = m;
 #pragma unroll
             for (int u = 0; u < U; ++u) mn = fmaxf(mn, l[u]);
@@ -1124,6 +1147,7 @@ int decode_call(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v
         r.B = a.B; r.Hq = a.Hq; r.Hkv = a.Hkv; r.G = a.G; r.Qmax = a.Qmax; r.rows = a.rows; r.HG = HG;
         r.grid = (int32_t)grid; r.min_share = a.min_share;
         r.red_rows = plan.reduce_rows; r.red_col4 = plan.reduce_col4; r.red_lanes = plan.reduce_lanes;
+        r.spec = pr.B == 1 && grid % (pr.Hkv / HG) == 0 && grid / (pr.Hkv / HG) <= (int64_t)plan.reduce_lanes * kRedUnroll;
         const dim3 rgrid((unsigned)plan.reduce_groups), rblock((unsigned)kRedThreads);
         if (pr.D == 256) hipLaunchKernelGGL(reduce_kernel<256>, rgrid, rblock, 0, s, r);
         else if (pr.D == 128) hipLaunchKernelGGL(reduce_kernel<128>, rgrid, rblock, 0, s, r);

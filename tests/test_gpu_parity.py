@@ -62,6 +62,19 @@ def test_heads_per_workgroup(hg, groups):
         check(w, groups, label=f"hg{hg}/{name}/g{groups}", heads_per_group=hg)
 
 
+def test_calls_of_different_shapes_alternate_on_one_stream():
+    # one stream's workspace serves calls of every plan, whose layouts of
+    # partials, log-sum-exps and chunk prefix differ
+    names = ("long_ctx", "mtp_verify", "fp8", "llama3_8b", "mha", "d256", "long_ctx_bs256")
+    ws = {n: generate(SMALL[n]) for n in names}
+    refs = {n: oracle_out(w) for n, w in ws.items()}
+    for rnd in range(3):
+        for n in names if rnd % 2 == 0 else reversed(names):
+            note(f"[gpu] alternating shapes: round {rnd} {n}")
+            out = run_gpu(ws[n])
+            compare(out, refs[n], ws[n].query_lens, label=f"alternate{rnd}/{n}")
+
+
 @pytest.mark.parametrize("share", [2, 3, 40])
 def test_min_share(share):
     for name in ("llama3_8b", "fp8", "long_ctx"):
