@@ -14,7 +14,9 @@ tokens, 64 query / 8 kv heads, head_dim 128, bf16 KV).  Unless --only is
 given, the same line also carries the fp8-KV workload (16 sequences,
 contexts 512..32768, head_dim 64, e4m3fn with per-token scales) measured
 the same way ("fp8_config") and the read rate of a plain streaming kernel
-at both calls' byte counts ("read_ceiling").  --op stream sweeps the
+at both calls' byte counts ("read_ceiling"); each decode entry also
+carries "gather_ceiling", a plain kernel reading exactly the blocks the
+call reads (the paged access pattern's own ceiling).  --op stream sweeps the
 streaming probe's launch shapes alone.
 """
 from __future__ import annotations
@@ -63,6 +65,9 @@ def parse_args():
     ap.add_argument("--min-share", type=int, default=0, help="smallest share in 32-token chunks (0 = the planner's)")
     ap.add_argument("--copies", type=int, default=0, help="rotated KV copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time the gather probe over the workload's own blocks (on by default for the "
+                         "full long_ctx run)")
     ap.add_argument("--only", action="store_true",
                     help="with the default long_ctx workload: measure it alone (no fp8 config, no read ceiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -72,6 +77,9 @@ def parse_args():
                     help="turn rocprofv3 output directories of this workload into the text "
                          "summary and traffic record under profiles/ (no GPU needed)")
     ap.add_argument("--command", default="", help="with --summarize: the commands that made the runs")
+    ap.add_argument("--counters", nargs="*", default=[], metavar="DIR",
+                    help="with --summarize: rocprofv3 --pmc output directories of SQ/TA/TCP/GRBM counter "
+                         "passes of the same workload, summarised with derived figures")
     return ap.parse_args()
 
 
@@ -195,6 +203,8 @@ def summarize(args):
                       f"({100 * kvb / avg_ns / HBM_PEAK_GBS:.1f}% of 8 TB/s) at the traced average "
                       f"duration; HBM traffic {record.get(kname, 0) / kvb:.3f} x the "
                       f"algorithmic bytes."]
+    if args.counters:
+        lines += counter_lines(args.counters, kernels)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     fname = f"{kname}_{args.config}{'_bulk' + str(args.bulk) if args.op == 'cache_write' and args.bulk else ''}.md"
     with open(os.path.join(os.path.dirname(TRAFFIC_FILE), fname), "w") as f:
@@ -214,6 +224,55 @@ def summarize(args):
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(allrec, f, indent=1, sort_keys=True)
     print("\n".join(lines))
+
+
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4     # MI355X
+
+
+def counter_lines(dirs, kernels):
+    """Per-dispatch averages of the counter passes and figures derived from
+    them.  GRBM_GUI_ACTIVE is summed over the XCDs, so the kernel's own
+    cycles are GRBM_GUI_ACTIVE / 8; SIMD-cycles are those times 1024 SIMDs."""
+    vals = {}
+    for d in dirs:
+        for name, cname, v in _db_rows(d, "select kernel_name, counter_name, avg(value) from counters_collection "
+                                          "group by kernel_name, counter_name"):
+            for like, label in kernels:
+                if like.strip("%") in name:
+                    vals.setdefault(label, {})[cname] = v
+    out = ["", "Counters (rocprofv3 --pmc, averages per dispatch; derived figures below the table):", "",
+           "| kernel | counter | value |", "|---|---|---|"]
+    for label, cs in vals.items():
+        for c in sorted(cs):
+            out.append(f"| {label} | {c} | {cs[c]:.0f} |")
+    out += [""]
+    for label, cs in vals.items():
+        cyc = cs.get("GRBM_GUI_ACTIVE", 0) / XCDS
+        simd_cyc = cyc * CUS * SIMDS_PER_CU
+        fig = []
+        if cyc:
+            fig.append(f"kernel cycles (GRBM_GUI_ACTIVE / {XCDS}) {cyc:.0f}")
+        if simd_cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+            fig.append(f"MFMA busy {100 * cs['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cyc:.1f} % of SIMD-cycles")
+        if simd_cyc and "SQ_ACTIVE_INST_VALU" in cs:
+            fig.append(f"VALU busy {100 * 4 * cs['SQ_ACTIVE_INST_VALU'] / simd_cyc:.1f} % of SIMD-cycles "
+                       f"(SQ_ACTIVE_INST_VALU x 4)")
+        if cs.get("SQ_INSTS_MFMA"):
+            fig.append(f"{cs['SQ_INSTS_VALU'] / cs['SQ_INSTS_MFMA']:.1f} VALU instructions per MFMA")
+        if cs.get("SQ_WAVES"):
+            fig.append(f"per wave: {cs.get('SQ_INSTS_VALU', 0) / cs['SQ_WAVES']:.0f} VALU, "
+                       f"{cs.get('SQ_INSTS_MFMA', 0) / cs['SQ_WAVES']:.0f} MFMA, "
+                       f"{cs.get('SQ_INSTS_VMEM_RD', 0) / cs['SQ_WAVES']:.0f} vector-memory reads")
+        if cs.get("TCP_TCC_READ_REQ_sum"):
+            fig.append(f"average L2 read latency {cs['TCP_TCC_READ_REQ_LATENCY_sum'] / cs['TCP_TCC_READ_REQ_sum']:.0f} "
+                       f"cycles (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ)")
+        if cyc and "TA_BUSY_avr" in cs:
+            fig.append(f"TA busy {100 * cs['TA_BUSY_avr'] / cyc:.0f} % of cycles")
+        if cyc and "TA_ADDR_STALLED_BY_TC_CYCLES_sum" in cs:
+            fig.append(f"TA address path stalled by the L1 {100 * cs['TA_ADDR_STALLED_BY_TC_CYCLES_sum'] / CUS / cyc:.0f} "
+                       f"% of cycles (per CU)")
+        out.append(f"{label}: " + "; ".join(fig) + ".")
+    return out
 
 
 def calibrate_copy():
@@ -513,7 +572,55 @@ def stream_ceiling(nbytes_list=(1 << 30,), steps: int = 20, warmup: int = 3):
     return out
 
 
-def bench_decode(args, config: str, cpu_seconds: float):
+def gather_ceiling(spec, w, pools, steps: int = 10, warmup: int = 2):
+    """Read rate of the gather probe over exactly the bytes and places a
+    decode call of this workload reads: every used block (all kv heads) of
+    K, V and, for fp8, both scale arrays, from the same rotated pool copies;
+    the best of a sweep of launch shapes."""
+    import torch
+
+    from paged_attention_decode_attn_amd import binding as B
+    bt = w.block_tables.cpu()
+    ids = []
+    for b in range(spec.batch):
+        L = int(w.context_lens[b])
+        ids.append(bt[b, :(L + spec.block_size - 1) // spec.block_size])
+    ids = torch.cat(ids).to(torch.int32).cuda()
+    k0 = pools[0][0]
+    nb = k0.shape[0]
+    kvb = k0.stride(0) * k0.element_size()
+    arrays = []
+    for kc, vc, ks, vs in pools:
+        a = [(kc, kvb, kvb), (vc, kvb, kvb)]
+        if ks is not None:
+            sb = ks.stride(0) * 4
+            a += [(ks, sb, sb), (vs, sb, sb)]
+        arrays.append(a)
+    nbytes = ids.numel() * sum(x[2] for x in arrays[0])
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for wg in (cus, 2 * cus, 4 * cus):
+        for t in (256, 512, 1024):
+            for u in (4, 8, 16):
+                for i in range(warmup):
+                    B.paged_attn_probe_gather_read(arrays[i % len(arrays)], ids, nb, wg, t, u, sink)
+                torch.cuda.synchronize()
+                start.record()
+                for i in range(steps):
+                    B.paged_attn_probe_gather_read(arrays[i % len(arrays)], ids, nb, wg, t, u, sink)
+                stop.record()
+                torch.cuda.synchronize()
+                us = start.elapsed_time(stop) * 1e3 / steps
+                rows.append((nbytes / us / 1e3, us, wg, t, u))
+    best = max(rows)
+    return {"bytes": nbytes, "blocks": int(ids.numel()), "best_GBs": round(best[0], 1),
+            "best_frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4), "best_us": round(best[1], 3),
+            "best_shape": {"workgroups": best[2], "threads": best[3], "loads_in_flight": best[4]}}
+
+
+def bench_decode(args, config: str, cpu_seconds: float, ceiling: bool = False):
     """One decode workload: eager steps (the value), the same steps with
     per-kernel HIP events (the roofline's kernel time), and a graph replay."""
     import torch
@@ -645,6 +752,9 @@ def bench_decode(args, config: str, cpu_seconds: float):
                      "traffic": traffic, "algorithmic_bytes": kvb,
                      "kernel": "partition_kernel"},
     }
+    if ceiling and spec.sliding_window == 0:
+        print(f"[bench] {config}: gather-probe ceiling", file=sys.stderr, flush=True)
+        res["gather_ceiling"] = gather_ceiling(spec, w, pools)
     if cpu_seconds > 0:
         print(f"[bench] {config}: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
@@ -688,12 +798,13 @@ def main():
         return
 
     cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
-    res = bench_decode(args, args.config, cpu_s)
-    if args.config == "long_ctx" and not args.only:
+    full = args.config == "long_ctx" and not args.only
+    res = bench_decode(args, args.config, cpu_s, ceiling=full or args.ceiling)
+    if full:
         # the second target configuration, measured the same way in the
         # same run, and the read ceiling of a plain streaming kernel at the
         # two calls' byte counts
-        res["fp8_config"] = bench_decode(args, "fp8", min(cpu_s, 5.0))
+        res["fp8_config"] = bench_decode(args, "fp8", min(cpu_s, 5.0), ceiling=True)
         print("[bench] streaming-read probe", file=sys.stderr, flush=True)
         ceil = stream_ceiling((res["kv_bytes_per_call"], res["fp8_config"]["kv_bytes_per_call"]),
                               steps=max(5, min(args.steps, 20)), warmup=3)

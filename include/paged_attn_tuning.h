@@ -64,6 +64,22 @@ int paged_attn_profile_end(double* partition_ms, double* reduce_ms, int32_t* cal
 int paged_attn_probe_stream_read(const void* src, int64_t bytes, int32_t workgroups, int32_t threads,
                                  int32_t unroll, int32_t grid_stride, void* sink, void* stream);
 
+/*
+ * paged_attn_probe_gather_read -- the gather probe: reads, for each of the
+ * n block ids (device int32, clamped into [0, num_blocks)), block_bytes[j]
+ * bytes at arrays[j] + id * block_strides[j] for j = 0..3 (block_bytes[j]
+ * a multiple of 16, 0 for an unused array; arrays 16-byte aligned device
+ * memory of num_blocks blocks each), in `workgroups` workgroups of
+ * `threads` threads with `unroll` (4, 8 or 16) 16-byte loads in flight per
+ * thread.  With a cache's K and V (and its two scale arrays) and the block
+ * ids a decode call reads, it moves the same bytes from the same places.
+ * `sink`: 4 bytes of device memory the probe may write.
+ */
+int paged_attn_probe_gather_read(const void* const* arrays, const int64_t* block_strides,
+                                 const int32_t* block_bytes, const int32_t* block_ids, int32_t n,
+                                 int32_t num_blocks, int32_t workgroups, int32_t threads, int32_t unroll,
+                                 void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

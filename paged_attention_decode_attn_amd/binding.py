@@ -93,6 +93,9 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_reserve.argtypes = [ctypes.c_int64, ctypes.c_void_p]
                 L.paged_attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
                     ctypes.c_void_p, ctypes.c_void_p]
+                L.paged_attn_probe_gather_read.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
+                                                           ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p] + [
+                    ctypes.c_int32] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
                 i32p = ctypes.POINTER(ctypes.c_int32)
                 L.paged_attn_check_metadata.argtypes = [i32p, i32p, i32p] + [ctypes.c_int64] * 6 + [ctypes.c_int32]
                 L.paged_attn_profile_begin.argtypes = [ctypes.c_int32]
@@ -110,7 +113,7 @@ def lib() -> ctypes.CDLL:
                              "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
                              "paged_attn_set_workgroups", "paged_attn_set_min_share",
                              "paged_attn_set_heads_per_group",
-                             "paged_attn_reserve", "paged_attn_probe_stream_read",
+                             "paged_attn_reserve", "paged_attn_probe_stream_read", "paged_attn_probe_gather_read",
                              "paged_attn_check_metadata", "paged_attn_profile_begin",
                              "paged_attn_profile_end"):
                     getattr(L, name).restype = ctypes.c_int
@@ -383,6 +386,21 @@ def paged_attn_probe_stream_read(src: torch.Tensor, workgroups: int, threads: in
                                             int(workgroups), int(threads), int(unroll), int(bool(grid_stride)),
                                             ctypes.c_void_p(sink.data_ptr()), _stream_handle(src, stream))
     _raise(st, "paged_attn_probe_stream_read")
+
+
+def paged_attn_probe_gather_read(arrays, block_ids: torch.Tensor, num_blocks: int, workgroups: int, threads: int,
+                                 unroll: int, sink: torch.Tensor, stream=None) -> None:
+    """The gather probe (measurement only): ``arrays`` is up to four
+    (tensor, block stride in bytes, bytes read per block) triples."""
+    arrays = list(arrays) + [(None, 0, 0)] * (4 - len(arrays))
+    ptrs = (ctypes.c_void_p * 4)(*[None if t is None else t.data_ptr() for t, _, _ in arrays])
+    strides = (ctypes.c_int64 * 4)(*[int(st) for _, st, _ in arrays])
+    nbytes = (ctypes.c_int32 * 4)(*[int(nb) for _, _, nb in arrays])
+    st = lib().paged_attn_probe_gather_read(ptrs, strides, nbytes, ctypes.c_void_p(block_ids.data_ptr()),
+                                            int(block_ids.numel()), int(num_blocks), int(workgroups), int(threads),
+                                            int(unroll), ctypes.c_void_p(sink.data_ptr()),
+                                            _stream_handle(block_ids, stream))
+    _raise(st, "paged_attn_probe_gather_read")
 
 
 def paged_attn_strerror(status: int) -> str:
