@@ -58,6 +58,8 @@ def parse_args():
                          "prefill: packed prefill chunks over the paged cache (--config prefill_8k or "
                          "chunked_prefill); stream: the streaming-read probe's ceiling over launch "
                          "shapes")
+    ap.add_argument("--write-pieces", type=int, default=0,
+                    help="with --op cache_write: 16-byte pieces per thread (0 = the library's choice)")
     ap.add_argument("--bulk", type=int, default=0,
                     help="with --op cache_write: write this many tokens to distinct random slots "
                          "of a large pool instead of the config's decode step")
@@ -456,6 +458,7 @@ def bench_cache_write(args):
     from paged_attention_decode_attn_amd.workloads import write_bytes
 
     spec, cw, name, wb = cache_write_workload(args)
+    B.paged_attn_set_write_pieces(args.write_pieces)
     d = cw.to("cuda")
     w = d.base
     row_bytes = 2 * d.k_new.numel() * 2

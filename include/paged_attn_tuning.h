@@ -39,6 +39,13 @@ int paged_attn_set_min_share(int32_t chunks);
 int paged_attn_set_heads_per_group(int32_t heads);
 
 /*
+ * paged_attn_set_write_pieces -- override how many 16-byte row pieces each
+ * thread of paged_attn_reshape_and_cache moves (1, 2 or 4), or 0 for the
+ * automatic choice (1).
+ */
+int paged_attn_set_write_pieces(int32_t pieces);
+
+/*
  * Kernel timing for measurement: after paged_attn_profile_begin(n), the
  * next n calls of paged_attn_decode or paged_attn_decode_ext (on any
  * stream) record HIP events

@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
                 L.paged_attn_set_workgroups.argtypes = [ctypes.c_int32]
                 L.paged_attn_set_min_share.argtypes = [ctypes.c_int32]
                 L.paged_attn_set_heads_per_group.argtypes = [ctypes.c_int32]
+                L.paged_attn_set_write_pieces.argtypes = [ctypes.c_int32]
                 L.paged_attn_reserve.argtypes = [ctypes.c_int64, ctypes.c_void_p]
                 L.paged_attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
                     ctypes.c_void_p, ctypes.c_void_p]
@@ -112,7 +113,7 @@ def lib() -> ctypes.CDLL:
                              "paged_attn_prefill_ext", "paged_attn_check_prefill_ext",
                              "paged_attn_reshape_and_cache", "paged_attn_check_reshape_and_cache",
                              "paged_attn_set_workgroups", "paged_attn_set_min_share",
-                             "paged_attn_set_heads_per_group",
+                             "paged_attn_set_heads_per_group", "paged_attn_set_write_pieces",
                              "paged_attn_reserve", "paged_attn_probe_stream_read", "paged_attn_probe_gather_read",
                              "paged_attn_check_metadata", "paged_attn_profile_begin",
                              "paged_attn_profile_end"):
@@ -345,6 +346,10 @@ def paged_attn_set_min_share(chunks: int) -> None:
 
 def paged_attn_set_heads_per_group(heads: int) -> None:
     _raise(lib().paged_attn_set_heads_per_group(int(heads)), "paged_attn_set_heads_per_group")
+
+
+def paged_attn_set_write_pieces(pieces: int) -> None:
+    _raise(lib().paged_attn_set_write_pieces(int(pieces)), "paged_attn_set_write_pieces")
 
 
 def paged_attn_reserve(nbytes: int, stream=None) -> None:

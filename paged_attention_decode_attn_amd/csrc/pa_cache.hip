@@ -9,15 +9,17 @@
 // Inference", "Attention Input Fusion" (fp8 scales calculated as K/V are
 // written into the paged cache).  Scale rule: the row's absolute maximum
 // divided by 448, the largest finite e4m3fn value (1 for an all-zero row);
-// every element is divided by that stored scale (correctly rounded float32
-// division, so a code is the rounding of exactly the quotient that
+// every element is divided by that stored scale (the correctly rounded
+// float32 quotient, so a code is the rounding of exactly the quotient that
 // dequantisation multiplies back) and the codes round to nearest, ties to
 // even.
 //
-// One thread takes 8 consecutive elements (16 bytes of bf16) of one
-// (token, kv head) row of both K and V, so a wave reads and writes whole
-// contiguous token rows.  The D/8 threads of a row sit in one aligned lane
-// group of the wave and reduce the row's maximum with cross-lane exchanges.
+// A thread takes 8 consecutive elements (16 bytes of bf16) of one (token,
+// kv head) row of both K and V, so a wave reads and writes whole contiguous
+// token rows (a tuning override gives each thread several such pieces, one
+// grid apart, all loads issued before the stores).  The D/8 threads of a
+// row sit in one aligned lane group of the wave and reduce the row's maximum
+// with cross-lane exchanges.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -46,22 +48,45 @@ struct WriteArgs {
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// x / s clamped to +-448 for the two bf16 values of one dword
-__device__ __forceinline__ float q_lo(unsigned w, float s) {
-    return fminf(fmaxf(__fdiv_rn(bf16_lo(w), s), -kFp8Max), kFp8Max);
-}
-__device__ __forceinline__ float q_hi(unsigned w, float s) {
-    return fminf(fmaxf(__fdiv_rn(bf16_hi(w), s), -kFp8Max), kFp8Max);
+// Quotients x / s whose e4m3fn code equals that of the correctly rounded
+// float32 quotient, from r = RN(1 / s): q = RN(x r), the residual
+// e = RN(x - s q) (one fused multiply-add) and RN(q + e r) (another) give
+// RN(x / s) (Markstein's correction of a quotient by a correctly rounded
+// reciprocal; an exact-arithmetic emulation of these three roundings
+// matched the correctly rounded quotient for every pair of bf16 mantissas
+// of x and of the row maximum, at every ratio of their magnitudes that
+// leaves the quotient between 2^-12 and 448).  Below 2^-12 a quotient's
+// code is a signed zero whatever its low bits, so it is replaced by zero
+// with the sign of x.  For rows with s below 2^-80 the reciprocal or the
+// residual could leave the normal range, and those rows divide instead.
+constexpr float kTinyQuot = 0x1p-12f;
+constexpr float kSmallScale = 0x1p-80f;
+
+__device__ __forceinline__ float quot(float x, float s, float r, bool divide) {
+    if (divide) return __fdiv_rn(x, s);
+    const float q = x * r;
+    const float e = __builtin_fmaf(-q, s, x);
+    const float qc = __builtin_fmaf(e, r, q);
+    return fabsf(qc) < kTinyQuot ? copysignf(0.f, x) : qc;
 }
 
-// 8 bf16 values -> 8 e4m3fn bytes of x / s: each conversion packs two
-// codes into the low or the high half of a dword.
-__device__ __forceinline__ u32x2 encode8(const u32x4& x, float s) {
+// x / s clamped to +-448 for the two bf16 values of one dword
+__device__ __forceinline__ float q_lo(unsigned w, float s, float r, bool divide) {
+    return fminf(fmaxf(quot(bf16_lo(w), s, r, divide), -kFp8Max), kFp8Max);
+}
+__device__ __forceinline__ float q_hi(unsigned w, float s, float r, bool divide) {
+    return fminf(fmaxf(quot(bf16_hi(w), s, r, divide), -kFp8Max), kFp8Max);
+}
+
+// 8 bf16 values -> 8 e4m3fn bytes of x / s (r = RN(1 / s)): each
+// conversion packs two codes into the low or the high half of a dword.
+__device__ __forceinline__ u32x2 encode8(const u32x4& x, float s, float r) {
+    const bool d = s < kSmallScale;
     u32x2 out;
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[0], s), q_hi(x[0], s), 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[1], s), q_hi(x[1], s), w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[2], s), q_hi(x[2], s), 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[3], s), q_hi(x[3], s), w1, true);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[0], s, r, d), q_hi(x[0], s, r, d), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[1], s, r, d), q_hi(x[1], s, r, d), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[2], s, r, d), q_hi(x[2], s, r, d), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[3], s, r, d), q_hi(x[3], s, r, d), w1, true);
     out[0] = (unsigned)w0;
     out[1] = (unsigned)w1;
     return out;
@@ -74,57 +99,87 @@ __device__ __forceinline__ float absmax8(const u32x4& x) {
     return m;
 }
 
-template <bool FP8, int R8>
+// Thread piece `item` of the row grid: token t, kv head h, 8-element piece r.
+struct Piece {
+    int64_t t;
+    int h, r;
+};
+
+template <int R8>
+__device__ __forceinline__ Piece piece_of(const WriteArgs& a, int64_t item) {
+    const int64_t per_token = (int64_t)a.Hkv * R8;
+    const int64_t t = item / per_token;
+    const int rem = (int)(item - t * per_token);
+    return Piece{t, rem / R8, rem - (rem / R8) * R8};
+}
+
+// U pieces per thread, item = gid + k * (threads launched), k < U: every
+// load of the thread goes out before its first store.
+template <bool FP8, int R8, int U>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
-    const int64_t per_token = (int64_t)a.Hkv * R8;
-    const int64_t t = gid / per_token;
-    const int rem = (int)(gid - t * per_token);
-    const int h = rem / R8, r = rem - h * R8;
-    // every lane of a row group takes part in the reductions below, so the
-    // group is either wholly in range or wholly out (R8 divides 64)
-    const bool live_token = t < a.T;
-    const int64_t slot = live_token ? (int64_t)a.slots[t * a.slot_s] : -1;
-    const bool live = slot >= 0 && slot < a.slots_total;
-    u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
-    if (live) {
-        k = *reinterpret_cast<const u32x4*>(a.k_new + t * a.n_st + h * a.n_sh + 16 * r);
-        v = *reinterpret_cast<const u32x4*>(a.v_new + t * a.vn_st + h * a.vn_sh + 16 * r);
-    }
-    // slots are below 2^31, so the block / position split is 32-bit
-    const uint32_t us = (uint32_t)max<int64_t>(slot, 0);
-    const int64_t blk = us / a.bs, pos = us - (uint32_t)blk * a.bs;
-    if constexpr (!FP8) {
-        if (live) {
-            *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k;
-            *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) = v;
-        }
-    } else {
-        float mk = absmax8(k), mv = absmax8(v);
+    const int64_t nthreads = (int64_t)gridDim.x * kWriteThreads;
+    u32x4 k[U], v[U];
+    int64_t slot[U];
+    bool live[U];
 #pragma unroll
-        for (int o = 1; o < R8; o <<= 1) {
-            mk = fmaxf(mk, __shfl_xor(mk, o));
-            mv = fmaxf(mv, __shfl_xor(mv, o));
+    for (int u = 0; u < U; ++u) {
+        // every lane of a row group takes part in the reductions below, so
+        // the group is either wholly in range or wholly out (R8 divides 64,
+        // and the stride between a thread's pieces is a multiple of 64)
+        const Piece pc = piece_of<R8>(a, gid + u * nthreads);
+        const bool live_token = pc.t < a.T;
+        slot[u] = live_token ? (int64_t)a.slots[pc.t * a.slot_s] : -1;
+        live[u] = slot[u] >= 0 && slot[u] < a.slots_total;
+        k[u] = u32x4{0u, 0u, 0u, 0u};
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (live[u]) {
+            k[u] = *reinterpret_cast<const u32x4*>(a.k_new + pc.t * a.n_st + pc.h * a.n_sh + 16 * pc.r);
+            v[u] = *reinterpret_cast<const u32x4*>(a.v_new + pc.t * a.vn_st + pc.h * a.vn_sh + 16 * pc.r);
         }
-        // scale = absmax / 448 (stored); every element divided by it
-        const float sk = mk > 0.f ? __fdiv_rn(mk, kFp8Max) : 1.f;
-        const float sv = mv > 0.f ? __fdiv_rn(mv, kFp8Max) : 1.f;
-        if (live) {
-            *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) = encode8(k, sk);
-            *reinterpret_cast<u32x2*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 8 * r) = encode8(v, sv);
-            if (r == 0) {
-                a.ks[blk * a.ks_sblk + h * a.ks_sh + pos] = sk;
-                a.vs[blk * a.vs_sblk + h * a.vs_sh + pos] = sv;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const Piece pc = piece_of<R8>(a, gid + u * nthreads);
+        const int h = pc.h, r = pc.r;
+        // slots are below 2^31, so the block / position split is 32-bit
+        const uint32_t us = (uint32_t)max<int64_t>(slot[u], 0);
+        const int64_t blk = us / a.bs, pos = us - (uint32_t)blk * a.bs;
+        if constexpr (!FP8) {
+            if (live[u]) {
+                *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k[u];
+                *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) = v[u];
+            }
+        } else {
+            float mk = absmax8(k[u]), mv = absmax8(v[u]);
+#pragma unroll
+            for (int o = 1; o < R8; o <<= 1) {
+                mk = fmaxf(mk, __shfl_xor(mk, o));
+                mv = fmaxf(mv, __shfl_xor(mv, o));
+            }
+            // scale = absmax / 448 (stored); every element divided by it
+            const float sk = mk > 0.f ? __fdiv_rn(mk, kFp8Max) : 1.f;
+            const float sv = mv > 0.f ? __fdiv_rn(mv, kFp8Max) : 1.f;
+            const float rk = __fdiv_rn(1.f, sk), rv = __fdiv_rn(1.f, sv);
+            if (live[u]) {
+                *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) =
+                    encode8(k[u], sk, rk);
+                *reinterpret_cast<u32x2*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 8 * r) =
+                    encode8(v[u], sv, rv);
+                if (r == 0) {
+                    a.ks[blk * a.ks_sblk + h * a.ks_sh + pos] = sk;
+                    a.vs[blk * a.vs_sblk + h * a.vs_sh + pos] = sv;
+                }
             }
         }
     }
 }
 
-template <bool FP8>
+template <bool FP8, int U>
 const void* write_kernel_of(int D) {
-    return D == 256 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 32>)
-         : D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 16>)
-                    : reinterpret_cast<const void*>(&cache_write_kernel<FP8, 8>);
+    return D == 256 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 32, U>)
+         : D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 16, U>)
+                    : reinterpret_cast<const void*>(&cache_write_kernel<FP8, 8, U>);
 }
 
 }  // namespace
@@ -149,9 +204,15 @@ extern "C" int paged_attn_reshape_and_cache(const pa_tensor* k_new, const pa_ten
     a.vs = p.vs; a.vs_sblk = p.vs_sblk; a.vs_sh = p.vs_sh;
     a.T = p.T; a.slots_total = p.NB * p.BS;
     a.Hkv = (int32_t)p.Hkv; a.D = (int32_t)p.D; a.bs = (uint32_t)p.BS;
-    const int64_t threads = p.T * p.Hkv * (p.D / 8);
+    // pieces of 8 elements, one per thread unless the tuning override asks
+    // for more (2 or 4 pieces per thread measured no faster on bulk writes)
+    const int64_t pieces = p.T * p.Hkv * (p.D / 8);
+    const int upt = g_write_pieces.load() > 0 ? g_write_pieces.load() : 1;
+    const int64_t threads = (pieces + upt - 1) / upt;
     const int64_t groups = (threads + kWriteThreads - 1) / kWriteThreads;
-    const void* fn = p.fp8 ? write_kernel_of<true>((int)p.D) : write_kernel_of<false>((int)p.D);
+    const void* fn = upt == 4 ? (p.fp8 ? write_kernel_of<true, 4>((int)p.D) : write_kernel_of<false, 4>((int)p.D))
+                   : upt == 2 ? (p.fp8 ? write_kernel_of<true, 2>((int)p.D) : write_kernel_of<false, 2>((int)p.D))
+                              : (p.fp8 ? write_kernel_of<true, 1>((int)p.D) : write_kernel_of<false, 1>((int)p.D));
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3((unsigned)groups), dim3(kWriteThreads), args, 0,
                         static_cast<hipStream_t>(stream)) != hipSuccess)

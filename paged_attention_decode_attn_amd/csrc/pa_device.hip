@@ -192,16 +192,19 @@ struct BlockRef {
 // window and no sink, and none of their code is emitted.
 template <int D, bool FP8, bool GEN>
 __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, const HeadBase& hb, BlockRef br,
-                                          int step, int nsteps, int last_blk,
+                                          int step, int nsteps, int last_blk, int lo_blk,
                                           const unsigned (&koff)[Step<D, FP8>::KL], const unsigned (&voff)[4],
                                           unsigned soff) {
     typedef typename VLoad<D, FP8>::T VT;
     // For step < nsteps, sub-block 2*step holds keys of the sequence and
-    // sub-block 2*step + 1 may lie past it; a sub-block past the sequence, or
-    // a whole step past the window (a prefetch beyond its end), reads as
-    // zeros through an empty range, which costs no memory traffic.
-    const bool has0 = step < nsteps;
-    const bool has1 = has0 && 2 * step + 1 <= last_blk;
+    // sub-block 2*step + 1 may lie past it; a sub-block past the sequence, a
+    // whole step past the window (a prefetch beyond its end) or, with a
+    // sliding window, a sub-block below lo_blk (wholly below every row's
+    // window) reads as zeros through an empty range, which costs no memory
+    // traffic.
+    const bool in = step < nsteps;
+    const bool has0 = in && (!GEN || 2 * step >= lo_blk);
+    const bool has1 = in && 2 * step + 1 <= last_blk && (!GEN || 2 * step + 1 >= lo_blk);
     const int sc = min(step, nsteps - 1);
     const int l0 = 2 * sc, l1 = min(2 * sc + 1, last_blk);
     const uint32_t u0 = (uint32_t)__builtin_amdgcn_readlane(br.blk, l0);
@@ -600,8 +603,10 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         // sees; with a sliding window every step takes the masked variant
         // (a window's range is short, and its first steps are masked anyway)
         const int nclean = GEN && a.window > 0 ? 0 : min(nsteps, max(0, L - nq + 1 - tok0) / kChunkTokens);
-        // last 16-token sub-block of the sequence, relative to the window
+        // last 16-token sub-block of the sequence, relative to the window;
+        // with a sliding window, the first one holding a key some row sees
         const int last_blk = (L + 15) / 16 - 1 - 2 * pc;
+        const int lo_blk = GEN && a.window > 0 ? (vlo >> 4) - 2 * pc : 0;
         // A ring of R register buffers: while a step computes, the loads of
         // the next R-1 steps are in flight.  Loads are issued on every path
         // (past the window they read nothing), so the code between a load
@@ -609,7 +614,7 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         // the last steps of the piece take the masked variant.
         Step<D, FP8> buf[R];
 #pragma unroll
-        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8, GEN>(buf[i], a, hb, br, i, nsteps, last_blk, koff, voff, soff);
+        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8, GEN>(buf[i], a, hb, br, i, nsteps, last_blk, lo_blk, koff, voff, soff);
         // Every kLockstep steps the workgroup's waves meet at a barrier.  Two
         // waves share each SIMD, and the older one otherwise wins the issue
         // and memory arbitration until it is done, leaving the younger to
@@ -620,7 +625,8 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         for (; st + R <= nclean; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, lo_blk, koff, voff,
+                                       soff);
                 if (((st + i) & (kLockstep - 1)) == 0) __syncthreads();
                 compute_step<D, FP8, NT, false, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
             }
@@ -628,7 +634,8 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         for (; st < nsteps; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, koff, voff, soff);
+                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, lo_blk, koff, voff,
+                                       soff);
                 if (st + i < nsteps)
                     compute_step<D, FP8, NT, true, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
             }

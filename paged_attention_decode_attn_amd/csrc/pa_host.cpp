@@ -20,6 +20,8 @@ std::atomic<int32_t> g_share_override{0};
 
 }  // namespace
 
+std::atomic<int32_t> g_write_pieces{0};
+
 int64_t elem_bytes(int32_t dtype) {
     switch (dtype) {
         case PA_DTYPE_BF16: return 2;
@@ -502,6 +504,13 @@ int paged_attn_set_workgroups(int32_t workgroups) {
 int paged_attn_set_min_share(int32_t chunks) {
     if (chunks < 0) return pa::fail(PA_ERR_ARG, "min share must be 0 (automatic) or positive");
     pa::g_share_override.store(chunks);
+    return PA_OK;
+}
+
+int paged_attn_set_write_pieces(int32_t pieces) {
+    if (pieces != 0 && pieces != 1 && pieces != 2 && pieces != 4)
+        return pa::fail(PA_ERR_ARG, "write pieces per thread must be 0 (automatic), 1, 2 or 4");
+    pa::g_write_pieces.store(pieces);
     return PA_OK;
 }
 

@@ -2,6 +2,7 @@
 // (pa_host.cpp, plain C++) and the HIP launch code (pa_device.hip).
 #pragma once
 
+#include <atomic>
 #include <cstdint>
 
 #include "paged_attn.h"
@@ -61,6 +62,9 @@ int64_t max_context_tokens(int64_t block_size, int64_t table_width, int32_t wind
 // The split-context plan (see pa_plan in paged_attn.h).
 int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64_t max_context,
               bool fp8, int32_t num_cus, pa_plan* plan);
+
+// Cache-write pieces per thread override (paged_attn_tuning.h; 0 = automatic).
+extern std::atomic<int32_t> g_write_pieces;
 
 // Records a failure description for paged_attn_last_error() and returns `status`.
 int fail(int status, const char* fmt, ...);

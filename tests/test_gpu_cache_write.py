@@ -66,9 +66,12 @@ def test_decode_step_write_matches_oracle(name, kv):
     _check_pool(cw, d, f"{name}/{kv}")
 
 
+@pytest.mark.parametrize("pieces", [0, 2, 4])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
 @pytest.mark.parametrize("hkv,d", [(1, 64), (2, 128), (8, 64), (8, 128), (3, 128), (2, 256), (8, 256)])
-def test_bulk_write_with_padding_and_out_of_pool_slots(kv, hkv, d):
+def test_bulk_write_with_padding_and_out_of_pool_slots(kv, hkv, d, pieces):
+    # pieces: 16-byte row pieces per thread (0: the library's choice, one
+    # for writes this small); a ragged last round leaves threads idle
     spec = CONFIGS["llama3_8b"].replace(batch=2, hq=hkv, hkv=hkv, head_dim=d, kv_dtype=kv, ctx_lo=16,
                                         ctx_hi=64, pool_blocks=90)
     cw = generate_cache_write(spec, bulk_tokens=1000, pad=5)
@@ -76,9 +79,45 @@ def test_bulk_write_with_padding_and_out_of_pool_slots(kv, hkv, d):
     s[3] = 90 * 16 + 7                                     # past the pool: skipped
     s[4] = -7                                              # any negative: skipped
     cw.slot_mapping = s
-    note(f"[gpu] bulk cache write hkv={hkv} d={d} {kv}")
-    d_ = _gpu_write(cw)
-    _check_pool(cw, d_, f"bulk/{hkv}/{d}/{kv}")
+    note(f"[gpu] bulk cache write hkv={hkv} d={d} {kv} pieces={pieces}")
+    B.paged_attn_set_write_pieces(pieces)
+    try:
+        d_ = _gpu_write(cw)
+    finally:
+        B.paged_attn_set_write_pieces(0)
+    _check_pool(cw, d_, f"bulk/{hkv}/{d}/{kv}/{pieces}")
+
+
+def test_fp8_quotients_for_every_pair_of_mantissas():
+    # Every bf16 mantissa of the row's absolute maximum (the scale is
+    # absmax / 448) against every bf16 mantissa of an element, at element
+    # magnitudes that put the quotient anywhere from below the smallest
+    # e4m3fn subnormal to 448, both signs: each code must be the rounding of
+    # the correctly rounded float32 quotient, as the oracle's division gives
+    D = 64
+    man = 1.0 + np.arange(128) / 128.0                      # the 128 bf16 mantissas in [1, 2)
+    xs = np.concatenate([man * 2.0 ** e for e in range(-20, 1)])
+    xs = np.concatenate([xs, -xs])                          # 5376 elements of magnitude below 2
+    per_row = D - 1
+    rows = []
+    for am in man:                                          # absmax in [1, 2): its scale am / 448
+        for i in range(0, len(xs), per_row):
+            r = np.zeros(D, np.float32)
+            r[0] = am
+            chunk = xs[i:i + per_row]
+            r[1:1 + len(chunk)] = np.clip(chunk, -am, am)
+            rows.append(r)
+    x = np.stack(rows)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert torch.equal(xb.float(), torch.from_numpy(x))   # all exact bf16 values
+    T = xb.shape[0]
+    spec = CONFIGS["fp8"].replace(batch=1, hq=1, hkv=1, head_dim=D, ctx_lo=16, ctx_hi=16, pool_blocks=T // 16 + 4)
+    cw = generate_cache_write(spec, bulk_tokens=T)
+    cw.k_new = xb[:, None, :].contiguous()
+    cw.v_new = (-xb * 2.0 ** -100)[:, None, :].contiguous()   # the same pairs at tiny magnitudes
+    note(f"[gpu] fp8 mantissa-pair sweep: {T} rows")
+    d = _gpu_write(cw)
+    _check_pool(cw, d, "mantissa-pairs")
 
 
 def test_strided_new_rows():
