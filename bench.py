@@ -273,6 +273,16 @@ def counter_lines(dirs, kernels):
         if cyc and "TA_ADDR_STALLED_BY_TC_CYCLES_sum" in cs:
             fig.append(f"TA address path stalled by the L1 {100 * cs['TA_ADDR_STALLED_BY_TC_CYCLES_sum'] / CUS / cyc:.0f} "
                        f"% of cycles (per CU)")
+        if simd_cyc and "SQ_VALU_MFMA_COEXEC_CYCLES" in cs:
+            fig.append(f"VALU issued while the MFMA unit is busy {100 * cs['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd_cyc:.1f} "
+                       f"% of SIMD-cycles")
+        if cyc and "SQ_LDS_IDX_ACTIVE" in cs:
+            fig.append(f"LDS active {100 * cs['SQ_LDS_IDX_ACTIVE'] / CUS / cyc:.0f} % of cycles (per CU), "
+                       f"bank-conflict cycles {100 * cs.get('SQ_LDS_BANK_CONFLICT', 0) / max(cs['SQ_LDS_IDX_ACTIVE'], 1):.0f} "
+                       f"% of LDS-active cycles")
+        if cs.get("SQ_INSTS_LDS") and "SQ_WAIT_INST_LDS" in cs:
+            fig.append(f"waves waiting on LDS results {cs['SQ_WAIT_INST_LDS'] / max(cs['SQ_INSTS_LDS'], 1):.1f} "
+                       f"wave-cycles (in units of 4) per LDS instruction")
         out.append(f"{label}: " + "; ".join(fig) + ".")
     return out
 

@@ -11,21 +11,33 @@
 // partitions.  The partition size is chosen from shapes and the CU count
 // (pa_host.cpp), never from device data.
 //
-// Partition kernel, one 64-lane wave per (sequence b, kv head g, partition p):
+// Partition kernel: a persistent grid of at most one workgroup per resident
+// slot.  The chunks (32-token pieces) of every (sequence, kv-head group)
+// segment are numbered sequence-major and split into even shares, one per
+// workgroup, so every workgroup streams the same number of chunks to within
+// one whatever the ragged context lengths; a share may start or end inside
+// a segment.  A workgroup is HG waves, wave v serving kv head gg*HG + v of
+// each segment it meets, so a CU reads adjacent head rows of the same
+// tokens.  A segment wholly inside one share writes its output rows; a
+// split one leaves an fp32 partial and a base-2 log-sum-exp per row.
 //  * All G*Qmax query rows that share kv head g form the N side of 16x16
 //    MFMA tiles (rows r = t*G + h_local; tiles of 16 rows), so every K/V
 //    byte is read from HBM once per kv head.
-//  * The wave walks its partition in 32-token steps (two 16-token blocks),
-//    prefetching the next step's K and V while computing the current one.
-//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: block mt of the step is the
-//    M side (token slot = lane % 16), head_dim the reduction.  Each lane then
-//    holds 8 scores of one query row: block (i / 4), slot 4*(lane/16) + i%4.
+//  * A wave walks its piece of a segment in 32-token steps (two 16-token
+//    sub-blocks) through a ring of register buffers: raw buffer loads of
+//    the next steps are in flight while the current one computes; loads
+//    past the sequence or below a sliding window go through an empty
+//    range, so the code between a load and its use is straight-line.
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: sub-block mt of the step is
+//    the M side (token slot = lane % 16), head_dim the reduction.  Each lane
+//    then holds 8 scores of one query row.
 //  * O^T += V^T P^T with the same MFMA: head_dim is the M side, the 32
 //    tokens the reduction, P (bf16) the N side.  The lane's 8 probabilities
 //    are already in B-operand order; V^T is formed in registers from 16-byte
-//    row loads by byte permutes (bf16) or fp8->f32 conversions (fp8).  The
-//    output tile puts a query row's accumulators in the same lanes as that
-//    row's softmax state, so rescaling needs no cross-lane traffic.
+//    row loads by lane permutes (bf16) or by the fp8->bf16 conversions,
+//    which place the bytes as the operand needs them.  The output tile puts
+//    a query row's accumulators in the same lanes as that row's softmax
+//    state, so rescaling needs no cross-lane traffic.
 //  * fp8 e4m3fn K/V are widened exactly to bf16 in registers; the
 //    per-(token, kv head) scales fold into the score column (k) and the
 //    probability (v) instead of multiplying every element.

@@ -14,14 +14,16 @@
 // 32 (prefill_shape).  Wave w owns positions p0 + wP .. p0 + wP + P - 1 of
 // the chunk for all G query heads of the kv head (row r = position r / G,
 // head r % G), the N side of 16x16 MFMA tiles as in the decode kernel.  The
-// workgroup walks the keys in 32-token tiles: all threads load the next
-// tile's K and V rows (16-byte buffer loads, sub-block addressing through a
-// per-wave block-table window) into one of two padded LDS buffers while the
-// waves compute on the other, so every K/V byte read from L2 serves every
-// row of the workgroup.  Per tile and wave: S^T = K Q^T and O^T += V^T P^T
-// with v_mfma_f32_16x16x32_bf16 (the V^T operand by transposing LDS reads),
-// online softmax in base 2 with a lazy rescale, row sums by the matrix
-// unit.  A wave skips the tiles past its last position; tiles that reach
+// workgroup walks the keys in 32-token tiles, T at a time: all threads load
+// the next T tiles' K and V rows (16-byte buffer loads, sub-block addressing
+// through a per-wave block-table window) into one group of padded LDS
+// buffers while the waves compute on the other, so every K/V byte read from
+// L2 serves every row of the workgroup.  Per tile and wave: S^T = K Q^T and
+// O^T += V^T P^T with v_mfma_f32_16x16x32_bf16 (the V^T operand by
+// transposing LDS reads), online softmax in base 2 with a lazy rescale, row
+// sums by the matrix unit.  head_dim 64 runs the same schedule on
+// v_mfma_f32_32x32x16_bf16 (prefill_kernel32: a wave's 32 rows are one
+// 32-wide N side).  A wave skips the tiles past its last position; tiles that reach
 // past its first position's causal limit take the masked step.  Keys past
 // L_b are zero-filled in LDS, so unwritten cache slots never reach the
 // output.  Workgroups are ordered longest first (work_order), which also
@@ -47,6 +49,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -119,6 +122,15 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
 constexpr int kRowPad = 32;
 template <int D> constexpr int kRowBytes = 2 * D + kRowPad;
 template <int D> constexpr int kTileBytes = kTile * kRowBytes<D>;
+// The V tile of the 32-row kernel: its transposing reads take four key rows
+// at two 16-column spans per half wave, so rows 16 dwords apart (mod the 64
+// banks) keep the half wave's 32 lanes on distinct banks
+template <int D, bool R32> constexpr int kRowBytesV = R32 ? 2 * D + 64 : kRowBytes<D>;
+template <int D, bool R32> constexpr int kTileBytesV = kTile * kRowBytesV<D, R32>;
+// The K tile of the 32-row kernel: 16 consecutive rows on distinct banks
+// (a 16-byte pad: rows 4 dwords apart mod 64)
+template <int D, bool R32> constexpr int kRowBytesK = R32 ? 2 * D + 16 : kRowBytes<D>;
+template <int D, bool R32> constexpr int kTileBytesK = kTile * kRowBytesK<D, R32>;
 // 16-byte pieces of one row, and per thread of a tile
 template <int D> constexpr int kPieces = D / 8;
 // (rounded up: with head_dim 64 and 8 waves half the threads load nothing)
@@ -128,7 +140,16 @@ template <int D, int W> constexpr int kPerThread = (kTile * kPieces<D> + 64 * W 
 template <int D> constexpr int kPieces8 = D / 8;
 template <int D, int W> constexpr int kPerThread8 = (kTile * kPieces8<D> + 64 * W - 1) / (64 * W);
 // one LDS buffer: K tile, V tile, and with fp8 the tile's 32 K scales
-template <int D, bool FP8> constexpr int kBufBytes = 2 * kTileBytes<D> + (FP8 ? 4 * kTile : 0);
+template <int D, bool FP8, bool R32 = false>
+constexpr int kBufBytes = kTileBytesK<D, R32> + kTileBytesV<D, R32> + (FP8 ? 4 * kTile : 0);
+// 32-key tiles staged per barrier (two LDS groups of this many buffers).
+// Two: between barriers the two waves of a SIMD drift apart, so one's
+// softmax overlaps the other's matrix work (measured on MI355X: 2k-row
+// chunks +4-6 %, 8k prompts +2 %, head_dim 256 +3 %; four tiles were no
+// better).  One for the head_dim-64 kernel (its windowed prefill measured
+// 2 % faster) and for 64-row waves (a second tile's staging registers
+// spill there).
+template <int D, int NT> constexpr int kTilesPerBarrier = D == 64 || NT == 4 ? 1 : 2;
 
 // The block-table window: lane l holds sub-block 2*t0 + l of sequence b.
 struct BlockRef {
@@ -214,7 +235,7 @@ __device__ __forceinline__ unsigned fp8x2_scaled_bf16x2(unsigned w, float s) {
 // K becomes bf16 exactly and its scales go to lds_ks (applied to the
 // scores, so K stays exact); V is scaled and rounded to bf16 (one rounding,
 // as a bf16 cache has).
-template <int D, int W, bool FP8>
+template <int D, int W, bool FP8, bool R32 = false>
 __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, float* lds_ks, const Pieces<D, W, FP8>& pc,
                                            int tile, int L, int vlo, int tid) {
 #pragma unroll
@@ -236,14 +257,15 @@ __device__ __forceinline__ void store_tile(char* lds_k, char* lds_v, float* lds_
             k = pc.k[i];
             v = pc.v[i];
         }
-        *reinterpret_cast<u32x4*>(lds_k + tok * kRowBytes<D> + 16 * col) = keep ? k : z;
-        *reinterpret_cast<u32x4*>(lds_v + tok * kRowBytes<D> + 16 * col) = keep ? v : z;
+        *reinterpret_cast<u32x4*>(lds_k + tok * kRowBytesK<D, R32> + 16 * col) = keep ? k : z;
+        *reinterpret_cast<u32x4*>(lds_v + tok * kRowBytesV<D, R32> + 16 * col) = keep ? v : z;
     }
 }
 
 template <int D, int NT>
 struct Acc {
     float m[NT];
+    float nm[NT <= 2 ? NT : 1];  // -m, or 0 while m is -inf (32-row waves)
     f32x4 l[NT];                 // row sums: every element holds the lane's row's sum
     float t[NT];                 // score above which m must rise: (m + kRescaleLog2) / c
     f32x4 o[NT][D / 16];
@@ -289,7 +311,8 @@ constexpr TilePrio kTilePrio = NT == 4 ? kPrioNone
 template <int D, int NT, bool FP8>
 __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D / 32], const char* lds_k,
                                           const char* lds_v, const float* lds_ks, const int (&lim)[NT],
-                                          const int (&low)[NT], int kbase, float c, int lane, bool masked) {
+                                          const int (&low)[NT], int kbase, float c, int lane, bool masked,
+                                          bf16x8 ones) {
     constexpr int J = D / 16;
     constexpr TilePrio P = kTilePrio<D, NT, FP8>;
     const int n16 = lane & 15, grp = lane >> 4;
@@ -362,9 +385,14 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
 #pragma unroll
             for (int j = 0; j < J; ++j) s.o[nt][j] *= alpha;
             s.m[nt] = m_new;
+            if constexpr (NT <= 2) s.nm[nt] = m_new == -__builtin_inff() ? 0.f : -m_new;
             s.t[nt] = (m_new + kRescaleLog2) / c;
         }
-        const float neg_m = s.m[nt] == -__builtin_inff() ? 0.f : -s.m[nt];
+        // 32-row waves keep -m as state (set at a rescale); 64-row waves
+        // recompute it (no registers to spare)
+        float neg_m;
+        if constexpr (NT <= 2) neg_m = s.nm[nt];
+        else neg_m = s.m[nt] == -__builtin_inff() ? 0.f : -s.m[nt];
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c, neg_m));
@@ -379,11 +407,120 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
         // row sums by the matrix unit: an all-ones A operand sums the 32 keys
         // of P for every row, already across the lanes holding the row, and
         // from the same bf16 P as the accumulators
-        s.l[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{kOnes, kOnes, kOnes, kOnes}), pb, s.l[nt],
-                                                         0, 0, 0);
+        if constexpr (NT <= 2)
+            s.l[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, s.l[nt], 0, 0, 0);
+        else
+            s.l[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{kOnes, kOnes, kOnes, kOnes}), pb,
+                                                             s.l[nt], 0, 0, 0);
         if constexpr (P == kPrioMatrix || P == kPrioValue) __builtin_amdgcn_s_setprio(0);
     }
     if constexpr (P == kPrioTile) __builtin_amdgcn_s_setprio(0);
+}
+
+// 32-row waves on the 32x32x16 matrix instruction, used for head_dim 64:
+// per 32-key tile 8 matrix instructions instead of 18 of the 16x16x32 shape,
+// one cross-lane step for a row's max instead of two, and row sums by the
+// vector unit; measured 26-28 % faster on windowed head_dim-64 prompts.  (At
+// head_dim 128 it measured 5 % slower than the 16-row kernel for bf16 caches
+// and level for fp8 ones, so those keep the 16-row kernel.)
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (lane l, n = l % 32, h = l / 32):
+// A lane l holds A[n][8h .. 8h+7], B lane l holds B[8h .. 8h+7][n], and
+// element i of the f32x16 result is D[8 (i / 4) + 4h + i % 4][n].
+//  * S^T = K Q^T: keys are M (the tile's 32), the wave's 32 query rows N, head_dim
+//    the reduction in steps of 16: element i of the scores is key
+//    8 (i / 4) + 4h + i % 4 of row n, so a lane holds 16 scores of one row and
+//    the row's other 16 sit in lane l ^ 32.
+//  * O^T += V^T P^T: head_dim blocks of 32 are M, the 32 keys the reduction in
+//    two steps of 16.  Step ks takes the lane's probabilities 8 ks .. 8 ks + 7
+//    as its B operand as they stand (keys 16 ks + 8 (j / 4) + 4h + j % 4), so
+//    the V^T operand of lane l holds those keys at head_dim 32 mb + n: two
+//    transposing LDS reads of four keys each.
+//  * Row sums: v_dot2 of the bf16 probabilities with ones, per lane (its 16
+//    keys), combined with lane l ^ 32 in the epilogue.
+template <int D>
+struct Acc32 {
+    float m, nm, t;          // running max (log2 units), -m (0 while m is -inf), rescale threshold
+    float l;                 // this lane's part of the row sum
+    f32x16 o[D / 32];        // element i: head_dim 32 mb + 8 (i / 4) + 4h + i % 4 of row n
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ void tile_step32(Acc32<D>& s, const u32x4 (&qf)[D / 16], const char* lds_k,
+                                            const char* lds_v, const float* lds_ks, int lim, int low, int kbase,
+                                            float c, int lane, bool masked) {
+    const int n = lane & 31, h = lane >> 5;
+    f32x16 sc = {};
+    const char* krow = lds_k + n * kRowBytesK<D, true> + 16 * h;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * kk)),
+                                                     as_bf16x8(qf[kk]), sc, 0, 0, 0);
+    // V^T operands: lane (g = lane / 16, s = lane % 16) reads key 4h + s / 4 (+ 16 ks,
+    // + 8), head_dim 32 mb + 16 (g % 2) + 4 (s % 4)
+    constexpr int RV = kRowBytesV<D, true>;
+    const char* vbase = lds_v + (4 * h + ((lane & 15) >> 2)) * RV + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    u32x4 vt[2][D / 32];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) {
+            const u32x2 lo = read_vt(vbase + 16 * ks * RV + 64 * mb);
+            const u32x2 hi = read_vt(vbase + (16 * ks + 8) * RV + 64 * mb);
+            vt[ks][mb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    float y[16];
+    if constexpr (FP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 kq = *reinterpret_cast<const f32x4*>(lds_ks + 8 * q + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[4 * q + e] = sc[4 * q + e] * kq[e];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = sc[i];
+    }
+    if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tok = kbase + 8 * (i >> 2) + 4 * h + (i & 3);
+            y[i] = (tok > lim || tok < low) ? -__builtin_inff() : y[i];
+        }
+    }
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) over |= y[i] > s.t;
+    if (__any(over)) {
+        float mx = y[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
+        mx = pair_max(mx, true);
+        const float m_new = fmaxf(s.m, c * mx);
+        const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(s.m - m_new);
+        s.l *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) s.o[mb] *= alpha;
+        s.m = m_new;
+        s.nm = m_new == -__builtin_inff() ? 0.f : -m_new;
+        s.t = (m_new + kRescaleLog2) / c;
+    }
+    // the packed probabilities as separate words (the row-sum dot products
+    // read them one by one; taken as elements of a vector, the compiler fed
+    // the first element to all four)
+    unsigned pk[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+        pk[w] = pack_bf16_rne(__builtin_amdgcn_exp2f(__builtin_fmaf(y[2 * w], c, s.nm)),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(y[2 * w + 1], c, s.nm)));
+    const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+            s.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vt[ks][mb]), as_bf16x8(pw[ks]), s.o[mb], 0, 0, 0);
+    const bf16x2 one2 = __builtin_bit_cast(bf16x2, kOnes);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) s.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[w]), one2, s.l, false);
 }
 
 // Longest work first.  Workgroup (b, qb, g) reads the keys below
@@ -548,42 +685,100 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         s.m[nt] = -__builtin_inff();
+        if constexpr (NT <= 2) s.nm[nt] = 0.f;
         s.t[nt] = -__builtin_inff();
         s.l[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < J; ++j) s.o[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float c = a.scale_log2;
+    // the all-ones operand of the row-sum MFMA, held in registers for the
+    // whole loop with 32-row waves (rebuilt per tile it costs three moves;
+    // 64-row waves have no registers to spare for it)
+    bf16x8 ones = as_bf16x8(u32x4{kOnes, kOnes, kOnes, kOnes});
+    if constexpr (NT <= 2) asm volatile("" : "+v"(ones));
 
-    // tile jstart into its buffer (tile j lives in buffer j & 1)
-    BlockRef br = load_window(a, b, jstart, lane);
-    int wbase = 2 * jstart;                                // first sub-block of the block-table window
-    Pieces<D, W, FP8> pc;
-    load_tile<D, W, FP8>(pc, a, kh, vh, sc, br, jstart, wbase, L, tid);
-    {
-        const int first = (jstart & 1) * BB;
-        store_tile<D, W, FP8>(lds + first, lds + first + TB, reinterpret_cast<float*>(lds + first + 2 * TB), pc,
-                              jstart, L, vlo, tid);
-    }
-    __syncthreads();
-    for (int j = jstart; j < ntiles; ++j) {
-        const bool more = j + 1 < ntiles;
-        if (more) {
-            // a block-table window holds 64 sub-blocks = 32 tiles
-            if (((j + 1 - jstart) & 31) == 0) {
-                br = load_window(a, b, j + 1, lane);
-                wbase = 2 * (j + 1);
-            }
-            load_tile<D, W, FP8>(pc, a, kh, vh, sc, br, j + 1, wbase, L, tid);
+    constexpr int T = kTilesPerBarrier<D, NT>;
+    if constexpr (T == 1) {
+        // tile jstart into its buffer (tile j lives in buffer j & 1)
+        BlockRef br = load_window(a, b, jstart, lane);
+        int wbase = 2 * jstart;                                // first sub-block of the block-table window
+        Pieces<D, W, FP8> pc;
+        load_tile<D, W, FP8>(pc, a, kh, vh, sc, br, jstart, wbase, L, tid);
+        {
+            const int first = (jstart & 1) * BB;
+            store_tile<D, W, FP8>(lds + first, lds + first + TB, reinterpret_cast<float*>(lds + first + 2 * TB), pc,
+                                  jstart, L, vlo, tid);
         }
-        const int cur = (j & 1) * BB, nxt = BB - cur;
-        if (j >= wstart && j < wtiles)
-            tile_step<D, NT, FP8>(s, qf, lds + cur, lds + cur + TB, reinterpret_cast<const float*>(lds + cur + 2 * TB),
-                                  lim, low, kTile * j, c, lane, j >= wclean || kTile * j < wlow);
-        if (more)
-            store_tile<D, W, FP8>(lds + nxt, lds + nxt + TB, reinterpret_cast<float*>(lds + nxt + 2 * TB), pc, j + 1,
-                                  L, vlo, tid);
         __syncthreads();
+        for (int j = jstart; j < ntiles; ++j) {
+            const bool more = j + 1 < ntiles;
+            if (more) {
+                // a block-table window holds 64 sub-blocks = 32 tiles
+                if (((j + 1 - jstart) & 31) == 0) {
+                    br = load_window(a, b, j + 1, lane);
+                    wbase = 2 * (j + 1);
+                }
+                load_tile<D, W, FP8>(pc, a, kh, vh, sc, br, j + 1, wbase, L, tid);
+            }
+            const int cur = (j & 1) * BB, nxt = BB - cur;
+            if (j >= wstart && j < wtiles)
+                tile_step<D, NT, FP8>(s, qf, lds + cur, lds + cur + TB, reinterpret_cast<const float*>(lds + cur + 2 * TB),
+                                      lim, low, kTile * j, c, lane, j >= wclean || kTile * j < wlow, ones);
+            if (more)
+                store_tile<D, W, FP8>(lds + nxt, lds + nxt + TB, reinterpret_cast<float*>(lds + nxt + 2 * TB), pc, j + 1,
+                                      L, vlo, tid);
+            __syncthreads();
+        }
+    } else {
+        // T tiles per barrier: the group of tiles jstart + T i ... lives in
+        // buffers T (i & 1) ... T (i & 1) + T - 1, and the global loads of the
+        // next group are in flight while this one is computed
+        BlockRef br = load_window(a, b, jstart, lane);
+        int wbase = 2 * jstart;                                // first sub-block of the block-table window
+        Pieces<D, W, FP8> pc[T];
+    #pragma unroll
+        for (int h = 0; h < T; ++h)
+            if (jstart + h < ntiles) load_tile<D, W, FP8>(pc[h], a, kh, vh, sc, br, jstart + h, wbase, L, tid);
+    #pragma unroll
+        for (int h = 0; h < T; ++h)
+            if (jstart + h < ntiles)
+                store_tile<D, W, FP8>(lds + h * BB, lds + h * BB + TB, reinterpret_cast<float*>(lds + h * BB + 2 * TB), pc[h],
+                                      jstart + h, L, vlo, tid);
+        __syncthreads();
+        for (int j = jstart, it = 0; j < ntiles; j += T, ++it) {
+            const bool more = j + T < ntiles;
+            if (more) {
+                // a block-table window holds 64 sub-blocks = 32 tiles (T divides 32,
+                // so a group never straddles two)
+                if (((j + T - jstart) & 31) == 0) {
+                    br = load_window(a, b, j + T, lane);
+                    wbase = 2 * (j + T);
+                }
+    #pragma unroll
+                for (int h = 0; h < T; ++h)
+                    if (j + T + h < ntiles) load_tile<D, W, FP8>(pc[h], a, kh, vh, sc, br, j + T + h, wbase, L, tid);
+            }
+            const int cur = (it & 1) * T * BB, nxt = T * BB - cur;
+    #pragma unroll
+            for (int h = 0; h < T; ++h) {
+                const int jj = j + h;
+                const int base = cur + h * BB;
+                if (jj >= wstart && jj < wtiles)
+                    tile_step<D, NT, FP8>(s, qf, lds + base, lds + base + TB,
+                                          reinterpret_cast<const float*>(lds + base + 2 * TB), lim, low, kTile * jj, c,
+                                          lane, jj >= wclean || kTile * jj < wlow, ones);
+            }
+            if (more) {
+    #pragma unroll
+                for (int h = 0; h < T; ++h)
+                    if (j + T + h < ntiles)
+                        store_tile<D, W, FP8>(lds + nxt + h * BB, lds + nxt + h * BB + TB,
+                                              reinterpret_cast<float*>(lds + nxt + h * BB + 2 * TB), pc[h], j + T + h, L, vlo,
+                                              tid);
+            }
+            __syncthreads();
+        }
     }
 
     // epilogue: lane holds d = 16 j + 4 grp + i of row 16 nt + n16
@@ -611,6 +806,172 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// NT: 16-row tiles per wave (rows = 16 NT = positions P x query heads G);
+// W: waves per workgroup.
+template <int D, int W, bool FP8>
+__global__ __launch_bounds__(64 * W) void prefill_kernel32(PrefillArgs a) {
+    constexpr int NT = 2;
+    constexpr int J = D / 16;
+    extern __shared__ __align__(16) char lds[];            // [2 buffers][K tile, V tile (, K scales)]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, grp = lane >> 4;
+    int b, qb, g;
+    if (a.B > 1 && a.B <= 64 && a.window <= 0) {
+        if (!work_order(a, (int)blockIdx.x, lane, W * a.P, b, qb, g)) return;
+    } else {
+        // one sequence (the same order), many, or a sliding window (every
+        // workgroup then has about the same work): the highest position
+        // blocks of every (sequence, kv head) first
+        const int pairs = a.B * a.Hkv;
+        qb = a.qblocks - 1 - (int)(blockIdx.x / pairs);
+        const int pr = blockIdx.x % pairs;
+        b = pr / a.Hkv;
+        g = pr - b * a.Hkv;
+    }
+    // the chunk's rows, clamped to the packed rows and to the sequence
+    const int c0 = min(max(a.cu[(int64_t)b * a.cu_s], 0), a.T);
+    const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
+    const int n = min(min(a.cu[(int64_t)(b + 1) * a.cu_s], a.T) - c0, L);
+    const int p0 = qb * W * a.P;                      // first position (in the chunk) of the workgroup
+    if (n <= 0 || p0 >= n) return;
+    const int pw = p0 + wave * a.P;                        // first position of this wave
+    // keys the workgroup needs: below L - n + min(p0 + W P, n); this wave's
+    // rows need keys below L - n + min(pw + P, n) (none if pw >= n).  With
+    // a sliding window w the row at position a sees keys a - w + 1 .. a, so
+    // the workgroup starts at its first row's window (jstart, keys below
+    // vlo are outside every row's window) and a wave at its own (wstart).
+    const int w = a.window;
+    const int kend = L - n + min(p0 + W * a.P, n);
+    const int wend = pw < n ? L - n + min(pw + a.P, n) : 0;
+    const int ntiles = (kend + kTile - 1) / kTile;
+    const int wtiles = (wend + kTile - 1) / kTile;
+    const int vlo = w > 0 ? max(0, L - n + p0 - w + 1) : 0;
+    const int jstart = vlo / kTile;
+    const int wstart = w > 0 && pw < n ? max(0, L - n + pw - w + 1) / kTile : 0;
+    // tiles wholly at or below every row's causal limit (the first row's
+    // limit is L - n + pw) and, with a window, wholly at or above every
+    // row's lower limit (the last row's is L - n + min(pw + P, n) - w) take
+    // the step without masks
+    const int wclean = pw < n ? (L - n + pw + 1) / kTile : 0;
+    const int wlow = w > 0 && pw < n ? L - n + min(pw + a.P, n) - w : 0;
+
+    // query fragments (B operand: row n, head_dim 16 kk + 8h ..) and the row's
+    // causal limit (and lower limit)
+    u32x4 qf[D / 16];
+    int lim, low;
+    {
+        const int row = lane & 31, hh = lane >> 5;
+        const int t = row / a.G, hl = row - t * a.G;
+        const int pos = pw + t;
+        const bool live = t < a.P && pos < n;
+        lim = live ? L - n + pos : L - 1;
+        low = w > 0 && live ? L - n + pos - w + 1 : INT_MIN;
+        const char* qrow = a.q + (int64_t)(c0 + (live ? pos : 0)) * a.q_st + (int64_t)(g * a.G + hl) * a.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 x = live ? *reinterpret_cast<const u32x4*>(qrow + 2 * (16 * kk + 8 * hh)) : u32x4{0u, 0u, 0u, 0u};
+            qf[kk] = a.q_neg ? x ^ 0x80008000u : x;
+        }
+    }
+
+    const char* kh = a.k + (int64_t)g * a.k_sh;
+    const char* vh = a.v + (int64_t)g * a.v_sh;
+    // buffer i at lds + i * BB: K tile, V tile at + TB, with fp8 the K scales
+    // at + 2 TB (plain arithmetic on the shared array keeps the accesses in
+    // LDS instructions)
+    constexpr int TB = kTileBytesK<D, true>, TBV = kTileBytesV<D, true>, BB = kBufBytes<D, FP8, true>;
+    ScaleBase sc = {nullptr, nullptr};
+    if constexpr (FP8) sc = ScaleBase{a.ks + (int64_t)g * a.ks_sh, a.vs + (int64_t)g * a.vs_sh};
+
+    Acc32<D> s;
+    s.m = -__builtin_inff();
+    s.nm = 0.f;
+    s.t = -__builtin_inff();
+    s.l = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) s.o[mb] = f32x16{};
+    const float c = a.scale_log2;
+
+    // T tiles per barrier: the group of tiles jstart + T i ... lives in
+    // buffers T (i & 1) ... T (i & 1) + T - 1, and the global loads of the
+    // next group are in flight while this one is computed
+    constexpr int T = kTilesPerBarrier<D, NT>;
+    BlockRef br = load_window(a, b, jstart, lane);
+    int wbase = 2 * jstart;                                // first sub-block of the block-table window
+    Pieces<D, W, FP8> pc[T];
+#pragma unroll
+    for (int h = 0; h < T; ++h)
+        if (jstart + h < ntiles) load_tile<D, W, FP8>(pc[h], a, kh, vh, sc, br, jstart + h, wbase, L, tid);
+#pragma unroll
+    for (int h = 0; h < T; ++h)
+        if (jstart + h < ntiles)
+            store_tile<D, W, FP8, true>(lds + h * BB, lds + h * BB + TB, reinterpret_cast<float*>(lds + h * BB + TB + TBV), pc[h],
+                                  jstart + h, L, vlo, tid);
+    __syncthreads();
+    for (int j = jstart, it = 0; j < ntiles; j += T, ++it) {
+        const bool more = j + T < ntiles;
+        if (more) {
+            // a block-table window holds 64 sub-blocks = 32 tiles (T divides 32,
+            // so a group never straddles two)
+            if (((j + T - jstart) & 31) == 0) {
+                br = load_window(a, b, j + T, lane);
+                wbase = 2 * (j + T);
+            }
+#pragma unroll
+            for (int h = 0; h < T; ++h)
+                if (j + T + h < ntiles) load_tile<D, W, FP8>(pc[h], a, kh, vh, sc, br, j + T + h, wbase, L, tid);
+        }
+        const int cur = (it & 1) * T * BB, nxt = T * BB - cur;
+#pragma unroll
+        for (int h = 0; h < T; ++h) {
+            const int jj = j + h;
+            const int base = cur + h * BB;
+            if (jj >= wstart && jj < wtiles)
+                tile_step32<D, FP8>(s, qf, lds + base, lds + base + TB,
+                                    reinterpret_cast<const float*>(lds + base + TB + TBV), lim, low, kTile * jj, c, lane,
+                                    jj >= wclean || kTile * jj < wlow);
+        }
+        if (more) {
+#pragma unroll
+            for (int h = 0; h < T; ++h)
+                if (j + T + h < ntiles)
+                    store_tile<D, W, FP8, true>(lds + nxt + h * BB, lds + nxt + h * BB + TB,
+                                          reinterpret_cast<float*>(lds + nxt + h * BB + TB + TBV), pc[h], j + T + h, L, vlo,
+                                          tid);
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds head_dim 32 mb + 8 q + 4h + e of row n (e < 4)
+    {
+        float a0, a1;
+        swap_pair(s.l, true, a0, a1);
+        float lt = a0 + a1;
+        const int row = lane & 31, hh = lane >> 5;
+        const int t = row / a.G, hl = row - t * a.G;
+        const int pos = pw + t;
+        if (t < a.P && pos < n) {
+            const int h = g * a.G + hl;
+            if (a.sinks) {
+                const float sk = a.sinks[(int64_t)h * a.sinks_s] * kLog2e;
+                if (sk > -__builtin_inff()) lt += __builtin_amdgcn_exp2f(sk - s.m);
+            }
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            char* orow = a.out + (int64_t)(c0 + pos) * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+            for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 wv = {pack_bf16_rne(s.o[mb][4 * q] * inv, s.o[mb][4 * q + 1] * inv),
+                                      pack_bf16_rne(s.o[mb][4 * q + 2] * inv, s.o[mb][4 * q + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + 2 * (32 * mb + 8 * q + 4 * hh)) = wv;
+                }
+        }
+    }
+}
+
+
 struct PrefillShape {
     int nt, waves;
 };
@@ -630,7 +991,8 @@ PrefillShape prefill_shape(int D, int G) {
 template <int D, bool FP8>
 const void* prefill_kernel_of_d(PrefillShape sh) {
     if (sh.nt == 4) return reinterpret_cast<const void*>(&prefill_kernel<D, 4, 4, FP8>);
-    return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8, FP8>);
+    if constexpr (D == 64) return reinterpret_cast<const void*>(&prefill_kernel32<64, 8, FP8>);
+    else return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8, FP8>);
 }
 
 template <bool FP8>
@@ -694,10 +1056,22 @@ int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const p
     const int64_t grid = (int64_t)a.qblocks * p.B * p.Hkv;
     if (grid >= (int64_t(1) << 31)) return fail(PA_ERR_UNSUPPORTED, "prefill: grid too large");
     const void* fn = prefill_kernel_of((int)p.D, p.fp8, sh);
-    const size_t buf = p.D == 256 ? (p.fp8 ? kBufBytes<256, true> : kBufBytes<256, false>)
-                       : p.D == 128 ? (p.fp8 ? kBufBytes<128, true> : kBufBytes<128, false>)
-                                    : (p.fp8 ? kBufBytes<64, true> : kBufBytes<64, false>);
-    const size_t lds = 2 * buf;
+    // LDS: two groups of T tile buffers (the 32-row kernel's buffers are laid
+    // out for its own reads)
+    const bool r32 = sh.nt == 2 && p.D == 64;
+    size_t buf, tpb;
+    if (p.D == 256) {
+        buf = p.fp8 ? kBufBytes<256, true> : kBufBytes<256, false>;
+        tpb = kTilesPerBarrier<256, 1>;
+    } else if (p.D == 128) {
+        buf = p.fp8 ? kBufBytes<128, true> : kBufBytes<128, false>;
+        tpb = sh.nt == 4 ? kTilesPerBarrier<128, 4> : kTilesPerBarrier<128, 2>;
+    } else {
+        buf = r32 ? (p.fp8 ? kBufBytes<64, true, true> : kBufBytes<64, false, true>)
+                  : (p.fp8 ? kBufBytes<64, true> : kBufBytes<64, false>);
+        tpb = kTilesPerBarrier<64, 2>;
+    }
+    const size_t lds = 2 * tpb * buf;
     void* args[] = {&a};
     if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * sh.waves), args, lds,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
