@@ -56,40 +56,53 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast
 // matched the correctly rounded quotient for every pair of bf16 mantissas
 // of x and of the row maximum, at every ratio of their magnitudes that
 // leaves the quotient between 2^-12 and 448).  Below 2^-12 a quotient's
-// code is a signed zero whatever its low bits, so it is replaced by zero
-// with the sign of x.  For rows with s below 2^-80 the reciprocal or the
-// residual could leave the normal range, and those rows divide instead.
-constexpr float kTinyQuot = 0x1p-12f;
+// code is a signed zero whatever its low bits, and RN(x / s) always has
+// the sign of x, so the codes take x's sign bit afterwards (the corrected
+// quotient of a tiny x can lose its sign when it rounds to zero).  For rows
+// with s below 2^-80 the reciprocal or the residual could leave the normal
+// range, and a wave holding such a row divides instead.
 constexpr float kSmallScale = 0x1p-80f;
 
-__device__ __forceinline__ float quot(float x, float s, float r, bool divide) {
-    if (divide) return __fdiv_rn(x, s);
+template <bool DIVIDE>
+__device__ __forceinline__ float quot(float x, float s, float r) {
+    if (DIVIDE && s < kSmallScale) return __fdiv_rn(x, s);
     const float q = x * r;
     const float e = __builtin_fmaf(-q, s, x);
-    const float qc = __builtin_fmaf(e, r, q);
-    return fabsf(qc) < kTinyQuot ? copysignf(0.f, x) : qc;
+    return __builtin_fmaf(e, r, q);
 }
 
 // x / s clamped to +-448 for the two bf16 values of one dword
-__device__ __forceinline__ float q_lo(unsigned w, float s, float r, bool divide) {
-    return fminf(fmaxf(quot(bf16_lo(w), s, r, divide), -kFp8Max), kFp8Max);
+template <bool DIVIDE>
+__device__ __forceinline__ float q_lo(unsigned w, float s, float r) {
+    return fminf(fmaxf(quot<DIVIDE>(bf16_lo(w), s, r), -kFp8Max), kFp8Max);
 }
-__device__ __forceinline__ float q_hi(unsigned w, float s, float r, bool divide) {
-    return fminf(fmaxf(quot(bf16_hi(w), s, r, divide), -kFp8Max), kFp8Max);
+template <bool DIVIDE>
+__device__ __forceinline__ float q_hi(unsigned w, float s, float r) {
+    return fminf(fmaxf(quot<DIVIDE>(bf16_hi(w), s, r), -kFp8Max), kFp8Max);
+}
+
+// The sign bits of the four bf16 values of dwords a (values 0, 1) and b
+// (values 2, 3) at the sign bits of four packed bytes.
+__device__ __forceinline__ unsigned signs4(unsigned a, unsigned b) {
+    return __builtin_amdgcn_perm(b, a, 0x07050301u) & 0x80808080u;
 }
 
 // 8 bf16 values -> 8 e4m3fn bytes of x / s (r = RN(1 / s)): each
 // conversion packs two codes into the low or the high half of a dword.
-__device__ __forceinline__ u32x2 encode8(const u32x4& x, float s, float r) {
-    const bool d = s < kSmallScale;
+template <bool DIVIDE>
+__device__ __forceinline__ u32x2 encode8_with(const u32x4& x, float s, float r) {
     u32x2 out;
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[0], s, r, d), q_hi(x[0], s, r, d), 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[1], s, r, d), q_hi(x[1], s, r, d), w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[2], s, r, d), q_hi(x[2], s, r, d), 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo(x[3], s, r, d), q_hi(x[3], s, r, d), w1, true);
-    out[0] = (unsigned)w0;
-    out[1] = (unsigned)w1;
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo<DIVIDE>(x[0], s, r), q_hi<DIVIDE>(x[0], s, r), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo<DIVIDE>(x[1], s, r), q_hi<DIVIDE>(x[1], s, r), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo<DIVIDE>(x[2], s, r), q_hi<DIVIDE>(x[2], s, r), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q_lo<DIVIDE>(x[3], s, r), q_hi<DIVIDE>(x[3], s, r), w1, true);
+    out[0] = (unsigned)w0 | signs4(x[0], x[1]);
+    out[1] = (unsigned)w1 | signs4(x[2], x[3]);
     return out;
+}
+__device__ __forceinline__ u32x2 encode8(const u32x4& x, float s, float r) {
+    if (__any(s < kSmallScale)) return encode8_with<true>(x, s, r);
+    return encode8_with<false>(x, s, r);
 }
 
 __device__ __forceinline__ float absmax8(const u32x4& x) {
