@@ -21,9 +21,9 @@
 // L2 serves every row of the workgroup.  Per tile and wave: S^T = K Q^T and
 // O^T += V^T P^T with v_mfma_f32_16x16x32_bf16 (the V^T operand by
 // transposing LDS reads), online softmax in base 2 with a lazy rescale, row
-// sums by the matrix unit.  head_dim 64 runs the same schedule on
-// v_mfma_f32_32x32x16_bf16 (prefill_kernel32: a wave's 32 rows are one
-// 32-wide N side).  A wave skips the tiles past its last position; tiles that reach
+// sums by the matrix unit.  Waves of 32 rows at head_dim 64 and 128 run the
+// same schedule on v_mfma_f32_32x32x16_bf16 (prefill_kernel32: a wave's 32
+// rows are one 32-wide N side).  A wave skips the tiles past its last position; tiles that reach
 // past its first position's causal limit take the masked step.  Keys past
 // L_b are zero-filled in LDS, so unwritten cache slots never reach the
 // output.  Workgroups are ordered longest first (work_order), which also
@@ -144,11 +144,11 @@ template <int D, bool FP8, bool R32 = false>
 constexpr int kBufBytes = kTileBytesK<D, R32> + kTileBytesV<D, R32> + (FP8 ? 4 * kTile : 0);
 // 32-key tiles staged per barrier (two LDS groups of this many buffers).
 // Two: between barriers the two waves of a SIMD drift apart, so one's
-// softmax overlaps the other's matrix work (measured on MI355X: 2k-row
-// chunks +4-6 %, 8k prompts +2 %, head_dim 256 +3 %; four tiles were no
-// better).  One for the head_dim-64 kernel (its windowed prefill measured
-// 2 % faster) and for 64-row waves (a second tile's staging registers
-// spill there).
+// softmax overlaps the other's matrix work (measured on MI355X with the
+// 16-row kernel: 2k-row chunks +4-6 %, 8k prompts +2 %, head_dim 256 +3 %;
+// four tiles were no better).  One at head_dim 64 (its windowed prefill
+// measured 2 % faster) and for 64-row waves (a second tile's staging
+// registers spill there).
 template <int D, int NT> constexpr int kTilesPerBarrier = D == 64 || NT == 4 ? 1 : 2;
 
 // The block-table window: lane l holds sub-block 2*t0 + l of sequence b.
@@ -417,12 +417,12 @@ __device__ __forceinline__ void tile_step(Acc<D, NT>& s, const u32x4 (&qf)[NT][D
     if constexpr (P == kPrioTile) __builtin_amdgcn_s_setprio(0);
 }
 
-// 32-row waves on the 32x32x16 matrix instruction, used for head_dim 64:
-// per 32-key tile 8 matrix instructions instead of 18 of the 16x16x32 shape,
-// one cross-lane step for a row's max instead of two, and row sums by the
-// vector unit; measured 26-28 % faster on windowed head_dim-64 prompts.  (At
-// head_dim 128 it measured 5 % slower than the 16-row kernel for bf16 caches
-// and level for fp8 ones, so those keep the 16-row kernel.)
+// 32-row waves on the 32x32x16 matrix instruction (head_dim 64 and 128): per
+// 32-key tile 8 or 16 matrix instructions instead of 18 or 34 of the
+// 16x16x32 shape, one cross-lane step for a row's max instead of two, row
+// sums by the vector unit; measured on MI355X 26-28 % faster on windowed
+// head_dim-64 prompts and 6.5-7 % with an fp8 cache at head_dim 128, level
+// (within 2 %) with a bf16 cache at head_dim 128.
 // Operand layouts of v_mfma_f32_32x32x16_bf16 (lane l, n = l % 32, h = l / 32):
 // A lane l holds A[n][8h .. 8h+7], B lane l holds B[8h .. 8h+7][n], and
 // element i of the f32x16 result is D[8 (i / 4) + 4h + i % 4][n].
@@ -991,8 +991,7 @@ PrefillShape prefill_shape(int D, int G) {
 template <int D, bool FP8>
 const void* prefill_kernel_of_d(PrefillShape sh) {
     if (sh.nt == 4) return reinterpret_cast<const void*>(&prefill_kernel<D, 4, 4, FP8>);
-    if constexpr (D == 64) return reinterpret_cast<const void*>(&prefill_kernel32<64, 8, FP8>);
-    else return reinterpret_cast<const void*>(&prefill_kernel<D, 2, 8, FP8>);
+    return reinterpret_cast<const void*>(&prefill_kernel32<D, 8, FP8>);
 }
 
 template <bool FP8>
@@ -1058,13 +1057,14 @@ int paged_attn_prefill_ext(const pa_tensor* q, const pa_tensor* k_cache, const p
     const void* fn = prefill_kernel_of((int)p.D, p.fp8, sh);
     // LDS: two groups of T tile buffers (the 32-row kernel's buffers are laid
     // out for its own reads)
-    const bool r32 = sh.nt == 2 && p.D == 64;
+    const bool r32 = sh.nt == 2 && p.D <= 128;
     size_t buf, tpb;
     if (p.D == 256) {
         buf = p.fp8 ? kBufBytes<256, true> : kBufBytes<256, false>;
         tpb = kTilesPerBarrier<256, 1>;
     } else if (p.D == 128) {
-        buf = p.fp8 ? kBufBytes<128, true> : kBufBytes<128, false>;
+        buf = r32 ? (p.fp8 ? kBufBytes<128, true, true> : kBufBytes<128, false, true>)
+                  : (p.fp8 ? kBufBytes<128, true> : kBufBytes<128, false>);
         tpb = sh.nt == 4 ? kTilesPerBarrier<128, 4> : kTilesPerBarrier<128, 2>;
     } else {
         buf = r32 ? (p.fp8 ? kBufBytes<64, true, true> : kBufBytes<64, false, true>)
