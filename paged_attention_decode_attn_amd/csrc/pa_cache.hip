@@ -43,6 +43,8 @@ struct WriteArgs {
     int64_t T, slots_total;
     int32_t Hkv, D;
     uint32_t bs;                                                              // tokens per block
+    int32_t bs_shift;                                                         // log2(bs), or -1
+    int32_t small;                                                            // every piece index < 2^31
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
@@ -120,10 +122,29 @@ struct Piece {
 
 template <int R8>
 __device__ __forceinline__ Piece piece_of(const WriteArgs& a, int64_t item) {
+    if (a.small) {
+        // 32-bit division (a few instructions instead of a 64-bit sequence)
+        const uint32_t per_token = (uint32_t)a.Hkv * R8;
+        const uint32_t t = (uint32_t)item / per_token;
+        const int rem = (int)((uint32_t)item - t * per_token);
+        return Piece{(int64_t)t, rem / R8, rem % R8};
+    }
     const int64_t per_token = (int64_t)a.Hkv * R8;
     const int64_t t = item / per_token;
     const int rem = (int)(item - t * per_token);
     return Piece{t, rem / R8, rem - (rem / R8) * R8};
+}
+
+// The stored scale RN(m / 448) of a row maximum m > 0, by the same
+// correction with the correctly rounded constant 1 / 448 (checked against
+// the correctly rounded quotient for every positive finite bf16 m with
+// exact arithmetic); 1 for an all-zero row.
+constexpr float kInv448 = 1.0f / kFp8Max;
+__device__ __forceinline__ float scale_of(float m) {
+    if (!(m > 0.f)) return 1.f;
+    const float q = m * kInv448;
+    const float e = __builtin_fmaf(-q, kFp8Max, m);
+    return __builtin_fmaf(e, kInv448, q);
 }
 
 // U pieces per thread, item = gid + k * (threads launched), k < U: every
@@ -157,7 +178,8 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
         const int h = pc.h, r = pc.r;
         // slots are below 2^31, so the block / position split is 32-bit
         const uint32_t us = (uint32_t)max<int64_t>(slot[u], 0);
-        const int64_t blk = us / a.bs, pos = us - (uint32_t)blk * a.bs;
+        const uint32_t ublk = a.bs_shift >= 0 ? us >> a.bs_shift : us / a.bs;
+        const int64_t blk = ublk, pos = us - ublk * a.bs;
         if constexpr (!FP8) {
             if (live[u]) {
                 *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k[u];
@@ -171,8 +193,8 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
                 mv = fmaxf(mv, __shfl_xor(mv, o));
             }
             // scale = absmax / 448 (stored); every element divided by it
-            const float sk = mk > 0.f ? __fdiv_rn(mk, kFp8Max) : 1.f;
-            const float sv = mv > 0.f ? __fdiv_rn(mv, kFp8Max) : 1.f;
+            const float sk = scale_of(mk);
+            const float sv = scale_of(mv);
             const float rk = __fdiv_rn(1.f, sk), rv = __fdiv_rn(1.f, sv);
             if (live[u]) {
                 *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) =
@@ -217,12 +239,15 @@ extern "C" int paged_attn_reshape_and_cache(const pa_tensor* k_new, const pa_ten
     a.vs = p.vs; a.vs_sblk = p.vs_sblk; a.vs_sh = p.vs_sh;
     a.T = p.T; a.slots_total = p.NB * p.BS;
     a.Hkv = (int32_t)p.Hkv; a.D = (int32_t)p.D; a.bs = (uint32_t)p.BS;
+    a.bs_shift = (p.BS & (p.BS - 1)) == 0 ? __builtin_ctzll((unsigned long long)p.BS) : -1;
     // pieces of 8 elements, one per thread unless the tuning override asks
     // for more (2 or 4 pieces per thread measured no faster on bulk writes)
     const int64_t pieces = p.T * p.Hkv * (p.D / 8);
     const int upt = g_write_pieces.load() > 0 ? g_write_pieces.load() : 1;
     const int64_t threads = (pieces + upt - 1) / upt;
     const int64_t groups = (threads + kWriteThreads - 1) / kWriteThreads;
+    // the largest piece index the grid forms is below groups * 256 * upt
+    a.small = groups * kWriteThreads * upt < (int64_t(1) << 31);
     const void* fn = upt == 4 ? (p.fp8 ? write_kernel_of<true, 4>((int)p.D) : write_kernel_of<false, 4>((int)p.D))
                    : upt == 2 ? (p.fp8 ? write_kernel_of<true, 2>((int)p.D) : write_kernel_of<false, 2>((int)p.D))
                               : (p.fp8 ? write_kernel_of<true, 1>((int)p.D) : write_kernel_of<false, 1>((int)p.D));
