@@ -15,11 +15,11 @@
 // even.
 //
 // A thread takes 8 consecutive elements (16 bytes of bf16) of one (token,
-// kv head) row of both K and V, so a wave reads and writes whole contiguous
-// token rows (a tuning override gives each thread several such pieces, one
-// grid apart, all loads issued before the stores).  The D/8 threads of a
-// row sit in one aligned lane group of the wave and reduce the row's maximum
-// with cross-lane exchanges.
+// kv head) row of both K and V for a bf16 cache, 16 for fp8, so a wave
+// reads and writes whole contiguous token rows (a tuning override gives each
+// thread several such pieces, one grid apart, all loads issued before the
+// stores).  The threads of a row sit in one aligned lane group of the wave
+// and reduce the row's maximum with cross-lane exchanges.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -114,25 +114,26 @@ __device__ __forceinline__ float absmax8(const u32x4& x) {
     return m;
 }
 
-// Thread piece `item` of the row grid: token t, kv head h, 8-element piece r.
+// Thread piece `item` of the row grid: token t, kv head h, piece r of the
+// row (8 elements for a bf16 cache, 16 for fp8).
 struct Piece {
     int64_t t;
     int h, r;
 };
 
-template <int R8>
+template <int RP>
 __device__ __forceinline__ Piece piece_of(const WriteArgs& a, int64_t item) {
     if (a.small) {
         // 32-bit division (a few instructions instead of a 64-bit sequence)
-        const uint32_t per_token = (uint32_t)a.Hkv * R8;
+        const uint32_t per_token = (uint32_t)a.Hkv * RP;
         const uint32_t t = (uint32_t)item / per_token;
         const int rem = (int)((uint32_t)item - t * per_token);
-        return Piece{(int64_t)t, rem / R8, rem % R8};
+        return Piece{(int64_t)t, rem / RP, rem % RP};
     }
-    const int64_t per_token = (int64_t)a.Hkv * R8;
+    const int64_t per_token = (int64_t)a.Hkv * RP;
     const int64_t t = item / per_token;
     const int rem = (int)(item - t * per_token);
-    return Piece{t, rem / R8, rem - (rem / R8) * R8};
+    return Piece{t, rem / RP, rem - (rem / RP) * RP};
 }
 
 // The stored scale RN(m / 448) of a row maximum m > 0, by the same
@@ -147,34 +148,43 @@ __device__ __forceinline__ float scale_of(float m) {
     return __builtin_fmaf(e, kInv448, q);
 }
 
-// U pieces per thread, item = gid + k * (threads launched), k < U: every
-// load of the thread goes out before its first store.
-template <bool FP8, int R8, int U>
+// A thread takes NV 16-byte vectors (8 bf16 each) of one row of K and of V:
+// one for a bf16 cache (a plain copy), two for fp8, so that the row's
+// scale work (the maximum's cross-lane reduction, the scale and its
+// reciprocal, the slot's addresses) is shared by 16 elements per lane and
+// every code store is 16 bytes.  RP = D / (8 NV) lanes hold a row, an
+// aligned lane group.  U pieces per thread, item = gid + k * (threads
+// launched), k < U: every load of the thread goes out before its first store.
+template <bool FP8, int RP, int U>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a) {
+    constexpr int NV = FP8 ? 2 : 1;
     const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
     const int64_t nthreads = (int64_t)gridDim.x * kWriteThreads;
-    u32x4 k[U], v[U];
+    u32x4 k[U][NV], v[U][NV];
     int64_t slot[U];
     bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         // every lane of a row group takes part in the reductions below, so
-        // the group is either wholly in range or wholly out (R8 divides 64,
+        // the group is either wholly in range or wholly out (RP divides 64,
         // and the stride between a thread's pieces is a multiple of 64)
-        const Piece pc = piece_of<R8>(a, gid + u * nthreads);
+        const Piece pc = piece_of<RP>(a, gid + u * nthreads);
         const bool live_token = pc.t < a.T;
         slot[u] = live_token ? (int64_t)a.slots[pc.t * a.slot_s] : -1;
         live[u] = slot[u] >= 0 && slot[u] < a.slots_total;
-        k[u] = u32x4{0u, 0u, 0u, 0u};
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (live[u]) {
-            k[u] = *reinterpret_cast<const u32x4*>(a.k_new + pc.t * a.n_st + pc.h * a.n_sh + 16 * pc.r);
-            v[u] = *reinterpret_cast<const u32x4*>(a.v_new + pc.t * a.vn_st + pc.h * a.vn_sh + 16 * pc.r);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            k[u][i] = u32x4{0u, 0u, 0u, 0u};
+            v[u][i] = u32x4{0u, 0u, 0u, 0u};
+            if (live[u]) {
+                k[u][i] = *reinterpret_cast<const u32x4*>(a.k_new + pc.t * a.n_st + pc.h * a.n_sh + 16 * (NV * pc.r + i));
+                v[u][i] = *reinterpret_cast<const u32x4*>(a.v_new + pc.t * a.vn_st + pc.h * a.vn_sh + 16 * (NV * pc.r + i));
+            }
         }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const Piece pc = piece_of<R8>(a, gid + u * nthreads);
+        const Piece pc = piece_of<RP>(a, gid + u * nthreads);
         const int h = pc.h, r = pc.r;
         // slots are below 2^31, so the block / position split is 32-bit
         const uint32_t us = (uint32_t)max<int64_t>(slot[u], 0);
@@ -182,13 +192,14 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
         const int64_t blk = ublk, pos = us - ublk * a.bs;
         if constexpr (!FP8) {
             if (live[u]) {
-                *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k[u];
-                *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) = v[u];
+                *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k[u][0];
+                *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) = v[u][0];
             }
         } else {
-            float mk = absmax8(k[u]), mv = absmax8(v[u]);
+            float mk = fmaxf(absmax8(k[u][0]), absmax8(k[u][1]));
+            float mv = fmaxf(absmax8(v[u][0]), absmax8(v[u][1]));
 #pragma unroll
-            for (int o = 1; o < R8; o <<= 1) {
+            for (int o = 1; o < RP; o <<= 1) {
                 mk = fmaxf(mk, __shfl_xor(mk, o));
                 mv = fmaxf(mv, __shfl_xor(mv, o));
             }
@@ -197,10 +208,12 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
             const float sv = scale_of(mv);
             const float rk = __fdiv_rn(1.f, sk), rv = __fdiv_rn(1.f, sv);
             if (live[u]) {
-                *reinterpret_cast<u32x2*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 8 * r) =
-                    encode8(k[u], sk, rk);
-                *reinterpret_cast<u32x2*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 8 * r) =
-                    encode8(v[u], sv, rv);
+                const u32x2 k0 = encode8(k[u][0], sk, rk), k1 = encode8(k[u][1], sk, rk);
+                const u32x2 v0 = encode8(v[u][0], sv, rv), v1 = encode8(v[u][1], sv, rv);
+                *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) =
+                    u32x4{k0[0], k0[1], k1[0], k1[1]};
+                *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) =
+                    u32x4{v0[0], v0[1], v1[0], v1[1]};
                 if (r == 0) {
                     a.ks[blk * a.ks_sblk + h * a.ks_sh + pos] = sk;
                     a.vs[blk * a.vs_sblk + h * a.vs_sh + pos] = sv;
@@ -212,9 +225,11 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
 
 template <bool FP8, int U>
 const void* write_kernel_of(int D) {
-    return D == 256 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 32, U>)
-         : D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 16, U>)
-                    : reinterpret_cast<const void*>(&cache_write_kernel<FP8, 8, U>);
+    // lanes per row: D / 8 for bf16 (8 elements each), D / 16 for fp8 (16)
+    constexpr int S = FP8 ? 16 : 8;
+    return D == 256 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 256 / S, U>)
+         : D == 128 ? reinterpret_cast<const void*>(&cache_write_kernel<FP8, 128 / S, U>)
+                    : reinterpret_cast<const void*>(&cache_write_kernel<FP8, 64 / S, U>);
 }
 
 }  // namespace
@@ -240,9 +255,10 @@ extern "C" int paged_attn_reshape_and_cache(const pa_tensor* k_new, const pa_ten
     a.T = p.T; a.slots_total = p.NB * p.BS;
     a.Hkv = (int32_t)p.Hkv; a.D = (int32_t)p.D; a.bs = (uint32_t)p.BS;
     a.bs_shift = (p.BS & (p.BS - 1)) == 0 ? __builtin_ctzll((unsigned long long)p.BS) : -1;
-    // pieces of 8 elements, one per thread unless the tuning override asks
-    // for more (2 or 4 pieces per thread measured no faster on bulk writes)
-    const int64_t pieces = p.T * p.Hkv * (p.D / 8);
+    // pieces of 8 (bf16) or 16 (fp8) elements, one per thread unless the
+    // tuning override asks for more (2 or 4 pieces per thread measured no
+    // faster on bulk writes)
+    const int64_t pieces = p.T * p.Hkv * (p.D / (p.fp8 ? 16 : 8));
     const int upt = g_write_pieces.load() > 0 ? g_write_pieces.load() : 1;
     const int64_t threads = (pieces + upt - 1) / upt;
     const int64_t groups = (threads + kWriteThreads - 1) / kWriteThreads;
