@@ -88,6 +88,20 @@ def test_bulk_write_with_padding_and_out_of_pool_slots(kv, hkv, d, pieces):
     _check_pool(cw, d_, f"bulk/{hkv}/{d}/{kv}/{pieces}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("bs", [32, 48, 80, 256])
+def test_bulk_write_block_sizes(kv, bs):
+    # a slot's block and position come from a shift for power-of-two block
+    # sizes and from a division otherwise
+    nb = -(-1500 // bs) + 2
+    spec = CONFIGS["llama3_8b"].replace(batch=2, hq=8, hkv=8, head_dim=64, kv_dtype=kv, block_size=bs, ctx_lo=16,
+                                        ctx_hi=2 * bs, pool_blocks=nb)
+    cw = generate_cache_write(spec, bulk_tokens=1000, pad=3)
+    note(f"[gpu] bulk cache write block_size={bs} {kv}")
+    d_ = _gpu_write(cw)
+    _check_pool(cw, d_, f"bulk/bs{bs}/{kv}")
+
+
 def test_fp8_quotients_for_every_pair_of_mantissas():
     # Every bf16 mantissa of the row's absolute maximum (the scale is
     # absmax / 448) against every bf16 mantissa of an element, at element
