@@ -204,16 +204,20 @@ struct BlockRef {
 // window and no sink, and none of their code is emitted.
 template <int D, bool FP8, bool GEN>
 __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, const HeadBase& hb, BlockRef br,
-                                          int step, int nsteps, int last_blk, int lo_blk,
+                                          int step, int nsteps, int hi_key, int lo_key,
                                           const unsigned (&koff)[Step<D, FP8>::KL], const unsigned (&voff)[4],
                                           unsigned soff) {
     typedef typename VLoad<D, FP8>::T VT;
-    // For step < nsteps, sub-block 2*step holds keys of the sequence and
-    // sub-block 2*step + 1 may lie past it; a sub-block past the sequence, a
-    // whole step past the window (a prefetch beyond its end) or, with a
-    // sliding window, a sub-block below lo_blk (wholly below every row's
-    // window) reads as zeros through an empty range, which costs no memory
-    // traffic.
+    constexpr int KL = Step<D, FP8>::KL;
+    // hi_key: the keys of the sequence, counted from the piece's first token;
+    // lo_key: with a sliding window, the first key that some row sees,
+    // counted the same way.  For step < nsteps, sub-block 2*step holds keys
+    // of the sequence and sub-block 2*step + 1 may lie past it; a sub-block
+    // past the sequence, a whole step past the window (a prefetch beyond its
+    // end) or a sub-block wholly below lo_key reads as zeros through an empty
+    // range, which costs no memory traffic.
+    const int last_blk = ((hi_key + 15) >> 4) - 1;
+    const int lo_blk = lo_key >> 4;
     const bool in = step < nsteps;
     const bool has0 = in && (!GEN || 2 * step >= lo_blk);
     const bool has1 = in && 2 * step + 1 <= last_blk && (!GEN || 2 * step + 1 >= lo_blk);
@@ -227,10 +231,39 @@ __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, c
     const Rsrc k1 = make_rsrc(hb.k + (uint64_t)u1 * a.k_sblk + s1 * a.k_ssub, has1 ? a.k_span : 0);
     const Rsrc v0 = make_rsrc(hb.v + (uint64_t)u0 * a.v_sblk + s0 * a.v_ssub, has0 ? a.v_span : 0);
     const Rsrc v1 = make_rsrc(hb.v + (uint64_t)u1 * a.v_sblk + s1 * a.v_ssub, has1 ? a.v_span : 0);
+    // In the step holding lo_key, the K and V rows of lanes whose token lies
+    // below it are skipped too (an offset past every range reads zeros
+    // without a memory access), so a window is read from its first token,
+    // not from the start of its first sub-block.  Lane tokens: K 16*mt + n16;
+    // V 16*(s/4) + 4*grp + s%4 (with quad-shared V, 16*mt + 4*grp + n16%4).
+    unsigned ko[2][KL], vo[8];
 #pragma unroll
-    for (int c = 0; c < Step<D, FP8>::KL; ++c) {
-        st.k[0][c] = bload<u32x4>(k0, koff[c]);
-        st.k[1][c] = bload<u32x4>(k1, koff[c]);
+    for (int c = 0; c < KL; ++c) ko[0][c] = ko[1][c] = koff[c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vo[i] = voff[kQuadV<D, FP8> ? 0 : (i & 3)];
+    if constexpr (GEN) {
+        const int lo = lo_key - kChunkTokens * step;
+        if (lo > 0) {
+            const int n16 = __lane_id() & 15, grp = __lane_id() >> 4;
+            constexpr unsigned kNoRead = 0x80000000u;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                if (16 * mt + n16 < lo) {
+#pragma unroll
+                    for (int c = 0; c < KL; ++c) ko[mt][c] = kNoRead;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int tok = kQuadV<D, FP8> ? 16 * (i & 1) + 4 * grp + (n16 & 3) : 16 * (i >> 2) + 4 * grp + (i & 3);
+                if (tok < lo) vo[i] = kNoRead;
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < KL; ++c) {
+        st.k[0][c] = bload<u32x4>(k0, ko[0][c]);
+        st.k[1][c] = bload<u32x4>(k1, ko[1][c]);
     }
     if constexpr (kQuadV<D, FP8>) {
         // lane (n16 = 4q + r, grp): bytes 16q..16q+15 of slot 4grp + r of
@@ -238,8 +271,8 @@ __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, c
         // block 0 or 1 or v scales of block 0 or 1, slots 4grp..4grp+3 (the
         // block ids are valid pool blocks, so the plain load stays in bounds;
         // scales of positions past L are zeroed before use)
-        st.vq[0] = bload<u32x4>(v0, voff[0]);
-        st.vq[1] = bload<u32x4>(v1, voff[0]);
+        st.vq[0] = bload<u32x4>(v0, vo[0]);
+        st.vq[1] = bload<u32x4>(v1, vo[1]);
         const int r = __lane_id() & 3;
         const char* base = (r & 2) ? hb.vs : hb.ks;
         const uint64_t sblk = (r & 2) ? a.vs_sblk : a.ks_sblk;
@@ -249,7 +282,7 @@ __device__ __forceinline__ void load_step(Step<D, FP8>& st, const PartArgs& a, c
         return;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) st.v[s] = bload<VT>(s < 4 ? v0 : v1, voff[s & 3]);
+    for (int s = 0; s < 8; ++s) st.v[s] = bload<VT>(s < 4 ? v0 : v1, vo[s]);
     if constexpr (FP8) {
         // one block's 16 slot scales of this kv head are contiguous (64 bytes)
         const Rsrc ks0 = make_rsrc(hb.ks + (uint64_t)u0 * a.ks_sblk + 64u * s0, has0 ? 64 : 0);
@@ -351,31 +384,29 @@ __device__ __forceinline__ void vt_fp8(const typename VLoad<D, true>::T (&v)[8],
     }
 }
 
-// K fragments (A operand of S^T) of block mt as bf16.
-template <int D, bool FP8>
-__device__ __forceinline__ void build_kf(const Step<D, FP8>& st, bf16x8 (&kf)[2][D / 32]) {
+// fp8 K fragments (A operand of S^T) of block mt, widened to bf16 once for
+// every row tile.  (A bf16 load is its own fragment and goes to the matrix
+// unit as loaded: copying it into a fragment array first made the compiler
+// keep part of the register ring in scratch memory for one variant.)
+template <int D>
+__device__ __forceinline__ void build_kf(const Step<D, true>& st, bf16x8 (&kf)[2][D / 32]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        if constexpr (!FP8) {
+        // load c holds bytes e = 0..15 of d = (D/4)*grp + 16c + e; MFMA
+        // step kk = 2c + h takes bytes 8h .. 8h+7, i.e. the adjacent-d
+        // pairs of two words
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) kf[mt][kk] = as_bf16x8(st.k[mt][kk]);
-        } else {
-            // load c holds bytes e = 0..15 of d = (D/4)*grp + 16c + e;
-            // MFMA step kk = 2c + h takes bytes 8h .. 8h+7, i.e. the
-            // adjacent-d pairs of two words
+        for (int c = 0; c < D / 64; ++c) {
 #pragma unroll
-            for (int c = 0; c < D / 64; ++c) {
+            for (int h = 0; h < 2; ++h) {
+                u32x4 x;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x4 x;
-#pragma unroll
-                    for (int p2 = 0; p2 < 2; ++p2) {
-                        const unsigned word = st.k[mt][c][2 * h + p2];
-                        x[2 * p2] = fp8x2_to_bf16x2<false>(word);
-                        x[2 * p2 + 1] = fp8x2_to_bf16x2<true>(word);
-                    }
-                    kf[mt][2 * c + h] = as_bf16x8(x);
+                for (int p2 = 0; p2 < 2; ++p2) {
+                    const unsigned word = st.k[mt][c][2 * h + p2];
+                    x[2 * p2] = fp8x2_to_bf16x2<false>(word);
+                    x[2 * p2 + 1] = fp8x2_to_bf16x2<true>(word);
                 }
+                kf[mt][2 * c + h] = as_bf16x8(x);
             }
         }
     }
@@ -417,7 +448,7 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
     }
 
     bf16x8 kf[2][D / 32];
-    build_kf<D, FP8>(st, kf);
+    if constexpr (FP8) build_kf<D>(st, kf);
     u32x4 vtf[FP8 ? J : 1];
     if constexpr (FP8) vt_fp8<D>(st.v, vtf);
     const float c = a.scale_log2;
@@ -428,8 +459,16 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             const bf16x8 qb = as_bf16x8(qf[nt][kk]);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qb, s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qb, s1, 0, 0, 0);
+            bf16x8 k0, k1;
+            if constexpr (FP8) {
+                k0 = kf[0][kk];
+                k1 = kf[1][kk];
+            } else {
+                k0 = as_bf16x8(st.k[0][kk]);
+                k1 = as_bf16x8(st.k[1][kk]);
+            }
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb, s1, 0, 0, 0);
         }
         float y[8];
 #pragma unroll
@@ -615,10 +654,9 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         // sees; with a sliding window every step takes the masked variant
         // (a window's range is short, and its first steps are masked anyway)
         const int nclean = GEN && a.window > 0 ? 0 : min(nsteps, max(0, L - nq + 1 - tok0) / kChunkTokens);
-        // last 16-token sub-block of the sequence, relative to the window;
-        // with a sliding window, the first one holding a key some row sees
-        const int last_blk = (L + 15) / 16 - 1 - 2 * pc;
-        const int lo_blk = GEN && a.window > 0 ? (vlo >> 4) - 2 * pc : 0;
+        // with a sliding window, the first key some row sees, counted from
+        // the piece's first token
+        const int lo_key = GEN && a.window > 0 ? vlo - tok0 : 0;
         // A ring of R register buffers: while a step computes, the loads of
         // the next R-1 steps are in flight.  Loads are issued on every path
         // (past the window they read nothing), so the code between a load
@@ -626,7 +664,7 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         // the last steps of the piece take the masked variant.
         Step<D, FP8> buf[R];
 #pragma unroll
-        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8, GEN>(buf[i], a, hb, br, i, nsteps, last_blk, lo_blk, koff, voff, soff);
+        for (int i = 0; i + 1 < R; ++i) load_step<D, FP8, GEN>(buf[i], a, hb, br, i, nsteps, L - tok0, lo_key, koff, voff, soff);
         // Every kLockstep steps the workgroup's waves meet at a barrier.  Two
         // waves share each SIMD, and the older one otherwise wins the issue
         // and memory arbitration until it is done, leaving the younger to
@@ -637,7 +675,7 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         for (; st + R <= nclean; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, lo_blk, koff, voff,
+                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, L - tok0, lo_key, koff, voff,
                                        soff);
                 if (((st + i) & (kLockstep - 1)) == 0) __syncthreads();
                 compute_step<D, FP8, NT, false, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
@@ -646,7 +684,7 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         for (; st < nsteps; st += R) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, last_blk, lo_blk, koff, voff,
+                load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, L - tok0, lo_key, koff, voff,
                                        soff);
                 if (st + i < nsteps)
                     compute_step<D, FP8, NT, true, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);

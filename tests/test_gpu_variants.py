@@ -85,30 +85,46 @@ def test_sink_extremes():
         check(w, groups, label=f"sink-extremes/g{groups}")
 
 
-def test_window_never_reads_what_lies_below_it():
+@pytest.mark.parametrize("bs", [16, 48])
+@pytest.mark.parametrize("kv,d", [("bf16", 128), ("bf16", 64), ("fp8_e4m3fn", 64), ("fp8_e4m3fn", 128)])
+def test_window_never_reads_what_lies_below_it(bs, kv, d):
     # Blocks wholly below the earliest row's window are freed in a windowed
     # cache: their table entries hold garbage ids and the blocks NaN.  The
-    # output must equal the oracle's on the intact cache.
-    bs, window = 16, 40
-    spec = _ragged(bs, qlen=2, window=window, sinks=True, batch=5, ctx_hi=600, seed=33)
-    w = generate(spec, context_lens=[2, 45, 100, 333, 600])
+    # token rows below the window in the block holding its first key hold
+    # NaN as well (and, for fp8, NaN codes and scales).  The output must
+    # equal the oracle's on the intact cache.
+    window = 40
+    spec = _ragged(bs, kv=kv, d=d, qlen=2, window=window, sinks=True, batch=5, ctx_hi=600, seed=33)
+    lens = [2, 45, 100, 333, 600]
+    w = generate(spec, context_lens=lens)
     ref = oracle_out(w)
-    bad = generate(spec, context_lens=[2, 45, 100, 333, 600])
+    bad = generate(spec, context_lens=lens)
     t = bad.block_tables.clone()
-    nan = torch.tensor(0x7FC0, dtype=torch.int16)
+    fp8 = kv != "bf16"
+
+    def poison(blk, rows=slice(None)):
+        for c in (bad.k_cache, bad.v_cache):
+            if fp8:
+                c[blk, rows].view(torch.uint8).fill_(0x7F)
+            else:
+                c[blk, rows].view(torch.int16).fill_(0x7FC0)
+        if fp8:
+            bad.k_scale[blk, rows] = float("nan")
+            bad.v_scale[blk, rows] = float("nan")
+
     for b in range(spec.batch):
         L, n = int(bad.context_lens[b]), int(bad.query_lens[b])
         lo = max(0, L - n - window + 1)
         for i in range(lo // bs):
-            blk = int(t[b, i])
-            bad.k_cache[blk].view(torch.int16).fill_(nan)
-            bad.v_cache[blk].view(torch.int16).fill_(nan)
+            poison(int(t[b, i]))
             t[b, i] = -7 if i % 2 else 1 << 30
+        if lo % bs:
+            poison(int(t[b, lo // bs]), slice(0, lo % bs))
     bad.block_tables = t
     for groups in (0, 1, 100000):
-        note(f"[gpu] freed-below-window/g{groups}")
+        note(f"[gpu] freed-below-window/{kv}/d{d}/bs{bs}/g{groups}")
         out = run_gpu(bad, groups)
-        compare(out, ref, w.query_lens, label=f"freed-below-window/g{groups}")
+        compare(out, ref, w.query_lens, label=f"freed-below-window/{kv}/d{d}/bs{bs}/g{groups}")
 
 
 @pytest.mark.parametrize("hq,hkv,qlen", [(8, 8, 1), (32, 32, 2), (64, 1, 1), (16, 1, 4)])
