@@ -148,6 +148,16 @@ __device__ __forceinline__ float scale_of(float m) {
     return __builtin_fmaf(e, kInv448, q);
 }
 
+// A 16-byte piece of a new row.  The bf16 write is a plain copy and streams
+// its rows with non-temporal loads and stores (1.3 % faster on 65536-token
+// writes); the fp8 write, which does arithmetic between them, was 3-7 %
+// slower that way and keeps plain ones.
+template <bool FP8>
+__device__ __forceinline__ u32x4 load_row(const char* p) {
+    if constexpr (FP8) return *reinterpret_cast<const u32x4*>(p);
+    else return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // A thread takes NV 16-byte vectors (8 bf16 each) of one row of K and of V:
 // one for a bf16 cache (a plain copy), two for fp8, so that the row's
 // scale work (the maximum's cross-lane reduction, the scale and its
@@ -177,8 +187,8 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
             k[u][i] = u32x4{0u, 0u, 0u, 0u};
             v[u][i] = u32x4{0u, 0u, 0u, 0u};
             if (live[u]) {
-                k[u][i] = *reinterpret_cast<const u32x4*>(a.k_new + pc.t * a.n_st + pc.h * a.n_sh + 16 * (NV * pc.r + i));
-                v[u][i] = *reinterpret_cast<const u32x4*>(a.v_new + pc.t * a.vn_st + pc.h * a.vn_sh + 16 * (NV * pc.r + i));
+                k[u][i] = load_row<FP8>(a.k_new + pc.t * a.n_st + pc.h * a.n_sh + 16 * (NV * pc.r + i));
+                v[u][i] = load_row<FP8>(a.v_new + pc.t * a.vn_st + pc.h * a.vn_sh + 16 * (NV * pc.r + i));
             }
         }
     }
@@ -192,8 +202,10 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(WriteArgs a)
         const int64_t blk = ublk, pos = us - ublk * a.bs;
         if constexpr (!FP8) {
             if (live[u]) {
-                *reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok + h * a.k_sh + 16 * r) = k[u][0];
-                *reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok + h * a.v_sh + 16 * r) = v[u][0];
+                __builtin_nontemporal_store(k[u][0], reinterpret_cast<u32x4*>(a.kc + blk * a.k_sblk + pos * a.k_stok +
+                                                                              h * a.k_sh + 16 * r));
+                __builtin_nontemporal_store(v[u][0], reinterpret_cast<u32x4*>(a.vc + blk * a.v_sblk + pos * a.v_stok +
+                                                                              h * a.v_sh + 16 * r));
             }
         } else {
             float mk = fmaxf(absmax8(k[u][0]), absmax8(k[u][1]));
