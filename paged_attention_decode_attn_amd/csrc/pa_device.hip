@@ -770,9 +770,10 @@ __device__ __forceinline__ int share_owner(int64_t c, int64_t C, int n) {
 // adjacent head rows of the same tokens (whole contiguous token rows of the
 // cache).  Every workgroup gets the same number of chunks to within one,
 // whatever the ragged context lengths: a share may start and end inside a
-// sequence and may hold several whole sequences.  Wave 0 scans the
-// per-sequence chunk counts into LDS (workgroup 0 also stores the scan for
-// the merge kernel); every wave finds a chunk's sequence with a 64-wide
+// sequence and may hold several whole sequences.  The per-sequence chunk
+// counts are scanned (workgroup 0 also stores the scan for the merge
+// kernel): for up to 64 sequences by every wave in its own lanes, else by
+// wave 0 into LDS; every wave finds a chunk's sequence with a 64-wide
 // ballot over that prefix (a share's chunks only increase).
 template <int D, bool FP8, int NT, bool GEN>
 __global__ __launch_bounds__(NT == 1 && D <= 128 ? 512 : 256)
@@ -790,6 +791,42 @@ void partition_kernel(PartArgs a) {
         const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
         const int cb = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens - first_chunk<GEN>(a, L, nq) : 0;
         if (cb > 0) process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, 0, cb, cb, blockIdx.x, 0, lane);
+        return;
+    }
+    const int ngrp = a.Hkv / a.HG;
+    if (a.B <= 64) {
+        // up to 64 sequences: every wave scans the chunk counts itself (lane
+        // b: sequence b) and keeps the prefix in a register, so no wave
+        // waits for an LDS round and a barrier before its first loads
+        int nc = 0;
+        if (lane < a.B) {
+            const int L = min(a.ctx[(int64_t)lane * a.ctx_s], 16 * a.wsub);
+            const int nq = min(a.ql ? a.ql[(int64_t)lane * a.ql_s] : a.Qmax, a.Qmax);
+            nc = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens - first_chunk<GEN>(a, L, nq) : 0;
+        }
+        int x = nc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (blockIdx.x == 0 && wave == 0 && a.ws_pre && lane < a.B) a.ws_pre[lane] = x;
+        const int64_t C = (int64_t)__builtin_amdgcn_readlane(x, a.B - 1) * ngrp;
+        const int n = share_count((int)gridDim.x, C, a.min_share);
+        const int w = blockIdx.x;
+        if (w >= n) return;
+        const int64_t lo = share_begin(w, C, n), hi = share_begin(w + 1, C, n);
+        for (int64_t pos = lo; pos < hi;) {
+            const int b = __popcll(__ballot(lane < a.B && (int64_t)x * ngrp <= pos));
+            const int pre = b > 0 ? __builtin_amdgcn_readlane(x, b - 1) : 0;
+            const int cb = __builtin_amdgcn_readlane(x, b) - pre;
+            const int within = (int)(pos - (int64_t)pre * ngrp);
+            const int gg = within / cb;
+            const int c0 = within - gg * cb;
+            const int c1 = (int)min<int64_t>(cb, c0 + (hi - pos));
+            process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, c0, c1, cb, w, pos == lo ? 0 : 1, lane);
+            pos += c1 - c0;
+        }
         return;
     }
     if (wave == 0) {
@@ -816,7 +853,6 @@ void partition_kernel(PartArgs a) {
         }
     }
     __syncthreads();
-    const int ngrp = a.Hkv / a.HG;
     const int64_t C = (int64_t)(a.B > 0 ? s_pre[a.B - 1] : 0) * ngrp;
     const int n = share_count((int)gridDim.x, C, a.min_share);
     const int w = blockIdx.x;

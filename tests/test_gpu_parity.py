@@ -107,6 +107,22 @@ def test_two_query_rows_short_and_ragged(groups):
     check(w, groups, label=f"qlen2-ragged/g{groups}")
 
 
+@pytest.mark.parametrize("batch", [1, 63, 64, 65, 130])
+@pytest.mark.parametrize("groups", [0, 7, 100000])
+def test_batches_across_the_one_wave_scan(batch, groups):
+    # up to 64 sequences every wave scans the chunk counts in its own lanes;
+    # more go through the workgroup's LDS scan.  Ragged lengths with empty
+    # sequences and query rows, contexts long enough for the split schedule.
+    rng = np.random.default_rng(900 + batch)
+    ctx = rng.integers(1, 1300, size=batch)
+    ctx[rng.random(batch) < 0.1] = 0
+    ql = np.minimum(rng.integers(0, 3, size=batch), ctx)
+    spec = CONFIGS["mtp_verify"].replace(batch=batch, ctx_lo=1, ctx_hi=1300, hq=16, hkv=2, head_dim=64,
+                                         pool_blocks=batch * 82 + 4)
+    w = generate(spec, context_lens=ctx.tolist(), query_lens=ql.tolist())
+    check(w, groups, label=f"batch{batch}/g{groups}")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq,hkv,qlen", [(8, 8, 1), (8, 1, 1), (32, 8, 1), (64, 4, 1),
