@@ -3,7 +3,8 @@ oracle at the usual tolerance (|gpu - ref| <= 1e-2 + 1e-2 |ref| on every
 produced element, relative L2 <= 1e-2): batch, q/kv heads, head_dim, KV
 dtype, block size, query lengths (ragged), context and chunk lengths, a
 sliding window and sinks are all drawn, so combinations no hand-written
-case names still meet the oracle."""
+case names still meet the oracle; a second decode set draws batches of
+60-200 sequences and forced grids."""
 import numpy as np
 import pytest
 
@@ -14,6 +15,7 @@ from test_gpu_prefill import _check as check_prefill
 pytestmark = pytest.mark.gpu
 
 DECODE_CASES = 24
+WIDE_DECODE_CASES = 24
 PREFILL_CASES = 24
 
 
@@ -35,6 +37,29 @@ def decode_spec(i):
         hq=hkv * g, hkv=hkv, head_dim=d, kv_dtype=str(rng.choice(["bf16", "fp8_e4m3fn"])),
         ctx_lo=ctx_lo, ctx_hi=ctx_hi, block_size=bs, pool_blocks=batch * (-(-ctx_hi // bs)) + 4,
         seed=6000 + i, sliding_window=window, sinks=bool(rng.integers(0, 2)))
+
+
+def wide_decode_spec(i):
+    # batches on both sides of 64 sequences (the partition kernel scans the
+    # chunk counts in the wave's lanes up to 64, in LDS beyond) and forced grids
+    rng = np.random.default_rng(9000 + i)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    qlen = int(rng.integers(1, 5))
+    max_rows = 16 if d == 256 else 64
+    g = int(rng.choice([x for x in (1, 2, 4, 8, 16) if x * qlen <= max_rows]))
+    bs = int(rng.choice([16, 16, 32, 64, 256]))
+    batch = int(rng.choice([int(rng.integers(60, 70)), int(rng.integers(100, 200))]))
+    ctx_hi = int(rng.integers(qlen, 400))
+    ctx_lo = int(rng.integers(qlen, ctx_hi + 1))
+    window = int(rng.choice([0, 0, int(rng.integers(1, 300))]))
+    spec = CONFIGS["mtp_verify"].replace(
+        name=f"random_wide_decode_{i}", batch=batch, qlen=qlen, qlen_lo=int(rng.integers(1, qlen + 1)),
+        hq=hkv * g, hkv=hkv, head_dim=d, kv_dtype=str(rng.choice(["bf16", "fp8_e4m3fn"])),
+        ctx_lo=ctx_lo, ctx_hi=ctx_hi, block_size=bs, pool_blocks=batch * (-(-ctx_hi // bs)) + 4,
+        seed=10000 + i, sliding_window=window, sinks=bool(rng.integers(0, 2)))
+    grid = int(rng.choice([0, 0, int(rng.integers(1, 64)), int(rng.integers(64, 3000))]))
+    return spec, grid
 
 
 def prefill_spec(i):
@@ -64,6 +89,13 @@ def test_random_decode(i):
     spec = decode_spec(i)
     check(generate(spec), label=f"{spec.name}: {spec.hq}/{spec.hkv} d{spec.head_dim} {spec.kv_dtype} "
                                 f"qlen {spec.qlen_lo}..{spec.qlen}")
+
+
+@pytest.mark.parametrize("i", range(WIDE_DECODE_CASES))
+def test_random_wide_decode(i):
+    spec, grid = wide_decode_spec(i)
+    check(generate(spec), grid, label=f"{spec.name}: B{spec.batch} {spec.hq}/{spec.hkv} d{spec.head_dim} "
+                                      f"{spec.kv_dtype} qlen {spec.qlen_lo}..{spec.qlen} grid {grid or 'auto'}")
 
 
 @pytest.mark.parametrize("i", range(PREFILL_CASES))
