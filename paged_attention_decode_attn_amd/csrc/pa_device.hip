@@ -982,6 +982,22 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
             m = mn;
         }
     }
+    // The partial lanes of one (row, column) are `stride` threads apart:
+    // those in one wave combine by lane exchanges first, so the LDS round
+    // below takes one entry per wave instead of one per lane.
+    const int stride = CB * RG;
+    for (int o = stride; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(m, o), w2 = __shfl_xor(wsum, o);
+        f32x4 a2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a2[k] = __shfl_xor(acc[k], o);
+        const float mn = fmaxf(m, m2);
+        const float mu = mn == ninf ? 0.f : mn;
+        const float s1 = __builtin_amdgcn_exp2f(m - mu), s2 = __builtin_amdgcn_exp2f(m2 - mu);
+        wsum = wsum * s1 + w2 * s2;
+        acc = acc * s1 + a2 * s2;
+        m = mn;
+    }
     __shared__ float sm[kRedThreads], sw[kRedThreads];
     __shared__ f32x4 sacc[kRedThreads];
     sm[tid] = m;
@@ -989,16 +1005,16 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(RedArgs a) {
     sacc[tid] = acc;
     __syncthreads();
     if (active && pl == 0) {
-        const int stride = CB * RG;
+        const int qstep = stride < 64 ? 64 / stride : 1;   // partial lanes per wave
         const int h = g * a.G + hl;
         // a sink is one more partial: log-sum-exp = the sink, output 0
         const float sk = sink_log2(a.sinks, a.sinks_s, h);
         float M = fmaxf(m, sk);
-        for (int q = 1; q < PL; ++q) M = fmaxf(M, sm[tid + q * stride]);
+        for (int q = qstep; q < PL; q += qstep) M = fmaxf(M, sm[tid + q * stride]);
         const float Mu = M == ninf ? 0.f : M;
         f32x4 tot = {0.f, 0.f, 0.f, 0.f};
         float wt = sk > ninf ? __builtin_amdgcn_exp2f(sk - Mu) : 0.f;
-        for (int q = 0; q < PL; ++q) {
+        for (int q = 0; q < PL; q += qstep) {
             const float sc = __builtin_amdgcn_exp2f(sm[tid + q * stride] - Mu);
             tot += sc * sacc[tid + q * stride];
             wt += sc * sw[tid + q * stride];
