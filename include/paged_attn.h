@@ -48,7 +48,8 @@ extern "C" {
 #define PA_BLOCK_SIZE 16      /* default tokens per KV-cache block; a block
                                  holds any multiple of 16 up to 4096 tokens  */
 #define PA_MAX_ROWS   64      /* max (q_heads / kv_heads) * query_len       */
-#define PA_MAX_ROWS_D256 16   /* the same limit for head_dim 256            */
+#define PA_MAX_ROWS_D256 16   /* prefill at head_dim 256: max q_heads /
+                                 kv_heads (decode serves PA_MAX_ROWS)       */
 
 typedef enum pa_dtype {
     PA_DTYPE_BF16        = 1,  /* bfloat16                                  */
@@ -118,7 +119,7 @@ typedef struct pa_tensor {
  *   stream        hipStream_t as void*, NULL = default stream.
  *
  * Query head h reads KV head h / (Hq / Hkv).  D must be 64, 128 or 256,
- * (Hq / Hkv) * Qmax <= 64 (<= 16 for D 256).  Inner strides of q, out, caches and block_tables
+ * (Hq / Hkv) * Qmax <= 64.  Inner strides of q, out, caches and block_tables
  * must be 1, the other strides of q/out/caches multiples of 16 bytes, data
  * pointers 16-byte aligned; k_scale/v_scale strides of dims 0 and 2
  * multiples of 4 and data 16-byte aligned.
@@ -353,8 +354,8 @@ int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* 
  * holds the earliest row's first key); the chunks of all segments,
  * sequence-major, are
  * dealt out in equal contiguous shares (to within one chunk) to
- * `workgroups` workgroups of `heads_per_group` waves (one wave per kv head
- * of the group).  A share may start and end inside a sequence, so each
+ * `workgroups` workgroups of `heads_per_group` kv heads, each served by
+ * `row_waves` waves (one; at head_dim 256 one per 16-row tile).  A share may start and end inside a sequence, so each
  * workgroup leaves at most two fp32 partial results (online-softmax state
  * of the segments cut by its share boundaries) per wave and query row; a
  * segment inside one share is written to `out` directly.  The merge kernel
@@ -371,14 +372,15 @@ int paged_attn_check_reshape_and_cache(const pa_tensor* k_new, const pa_tensor* 
 typedef struct pa_plan {
     int32_t rows;               /* (Hq / Hkv) * Qmax query rows per kv head */
     int32_t row_tiles;          /* ceil(rows / 16)                         */
-    int32_t heads_per_group;    /* kv heads (one wave each) per workgroup  */
+    int32_t heads_per_group;    /* kv heads per workgroup                  */
     int32_t min_share_chunks;   /* smallest share, in 32-token chunks      */
     int32_t reduce_rows;        /* merge workgroup: query rows,            */
     int32_t reduce_col4;        /*   float4 columns per row,               */
     int32_t reduce_lanes;       /*   partial lanes per (row, column)       */
     int32_t expected_partials;  /* partials per row for alike lengths      */
     int32_t whole_segments;     /* 1: one workgroup per segment, no merge  */
-    int32_t reserved;           /* 0                                       */
+    int32_t row_waves;          /* waves per kv head: row_tiles at head_dim
+                                   256 (a wave holds one 16-row tile), else 1 */
     int64_t workgroups;         /* partition-kernel grid                   */
     int64_t reduce_groups;      /* workgroups of the merge kernel (0: none) */
     int64_t workspace_bytes;    /* fp32 partials + log-sum-exp + chunk scan */

@@ -32,9 +32,9 @@ int paged_attn_set_min_share(int32_t chunks);
 /*
  * paged_attn_set_heads_per_group -- override the planner's kv heads per
  * partition workgroup for every later call in the process (1..8; it must
- * divide kv_heads, and be at most 4 when (Hq / Hkv) * Qmax > 16 or head_dim is
- * 256, or the call
- * fails with PA_ERR_ARG), or 0 for the automatic choice.  A tuning hook.
+ * divide kv_heads, and be at most 4 when (Hq / Hkv) * Qmax > 16, at most
+ * 4 / ceil((Hq / Hkv) * Qmax / 16) at head_dim 256, or the call fails with
+ * PA_ERR_ARG), or 0 for the automatic choice.  A tuning hook.
  */
 int paged_attn_set_heads_per_group(int32_t heads);
 

@@ -41,7 +41,7 @@ class PaPlan(ctypes.Structure):
                 ("heads_per_group", ctypes.c_int32), ("min_share_chunks", ctypes.c_int32),
                 ("reduce_rows", ctypes.c_int32), ("reduce_col4", ctypes.c_int32),
                 ("reduce_lanes", ctypes.c_int32), ("expected_partials", ctypes.c_int32),
-                ("whole_segments", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("whole_segments", ctypes.c_int32), ("row_waves", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("reduce_groups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
 

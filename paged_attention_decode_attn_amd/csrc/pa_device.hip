@@ -111,6 +111,7 @@ struct PartArgs {
     int32_t window;                                   // sliding window in tokens, 0 = none
     int32_t B, Hq, Hkv, G, Qmax, NB, rows, HG, min_share;
     int32_t whole;                                    // 1: workgroup w runs segment w whole
+    int32_t P;                                        // waves per kv head (16-row tiles; head_dim 256)
 };
 
 struct RedArgs {
@@ -425,7 +426,8 @@ __device__ __forceinline__ void build_kf(const Step<D, true>& st, bf16x8 (&kf)[2
 // The result is the same: m, l and O all refer to one m.
 template <int D, bool FP8, int NT, bool MASK, bool GEN>
 __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>& s, const u32x4 (&qf)[NT][D / 32],
-                                             const PartArgs& a, int cbase, int L, int nq, int vlo, int lane) {
+                                             const PartArgs& a, int cbase, int L, int nq, int vlo, int lane,
+                                             int r0) {
     constexpr int J = D / 16;
     const int n16 = lane & 15, grp = lane >> 4;
     if constexpr (kQuadV<D, FP8>) unpack_quad<D, FP8>(st, lane);
@@ -485,7 +487,7 @@ __device__ __forceinline__ void compute_step(Step<D, FP8>& st, State<D, FP8, NT>
         if constexpr (MASK) {
             // row t sees keys lo .. lim: its causal limit and, with a
             // sliding window, the window's first position
-            const int row = 16 * nt + n16;
+            const int row = r0 + 16 * nt + n16;
             const int t = row / a.G;
             const int lim = (row < a.rows && t < nq) ? L - nq + t : L - 1;
             const int lo = GEN && a.window > 0 ? lim - a.window + 1 : 0;
@@ -572,7 +574,7 @@ __device__ __forceinline__ float sink_log2(const float* sinks, int64_t stride, i
 // pieces of up to 32 (one 64-entry block-table window per piece).
 template <int D, bool FP8, int NT, bool GEN>
 __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g, int wave, int c0, int c1, int cb,
-                                                int w, int slot, int lane) {
+                                                int w, int slot, int lane, int r0) {
     constexpr int J = D / 16;
     constexpr int KL = Step<D, FP8>::KL;
     constexpr int E = FP8 ? 1 : 2;
@@ -595,12 +597,13 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
         c1 += cs;
     }
     BlockRef br = load_window<GEN>(a, b, c0, lane);
-    // query fragments: row r = 16*nt + n16 -> (t, h_local) = (r / G, r % G);
-    // rows t < Qmax are in bounds, rows past query_len are zeroed below
+    // query fragments: row r = r0 + 16*nt + n16 -> (t, h_local) = (r / G,
+    // r % G); rows t < Qmax are in bounds, rows past query_len are zeroed
+    // below
     u32x4 qf[NT][D / 32];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int row = 16 * nt + n16;
+        const int row = r0 + 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         const char* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)t * a.q_st + (int64_t)(g * a.G + hl) * a.q_sh;
 #pragma unroll
@@ -615,7 +618,7 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
     const int vlo = GEN && a.window > 0 ? L - nq - a.window + 1 : 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int row = 16 * nt + n16;
+        const int row = r0 + 16 * nt + n16;
         const bool live = row / a.G < nq;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
@@ -678,7 +681,8 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
                 load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, L - tok0, lo_key, koff, voff,
                                        soff);
                 if (((st + i) & (kLockstep - 1)) == 0) __syncthreads();
-                compute_step<D, FP8, NT, false, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
+                compute_step<D, FP8, NT, false, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane,
+                                                     r0);
             }
         }
         for (; st < nsteps; st += R) {
@@ -687,18 +691,19 @@ __device__ __forceinline__ void process_segment(const PartArgs& a, int b, int g,
                 load_step<D, FP8, GEN>(buf[(i + R - 1) % R], a, hb, br, st + i + R - 1, nsteps, L - tok0, lo_key, koff, voff,
                                        soff);
                 if (st + i < nsteps)
-                    compute_step<D, FP8, NT, true, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo, lane);
+                    compute_step<D, FP8, NT, true, GEN>(buf[i], s, qf, a, tok0 + kChunkTokens * (st + i), L, nq, vlo,
+                                                        lane, r0);
             }
         }
     }
 
-    // epilogue: lane holds d = (D/16)*(4*grp + i) + j, j < D/16, of row 16*nt + n16
+    // epilogue: lane holds d = (D/16)*(4*grp + i) + j, j < D/16, of row r0 + 16*nt + n16
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float lt = s.l[nt];
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
-        const int row = 16 * nt + n16;
+        const int row = r0 + 16 * nt + n16;
         const int t = row / a.G, hl = row - t * a.G;
         if (!(row < a.rows && t < nq)) continue;
         const int h = g * a.G + hl;
@@ -766,9 +771,9 @@ __device__ __forceinline__ int share_owner(int64_t c, int64_t C, int n) {
 }
 
 // Partition kernel.  A workgroup is HG waves, wave v serving kv head
-// gg*HG + v of the segments in its share, so the waves of a CU read the
-// adjacent head rows of the same tokens (whole contiguous token rows of the
-// cache).  Every workgroup gets the same number of chunks to within one,
+// gg*HG + v of the segments in its share (at head_dim 256 with more than 16
+// rows, HG*P waves, P per kv head), so the waves of a CU read the adjacent
+// head rows of the same tokens (whole contiguous token rows of the cache).  Every workgroup gets the same number of chunks to within one,
 // whatever the ragged context lengths: a share may start and end inside a
 // sequence and may hold several whole sequences.  The per-sequence chunk
 // counts are scanned (workgroup 0 also stores the scan for the merge
@@ -782,6 +787,12 @@ void partition_kernel(PartArgs a) {
     extern __shared__ int s_pre[];               // inclusive prefix of chunks per sequence
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // At head_dim 256 a wave holds one 16-row tile; a kv head with more
+    // rows gets P waves, wave hk*P + i taking rows 16i .. 16i+15.  They run
+    // the same chunks in step, so the K/V rows they share come from the
+    // CU's caches after the first of them has read them.
+    const int hk = D == 256 ? wave / a.P : wave;         // kv head within the group
+    const int r0 = D == 256 ? 16 * (wave - hk * a.P) : 0;
     if (GEN && a.whole) {
         // one workgroup per (sequence, kv-head group) segment, run whole:
         // no scan, no partials, no merge
@@ -790,7 +801,7 @@ void partition_kernel(PartArgs a) {
         const int L = min(a.ctx[(int64_t)b * a.ctx_s], 16 * a.wsub);
         const int nq = min(a.ql ? a.ql[(int64_t)b * a.ql_s] : a.Qmax, a.Qmax);
         const int cb = (L > 0 && nq > 0) ? (L + kChunkTokens - 1) / kChunkTokens - first_chunk<GEN>(a, L, nq) : 0;
-        if (cb > 0) process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, 0, cb, cb, blockIdx.x, 0, lane);
+        if (cb > 0) process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + hk, hk, 0, cb, cb, blockIdx.x, 0, lane, r0);
         return;
     }
     const int ngrp = a.Hkv / a.HG;
@@ -824,7 +835,7 @@ void partition_kernel(PartArgs a) {
             const int gg = within / cb;
             const int c0 = within - gg * cb;
             const int c1 = (int)min<int64_t>(cb, c0 + (hi - pos));
-            process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, c0, c1, cb, w, pos == lo ? 0 : 1, lane);
+            process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + hk, hk, c0, c1, cb, w, pos == lo ? 0 : 1, lane, r0);
             pos += c1 - c0;
         }
         return;
@@ -876,7 +887,7 @@ void partition_kernel(PartArgs a) {
         const int gg = within / cb;
         const int c0 = within - gg * cb;
         const int c1 = (int)min<int64_t>(cb, c0 + (hi - pos));
-        process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + wave, wave, c0, c1, cb, w, pos == lo ? 0 : 1, lane);
+        process_segment<D, FP8, NT, GEN>(a, b, gg * a.HG + hk, hk, c0, c1, cb, w, pos == lo ? 0 : 1, lane, r0);
         pos += c1 - c0;
     }
 }
@@ -1143,8 +1154,9 @@ const void* kernel_of(bool fp8, int nt, bool gen) {
     return gen ? kernel_of<D, false, true>(nt) : kernel_of<D, false, false>(nt);
 }
 
-// head_dim 256 serves at most 16 rows (one tile: with two, the step, the
-// query fragments and the accumulators no longer fit the register file)
+// head_dim 256 runs one 16-row tile per wave (with two, the step, the query
+// fragments and the accumulators no longer fit the register file); more
+// rows take more waves per kv head
 template <bool FP8, bool GEN>
 const void* kernel256_of(int) {
     return reinterpret_cast<const void*>(&partition_kernel<256, FP8, 1, GEN>);
@@ -1229,6 +1241,7 @@ int decode_call(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v
     a.whole = plan.whole_segments;
     a.NB = (int32_t)std::min<int64_t>(pr.NB, INT32_MAX);
     a.rows = plan.rows; a.HG = HG; a.min_share = plan.min_share_chunks;
+    a.P = plan.row_waves;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr;
@@ -1243,7 +1256,7 @@ int decode_call(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v
     if (e0) (void)hipEventRecord(e0, s);
     {
         void* args[] = {&a};
-        if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * HG), args, lds, s) != hipSuccess)
+        if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * HG * a.P), args, lds, s) != hipSuccess)
             return fail(PA_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(hipGetLastError()));
     }
     if (e1) (void)hipEventRecord(e1, s);

@@ -165,9 +165,6 @@ int validate(const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc, const
     if (G > PA_MAX_ROWS || Qmax > PA_MAX_ROWS || G * Qmax > PA_MAX_ROWS)
         return fail(PA_ERR_UNSUPPORTED, "(q_heads / kv_heads) * query_len = %lld exceeds %d",
                     (long long)(G * Qmax), PA_MAX_ROWS);
-    if (D == 256 && G * Qmax > PA_MAX_ROWS_D256)
-        return fail(PA_ERR_UNSUPPORTED, "head_dim 256: (q_heads / kv_heads) * query_len = %lld exceeds %d",
-                    (long long)(G * Qmax), PA_MAX_ROWS_D256);
     if (bt->shape[0] != B)
         return fail(PA_ERR_SHAPE, "block_tables: %lld rows, batch is %lld", (long long)bt->shape[0], (long long)B);
     if (B > kMaxBatch)
@@ -348,13 +345,13 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
         return fail(PA_ERR_UNSUPPORTED, "plan: sizes outside what the kernels serve");
     const int64_t rows = (Hq / Hkv) * Qmax;
     const int64_t row_tiles = (rows + 15) / 16;
-    if (D == 256 && rows > PA_MAX_ROWS_D256)
-        return fail(PA_ERR_UNSUPPORTED, "plan: head_dim 256 serves at most %d rows", PA_MAX_ROWS_D256);
+    // waves per kv head: a head_dim-256 wave holds one 16-row tile
+    const int64_t P = D == 256 ? row_tiles : 1;
     // waves one CU holds for the kernel variant (register budget) and the
-    // largest kv-head group (one wave per head) a workgroup may carry
+    // largest kv-head group (P waves per head) a workgroup may carry
     const bool one_tile = row_tiles == 1 && D <= 128;
     const int64_t cu_waves = one_tile ? (fp8 && D == 64 ? 12 : 8) : 4;
-    const int64_t hg_cap = one_tile ? 8 : 4;
+    const int64_t hg_cap = (one_tile ? 8 : 4) / P;
     // chunk space: 32-token chunks of every (sequence, head group) segment;
     // only its upper bound is known here (lengths live on the device)
     const int64_t seq_chunks = (max_context + kChunkTokens - 1) / kChunkTokens;
@@ -366,7 +363,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     // amortise, while a call that is short overall wants many CUs.
     const int64_t per_seq = B > 1 ? (seq_chunks + 1) / 2 : seq_chunks;
     const int64_t wave_slots = int64_t(num_cus) * cu_waves;
-    const int64_t waves = std::max<int64_t>(std::min<int64_t>(B * Hkv * per_seq / kStepsPerWave, wave_slots),
+    const int64_t waves = std::max<int64_t>(std::min<int64_t>(B * Hkv * P * per_seq / kStepsPerWave, wave_slots),
                                             std::max<int64_t>(1, num_cus / 4));
     // Heads per workgroup: the largest group that divides kv_heads, fits the
     // CU and still leaves a workgroup for every CU.  The waves of a workgroup
@@ -379,7 +376,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
         HG = hg_over;
     } else {
         for (int64_t h = hg_cap; h >= 1; --h)
-            if (Hkv % h == 0 && h <= cu_waves && waves / h >= num_cus) { HG = h; break; }
+            if (Hkv % h == 0 && h * P <= cu_waves && waves / (h * P) >= num_cus) { HG = h; break; }
     }
     if (Hkv % HG || HG > hg_cap) return fail(PA_ERR_ARG, "plan: heads per group must divide kv_heads and fit the kernel");
     const int64_t max_chunks = B * (Hkv / HG) * seq_chunks;
@@ -391,7 +388,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
         int64_t hg = hg_over > 0 ? HG : 1;
         if (hg_over <= 0)
             for (int64_t h = hg_cap; h >= 1; --h)
-                if (Hkv % h == 0 && h <= cu_waves && B * (Hkv / h) >= num_cus) { hg = h; break; }
+                if (Hkv % h == 0 && h * P <= cu_waves && B * (Hkv / h) >= num_cus) { hg = h; break; }
         if (B * (Hkv / hg) >= num_cus) {
             plan->rows = int32_t(rows);
             plan->row_tiles = int32_t(row_tiles);
@@ -400,7 +397,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
             plan->reduce_rows = plan->reduce_col4 = plan->reduce_lanes = 1;
             plan->expected_partials = 0;
             plan->whole_segments = 1;
-            plan->reserved = 0;
+            plan->row_waves = int32_t(P);
             plan->workgroups = B * (Hkv / hg);
             plan->reduce_groups = 0;
             plan->workspace_bytes = 0;
@@ -409,9 +406,9 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     }
     const int64_t share_over = g_share_override.load();
     const int64_t min_share = share_over > 0 ? share_over : kDefaultMinShare;
-    const int64_t slots = int64_t(num_cus) * std::max<int64_t>(1, cu_waves / HG);
+    const int64_t slots = int64_t(num_cus) * std::max<int64_t>(1, cu_waves / (HG * P));
     const int64_t grid_over = g_grid_override.load();
-    int64_t n = grid_over > 0 ? grid_over : std::min<int64_t>(std::max<int64_t>(1, waves / HG), slots);
+    int64_t n = grid_over > 0 ? grid_over : std::min<int64_t>(std::max<int64_t>(1, waves / (HG * P)), slots);
     n = std::max<int64_t>(1, std::min<int64_t>(n, max_chunks / min_share));
     // Two waves per SIMD whose token-head rows are 256 bytes or more: the
     // same grid with half the heads per workgroup, one wave per SIMD, each
@@ -450,7 +447,7 @@ int make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Qmax, int64
     plan->reduce_lanes = int32_t(PL);
     plan->expected_partials = int32_t(std::min<int64_t>(expected, INT32_MAX));
     plan->whole_segments = 0;
-    plan->reserved = 0;
+    plan->row_waves = int32_t(P);
     plan->workgroups = n;
     plan->reduce_groups = n > 1 ? B * Qmax * Hkv * (G / RG) * (col4 / CB) : 0;
     plan->workspace_bytes = n > 1 ? 2 * n * HG * rows * (D + 1) * int64_t(sizeof(float)) + B * int64_t(sizeof(int32_t)) : 0;

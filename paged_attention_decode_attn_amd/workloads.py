@@ -143,8 +143,15 @@ CONFIGS.update({
 # decode kernel): a Gemma-2-9B-shaped layer, 16 query / 8 kv heads.
 CONFIGS["d256"] = WorkloadSpec("d256_b8_q16kv8_ctx1k-8k_bf16", batch=8, qlen=1, hq=16, hkv=8, head_dim=256,
                                kv_dtype="bf16", ctx_lo=1024, ctx_hi=8192, pool_blocks=4096, seed=12)
+# head_dim 256 with more than 16 query rows per kv head: a verify step of
+# four tokens over a Qwen3-Next-shaped full-attention layer (the landing
+# page's model table lists Qwen3-Next and its MTP module; 16 query / 2 kv
+# heads of dimension 256 is its published attention shape), 8 x 4 = 32 rows.
+CONFIGS["d256_mtp"] = WorkloadSpec("d256_mtp_b16_qlen4_q16kv2_ctx1k-16k_bf16", batch=16, qlen=4, hq=16, hkv=2,
+                                   head_dim=256, kv_dtype="bf16", ctx_lo=1024, ctx_hi=16384,
+                                   pool_blocks=16400, seed=13)
 NEXT_CONFIG_ORDER = ["mtp_verify_q4", "mtp_verify_ragged", "long_ctx_bs256", "mha", "swa_sinks",
-                     "full_sinks", "d256"]
+                     "full_sinks", "d256", "d256_mtp"]
 
 
 @dataclass

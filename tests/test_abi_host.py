@@ -95,7 +95,7 @@ def test_validation_errors(mutate, expect):
     (dict(block=8), "PA_ERR_UNSUPPORTED"),
     (dict(d=96), "PA_ERR_UNSUPPORTED"),
     (dict(d=512), "PA_ERR_UNSUPPORTED"),
-    (dict(d=256, hq=32, hkv=2, qmax=2), "PA_ERR_UNSUPPORTED"),  # 32 rows at head_dim 256
+    (dict(d=256, hq=40, hkv=1, qmax=2), "PA_ERR_UNSUPPORTED"),  # 80 rows at head_dim 256
     (dict(hq=6, hkv=4), "PA_ERR_UNSUPPORTED"),
     (dict(hq=40, hkv=1, qmax=2), "PA_ERR_UNSUPPORTED"),      # 80 rows per kv head
 ])
@@ -146,14 +146,29 @@ def test_check_ext_window_and_sinks():
 def test_rows_limit_is_inclusive():
     assert _check(**_tensors(hq=32, hkv=1, qmax=2)) == B.PA_OK      # exactly 64 rows
     assert _check(**_tensors(d=256, hq=16, hkv=2, qmax=2)) == B.PA_OK          # 16 rows at head_dim 256
+    assert _check(**_tensors(d=256, hq=32, hkv=1, qmax=2)) == B.PA_OK          # 64 rows at head_dim 256
     assert _check(**_tensors("fp8", d=256, hq=8, hkv=8, qmax=1)) == B.PA_OK
 
 
-def test_head_dim_256_plans_one_tile_and_small_groups():
+def test_head_dim_256_plans_one_wave_per_16_rows():
+    # a head_dim-256 wave holds one 16-row tile: more rows take more waves
+    # per kv head, and a workgroup stays at 4 waves
     p = B.paged_attn_plan(8, 16, 8, 256, 1, 8192)
-    assert p["row_tiles"] == 1 and p["heads_per_group"] <= 4
-    with pytest.raises(B.PagedAttnError):
-        B.paged_attn_plan(8, 32, 2, 256, 2, 8192)                  # 32 rows
+    assert p["row_tiles"] == 1 and p["row_waves"] == 1 and p["heads_per_group"] <= 4
+    for hq, hkv, qlen, tiles in ((32, 2, 2, 2), (16, 2, 3, 2), (48, 2, 2, 3), (64, 4, 4, 4), (32, 1, 2, 4)):
+        p = B.paged_attn_plan(8, hq, hkv, 256, qlen, 8192)
+        assert p["row_tiles"] == tiles and p["row_waves"] == tiles, (hq, hkv, qlen, p)
+        assert p["heads_per_group"] * tiles <= 4 and hkv % p["heads_per_group"] == 0
+        assert p["workspace_bytes"] == 2 * p["workgroups"] * p["heads_per_group"] * p["rows"] * 257 * 4 + 8 * 4
+    for d in (64, 128):                                   # other head dims: one wave per kv head
+        assert B.paged_attn_plan(8, 32, 2, d, 2, 8192)["row_waves"] == 1
+    B.paged_attn_set_heads_per_group(2)
+    try:
+        assert B.paged_attn_plan(8, 32, 2, 256, 2, 8192)["heads_per_group"] == 2      # 2 x 2 waves
+        with pytest.raises(B.PagedAttnError):
+            B.paged_attn_plan(8, 48, 2, 256, 2, 8192)                                  # 2 x 3 waves
+    finally:
+        B.paged_attn_set_heads_per_group(0)
 
 
 def test_fp8_scale_rules():

@@ -316,7 +316,7 @@ def test_profile_events_measure_both_kernels():
     ("tiny", None), ("llama3_8b", None), ("long_ctx", None), ("fp8", [0, 7, 15]),
     ("mtp_verify", [0, 21, 63]), ("mtp_verify_q4", [0, 33, 63]), ("mtp_verify_ragged", [1, 30, 62]),
     ("long_ctx_bs256", None), ("mha", [0, 5]), ("swa_sinks", [0, 17, 40, 63]), ("full_sinks", [2, 9, 15]),
-    ("d256", [0, 7]),
+    ("d256", [0, 7]), ("d256_mtp", [0, 9, 15]),
 ])
 def test_full_size_configs_sampled(name, subset):
     w = generate(CONFIGS[name])

@@ -187,6 +187,41 @@ def test_head_dim_256_window_sinks_and_whole_segments(bs):
     check(generate(spec), 0, label=f"d256/whole/bs{bs}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("hq,hkv,qlen,qlen_lo", [(32, 2, 2, None), (16, 2, 4, 1), (48, 8, 4, None), (64, 4, 4, None),
+                                                 (32, 1, 2, None), (17 * 2, 2, 1, None)])
+def test_head_dim_256_more_than_16_rows(kv, hq, hkv, qlen, qlen_lo):
+    # ceil(rows / 16) waves per kv head, each one 16-row tile (24 rows: the
+    # second tile half full; 17 rows: one row in the second tile)
+    w = generate(_ragged(kv=kv, qlen=qlen, qlen_lo=qlen_lo, hq=hq, hkv=hkv, d=256, batch=4, ctx_hi=1200,
+                         seed=70 + hq + qlen))
+    for groups in (0, 1, 7, 100000):
+        check(w, groups, label=f"d256/{hq}/{hkv}/q{qlen}/{kv}/g{groups}")
+
+
+@pytest.mark.parametrize("hg", [1, 2])
+def test_head_dim_256_32_rows_heads_per_group(hg):
+    w = generate(_ragged(qlen=4, hq=32, hkv=4, d=256, batch=5, ctx_hi=900, seed=75))
+    for groups in (0, 3, 100000):
+        check(w, groups, label=f"d256/32rows/hg{hg}/g{groups}", heads_per_group=hg)
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_head_dim_256_32_rows_window_sinks_whole_segments_and_many_sequences(bs):
+    w = generate(_ragged(bs, qlen=2, hq=32, hkv=2, d=256, window=50, sinks=True, batch=4, ctx_hi=900, seed=76))
+    for groups in (0, 3, 100000):
+        check(w, groups, label=f"d256/32rows/window/bs{bs}/g{groups}")
+    spec = _ragged(bs, qlen=4, qlen_lo=1, hq=64, hkv=8, d=256, window=64, sinks=True, batch=64, ctx_hi=600, seed=77)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = B.paged_attn_plan(64, 64, 8, 256, 4, 128, "bf16", cus)
+    assert plan["whole_segments"] == 1 and plan["row_waves"] == 2
+    check(generate(spec), 0, label=f"d256/32rows/whole/bs{bs}")
+    # more than 64 sequences: the chunk scan goes through LDS
+    w = generate(_ragged(bs, qlen=2, hq=32, hkv=2, d=256, batch=70, ctx_hi=300, seed=78))
+    for groups in (0, 5):
+        check(w, groups, label=f"d256/32rows/b70/bs{bs}/g{groups}")
+
+
 def test_ext_without_window_or_sinks_equals_decode_bitwise():
     w = generate(_ragged(qlen=2, seed=35)).to("cuda")
     a = torch.empty_like(w.q)
