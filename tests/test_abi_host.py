@@ -171,6 +171,30 @@ def test_head_dim_256_plans_one_wave_per_16_rows():
         B.paged_attn_set_heads_per_group(0)
 
 
+def test_head_dim_256_plans_fit_one_cu_for_every_shape():
+    # every head_dim-256 plan: one wave per 16-row tile, at most 4 waves per
+    # workgroup, kv heads split evenly, at most 4 waves per CU in the split
+    # schedule, and a workspace that holds every partial slot
+    cus = 256
+    for hkv in (1, 2, 3, 4, 8, 16):
+        for g in (1, 2, 3, 8, 16, 17, 32, 64):
+            for qlen in (1, 2, 3, 4):
+                if g * qlen > 64:
+                    continue
+                for batch in (1, 4, 64):
+                    for ctx in (128, 8192):
+                        p = B.paged_attn_plan(batch, hkv * g, hkv, 256, qlen, ctx, "bf16", cus)
+                        rows, tiles = g * qlen, -(-g * qlen // 16)
+                        hg = p["heads_per_group"]
+                        assert (p["rows"], p["row_tiles"], p["row_waves"]) == (rows, tiles, tiles)
+                        assert hkv % hg == 0 and hg * tiles <= 4, p
+                        if p["whole_segments"]:
+                            assert p["workgroups"] == batch * (hkv // hg) and p["workspace_bytes"] == 0
+                        else:
+                            assert p["workgroups"] * hg * tiles <= 4 * cus, p
+                            assert p["workspace_bytes"] == 2 * p["workgroups"] * hg * rows * 257 * 4 + batch * 4
+
+
 def test_fp8_scale_rules():
     t = _tensors("fp8")
     t["k_scale"] = None

@@ -38,6 +38,8 @@ SMALL = {
     "swa_sinks": small("swa_sinks", batch=7, ctx_lo=1, ctx_hi=3000, pool_blocks=1400),
     "full_sinks": small("full_sinks", batch=5, ctx_lo=100, ctx_hi=3000, pool_blocks=1000),
     "d256": small("d256", batch=3, ctx_lo=100, ctx_hi=1500, pool_blocks=300),
+    # head_dim 256 with 32 rows per kv head: two waves per kv head
+    "d256_mtp": small("d256_mtp", batch=5, ctx_lo=4, ctx_hi=1500, pool_blocks=480),
 }
 
 
@@ -65,7 +67,7 @@ def test_heads_per_workgroup(hg, groups):
 def test_calls_of_different_shapes_alternate_on_one_stream():
     # one stream's workspace serves calls of every plan, whose layouts of
     # partials, log-sum-exps and chunk prefix differ
-    names = ("long_ctx", "mtp_verify", "fp8", "llama3_8b", "mha", "d256", "long_ctx_bs256")
+    names = ("long_ctx", "mtp_verify", "fp8", "llama3_8b", "mha", "d256", "d256_mtp", "long_ctx_bs256")
     ws = {n: generate(SMALL[n]) for n in names}
     refs = {n: oracle_out(w) for n, w in ws.items()}
     for rnd in range(3):
@@ -326,8 +328,9 @@ def test_full_size_configs_sampled(name, subset):
 # --------------------------------------------------------------------------
 # graph capture: the call is graph-safe once its workspace exists
 # --------------------------------------------------------------------------
-def test_graph_capture_replays_match_eager():
-    w = generate(SMALL["mtp_verify"])
+@pytest.mark.parametrize("name", ["mtp_verify", "d256_mtp"])
+def test_graph_capture_replays_match_eager(name):
+    w = generate(SMALL[name])
     dev = w.to("cuda")
     ref = oracle_out(w)
     s = torch.cuda.Stream()
