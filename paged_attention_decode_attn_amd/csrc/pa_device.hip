@@ -18,11 +18,13 @@
 // one whatever the ragged context lengths; a share may start or end inside
 // a segment.  A workgroup is HG waves, wave v serving kv head gg*HG + v of
 // each segment it meets, so a CU reads adjacent head rows of the same
-// tokens.  A segment wholly inside one share writes its output rows; a
-// split one leaves an fp32 partial and a base-2 log-sum-exp per row.
+// tokens (at head_dim 256, P waves per kv head, one per 16-row tile).  A
+// segment wholly inside one share writes its output rows; a split one
+// leaves an fp32 partial and a base-2 log-sum-exp per row.
 //  * All G*Qmax query rows that share kv head g form the N side of 16x16
 //    MFMA tiles (rows r = t*G + h_local; tiles of 16 rows), so every K/V
-//    byte is read from HBM once per kv head.
+//    byte is read from HBM once per kv head (at head_dim 256 with more than
+//    16 rows, once per tile from the CU's caches).
 //  * A wave walks its piece of a segment in 32-token steps (two 16-token
 //    sub-blocks) through a ring of register buffers: raw buffer loads of
 //    the next steps are in flight while the current one computes; loads
